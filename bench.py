@@ -1,0 +1,263 @@
+"""Benchmark: tree-attention forward + backward on the navigation-episode spine
+tree (one GPU), plus per-kernel roofline, decode bandwidth and an oracle CPU
+baseline.  Prints ONE JSON line.
+
+Workload (the headline one): spine tree with a 512-token root, 44 history
+nodes of 96 tokens chained under it and a 264-token leaf (256 observation +
+8 action-query tokens) under every history node -- 16,352 unique tokens,
+K = 44 paths; 32 query / 8 KV heads, head dim 128, bf16, N(0,1) inputs,
+depth RoPE with base 10000.  A step is one tree_attn_fwd + tree_attn_bwd.
+FLOPs count visible (i, j) pairs only: P = sum_t (pos(t) + 1) per query head,
+4 d P Hq forward and 10 d P Hq backward.
+
+Also reported (fields beside the headline): the random agentic tree and the
+varlen forest (same heads and dtype), split-KV decode at 32K/64K/128K/256K
+(B = 8) in GB/s of KV read, the host planner time, and the per-kernel times
+from HIP events recorded between the library's launches.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "tree-attn fwd+bwd TFLOP/s on visible pairs (% bf16 MFMA peak); decode GB/s"
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "decode.hip", "common.h"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "prefix_shared_masked_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def make_inputs(n, Hq, Hkv, d, seed, dev):
+    import torch
+    g = torch.Generator(device=dev).manual_seed(seed)
+    mk = lambda h: torch.randn(n, h, d, generator=g, device=dev, dtype=torch.float32).bfloat16()
+    return mk(Hq), mk(Hkv), mk(Hkv), mk(Hq)
+
+
+def time_tree(pkg, tree, steps, warmup, dev, seed=0, Hq=32, Hkv=8, d=128, rope=10000.0):
+    """fwd+bwd timing with stage events.  Returns a dict of averages (ms)."""
+    import torch
+    t0 = time.perf_counter()
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    plan.device(dev)
+    upload_ms = (time.perf_counter() - t0) * 1e3
+    q, k, v, do = make_inputs(plan.n_tokens, Hq, Hkv, d, seed, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(Hq, plan.n_tokens, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wf = torch.empty(max(1, pkg.attn_ws_bytes(plan, 0, 1, Hq, Hkv, d, rope)), dtype=torch.uint8, device=dev)
+    wb = torch.empty(max(1, pkg.attn_ws_bytes(plan, 1, 1, Hq, Hkv, d, rope)), dtype=torch.uint8, device=dev)
+    ev = pkg.HipEvents(7 * steps)
+
+    def step(i=None):
+        ef = ev.slice(7 * i, 3) if i is not None else None
+        eb = ev.slice(7 * i + 3, 4) if i is not None else None
+        pkg.tree_attn_fwd(plan, q, k, v, rope_base=rope, o=o, lse=lse, ws=wf, events=ef)
+        pkg.tree_attn_bwd(plan, q, k, v, o, lse, do, rope_base=rope, dq=dq, dk=dk, dv=dv, ws=wb, events=eb)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3 / steps
+    avg = lambda a, b: sum(ev.elapsed_ms(7 * i + a, 7 * i + b) for i in range(steps)) / steps
+    P, flop_pair = plan.visible_pairs, d * Hq
+    res = dict(
+        n_tokens=plan.n_tokens, n_leaves=plan.n_leaves, n_flat=plan.n_flat, visible_pairs=P,
+        por=round(1.0 - plan.n_tokens / plan.n_flat, 4) if plan.n_flat else 0.0,
+        fwd_tile_efficiency=round(P / plan.computed_pairs_fwd, 4),
+        bwd_tile_efficiency=round(P / plan.computed_pairs_bwd, 4),
+        plan_ms=round(plan_ms, 3), upload_ms=round(upload_ms, 3),
+        ms_per_step=avg(0, 6), wall_ms_per_step=wall,
+        fwd_ms=avg(0, 2), bwd_ms=avg(3, 6),
+        k_fwd_prep_ms=avg(0, 1), k_fwd_ms=avg(1, 2), k_bwd_prep_ms=avg(3, 4), k_dq_ms=avg(4, 5), k_dkv_ms=avg(5, 6),
+        flops_fwd=4 * flop_pair * P, flops_bwd=10 * flop_pair * P,
+        flops_alg=dict(fwd=4 * flop_pair * P, dq=6 * flop_pair * P, dkv=8 * flop_pair * P))
+    res["tflops"] = (res["flops_fwd"] + res["flops_bwd"]) / (res["ms_per_step"] * 1e-3) / 1e12
+    del q, k, v, do, o, dq, dk, dv, wf, wb
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_decode(pkg, L, steps, warmup, dev, B=8, Hq=32, Hkv=8, d=128, seed=5):
+    import torch
+    g = torch.Generator(device=dev).manual_seed(seed)
+    q = torch.randn(B, Hq, d, generator=g, device=dev).bfloat16()
+    k = torch.randn(B * L, Hkv, d, generator=g, device=dev).bfloat16()
+    v = torch.randn(B * L, Hkv, d, generator=g, device=dev).bfloat16()
+    span_ptr = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    spans = torch.stack([torch.arange(B, dtype=torch.int32) * L, torch.full((B,), L, dtype=torch.int32)], 1)
+    spans = spans.to(torch.int32).contiguous().to(dev)
+    nbytes, n_splits = pkg.decode_ws_bytes(B, Hq, d, L)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    ev = pkg.HipEvents(3 * steps)
+    for _ in range(warmup):
+        pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L, o=o, lse=lse, ws=ws)
+    for i in range(steps):
+        pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L, o=o, lse=lse, ws=ws, events=ev.slice(3 * i, 3))
+    torch.cuda.synchronize()
+    call = sum(ev.elapsed_ms(3 * i, 3 * i + 2) for i in range(steps)) / steps
+    part = sum(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(steps)) / steps
+    kv_bytes = 2 * B * L * Hkv * d * 2
+    del k, v
+    torch.cuda.empty_cache()
+    return dict(L=L, n_splits=n_splits, kv_bytes=kv_bytes, call_us=call * 1e3, partial_us=part * 1e3,
+                GBps=kv_bytes / (call * 1e-3) / 1e9, partial_GBps=kv_bytes / (part * 1e-3) / 1e9)
+
+
+def cpu_baseline(tree, budget_s=20.0, seed=0):
+    """The float64 oracle (per-path attention, forward + backward) on a bounded
+    sample of the same workload: one KV head group (query heads 0-3), paths
+    taken in order until about budget_s seconds of work.  Reported in the
+    metric's unit (visible-pair FLOPs of the sampled paths per second)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    from oracle.plan import OraclePlan
+    op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    q, k, v, do = W.attention_inputs(seed, op.n_tokens, 32, 8, 128)
+    heads = [0, 1, 2, 3]
+    done_pairs, t_total, n_paths = 0, 0.0, 0
+    for idx in op.paths:
+        sub = OraclePlan(**{**op.__dict__, "paths": [idx]})
+        t0 = time.perf_counter()
+        oracle.per_path_attention(sub, q, k, v, rope_base=10000.0, dO=do, heads=heads, check_consistency=False)
+        t_total += time.perf_counter() - t0
+        L = len(idx)
+        done_pairs += L * (L + 1) // 2 * len(heads)
+        n_paths += 1
+        if t_total >= budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        cores = os.cpu_count()
+    flops = 14 * 128 * done_pairs
+    return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"per-path float64 oracle, fwd+bwd, query heads 0-3 (one KV group), first {n_paths} of "
+                       f"{len(op.paths)} root-to-leaf paths of the spine tree ({done_pairs} causal pairs), "
+                       f"{t_total:.1f} s", seconds=round(t_total, 2))
+
+
+def load_traffic(kernel):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: tree attention here runs on a single device "
+              "(no collectives between GPUs); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import prefix_shared_masked_amd as pkg
+    import workloads as W
+    pkg.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    spine = W.spine_tree()
+    print("[bench] spine tree fwd+bwd", flush=True)
+    head = time_tree(pkg, spine, args.steps, args.warmup, dev)
+    extra = {}
+    if not args.headline_only:
+        for name, tree in (("random_agentic_tree", W.random_agentic_tree(0)), ("varlen_forest", W.varlen_forest(0))):
+            print(f"[bench] {name} fwd+bwd", flush=True)
+            r = time_tree(pkg, tree, max(3, args.steps // 2), args.warmup, dev)
+            extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "flops_alg"}
+        extra["decode"] = []
+        for L in (32768, 65536, 131072, 262144):
+            print(f"[bench] decode L={L}", flush=True)
+            r = time_decode(pkg, L, args.steps, args.warmup, dev)
+            extra["decode"].append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()})
+
+    kernels = {"fwd": head["k_fwd_ms"], "dq": head["k_dq_ms"], "dkv": head["k_dkv_ms"]}
+    dom = max(kernels, key=kernels.get)
+    names = {"fwd": "fwd_bf16_kernel", "dq": "dq_bf16_kernel", "dkv": "dkv_bf16_kernel"}
+    achieved = head["flops_alg"][dom] / (kernels[dom] * 1e-3) / 1e12
+    roofline = dict(bound="mfma", kernel=names[dom], achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=load_traffic(names[dom]),
+                    avg_launch_ms=round(kernels[dom], 4))
+    per_kernel = {names[k2]: dict(ms=round(v, 4), tflops=round(head["flops_alg"][k2] / (v * 1e-3) / 1e12, 2))
+                  for k2, v in kernels.items()}
+    per_kernel["k_prep_fwd"] = dict(ms=round(head["k_fwd_prep_ms"], 4))
+    per_kernel["k_prep_bwd"] = dict(ms=round(head["k_bwd_prep_ms"], 4))
+
+    out = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "navigation-episode spine tree (512-token root, 44 x 96-token history nodes, "
+                               "44 x 264-token leaves), fwd+bwd, depth RoPE base 10000",
+                   "n_tokens": head["n_tokens"], "paths": head["n_leaves"], "n_flat": head["n_flat"],
+                   "heads_q": 32, "heads_kv": 8, "head_dim": 128, "visible_pairs_per_head": head["visible_pairs"]},
+        "frac_bf16_peak": round(head["tflops"] / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "per_kernel": per_kernel,
+        "fwd_ms": round(head["fwd_ms"], 4), "bwd_ms": round(head["bwd_ms"], 4),
+        "wall_ms_per_step": round(head["wall_ms_per_step"], 4),
+        "plan_ms": head["plan_ms"], "plan_upload_ms": head["upload_ms"],
+        "por": head["por"], "fwd_tile_efficiency": head["fwd_tile_efficiency"],
+        "bwd_tile_efficiency": head["bwd_tile_efficiency"],
+        "kernel_source_hash": source_hash(),
+    }
+    if extra:
+        out["secondary"] = extra
+        dec = extra["decode"]
+        out["decode_GBps"] = {str(r["L"]): r["GBps"] for r in dec}
+        out["decode_frac_hbm_peak"] = {str(r["L"]): round(r["GBps"] / PEAK_HBM_GBS, 4) for r in dec}
+    if not args.no_cpu_baseline:
+        print("[bench] oracle cpu baseline", flush=True)
+        out["cpu_baseline"] = cpu_baseline(spine, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,253 @@
+/*
+ * tree_attn.h -- C ABI of the tree-attention library (gfx950 / MI355X).
+ *
+ * The library computes exact softmax attention over a prefix tree that is
+ * packed in depth-first order, the g_t/K weighted negative log-likelihood of
+ * the packed tokens, and single-query decode over split KV with an
+ * associative (max, numerator, denominator) merge.
+ *
+ * Definitions the calls follow (page titles and sections):
+ *  - "Tree Training" post (tingdeliu.github.io, tree-training-prefix-reuse):
+ *      3.1  a node holds a token segment; each root-to-leaf path is one
+ *           training sequence; K = number of paths.
+ *      3.2  DFS serialisation: a node's tokens, then each child's
+ *           serialisation, so every node appears once.
+ *      4.2  the tree mask: packed token i reads key j iff j <= i and node(j)
+ *           is an ancestor-or-self of node(i); attention is
+ *           softmax(Q K^T / sqrt(d) + M) V.
+ *      4.3  production kernels must not build a dense N x N mask: they use the
+ *           DFS interval, parent, depth and an ancestor block table and skip
+ *           invisible blocks.
+ *      5    positions are tree depth: summed length of the strict ancestors
+ *           plus the offset inside the node.
+ *      6.2  g_t = number of root-to-leaf paths through t; the tree loss is
+ *           sum_t (g_t / K) l_t.
+ *      12   the TreeNode record and the packing outputs (packed order,
+ *           position ids, loss weights).
+ *  - Tree Attention notes (t6page.pages.dev, tree-attention): the three
+ *    mergeable quantities m, n = o e^(l-m), d = e^(l-m) and the decode
+ *    algorithm (local attention per KV shard, global max, sums, z = n/d).
+ *  - agent-rl tutorial chapter 14, section 14.1: sequence packing with a
+ *    block-diagonal causal mask and positions that restart per sequence;
+ *    here that is a forest (every sequence a root).
+ *
+ * Conventions for every call:
+ *  - All tensors are caller-owned, contiguous, and live in device memory
+ *    unless stated otherwise.  The library never allocates device memory; a
+ *    call that needs scratch space takes a caller-provided workspace whose
+ *    size the matching *_ws_bytes query returns.
+ *  - Kernel calls are asynchronous on the given HIP stream.  Validation
+ *    errors are returned before anything is launched; a failed launch
+ *    returns TA_EHIP.
+ *  - Plans are immutable after tree_plan returns and may be shared between
+ *    threads.  The library keeps no global mutable state.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum ta_status {
+  TA_OK = 0,
+  TA_EINVAL = 1,       /* null pointer, bad size, parent out of range, negative length, bad layout */
+  TA_ECYCLE = 2,       /* parent pointers do not form a forest */
+  TA_ERANGE = 3,       /* a count overflows the int32 index space of the kernels */
+  TA_ENOMEM = 4,       /* host allocation failed, or a caller buffer is too small */
+  TA_EUNSUPPORTED = 5, /* valid request the kernels are not built for (head dim, block sizes, dtype) */
+  TA_EHIP = 6          /* a HIP call or kernel launch failed */
+} ta_status;
+
+typedef enum ta_dtype { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
+
+/* Tile sizes the kernels are built for.  tree_plan accepts 0 (default) or
+ * exactly these values. */
+#define TA_BLOCK_M 32   /* query rows per forward tile */
+#define TA_BLOCK_N 64   /* key slots per gathered key chunk */
+#define TA_BLOCK_KV 32  /* keys per backward key tile (never crosses a node) */
+#define TA_CHUNK_INTS 16
+#define TA_CHUNK_MAX_SEG 4
+
+/* Layout of one gathered key chunk (TA_CHUNK_INTS int32):
+ *   [0] nseg      number of key segments (1..TA_CHUNK_MAX_SEG)
+ *   [1] nkeys     key slots in use (1..TA_BLOCK_N); slots >= nkeys are padding
+ *   [2] full      1 iff every row of the query tile reads every key of the chunk
+ *   [3] reserved
+ *   [4..7]   kstart[s]  first packed key index of segment s
+ *   [8..11]  vstart[s]  first slot of segment s (unused segments hold TA_BLOCK_N)
+ *   [12..15] kend[s]    end of the DFS interval of the node segment s lies in:
+ *                        row i reads key j of segment s iff j <= i < kend[s]. */
+
+typedef struct ta_plan ta_plan;
+
+/* Read-only view of a plan.  Every pointer is host memory owned by the plan
+ * and stays valid until tree_plan_free. */
+typedef struct ta_plan_view {
+  int32_t n_nodes;
+  int32_t n_tokens;          /* N: unique tokens */
+  int32_t n_leaves;          /* K: root-to-leaf paths (zero-length leaves count) */
+  int32_t max_pos;           /* largest depth position, -1 if N == 0 */
+  int32_t block_m, block_n, block_kv;
+  int32_t n_qtiles, n_chunks, n_ktiles;
+  int64_t n_flat;            /* sum over paths of the path length = sum_t g_t */
+  int64_t visible_pairs;     /* sum_t (pos(t) + 1): (i, j) pairs the mask allows, per head */
+  int64_t computed_pairs_fwd;/* pairs the forward tiles compute, per head (>= visible_pairs) */
+  int64_t computed_pairs_bwd;/* pairs the backward key tiles compute, per head */
+  const int32_t* dfs_order;  /* [n_nodes] node ids in visiting order */
+  const int32_t* node_start; /* [n_nodes] first packed index, by node id */
+  const int32_t* node_sub_end;/* [n_nodes] end of the node's DFS interval */
+  const int32_t* pos;        /* [N] depth position */
+  const int32_t* g;          /* [N] paths through the token */
+  const int32_t* node_of;    /* [N] owning node */
+  const int32_t* sub_end;    /* [N] node_sub_end[node_of[t]] */
+  const int32_t* anc_ptr;    /* [n_nodes + 1] CSR offsets into anc */
+  const int32_t* anc;        /* ancestor-or-self chains, root first, per node id */
+  const int32_t* fq_ptr;     /* [n_qtiles + 1] chunk range of each query tile */
+  const int32_t* fq_chunk;   /* [n_chunks * TA_CHUNK_INTS] gathered key chunks (layout above) */
+  const int32_t* fq_order;   /* [n_qtiles] query tiles, most chunks first */
+  const int32_t* bk;         /* [n_ktiles * 4] (k0, klen, q_end, node), most work first */
+} ta_plan_view;
+
+/* Build the plan of a prefix tree (host only, synchronous, deterministic).
+ * parent[i] = -1 marks a root (several roots: a forest, e.g. varlen packing);
+ * seg_len[i] >= 0 tokens in node i.  Children are serialised in ascending
+ * node id, roots in ascending id.  block_m / block_n: 0 or TA_BLOCK_M /
+ * TA_BLOCK_N.  On success *out owns all tables; free with tree_plan_free.
+ * Errors: TA_EINVAL (null pointer, n_nodes <= 0, negative length, parent out
+ * of range), TA_ECYCLE, TA_ERANGE (N, a table or sum_t depth does not fit
+ * int32), TA_EUNSUPPORTED (other block sizes), TA_ENOMEM.  On error *out is
+ * set to NULL. */
+ta_status tree_plan(const int32_t* parent, const int32_t* seg_len, int32_t n_nodes,
+                    int32_t block_m, int32_t block_n, ta_plan** out);
+
+ta_status tree_plan_view(const ta_plan* plan, ta_plan_view* view);
+
+/* Device copy of the tables the kernels read.  The caller allocates
+ * tree_plan_device_bytes bytes of device memory (256-byte aligned) and
+ * tree_plan_upload copies the tables in, asynchronously on the stream, from
+ * host memory owned by the plan (the plan must outlive the copy).  The
+ * kernels take that buffer as `dplan`; keep it alive while they run. */
+ta_status tree_plan_device_bytes(const ta_plan* plan, size_t* bytes);
+ta_status tree_plan_upload(const ta_plan* plan, void* dplan, size_t bytes, hipStream_t stream);
+
+/* NULL-safe. */
+void tree_plan_free(ta_plan* plan);
+
+/* Workspace bytes of tree_attn_fwd (op = 0) or tree_attn_bwd (op = 1) for
+ * this plan and shape; 0 when none is needed. */
+ta_status tree_attn_ws_bytes(const ta_plan* plan, int32_t op, ta_dtype dt, int32_t Hq, int32_t Hkv,
+                             int32_t d, float rope_base, size_t* bytes);
+
+/* Forward tree attention (Tree Training post, sections 4.2, 4.3 and 5).
+ * q, o: [N, Hq, d]; k, v: [N, Hkv, d] in dtype dt (TA_BF16: bf16 inputs,
+ * fp32 accumulation; TA_F32: fp32 throughout).  lse: [Hq, N] fp32, natural
+ * log of sum_j exp(scale q_i . k_j) over the visible keys.  Query head h
+ * reads KV head h / (Hq / Hkv).  d must be 64 or 128 (TA_BF16: 128).
+ * scale <= 0 selects 1/sqrt(d).  rope_base > 0 rotates q and k by depth
+ * position (rotate-half pairs (i, i + d/2), angle pos * base^(-2i/d));
+ * 0 disables it.  ws: tree_attn_ws_bytes(op = 0) bytes of device memory.
+ * Precision of the bf16 path: scores use fp16 copies of (rotated) Q and K,
+ * which hold every bf16 value of magnitude <= 65504 exactly and rotated
+ * values with 8x finer rounding than bf16 (larger magnitudes saturate);
+ * P is rounded to bf16 for P V; accumulation is fp32 throughout.
+ * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_ENOMEM (ws too small), TA_EHIP. */
+ta_status tree_attn_fwd(const ta_plan* plan, const void* dplan, ta_dtype dt, const void* q,
+                        const void* k, const void* v, int32_t Hq, int32_t Hkv, int32_t d,
+                        float scale, float rope_base, void* o, float* lse, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* Backward of tree_attn_fwd for upstream gradient dO [N, Hq, d].  o and lse
+ * are the forward's outputs.  dq [N, Hq, d], dk and dv [N, Hkv, d] are
+ * overwritten (not accumulated), in dtype dt.  The gradient of a shared key
+ * is the sum over every descendant query that reads it (section 7: shared
+ * prefixes receive the gradients of all branches).  Deterministic: the same
+ * inputs give bitwise-identical outputs (no atomics).
+ * ws: tree_attn_ws_bytes(op = 1) bytes.  Errors as tree_attn_fwd. */
+ta_status tree_attn_bwd(const ta_plan* plan, const void* dplan, ta_dtype dt, const void* q,
+                        const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, int32_t Hq, int32_t Hkv, int32_t d, float scale,
+                        float rope_base, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Stage timing.  The *_ex variants behave exactly like the plain calls and,
+ * when events is not NULL, also record events[i] (created by the caller with
+ * hipEventCreate) on the stream at the stage boundaries listed below; at most
+ * n_events are recorded.  Nothing else changes, so callers can time each
+ * kernel with hipEventElapsedTime.
+ *   tree_attn_fwd_ex:       [0] start, [1] after the K conversion/RoPE pass,
+ *                           [2] after the attention kernel.
+ *   tree_attn_bwd_ex:       [0] start, [1] after the K passes, [2] after the
+ *                           dQ kernel, [3] after the dK/dV kernel.
+ *   tree_decode_splitkv_ex: [0] start, [1] after the partial kernel,
+ *                           [2] after the merge kernel. */
+typedef struct ihipEvent_t* hipEvent_t;
+ta_status tree_attn_fwd_ex(const ta_plan* plan, const void* dplan, ta_dtype dt, const void* q,
+                           const void* k, const void* v, int32_t Hq, int32_t Hkv, int32_t d,
+                           float scale, float rope_base, void* o, float* lse, void* ws,
+                           size_t ws_bytes, hipEvent_t* events, int32_t n_events,
+                           hipStream_t stream);
+ta_status tree_attn_bwd_ex(const ta_plan* plan, const void* dplan, ta_dtype dt, const void* q,
+                           const void* k, const void* v, const void* o, const float* lse,
+                           const void* dO, int32_t Hq, int32_t Hkv, int32_t d, float scale,
+                           float rope_base, void* dq, void* dk, void* dv, void* ws,
+                           size_t ws_bytes, hipEvent_t* events, int32_t n_events,
+                           hipStream_t stream);
+
+/* Workspace bytes of tree_weighted_nll for N rows. */
+ta_status tree_nll_ws_bytes(int32_t N, int32_t V, size_t* bytes);
+
+/* g_t/K weighted negative log-likelihood (Tree Training post, sections 6.2,
+ * 6.3 and 12): loss = sum_t w_t [y_t != ignore_index] (logsumexp(x_t) -
+ * x_t[y_t]) -- a weighted SUM.  Labels are per packed token and already
+ * aligned with the position that predicts them (no shift).
+ * logits: [N, V] fp32 (dt must be TA_F32); labels: [N] int32; w: [N] fp32
+ * (normally g_t / K).  loss: one device fp32.  dlogits: [N, V] fp32
+ * w_t valid_t (softmax(x_t) - onehot(y_t)), or NULL for loss only.
+ * err_flag: device int32 or NULL; set to 1 when a label is neither
+ * ignore_index nor in [0, V) (that row then contributes 0).
+ * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_ENOMEM, TA_EHIP. */
+ta_status tree_weighted_nll(ta_dtype dt, const void* logits, const int32_t* labels, const float* w,
+                            int32_t N, int32_t V, int32_t ignore_index, float* loss, void* dlogits,
+                            int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of tree_decode_splitkv; *n_splits_out receives the split
+ * count it will use (n_splits = 0 picks one from the longest item). */
+ta_status tree_decode_ws_bytes(int32_t B, int32_t Hq, int32_t d, int32_t max_len, int32_t n_splits,
+                               size_t* bytes, int32_t* n_splits_out);
+
+/* Split-KV single-query decode (Tree Attention notes, decode algorithm):
+ * every workgroup attends one query token per (batch item, query head) to
+ * its slice of the item's KV rows and emits (m, n, d); a log-depth pairwise
+ * merge across the slices gives z = n/d and lse = m + log d.
+ * q, o: [B, Hq, d]; k, v: [L_total, Hkv, d]; lse: [B, Hq] fp32.
+ * span_ptr [B + 1] and spans [.., 2] (device int32): item b reads the rows
+ * spans[s] = (start, len) for s in [span_ptr[b], span_ptr[b+1]) in order
+ * (plain decode: one span; tree decode: the ancestor chain of a leaf).
+ * max_len bounds every item's total length.  dt: TA_BF16, d = 128.
+ * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_ENOMEM, TA_EHIP. */
+ta_status tree_decode_splitkv(ta_dtype dt, const void* q, const void* k, const void* v,
+                              const int32_t* span_ptr, const int32_t* spans, int32_t B,
+                              int32_t Hq, int32_t Hkv, int32_t d, int32_t max_len, float scale,
+                              int32_t n_splits, void* o, float* lse, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+ta_status tree_decode_splitkv_ex(ta_dtype dt, const void* q, const void* k, const void* v,
+                                 const int32_t* span_ptr, const int32_t* spans, int32_t B,
+                                 int32_t Hq, int32_t Hkv, int32_t d, int32_t max_len, float scale,
+                                 int32_t n_splits, void* o, float* lse, void* ws, size_t ws_bytes,
+                                 hipEvent_t* events, int32_t n_events, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* ta_status_string(ta_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

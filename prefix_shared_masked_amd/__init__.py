@@ -1,0 +1,375 @@
+"""Tree attention over a DFS-packed prefix tree on MI355X (gfx950).
+
+Thin ctypes binding of ``libtree_attn.so`` (C ABI in ``include/tree_attn.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals arguments, allocates outputs and workspaces with torch, and
+passes torch's current HIP stream.  There is no fallback: if the library is
+missing, every call raises.
+
+Calls mirror the C names:
+
+    plan = tree_plan(parent, seg_len)                     # host planner
+    o, lse = tree_attn_fwd(plan, q, k, v, rope_base=1e4)  # q [N,Hq,d], k/v [N,Hkv,d]
+    dq, dk, dv = tree_attn_bwd(plan, q, k, v, o, lse, do, rope_base=1e4)
+    loss, dlogits, err = tree_weighted_nll(logits, labels, w)
+    o, lse = tree_decode_splitkv(q, k, v, span_ptr, spans, max_len)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = ["TreeAttnError", "Plan", "HipEvents", "tree_plan", "tree_attn_fwd", "tree_attn_bwd", "tree_weighted_nll",
+           "tree_decode_splitkv", "library_path", "load_library", "TA_BLOCK_M", "TA_BLOCK_N", "TA_BLOCK_KV"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtree_attn.so")
+TA_BLOCK_M, TA_BLOCK_N, TA_BLOCK_KV, TA_CHUNK_INTS = 32, 64, 32, 16
+TA_F32, TA_BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "parent pointers contain a cycle",
+           3: "size exceeds the int32 index range", 4: "out of memory or buffer too small",
+           5: "unsupported configuration", 6: "HIP error"}
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        super().__init__(f"{call} failed: {_STATUS.get(status, 'unknown')} (status {status})")
+        self.status = status
+
+
+class _View(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_nodes", "n_tokens", "n_leaves", "max_pos", "block_m", "block_n", "block_kv",
+        "n_qtiles", "n_chunks", "n_ktiles")] + \
+        [(n, ctypes.c_int64) for n in ("n_flat", "visible_pairs", "computed_pairs_fwd", "computed_pairs_bwd")] + \
+        [(n, ctypes.POINTER(ctypes.c_int32)) for n in (
+            "dfs_order", "node_start", "node_sub_end", "pos", "g", "node_of", "sub_end", "anc_ptr", "anc",
+            "fq_ptr", "fq_chunk", "fq_order", "bk")]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libtree_attn.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise TreeAttnError("load_library", 6) from FileNotFoundError(
+            f"{_LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    pI32 = ctypes.POINTER(ctypes.c_int32)
+    sigs = {
+        "tree_plan": (I32, [pI32, pI32, I32, I32, I32, ctypes.POINTER(P)]),
+        "tree_plan_view": (I32, [P, ctypes.POINTER(_View)]),
+        "tree_plan_device_bytes": (I32, [P, ctypes.POINTER(SZ)]),
+        "tree_plan_upload": (I32, [P, P, SZ, P]),
+        "tree_plan_free": (None, [P]),
+        "tree_attn_ws_bytes": (I32, [P, I32, I32, I32, I32, I32, F32, ctypes.POINTER(SZ)]),
+        "tree_attn_fwd": (I32, [P, P, I32, P, P, P, I32, I32, I32, F32, F32, P, P, P, SZ, P]),
+        "tree_attn_bwd": (I32, [P, P, I32, P, P, P, P, P, P, I32, I32, I32, F32, F32, P, P, P, P, SZ, P]),
+        "tree_nll_ws_bytes": (I32, [I32, I32, ctypes.POINTER(SZ)]),
+        "tree_weighted_nll": (I32, [I32, P, P, P, I32, I32, I32, P, P, P, P, SZ, P]),
+        "tree_decode_ws_bytes": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(SZ), pI32]),
+        "tree_decode_splitkv": (I32, [I32, P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P, P, P, SZ, P]),
+        "tree_attn_fwd_ex": (I32, [P, P, I32, P, P, P, I32, I32, I32, F32, F32, P, P, P, SZ, P, I32, P]),
+        "tree_attn_bwd_ex": (I32, [P, P, I32, P, P, P, P, P, P, I32, I32, I32, F32, F32, P, P, P, P, SZ, P, I32,
+                                   P]),
+        "tree_decode_splitkv_ex": (I32, [I32, P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P, P, P, SZ, P, I32,
+                                         P]),
+        "ta_status_string": (ctypes.c_char_p, [I32]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(call, status):
+    if status != 0:
+        raise TreeAttnError(call, status)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class Plan:
+    """Host plan of a prefix tree (owned by the library; freed on deletion)."""
+
+    def __init__(self, parent, seg_len, block_m: int = 0, block_n: int = 0):
+        L = load_library()
+        parent, seg_len = _i32(parent), _i32(seg_len)
+        if parent.ndim != 1 or parent.shape != seg_len.shape:
+            raise ValueError("parent and seg_len must be 1-D arrays of equal length")
+        self._lib = L
+        self._ptr = ctypes.c_void_p()
+        pI32 = ctypes.POINTER(ctypes.c_int32)
+        _check("tree_plan", L.tree_plan(parent.ctypes.data_as(pI32), seg_len.ctypes.data_as(pI32),
+                                        int(parent.shape[0]), block_m, block_n, ctypes.byref(self._ptr)))
+        v = _View()
+        _check("tree_plan_view", L.tree_plan_view(self._ptr, ctypes.byref(v)))
+        self._v = v
+        self._dev = {}
+        for name in ("n_nodes", "n_tokens", "n_leaves", "max_pos", "block_m", "block_n", "block_kv",
+                     "n_qtiles", "n_chunks", "n_ktiles", "n_flat", "visible_pairs",
+                     "computed_pairs_fwd", "computed_pairs_bwd"):
+            setattr(self, name, int(getattr(v, name)))
+
+    def _arr(self, name, n):
+        if n == 0:
+            return np.zeros(0, np.int32)
+        return np.ctypeslib.as_array(getattr(self._v, name), shape=(n,)).copy()
+
+    def view(self) -> dict:
+        """Copies of every plan table as numpy arrays."""
+        n, N = self.n_nodes, self.n_tokens
+        anc_ptr = self._arr("anc_ptr", n + 1)
+        return dict(
+            dfs_order=self._arr("dfs_order", n), node_start=self._arr("node_start", n),
+            node_sub_end=self._arr("node_sub_end", n), pos=self._arr("pos", N), g=self._arr("g", N),
+            node_of=self._arr("node_of", N), sub_end=self._arr("sub_end", N), anc_ptr=anc_ptr,
+            anc=self._arr("anc", int(anc_ptr[-1])), fq_ptr=self._arr("fq_ptr", self.n_qtiles + 1),
+            fq_chunk=self._arr("fq_chunk", self.n_chunks * TA_CHUNK_INTS).reshape(-1, TA_CHUNK_INTS),
+            fq_order=self._arr("fq_order", self.n_qtiles), bk=self._arr("bk", self.n_ktiles * 4).reshape(-1, 4))
+
+    @property
+    def handle(self):
+        return self._ptr
+
+    def device(self, device=None):
+        """The plan's tables uploaded to device memory (a torch uint8 tensor, cached)."""
+        import torch
+        dev = torch.device(device if device is not None else "cuda")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        key = str(dev)
+        if key not in self._dev:
+            n = ctypes.c_size_t()
+            _check("tree_plan_device_bytes", self._lib.tree_plan_device_bytes(self._ptr, ctypes.byref(n)))
+            buf = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+            st = torch.cuda.current_stream(dev)
+            _check("tree_plan_upload", self._lib.tree_plan_upload(self._ptr, ctypes.c_void_p(buf.data_ptr()),
+                                                                   int(n.value), ctypes.c_void_p(st.cuda_stream)))
+            st.synchronize()  # the host tables are pageable: finish the copy before returning
+            self._dev[key] = buf
+        return self._dev[key]
+
+    def __del__(self):
+        ptr = getattr(self, "_ptr", None)
+        if ptr is not None and ptr.value:
+            self._lib.tree_plan_free(ptr)
+            self._ptr = None
+
+
+def tree_plan(parent, seg_len, block_m: int = 0, block_n: int = 0) -> Plan:
+    return Plan(parent, seg_len, block_m, block_n)
+
+
+def _dt(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TA_BF16
+    if t.dtype == torch.float32:
+        return TA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must live on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _events(events):
+    """Optional stage-timing events: a HipEvents slice (see HipEvents.slice)."""
+    if events is None:
+        return ctypes.c_void_p(0), 0
+    arr, n = events
+    return ctypes.cast(arr, ctypes.c_void_p), n
+
+
+class HipEvents:
+    """A pool of hipEvent_t created through the HIP runtime, for the *_ex
+    calls' stage timing (events must be recorded on the launch stream)."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        self.n = 0
+        for i in range(n):
+            e = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise TreeAttnError("hipEventCreate", 6)
+            self.arr[i] = e.value
+            self.n = i + 1
+
+    def slice(self, start: int, count: int):
+        base = ctypes.addressof(self.arr) + start * ctypes.sizeof(ctypes.c_void_p)
+        return (ctypes.c_void_p(base), count)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        self._hip.hipEventSynchronize(self.arr[b])
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[a], self.arr[b]) != 0:
+            raise TreeAttnError("hipEventElapsedTime", 6)
+        return float(ms.value)
+
+    def __del__(self):
+        for i in range(getattr(self, "n", 0)):
+            if self.arr[i]:
+                self._hip.hipEventDestroy(self.arr[i])
+
+
+def _workspace(nbytes, device, ws):
+    import torch
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() >= nbytes:
+        return ws, ws.numel()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return buf, nbytes
+
+
+def attn_ws_bytes(plan: Plan, op: int, dtype_code: int, Hq: int, Hkv: int, d: int, rope_base: float) -> int:
+    n = ctypes.c_size_t()
+    _check("tree_attn_ws_bytes", load_library().tree_attn_ws_bytes(plan.handle, op, dtype_code, Hq, Hkv, d,
+                                                                    float(rope_base), ctypes.byref(n)))
+    return int(n.value)
+
+
+def tree_attn_fwd(plan: Plan, q, k, v, scale: float = 0.0, rope_base: float = 0.0, o=None, lse=None, ws=None,
+                  events=None):
+    """Forward tree attention.  q [N,Hq,d], k/v [N,Hkv,d] (bf16 or fp32) ->
+    o [N,Hq,d] (same dtype), lse [Hq,N] fp32."""
+    import torch
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if N != plan.n_tokens:
+        raise ValueError(f"q has {N} tokens, the plan {plan.n_tokens}")
+    for name, t, shp in (("q", q, (N, Hq, d)), ("k", k, (N, Hkv, d)), ("v", v, (N, Hkv, d))):
+        _need(t, name, shp, q.dtype, dev)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(Hq, N, dtype=torch.float32, device=dev) if lse is None else lse
+    _need(o, "o", (N, Hq, d), q.dtype, dev)
+    _need(lse, "lse", (Hq, N), torch.float32, dev)
+    dt = _dt(q)
+    wsb = attn_ws_bytes(plan, 0, dt, Hq, Hkv, d, rope_base)
+    ws, wsn = _workspace(wsb, dev, ws)
+    ev, nev = _events(events)
+    _check("tree_attn_fwd", load_library().tree_attn_fwd_ex(
+        plan.handle, _ptr(plan.device(dev)), dt, _ptr(q), _ptr(k), _ptr(v), Hq, Hkv, d, float(scale),
+        float(rope_base), _ptr(o), _ptr(lse), _ptr(ws), wsn, ev, nev, _stream(q)))
+    return o, lse
+
+
+def tree_attn_bwd(plan: Plan, q, k, v, o, lse, dO, scale: float = 0.0, rope_base: float = 0.0,
+                  dq=None, dk=None, dv=None, ws=None, events=None):
+    """Backward of tree_attn_fwd -> (dq, dk, dv), overwritten, deterministic."""
+    import torch
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if N != plan.n_tokens:
+        raise ValueError(f"q has {N} tokens, the plan {plan.n_tokens}")
+    for name, t, shp in (("q", q, (N, Hq, d)), ("k", k, (N, Hkv, d)), ("v", v, (N, Hkv, d)),
+                         ("o", o, (N, Hq, d)), ("dO", dO, (N, Hq, d))):
+        _need(t, name, shp, q.dtype, dev)
+    _need(lse, "lse", (Hq, N), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dt = _dt(q)
+    wsb = attn_ws_bytes(plan, 1, dt, Hq, Hkv, d, rope_base)
+    ws, wsn = _workspace(wsb, dev, ws)
+    ev, nev = _events(events)
+    _check("tree_attn_bwd", load_library().tree_attn_bwd_ex(
+        plan.handle, _ptr(plan.device(dev)), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+        Hq, Hkv, d, float(scale), float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsn, ev, nev,
+        _stream(q)))
+    return dq, dk, dv
+
+
+def tree_weighted_nll(logits, labels, w, ignore_index: int = -100, need_grad: bool = True,
+                      loss=None, dlogits=None, err_flag=None, ws=None):
+    """sum_t w_t [y_t valid] (logsumexp(x_t) - x_t[y_t]) -> (loss [1] fp32, dlogits or None, err_flag [1] int32)."""
+    import torch
+    N, V = logits.shape
+    dev = logits.device
+    _need(logits, "logits", (N, V), torch.float32, dev)
+    _need(labels, "labels", (N,), torch.int32, dev)
+    _need(w, "w", (N,), torch.float32, dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
+    if need_grad and dlogits is None:
+        dlogits = torch.empty_like(logits)
+    if err_flag is None:
+        err_flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    n = ctypes.c_size_t()
+    L = load_library()
+    _check("tree_nll_ws_bytes", L.tree_nll_ws_bytes(N, V, ctypes.byref(n)))
+    ws, wsn = _workspace(int(n.value), dev, ws)
+    _check("tree_weighted_nll", L.tree_weighted_nll(
+        TA_F32, _ptr(logits), _ptr(labels), _ptr(w), N, V, int(ignore_index), _ptr(loss),
+        _ptr(dlogits if need_grad else None), _ptr(err_flag), _ptr(ws), wsn, _stream(logits)))
+    return loss, (dlogits if need_grad else None), err_flag
+
+
+def decode_ws_bytes(B, Hq, d, max_len, n_splits=0):
+    n = ctypes.c_size_t()
+    s = ctypes.c_int32()
+    _check("tree_decode_ws_bytes", load_library().tree_decode_ws_bytes(B, Hq, d, int(max_len), int(n_splits),
+                                                                        ctypes.byref(n), ctypes.byref(s)))
+    return int(n.value), int(s.value)
+
+
+def tree_decode_splitkv(q, k, v, span_ptr, spans, max_len: int, scale: float = 0.0, n_splits: int = 0,
+                        o=None, lse=None, ws=None, events=None):
+    """Split-KV single-query decode.  q [B,Hq,d] bf16; k/v [L,Hkv,d] bf16;
+    span_ptr [B+1], spans [S,2] int32 on the device -> o [B,Hq,d], lse [B,Hq]."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _need(q, "q", (B, Hq, d), torch.bfloat16, dev)
+    _need(k, "k", tuple(k.shape), torch.bfloat16, dev)
+    _need(v, "v", tuple(k.shape), torch.bfloat16, dev)
+    _need(span_ptr, "span_ptr", (B + 1,), torch.int32, dev)
+    _need(spans, "spans", tuple(spans.shape), torch.int32, dev)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev) if lse is None else lse
+    wsb, _ = decode_ws_bytes(B, Hq, d, max_len, n_splits)
+    ws, wsn = _workspace(wsb, dev, ws)
+    ev, nev = _events(events)
+    _check("tree_decode_splitkv", load_library().tree_decode_splitkv_ex(
+        TA_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(span_ptr), _ptr(spans), B, Hq, Hkv, d, int(max_len),
+        float(scale), int(n_splits), _ptr(o), _ptr(lse), _ptr(ws), wsn, ev, nev, _stream(q)))
+    return o, lse

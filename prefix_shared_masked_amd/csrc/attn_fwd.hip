@@ -1,0 +1,466 @@
+// Tree-attention forward on gfx950.
+//
+// Semantics (Tree Training post): packed token i reads key j iff j <= i and
+// node(j) is an ancestor-or-self of node(i) (section 4.2), which in DFS order
+// is j <= i < kend(j) with kend the end of node(j)'s DFS interval (section
+// 4.3); positions are tree depth (section 5).  O = softmax(scale Q K^T + M) V
+// and LSE = log sum_j exp(scale q_i . k_j).
+//
+// bf16 kernel layout, one workgroup = one 32-row query tile x up to four query
+// heads that share a KV head (one wavefront per head):
+//  - the tile's keys come from the plan's gathered chunk list (the ancestor
+//    block table): only keys some row may read are ever loaded, so invisible
+//    sibling subtrees cost nothing (section 4.3, "skip, do not mask");
+//  - each chunk of 64 key rows is gathered from HBM with 16-byte loads into
+//    LDS (double-buffered, prefetched through registers one chunk ahead);
+//  - S^T = K Q^T on 32x32x16 bf16 MFMA with Q resident in registers, so each
+//    lane owns one query column: the row max and row sum are in-register plus
+//    a single exchange with the lane 32 away;
+//  - the element mask j <= i < kend is evaluated only on chunks the plan did
+//    not flag as fully visible;
+//  - O^T += V^T P^T on MFMA, V^T read from LDS with the transpose read, P^T
+//    straight from the S^T accumulators;
+//  - the XCD round-robin of workgroups puts consecutive block ids on
+//    different XCDs, so blockIdx % Hkv picks the KV head and every XCD keeps
+//    re-reading the same KV head's ancestors in its own L2.
+#include <algorithm>
+#include <cstring>
+
+#include "common.h"
+#include "plan_internal.h"
+
+namespace ta {
+
+// ---------------------------------------------------------------------------
+// RoPE by depth position and/or dtype conversion: y[t, h, :] = R(pos[t])
+// x[t, h, :] (transpose=1 gives R^T; base <= 0 converts only).  Rotate-half
+// pairs (i, i + d/2), angle pos * base^(-2i/d), arithmetic in fp32.
+template <typename T>
+__device__ __forceinline__ T cvt_out(float x) { return (T)x; }
+template <>
+__device__ __forceinline__ f16 cvt_out<f16>(float x) { return to_f16_sat(x); }
+
+template <typename Ti, typename To>
+__global__ void rope_kernel(const Ti* x, To* y, const int32_t* __restrict__ pos,  // x may alias y
+                            int N, int H, int d, float base, int transpose) {
+  const int half = d / 2;
+  const size_t total = (size_t)N * H * half;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int i = (int)(idx % half);
+    const size_t th = idx / half;
+    const int t = (int)(th / H);
+    float s = 0.f, c = 1.f;
+    if (base > 0.f) rope_sincos(pos[t], i, d, base, &s, &c);
+    if (transpose) s = -s;
+    const size_t row = th * d;
+    const float x1 = (float)x[row + i], x2 = (float)x[row + i + half];
+    y[row + i] = cvt_out<To>(x1 * c - x2 * s);
+    y[row + i + half] = cvt_out<To>(x2 * c + x1 * s);
+  }
+}
+
+template <typename Ti, typename To>
+hipError_t launch_rope(const Ti* x, To* y, const int32_t* pos, int N, int H, int d, float base, int transpose,
+                       hipStream_t st) {
+  const size_t total = (size_t)N * H * (d / 2);
+  if (total == 0) return hipSuccess;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL((rope_kernel<Ti, To>), dim3(blocks), dim3(256), 0, st, x, y, pos, N, H, d, base, transpose);
+  return hipGetLastError();
+}
+
+template hipError_t launch_rope<float, float>(const float*, float*, const int32_t*, int, int, int, float, int,
+                                              hipStream_t);
+template hipError_t launch_rope<bf16, bf16>(const bf16*, bf16*, const int32_t*, int, int, int, float, int,
+                                            hipStream_t);
+template hipError_t launch_rope<bf16, f16>(const bf16*, f16*, const int32_t*, int, int, int, float, int,
+                                           hipStream_t);
+
+namespace fwd {
+
+constexpr int D = 128;
+constexpr int BM = TA_BLOCK_M;
+constexpr int BN = TA_BLOCK_N;
+constexpr int PK = D + 8;   // 272-byte K rows: 16-byte row reads hit distinct banks
+constexpr int PV = D + 16;  // 288-byte V rows: transpose reads hit distinct banks
+
+struct Params {
+  const bf16* q;
+  const f16* k;   // fp16 copy of K (rotated when RoPE is on) for the scores
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  const int32_t* pos;
+  const int32_t* fq_ptr;
+  const int32_t* fq_chunk;
+  const int32_t* fq_order;
+  int N, Hq, Hkv, G;
+  float scale_log2;  // softmax scale * log2(e)
+  float rope_base;
+};
+
+struct Stage {
+  uint4 k[4], v[4];
+  int j[4], e[4];
+};
+
+__device__ __forceinline__ void load_stage(const Params& P, int c, int kvh, Stage& s) {
+  const int32_t* ch = P.fq_chunk + (size_t)c * TA_CHUNK_INTS;
+  const int t = threadIdx.x, piece = t & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int v = (t >> 4) + 16 * r;
+    chunk_slot(ch, v, s.j[r], s.e[r]);
+    const size_t off = ((size_t)s.j[r] * P.Hkv + kvh) * D + piece * 8;
+    s.k[r] = *(const uint4*)(P.k + off);
+    s.v[r] = *(const uint4*)(P.v + off);
+  }
+}
+
+__device__ __forceinline__ void store_stage(const Stage& s, f16* sK, bf16* sV, int* sJ, int* sE) {
+  const int t = threadIdx.x, piece = t & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int v = (t >> 4) + 16 * r;
+    *(uint4*)(sK + v * PK + piece * 8) = s.k[r];
+    *(uint4*)(sV + v * PV + piece * 8) = s.v[r];
+    if (piece == 0) {
+      sJ[v] = s.j[r];
+      sE[v] = s.e[r];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
+  __shared__ __attribute__((aligned(16))) f16 sK[2][BN * PK];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][BN * PV];
+  __shared__ __attribute__((aligned(16))) int sJ[2][BN];
+  __shared__ __attribute__((aligned(16))) int sE[2][BN];
+
+  const int kvh = blockIdx.x % P.Hkv;
+  const int tile = P.fq_order[blockIdx.x / P.Hkv];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int hsub = blockIdx.y * 4 + wave;
+  const bool active = hsub < P.G;
+  const int h = kvh * P.G + (active ? hsub : 0);
+  const int qi = tile * BM + col;
+  const bool qvalid = qi < P.N;
+
+  // Q (rotated by depth position, fp16) as the B operand: lane = query
+  // column, k-slots s*16 + half*8 + e.
+  f16x8 qf[8];
+  {
+    const bf16* qrow = P.q + ((size_t)(qvalid ? qi : 0) * P.Hq + h) * D + half * 8;
+    const bool rot = P.rope_base > 0.f && qvalid;
+    const int p = qvalid ? P.pos[qi] : 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 t1 = *(const bf16x8*)(qrow + s * 16);
+      const bf16x8 t2 = *(const bf16x8*)(qrow + (s + 4) * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x1 = qvalid ? (float)t1[e] : 0.f, x2 = qvalid ? (float)t2[e] : 0.f;
+        if (rot) {
+          float sn, cs;
+          rope_sincos(p, s * 16 + half * 8 + e, D, P.rope_base, &sn, &cs);
+          const float y1 = x1 * cs - x2 * sn;
+          x2 = x2 * cs + x1 * sn;
+          x1 = y1;
+        }
+        qf[s][e] = to_f16_sat(x1);
+        qf[s + 4][e] = to_f16_sat(x2);
+      }
+    }
+  }
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+  const int c0 = P.fq_ptr[tile], c1 = P.fq_ptr[tile + 1];
+  Stage st;
+  load_stage(P, c0, kvh, st);
+  store_stage(st, sK[0], sV[0], sJ[0], sE[0]);
+  __syncthreads();
+
+  const int trow = half * 4 + ((lane & 15) >> 2);
+  const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+
+  for (int c = c0; c < c1; ++c) {
+    const int buf = (c - c0) & 1;
+    // prefetch the next chunk (the last iteration reloads its own chunk,
+    // which keeps the staging registers free of control flow)
+    load_stage(P, c + 1 < c1 ? c + 1 : c, kvh, st);
+    if (active) {
+      const f16* kb = sK[buf];
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 a0 = *(const f16x8*)(kb + col * PK + s * 16 + half * 8);
+        const f16x8 a1 = *(const f16x8*)(kb + (32 + col) * PK + s * 16 + half * 8);
+        s0 = mfma32h(a0, qf[s], s0);
+        s1 = mfma32h(a1, qf[s], s1);
+      }
+      // S^T register r of tile kt <-> key slot kt*32 + 8*(r/4) + 4*half + r%4
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] *= P.scale_log2;
+        s1[r] *= P.scale_log2;
+      }
+      const int full = P.fq_chunk[(size_t)c * TA_CHUNK_INTS + 2];
+      if (!full) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int v0 = r4 * 8 + half * 4;
+          const int4 J0 = *(const int4*)&sJ[buf][v0], E0 = *(const int4*)&sE[buf][v0];
+          const int4 J1 = *(const int4*)&sJ[buf][32 + v0], E1 = *(const int4*)&sE[buf][32 + v0];
+          const int j0[4] = {J0.x, J0.y, J0.z, J0.w}, e0[4] = {E0.x, E0.y, E0.z, E0.w};
+          const int j1[4] = {J1.x, J1.y, J1.z, J1.w}, e1[4] = {E1.x, E1.y, E1.z, E1.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (!(j0[u] <= qi && qi < e0[u])) s0[r4 * 4 + u] = -INFINITY;
+            if (!(j1[u] <= qi && qi < e1[u])) s1[r4 * 4 + u] = -INFINITY;
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m, mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = exp2f_fast(m - muse);
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = exp2f_fast(s0[r] - muse);
+        s1[r] = exp2f_fast(s1[r] - muse);
+        rs += s0[r] + s1[r];
+      }
+      l = l * alpha + rs;  // per-lane partial over this lane's key rows
+      m = mnew;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[0][e] = (bf16)s0[e];
+        pb[1][e] = (bf16)s0[8 + e];
+        pb[2][e] = (bf16)s1[e];
+        pb[3][e] = (bf16)s1[8 + e];
+      }
+      const bf16* vb = sV[buf];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x4 t0 = lds_read_tr(vb + (kk * 16 + trow) * PV + dt * 32 + tcol);
+          const bf16x4 t1 = lds_read_tr(vb + (kk * 16 + 8 + trow) * PV + dt * 32 + tcol);
+          acc[dt] = mfma32(cat(t0, t1), pb[kk], acc[dt]);
+        }
+    }
+    store_stage(st, sK[buf ^ 1], sV[buf ^ 1], sJ[buf ^ 1], sE[buf ^ 1]);
+    __syncthreads();
+  }
+
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (active && qvalid) {
+    bf16* orow = P.o + ((size_t)qi * P.Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = (bf16)(acc[dt][r4 * 4 + u] * inv);
+        *(bf16x4*)(orow + dt * 32 + r4 * 8 + half * 4) = w;
+      }
+    if (half == 0) P.lse[(size_t)h * P.N + qi] = (m + log2f(lt)) * TA_LN2;
+  }
+}
+
+}  // namespace fwd
+
+// ---------------------------------------------------------------------------
+// fp32 path: one thread per (query row, head), walking the same gathered
+// chunks; exact fp32 arithmetic for small problems and for checking.
+template <int D>
+__global__ __launch_bounds__(TA_BLOCK_M) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                              const float* __restrict__ v, float* __restrict__ o,
+                                                              float* __restrict__ lse, const int32_t* __restrict__ fq_ptr,
+                                                              const int32_t* __restrict__ fq_chunk, int N, int Hq, int Hkv,
+                                                              float scale) {
+  const int tile = blockIdx.x, h = blockIdx.y, G = Hq / Hkv, kvh = h / G;
+  const int i = tile * TA_BLOCK_M + threadIdx.x;
+  if (i >= N) return;
+  float qv[D], acc[D];
+  for (int x = 0; x < D; ++x) {
+    qv[x] = q[((size_t)i * Hq + h) * D + x];
+    acc[x] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int c = fq_ptr[tile]; c < fq_ptr[tile + 1]; ++c) {
+    const int32_t* ch = fq_chunk + (size_t)c * TA_CHUNK_INTS;
+    for (int slot = 0; slot < ch[1]; ++slot) {
+      int j, kend;
+      chunk_slot(ch, slot, j, kend);
+      if (!(j <= i && i < kend)) continue;
+      const float* kr = k + ((size_t)j * Hkv + kvh) * D;
+      const float* vr = v + ((size_t)j * Hkv + kvh) * D;
+      float s = 0.f;
+      for (int x = 0; x < D; ++x) s = fmaf(qv[x], kr[x], s);
+      s *= scale;
+      const float mn = fmaxf(m, s);
+      const float a = expf(m - mn), p = expf(s - mn);
+      l = l * a + p;
+      for (int x = 0; x < D; ++x) acc[x] = acc[x] * a + p * vr[x];
+      m = mn;
+    }
+  }
+  for (int x = 0; x < D; ++x) o[((size_t)i * Hq + h) * D + x] = acc[x] / l;
+  lse[(size_t)h * N + i] = m + logf(l);
+}
+
+}  // namespace ta
+
+using namespace ta;
+
+extern "C" ta_status tree_plan_upload(const ta_plan* p, void* dplan, size_t bytes, hipStream_t stream) {
+  if (!p || !dplan) return TA_EINVAL;
+  if (bytes < p->device_bytes) return TA_ENOMEM;
+  char* base = (char*)dplan;
+  struct Part {
+    size_t off;
+    const std::vector<int32_t>* vec;
+  } parts[] = {{p->off_pos, &p->pos},
+               {p->off_fq_ptr, &p->fq_ptr},
+               {p->off_fq_chunk, &p->fq_chunk},
+               {p->off_fq_order, &p->fq_order},
+               {p->off_bk, &p->bk}};
+  for (const Part& x : parts) {
+    if (x.vec->empty()) continue;
+    if (hipMemcpyAsync(base + x.off, x.vec->data(), x.vec->size() * sizeof(int32_t), hipMemcpyHostToDevice,
+                       stream) != hipSuccess)
+      return TA_EHIP;
+  }
+  return TA_OK;
+}
+
+namespace {
+
+ta_status check_common(const ta_plan* p, const void* dplan, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d) {
+  if (!p || !dplan) return TA_EINVAL;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return TA_EINVAL;
+  if (dt == TA_BF16) {
+    if (d != 128) return TA_EUNSUPPORTED;
+  } else if (dt == TA_F32) {
+    if (d != 64 && d != 128) return TA_EUNSUPPORTED;
+  } else {
+    return TA_EUNSUPPORTED;
+  }
+  if ((int64_t)p->n_tokens * Hq * d > ((int64_t)1 << 40)) return TA_ERANGE;
+  return TA_OK;
+}
+
+size_t fwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base) {
+  const size_t N = p->n_tokens;
+  if (dt == TA_BF16) return align256(N * Hkv * d * sizeof(f16));  // fp16 (rotated) K
+  if (rope_base <= 0.f) return 0;
+  return align256(N * Hq * d * sizeof(float)) + align256(N * Hkv * d * sizeof(float));
+}
+
+}  // namespace
+
+// Backward workspace (defined in attn_bwd.hip).
+size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base);
+
+extern "C" ta_status tree_attn_ws_bytes(const ta_plan* p, int32_t op, ta_dtype dt, int32_t Hq, int32_t Hkv,
+                                        int32_t d, float rope_base, size_t* bytes) {
+  if (!p || !bytes || (op != 0 && op != 1)) return TA_EINVAL;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return TA_EINVAL;
+  *bytes = op == 0 ? fwd_ws(p, dt, Hq, Hkv, d, rope_base) : ta_bwd_ws(p, dt, Hq, Hkv, d, rope_base);
+  return TA_OK;
+}
+
+extern "C" ta_status tree_attn_fwd(const ta_plan* p, const void* dplan, ta_dtype dt, const void* q, const void* k,
+                                   const void* v, int32_t Hq, int32_t Hkv, int32_t d, float scale, float rope_base,
+                                   void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return tree_attn_fwd_ex(p, dplan, dt, q, k, v, Hq, Hkv, d, scale, rope_base, o, lse, ws, ws_bytes, nullptr, 0,
+                          stream);
+}
+
+extern "C" ta_status tree_attn_fwd_ex(const ta_plan* p, const void* dplan, ta_dtype dt, const void* q, const void* k,
+                                      const void* v, int32_t Hq, int32_t Hkv, int32_t d, float scale, float rope_base,
+                                      void* o, float* lse, void* ws, size_t ws_bytes, hipEvent_t* ev, int32_t nev,
+                                      hipStream_t stream) {
+  ta_status st = check_common(p, dplan, dt, Hq, Hkv, d);
+  if (st != TA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return TA_EINVAL;
+  const size_t need = fwd_ws(p, dt, Hq, Hkv, d, rope_base);
+  if (need && (!ws || ws_bytes < need)) return TA_ENOMEM;
+  const int N = p->n_tokens;
+  if (N == 0) return TA_OK;
+  if (scale <= 0.f) scale = 1.f / sqrtf((float)d);
+  const char* base = (const char*)dplan;
+  const int32_t* pos = (const int32_t*)(base + p->off_pos);
+  const int32_t* fq_ptr = (const int32_t*)(base + p->off_fq_ptr);
+  const int32_t* fq_chunk = (const int32_t*)(base + p->off_fq_chunk);
+  const int32_t* fq_order = (const int32_t*)(base + p->off_fq_order);
+
+  mark(ev, nev, 0, stream);
+  if (dt == TA_BF16) {
+    f16* kk = (f16*)ws;
+    if (launch_rope<bf16, f16>((const bf16*)k, kk, pos, N, Hkv, d, rope_base, 0, stream) != hipSuccess)
+      return TA_EHIP;
+    mark(ev, nev, 1, stream);
+    fwd::Params P;
+    P.q = (const bf16*)q;
+    P.k = kk;
+    P.v = (const bf16*)v;
+    P.o = (bf16*)o;
+    P.lse = lse;
+    P.pos = pos;
+    P.fq_ptr = fq_ptr;
+    P.fq_chunk = fq_chunk;
+    P.fq_order = fq_order;
+    P.N = N;
+    P.Hq = Hq;
+    P.Hkv = Hkv;
+    P.G = Hq / Hkv;
+    P.scale_log2 = scale * TA_LOG2E;
+    P.rope_base = rope_base;
+    dim3 grid(p->n_qtiles * Hkv, (P.G + 3) / 4);
+    hipLaunchKernelGGL(fwd::fwd_bf16_kernel, grid, dim3(256), 0, stream, P);
+    TA_LAUNCH_CHECK();
+    mark(ev, nev, 2, stream);
+    return TA_OK;
+  }
+
+  const float* qq = (const float*)q;
+  const float* kk = (const float*)k;
+  if (rope_base > 0.f) {
+    float* qr = (float*)ws;
+    float* kr = (float*)((char*)ws + align256((size_t)N * Hq * d * sizeof(float)));
+    if (launch_rope<float, float>(qq, qr, pos, N, Hq, d, rope_base, 0, stream) != hipSuccess) return TA_EHIP;
+    if (launch_rope<float, float>(kk, kr, pos, N, Hkv, d, rope_base, 0, stream) != hipSuccess) return TA_EHIP;
+    qq = qr;
+    kk = kr;
+  }
+  mark(ev, nev, 1, stream);
+  dim3 grid(p->n_qtiles, Hq);
+  if (d == 64)
+    hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(TA_BLOCK_M), 0, stream, qq, kk, (const float*)v, (float*)o, lse,
+                       fq_ptr, fq_chunk, N, Hq, Hkv, scale);
+  else
+    hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(TA_BLOCK_M), 0, stream, qq, kk, (const float*)v, (float*)o,
+                       lse, fq_ptr, fq_chunk, N, Hq, Hkv, scale);
+  TA_LAUNCH_CHECK();
+  mark(ev, nev, 2, stream);
+  return TA_OK;
+}

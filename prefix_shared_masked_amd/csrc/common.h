@@ -1,0 +1,111 @@
+// Device helpers shared by the gfx950 kernels: bf16 vectors, MFMA wrappers,
+// the LDS transpose read, and launch error mapping.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "tree_attn.h"
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define TA_LOG2E 1.4426950408889634f
+#define TA_LN2 0.6931471805599453f
+
+namespace ta {
+
+// 32x32x16 bf16 MFMA: C[32x32] += A[32x16] B[16x32].  Lane l holds row l%32
+// of A and column l%32 of B, each with the 8 k-slots of half l/32; C is held
+// as 16 registers per lane, register r <-> row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Same shape with fp16 operands (same rate; 10 stored mantissa bits).
+__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> fp16 with saturation at the largest finite fp16 (65504), so an
+// out-of-range activation can never turn into inf inside a score.
+__device__ __forceinline__ f16 to_f16_sat(float x) { return (f16)fminf(fmaxf(x, -65504.f), 65504.f); }
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane x points at row x/4, columns 4*(x%4)..+3 of a 4x16 bf16 block and
+// receives column x of that block (its 4 rows).
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat(const bf16x4& a, const bf16x4& b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Rotary angle pos * base^(-2i/d): the product and the reduction by
+// quadrants (multiples of pi/2) are done in double precision, so long depths
+// lose no accuracy; sin and cos of the remainder r in [-pi/4, pi/4] come from
+// their Taylor series (truncation error below 2e-9 at |r| = pi/4).
+__device__ __forceinline__ void rope_sincos(int pos, int i, int d, float base, float* s, float* c) {
+  const double inv = exp2(-(2.0 * i / d) * log2((double)base));
+  const double ang = (double)pos * inv;
+  const double half_pi = 1.5707963267948966;
+  const double kq = rint(ang / half_pi);
+  const float r = (float)(ang - kq * half_pi);
+  const float r2 = r * r;
+  const float sr = r * (1.f + r2 * (-1.f / 6 + r2 * (1.f / 120 + r2 * (-1.f / 5040 + r2 * (1.f / 362880)))));
+  const float cr = 1.f + r2 * (-0.5f + r2 * (1.f / 24 + r2 * (-1.f / 720 + r2 * (1.f / 40320 + r2 * (-1.f / 3628800)))));
+  const int q = (int)((long long)kq & 3);
+  *s = q == 0 ? sr : q == 1 ? cr : q == 2 ? -sr : -cr;
+  *c = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
+}
+
+// Gathered key chunk of the plan: slot v -> packed key index and the end of
+// the DFS interval of the key's node (row i reads the key iff key <= i < kend).
+__device__ __forceinline__ void chunk_slot(const int32_t* __restrict__ ch, int v, int& phys, int& kend) {
+  int s = 0;
+#pragma unroll
+  for (int x = 1; x < TA_CHUNK_MAX_SEG; ++x) s = (ch[8 + x] <= v) ? x : s;
+  phys = ch[4 + s] + (v - ch[8 + s]);
+  kend = ch[12 + s];
+  if (v >= ch[1]) {  // padding slot: a valid row, never visible
+    phys = ch[4];
+    kend = 0;
+  }
+}
+
+// Order LDS traffic of one wavefront: earlier LDS writes complete before any
+// later LDS access is issued, and the compiler may not move memory accesses
+// across this point.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// RoPE / conversion pass over a [N, H, d] tensor (attn_fwd.hip).
+template <typename Ti, typename To>
+hipError_t launch_rope(const Ti* x, To* y, const int32_t* pos, int N, int H, int d, float base, int transpose,
+                       hipStream_t st);
+
+}  // namespace ta
+
+namespace ta {
+// Record events[i] on the stream when the caller asked for stage timing.
+inline void mark(hipEvent_t* ev, int32_t n, int32_t i, hipStream_t st) {
+  if (ev && i < n && ev[i]) (void)hipEventRecord(ev[i], st);
+}
+}  // namespace ta
+
+#define TA_LAUNCH_CHECK()                            \
+  do {                                               \
+    if (hipGetLastError() != hipSuccess) return TA_EHIP; \
+  } while (0)

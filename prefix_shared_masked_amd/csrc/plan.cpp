@@ -1,0 +1,353 @@
+// Host planner for tree attention over a DFS-packed prefix tree.
+//
+// Builds, from parent[] and seg_len[], everything the kernels need:
+//  - the DFS serialisation (Tree Training post, section 3.2) with children and
+//    roots in ascending node id, done with an explicit stack;
+//  - depth positions (section 5): a node's first position is its parent's
+//    first position plus the parent's length, propagated top-down;
+//  - g_t (section 6.2) as the leaf count of node(t)'s subtree, accumulated
+//    bottom-up over the reversed visiting order, and K = number of leaves;
+//  - the DFS interval [node_start, node_sub_end) of every node (section 4.3);
+//  - the forward "ancestor block table" (section 4.3): for each query tile
+//    of TA_BLOCK_M rows, the keys some row may read, as node segments packed
+//    into gathered chunks of TA_BLOCK_N key slots, flagged when every row
+//    reads every key so the kernel can skip the element mask;
+//  - the backward key tiles: at most TA_BLOCK_KV keys inside one node, read
+//    by the contiguous query range [k0, node_sub_end) (a key's readers are
+//    exactly the later tokens of its node's subtree).
+// Integer-only and deterministic.
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "tree_attn.h"
+#include "plan_internal.h"
+
+namespace {
+
+constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+
+struct Segment {
+  int32_t k0, k1, kend;  // keys [k0, k1) of one node; row i reads key j iff j <= i < kend
+  bool full;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_plan* p) {
+  p->n_nodes = n;
+  p->block_m = TA_BLOCK_M;
+  p->block_n = TA_BLOCK_N;
+  p->block_kv = TA_BLOCK_KV;
+
+  // children in ascending id via a counting sort on the parent
+  std::vector<int32_t> child_ptr(n + 1, 0), child(n), roots;
+  for (int32_t i = 0; i < n; ++i) {
+    if (parent[i] < 0) roots.push_back(i);
+    else child_ptr[parent[i] + 1]++;
+  }
+  for (int32_t i = 0; i < n; ++i) child_ptr[i + 1] += child_ptr[i];
+  {
+    std::vector<int32_t> fill(child_ptr.begin(), child_ptr.end() - 1);
+    for (int32_t i = 0; i < n; ++i)
+      if (parent[i] >= 0) child[fill[parent[i]]++] = i;
+  }
+
+  // preorder with an explicit stack: pushing in reverse pops in ascending id
+  p->dfs_order.reserve(n);
+  p->node_start.assign(n, 0);
+  std::vector<int64_t> pos0(n, 0);
+  std::vector<int32_t> stack;
+  stack.reserve(n);
+  for (auto it = roots.rbegin(); it != roots.rend(); ++it) stack.push_back(*it);
+  int64_t cursor = 0;
+  while (!stack.empty()) {
+    int32_t node = stack.back();
+    stack.pop_back();
+    p->dfs_order.push_back(node);
+    p->node_start[node] = static_cast<int32_t>(cursor);
+    pos0[node] = parent[node] < 0 ? 0 : pos0[parent[node]] + seg_len[parent[node]];
+    cursor += seg_len[node];
+    if (cursor > kI32Max) return TA_ERANGE;
+    for (int32_t c = child_ptr[node + 1] - 1; c >= child_ptr[node]; --c) stack.push_back(child[c]);
+  }
+  if (static_cast<int32_t>(p->dfs_order.size()) != n) return TA_ECYCLE;
+  const int32_t N = static_cast<int32_t>(cursor);
+  p->n_tokens = N;
+
+  // bottom-up: subtree token counts and leaf counts
+  std::vector<int64_t> sub_tok(n, 0), leaves(n, 0);
+  for (int32_t r = n - 1; r >= 0; --r) {
+    int32_t node = p->dfs_order[r];
+    sub_tok[node] += seg_len[node];
+    if (child_ptr[node + 1] == child_ptr[node]) leaves[node] = 1;
+    if (parent[node] >= 0) {
+      sub_tok[parent[node]] += sub_tok[node];
+      leaves[parent[node]] += leaves[node];
+    }
+  }
+  p->node_sub_end.assign(n, 0);
+  int64_t K = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    p->node_sub_end[i] = static_cast<int32_t>(p->node_start[i] + sub_tok[i]);
+    if (parent[i] < 0) K += leaves[i];
+  }
+  p->n_leaves = static_cast<int32_t>(K);
+
+  // per-token arrays
+  p->pos.resize(N);
+  p->g.resize(N);
+  p->node_of.resize(N);
+  p->sub_end.resize(N);
+  int64_t n_flat = 0, pairs = 0, max_pos = -1;
+  for (int32_t node : p->dfs_order) {
+    int32_t s = p->node_start[node];
+    for (int32_t j = 0; j < seg_len[node]; ++j) {
+      int64_t ps = pos0[node] + j;
+      p->pos[s + j] = static_cast<int32_t>(ps);
+      p->g[s + j] = static_cast<int32_t>(leaves[node]);
+      p->node_of[s + j] = node;
+      p->sub_end[s + j] = p->node_sub_end[node];
+      n_flat += leaves[node];
+      pairs += ps + 1;
+      max_pos = std::max(max_pos, ps);
+    }
+  }
+  p->n_flat = n_flat;
+  p->visible_pairs = pairs;
+  p->max_pos = static_cast<int32_t>(max_pos);
+
+  // ancestor-or-self chains, root first (depth = chain length)
+  std::vector<int32_t> depth(n, 0);
+  for (int32_t node : p->dfs_order) depth[node] = parent[node] < 0 ? 1 : depth[parent[node]] + 1;
+  p->anc_ptr.assign(n + 1, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t next = int64_t(p->anc_ptr[i]) + depth[i];
+    if (next > kI32Max) return TA_ERANGE;
+    p->anc_ptr[i + 1] = static_cast<int32_t>(next);
+  }
+  p->anc.resize(p->anc_ptr[n]);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t w = p->anc_ptr[i + 1];
+    for (int32_t a = i; a >= 0; a = parent[a]) p->anc[--w] = a;
+  }
+
+  // forward tiles: union of visible node segments, packed into key chunks
+  const int32_t BM = p->block_m, BN = p->block_n;
+  const int32_t n_qt = (N + BM - 1) / BM;
+  p->n_qtiles = n_qt;
+  p->fq_ptr.assign(n_qt + 1, 0);
+  std::vector<int32_t> stamp(n, -1);
+  std::vector<Segment> segs;
+  int64_t comp_fwd = 0;
+  for (int32_t t = 0; t < n_qt; ++t) {
+    const int32_t q0 = t * BM, q1 = std::min(N, q0 + BM);
+    segs.clear();
+    for (int32_t i = q0; i < q1;) {
+      const int32_t b = p->node_of[i];
+      const int32_t b_end = p->node_start[b] + seg_len[b];
+      const int32_t last = std::min(b_end, q1);  // rows [i, last) belong to b
+      for (int32_t a = b; a >= 0 && stamp[a] != t; a = parent[a]) {
+        stamp[a] = t;
+        const int32_t k0 = p->node_start[a];
+        const int32_t k1 = (a == b) ? last : k0 + seg_len[a];
+        if (k1 > k0) {
+          // keys <= q0 of a node whose DFS interval holds every row of the tile
+          // are read by every row; the rest needs the element mask
+          const int32_t kend = p->node_sub_end[a];
+          const int32_t split = (q1 <= kend) ? std::min(k1, q0 + 1) : k0;
+          if (split > k0) segs.push_back({k0, split, kend, true});
+          if (k1 > split) segs.push_back({std::max(k0, split), k1, kend, false});
+        }
+      }
+      i = last;
+    }
+    std::sort(segs.begin(), segs.end(), [](const Segment& x, const Segment& y) { return x.k0 < y.k0; });
+
+    int32_t ch[TA_CHUNK_INTS];
+    int32_t nseg = 0, nkeys = 0;
+    bool full = true;
+    auto reset = [&]() {
+      nseg = 0;
+      nkeys = 0;
+      full = true;
+      for (int s = 0; s < TA_CHUNK_MAX_SEG; ++s) {
+        ch[4 + s] = 0;
+        ch[8 + s] = BN;
+        ch[12 + s] = 0;
+      }
+    };
+    auto flush = [&]() {
+      if (nkeys == 0) return;
+      ch[0] = nseg;
+      ch[1] = nkeys;
+      ch[2] = (full && nkeys == BN) ? 1 : 0;
+      ch[3] = 0;
+      if (nseg < TA_CHUNK_MAX_SEG) {
+        for (int s = nseg; s < TA_CHUNK_MAX_SEG; ++s) ch[4 + s] = ch[4];
+      }
+      p->fq_chunk.insert(p->fq_chunk.end(), ch, ch + TA_CHUNK_INTS);
+      comp_fwd += int64_t(q1 - q0) * BN;
+      reset();
+    };
+    reset();
+    for (const Segment& sg : segs) {
+      int32_t k = sg.k0;
+      while (k < sg.k1) {
+        if (nkeys == BN || nseg == TA_CHUNK_MAX_SEG) flush();
+        const int32_t take = std::min(sg.k1 - k, BN - nkeys);
+        ch[4 + nseg] = k;
+        ch[8 + nseg] = nkeys;
+        ch[12 + nseg] = sg.kend;
+        full = full && sg.full;
+        ++nseg;
+        nkeys += take;
+        k += take;
+      }
+    }
+    flush();
+    const int64_t nch = int64_t(p->fq_chunk.size()) / TA_CHUNK_INTS;
+    if (nch * TA_CHUNK_INTS > kI32Max) return TA_ERANGE;
+    p->fq_ptr[t + 1] = static_cast<int32_t>(nch);
+  }
+  p->n_chunks = p->fq_ptr[n_qt];
+  p->computed_pairs_fwd = comp_fwd;
+
+  // longest chunk lists first (stable), so the tail of the grid is short work
+  p->fq_order.resize(n_qt);
+  std::iota(p->fq_order.begin(), p->fq_order.end(), 0);
+  std::stable_sort(p->fq_order.begin(), p->fq_order.end(), [&](int32_t x, int32_t y) {
+    return (p->fq_ptr[x + 1] - p->fq_ptr[x]) > (p->fq_ptr[y + 1] - p->fq_ptr[y]);
+  });
+
+  // backward key tiles, most work first
+  const int32_t BK = p->block_kv;
+  struct KT {
+    int32_t k0, klen, qe, node;
+    int64_t work;
+  };
+  std::vector<KT> kts;
+  int64_t comp_bwd = 0;
+  for (int32_t node : p->dfs_order) {
+    const int32_t s = p->node_start[node], e = s + seg_len[node], qe = p->node_sub_end[node];
+    for (int32_t k0 = s; k0 < e; k0 += BK) {
+      const int32_t kl = std::min(BK, e - k0);
+      const int64_t rows = qe - k0;
+      kts.push_back({k0, kl, qe, node, int64_t(kl) * rows});
+      comp_bwd += int64_t(BK) * ((rows + BK - 1) / BK) * BK;
+    }
+  }
+  std::stable_sort(kts.begin(), kts.end(), [](const KT& x, const KT& y) { return x.work > y.work; });
+  if (int64_t(kts.size()) * 4 > kI32Max) return TA_ERANGE;
+  p->n_ktiles = static_cast<int32_t>(kts.size());
+  p->bk.resize(kts.size() * 4);
+  for (size_t i = 0; i < kts.size(); ++i) {
+    p->bk[4 * i + 0] = kts[i].k0;
+    p->bk[4 * i + 1] = kts[i].klen;
+    p->bk[4 * i + 2] = kts[i].qe;
+    p->bk[4 * i + 3] = kts[i].node;
+  }
+  p->computed_pairs_bwd = comp_bwd;
+
+  // device image: pos | fq_ptr | fq_chunk | fq_order | bk, each 256-aligned
+  size_t off = 0;
+  p->off_pos = off;
+  off = align256(off + sizeof(int32_t) * size_t(std::max(N, 1)));
+  p->off_fq_ptr = off;
+  off = align256(off + sizeof(int32_t) * p->fq_ptr.size());
+  p->off_fq_chunk = off;
+  off = align256(off + sizeof(int32_t) * std::max<size_t>(p->fq_chunk.size(), 1));
+  p->off_fq_order = off;
+  off = align256(off + sizeof(int32_t) * std::max<size_t>(p->fq_order.size(), 1));
+  p->off_bk = off;
+  off = align256(off + sizeof(int32_t) * std::max<size_t>(p->bk.size(), 1));
+  p->device_bytes = off;
+  return TA_OK;
+}
+
+}  // namespace
+
+extern "C" ta_status tree_plan(const int32_t* parent, const int32_t* seg_len, int32_t n_nodes,
+                               int32_t block_m, int32_t block_n, ta_plan** out) {
+  if (!out) return TA_EINVAL;
+  *out = nullptr;
+  if (!parent || !seg_len || n_nodes <= 0) return TA_EINVAL;
+  if ((block_m != 0 && block_m != TA_BLOCK_M) || (block_n != 0 && block_n != TA_BLOCK_N))
+    return TA_EUNSUPPORTED;
+  for (int32_t i = 0; i < n_nodes; ++i) {
+    if (seg_len[i] < 0 || parent[i] < -1 || parent[i] >= n_nodes) return TA_EINVAL;
+    if (parent[i] == i) return TA_ECYCLE;
+  }
+  ta_plan* p = new (std::nothrow) ta_plan();
+  if (!p) return TA_ENOMEM;
+  ta_status st;
+  try {
+    st = build(parent, seg_len, n_nodes, p);
+  } catch (const std::bad_alloc&) {
+    st = TA_ENOMEM;
+  }
+  if (st != TA_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
+  return TA_OK;
+}
+
+extern "C" ta_status tree_plan_view(const ta_plan* p, ta_plan_view* v) {
+  if (!p || !v) return TA_EINVAL;
+  std::memset(v, 0, sizeof(*v));
+  v->n_nodes = p->n_nodes;
+  v->n_tokens = p->n_tokens;
+  v->n_leaves = p->n_leaves;
+  v->max_pos = p->max_pos;
+  v->block_m = p->block_m;
+  v->block_n = p->block_n;
+  v->block_kv = p->block_kv;
+  v->n_qtiles = p->n_qtiles;
+  v->n_chunks = p->n_chunks;
+  v->n_ktiles = p->n_ktiles;
+  v->n_flat = p->n_flat;
+  v->visible_pairs = p->visible_pairs;
+  v->computed_pairs_fwd = p->computed_pairs_fwd;
+  v->computed_pairs_bwd = p->computed_pairs_bwd;
+  v->dfs_order = p->dfs_order.data();
+  v->node_start = p->node_start.data();
+  v->node_sub_end = p->node_sub_end.data();
+  v->pos = p->pos.data();
+  v->g = p->g.data();
+  v->node_of = p->node_of.data();
+  v->sub_end = p->sub_end.data();
+  v->anc_ptr = p->anc_ptr.data();
+  v->anc = p->anc.data();
+  v->fq_ptr = p->fq_ptr.data();
+  v->fq_chunk = p->fq_chunk.data();
+  v->fq_order = p->fq_order.data();
+  v->bk = p->bk.data();
+  return TA_OK;
+}
+
+extern "C" ta_status tree_plan_device_bytes(const ta_plan* p, size_t* bytes) {
+  if (!p || !bytes) return TA_EINVAL;
+  *bytes = p->device_bytes;
+  return TA_OK;
+}
+
+extern "C" void tree_plan_free(ta_plan* p) { delete p; }
+
+extern "C" const char* ta_status_string(ta_status s) {
+  switch (s) {
+    case TA_OK: return "ok";
+    case TA_EINVAL: return "invalid argument";
+    case TA_ECYCLE: return "parent pointers contain a cycle";
+    case TA_ERANGE: return "size exceeds the int32 index range";
+    case TA_ENOMEM: return "out of memory or buffer too small";
+    case TA_EUNSUPPORTED: return "unsupported configuration";
+    case TA_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}

@@ -1,0 +1,81 @@
+"""The built library loads without a GPU and exports every call that
+include/tree_attn.h declares; argument validation that happens before any
+launch is checked without touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import prefix_shared_masked_amd as pkg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_attn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:ta_status|void|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("tree_plan", "tree_plan_view", "tree_plan_device_bytes", "tree_plan_upload", "tree_plan_free",
+              "tree_attn_ws_bytes", "tree_attn_fwd", "tree_attn_bwd", "tree_nll_ws_bytes", "tree_weighted_nll",
+              "tree_decode_ws_bytes", "tree_decode_splitkv", "ta_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = pkg.load_library()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", pkg.library_path()], capture_output=True, text=True)
+    if out.returncode == 0:
+        exported = {line.split()[-1] for line in out.stdout.splitlines() if line.strip()}
+        for n in declared_functions():
+            assert n in exported, n
+
+
+def test_status_strings():
+    L = pkg.load_library()
+    for code in range(7):
+        assert L.ta_status_string(code)
+    assert L.ta_status_string(99) == b"unknown status"
+
+
+def test_validation_before_launch():
+    """Calls that are invalid on their face return before touching a device."""
+    L = pkg.load_library()
+    plan = pkg.tree_plan([-1], [8])
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first
+    # null dplan
+    assert L.tree_attn_fwd(plan.handle, None, 1, fake, fake, fake, 4, 2, 128, 0.0, 0.0, fake, fake, None, 0,
+                           None) == 1
+    # Hq not a multiple of Hkv
+    assert L.tree_attn_fwd(plan.handle, fake, 1, fake, fake, fake, 3, 2, 128, 0.0, 0.0, fake, fake, None, 0,
+                           None) == 1
+    # bf16 needs d = 128; fp32 takes 64 or 128
+    assert L.tree_attn_fwd(plan.handle, fake, 1, fake, fake, fake, 4, 2, 64, 0.0, 0.0, fake, fake, None, 0,
+                           None) == 5
+    assert L.tree_attn_fwd(plan.handle, fake, 0, fake, fake, fake, 4, 2, 96, 0.0, 0.0, fake, fake, None, 0,
+                           None) == 5
+    # RoPE needs a workspace
+    assert L.tree_attn_fwd(plan.handle, fake, 1, fake, fake, fake, 4, 2, 128, 0.0, 10000.0, fake, fake, None, 0,
+                           None) == 4
+    assert L.tree_attn_bwd(plan.handle, fake, 1, fake, fake, fake, fake, fake, fake, 4, 2, 128, 0.0, 0.0, fake,
+                           fake, fake, None, 0, None) == 4
+    assert L.tree_weighted_nll(1, fake, fake, fake, 4, 8, -100, fake, None, None, fake, 1 << 20, None) == 5
+    assert L.tree_weighted_nll(0, fake, fake, fake, 4, 8, -100, fake, None, None, None, 0, None) == 4
+    assert L.tree_decode_splitkv(1, fake, fake, fake, fake, fake, 2, 4, 2, 64, 100, 0.0, 0, fake, fake, fake,
+                                 1 << 20, None) == 5
+    assert L.tree_decode_splitkv(1, fake, fake, fake, fake, fake, 2, 4, 2, 128, 100, 0.0, 0, fake, fake, None, 0,
+                                 None) == 4
+    n = ctypes.c_size_t()
+    s = ctypes.c_int32()
+    assert L.tree_decode_ws_bytes(8, 32, 128, 262144, 0, ctypes.byref(n), ctypes.byref(s)) == 0
+    assert 1 <= s.value <= 120 and n.value >= 8 * 32 * s.value * 130 * 4
+    assert L.tree_attn_ws_bytes(plan.handle, 2, 1, 4, 2, 128, 0.0, ctypes.byref(n)) == 1

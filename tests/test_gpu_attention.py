@@ -1,0 +1,149 @@
+"""GPU parity of tree_attn_fwd / tree_attn_bwd against the float64 oracle.
+
+Tolerances: fp32 path 1e-5 absolute; bf16 path |gpu - oracle| <= 2e-2 +
+1e-2 |oracle| elementwise.  bf16 inputs are rounded once on the host and the
+oracle sees exactly the rounded values, so input quantisation is not error.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefix_shared_masked_amd as pkg
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+ATOL_BF16, RTOL_BF16, ATOL_F32 = 2e-2, 1e-2, 1e-5
+
+
+def to_dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype)
+    return t, t.float().cpu().double().numpy()
+
+
+def close(name, got, ref, dtype, where=""):
+    got = got.float().cpu().double().numpy() if torch.is_tensor(got) else got
+    err = np.abs(got - ref)
+    if dtype == torch.float32:
+        bad = err > ATOL_F32
+    else:
+        bad = err > ATOL_BF16 + RTOL_BF16 * np.abs(ref)
+    assert not bad.any(), (f"{name}{where}: {int(bad.sum())} of {bad.size} outside tolerance, "
+                           f"max err {float(err.max()):.3e}")
+
+
+def run_case(tree, Hq, Hkv, d, dtype, rope, seed=0, grads=True, heads=None):
+    print(f"[case] {tree.name or 'tree'} N={tree.n_tokens} Hq={Hq} Hkv={Hkv} d={d} {dtype} rope={rope}",
+          flush=True)
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    q, k, v, do = W.attention_inputs(seed, plan.n_tokens, Hq, Hkv, d)
+    (Q, q64), (K, k64), (V, v64), (DO, do64) = (to_dev(x, dtype) for x in (q, k, v, do))
+    o, lse = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=rope)
+    res = dict(o=o, lse=lse)
+    if grads:
+        dq, dk, dv = pkg.tree_attn_bwd(plan, Q, K, V, o, lse, DO, rope_base=rope)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = oracle.per_path_attention(op, q64, k64, v64, rope_base=rope, dO=do64 if grads else None)
+    for name in res:
+        close(name, res[name], ref[name], dtype)
+    return plan, res, ref
+
+
+def test_six_node_fp32_with_and_without_rope():
+    for rope in (0.0, 10000.0):
+        run_case(W.six_node_tree(16), 1, 1, 64, torch.float32, rope)
+
+
+def test_fp32_random_trees_gqa():
+    rng = np.random.default_rng(1)
+    for c in range(4):
+        t = W.random_tree(rng, int(rng.integers(3, 12)), max_len=50, p_zero=0.1, n_roots=1 + c % 2)
+        run_case(t, 4, 2, 128, torch.float32, 10000.0, seed=c)
+
+
+def _small_trees():
+    rng = np.random.default_rng(7)
+    yield W.six_node_tree(16)
+    yield W.Tree(np.array([-1, 0, 0, 1], np.int32), np.array([129, 1, 15, 17], np.int32), "edges")
+    yield W.Tree(np.array([-1] + [0] * 64, np.int32), np.array([40] + [7] * 64, np.int32), "star64")
+    yield W.Tree(np.array([-1] * 5, np.int32), np.array([1, 64, 65, 127, 33], np.int32), "forest")
+    yield W.Tree(np.array([-1] + list(range(39)), np.int32), np.array([5] * 40, np.int32), "chain40")
+    yield W.spine_tree(64, 16, 24, 6)
+    for c in range(3):
+        yield W.random_tree(rng, int(rng.integers(5, 30)), max_len=90, p_zero=0.15, n_roots=1 + c % 3)
+
+
+@pytest.mark.parametrize("heads", [(8, 2), (4, 4), (16, 2), (4, 2)])
+def test_bf16_small_trees(heads):
+    Hq, Hkv = heads
+    for i, t in enumerate(_small_trees()):
+        run_case(t, Hq, Hkv, 128, torch.bfloat16, 10000.0 if i % 2 == 0 else 0.0, seed=i)
+
+
+def test_bf16_deterministic_and_sibling_leak():
+    """Same inputs -> bitwise-identical gradients; editing one branch leaves
+    the other branch's outputs bit-for-bit unchanged (leak test of the Tree
+    Training post, section 14.2)."""
+    t = W.six_node_tree(48)
+    plan = pkg.tree_plan(t.parent, t.seg_len)
+    view = plan.view()
+    q, k, v, do = W.attention_inputs(3, plan.n_tokens, 8, 2, 128)
+    Q, K, V, DO = (torch.from_numpy(x).to(DEV).bfloat16() for x in (q, k, v, do))
+    o1, l1 = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=10000.0)
+    g1 = pkg.tree_attn_bwd(plan, Q, K, V, o1, l1, DO, rope_base=10000.0)
+    o2, l2 = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=10000.0)
+    g2 = pkg.tree_attn_bwd(plan, Q, K, V, o2, l2, DO, rope_base=10000.0)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    node_of = view["node_of"]
+    branch = torch.from_numpy(np.isin(node_of, [1, 3, 4])).to(DEV)
+    other = torch.from_numpy(np.isin(node_of, [0, 2, 5])).to(DEV)
+    K2, V2, Q2 = K.clone(), V.clone(), Q.clone()
+    K2[branch] += 1.0
+    V2[branch] -= 0.5
+    Q2[branch] *= -1
+    o3, l3 = pkg.tree_attn_fwd(plan, Q2, K2, V2, rope_base=10000.0)
+    assert torch.equal(o3[other], o1[other]) and torch.equal(l3[:, other], l1[:, other])
+    assert not torch.equal(o3[branch], o1[branch])
+
+
+def _group_check(tree, seed, heads=(0, 1, 2, 3), rows_sample=64):
+    """Full-size parity for one KV group (query heads 0-3 share KV head 0):
+    O/LSE/dQ of those heads and dK/dV of KV head 0 against the dense-mask
+    oracle restricted to those heads; O/LSE of other heads on sampled rows."""
+    Hq, Hkv, d = 32, 8, 128
+    print(f"[full] {tree.name} N={tree.n_tokens}", flush=True)
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    q, k, v, do = W.attention_inputs(seed, plan.n_tokens, Hq, Hkv, d)
+    (Q, q64), (K, k64), (V, v64), (DO, do64) = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    o, lse = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=10000.0)
+    dq, dk, dv = pkg.tree_attn_bwd(plan, Q, K, V, o, lse, DO, rope_base=10000.0)
+    torch.cuda.synchronize()
+    hs = list(heads)
+    ref = oracle.dense_mask_attention(op, q64, k64, v64, rope_base=10000.0, dO=do64, heads=hs)
+    close("o", o[:, hs], ref["o"][:, hs], torch.bfloat16)
+    close("lse", lse[hs], ref["lse"][hs], torch.bfloat16)
+    close("dq", dq[:, hs], ref["dq"][:, hs], torch.bfloat16)
+    close("dk", dk[:, 0], ref["dk"][:, 0], torch.bfloat16)
+    close("dv", dv[:, 0], ref["dv"][:, 0], torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.integers(0, plan.n_tokens, rows_sample), [0, plan.n_tokens - 1]]))
+    other = [5, 17, 31]
+    ro, rl = oracle.rows_attention(op, q64, k64, v64, rows, other, rope_base=10000.0)
+    close("o(sampled)", o[rows][:, other], ro, torch.bfloat16)
+    close("lse(sampled)", lse[other][:, rows], rl, torch.bfloat16)
+
+
+@pytest.mark.timeout(600)
+def test_spine_full_size():
+    _group_check(W.spine_tree(), 0)
+
+
+@pytest.mark.timeout(600)
+def test_random_agentic_full_size():
+    _group_check(W.random_agentic_tree(0), 1)

@@ -1,0 +1,89 @@
+"""GPU parity of tree_weighted_nll and tree_decode_splitkv against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefix_shared_masked_amd as pkg
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("N,V", [(96, 256), (4, 151936), (33, 1000), (1, 1)])
+def test_nll_matches_oracle(N, V):
+    print(f"[nll] N={N} V={V}", flush=True)
+    logits, labels = W.nll_inputs(N + V, N, V)
+    w = np.random.default_rng(N).random(N).astype(np.float32)
+    loss, dl, err = pkg.tree_weighted_nll(*(torch.from_numpy(x).to(DEV) for x in (logits, labels, w)))
+    rl, rdl, _ = oracle.weighted_nll(logits, labels, w)
+    assert abs(loss.item() - rl) <= 1e-5 * max(1.0, abs(rl))
+    assert float(np.abs(dl.cpu().numpy() - rdl).max()) <= 1e-6
+    assert int(err.item()) == 0
+
+
+def test_nll_six_node_weights_and_bad_label():
+    t = W.six_node_tree(16)
+    plan = pkg.tree_plan(t.parent, t.seg_len)
+    op = oracle.oracle_plan(t.parent, t.seg_len)
+    logits, labels = W.nll_inputs(0, plan.n_tokens, 256)
+    w = (plan.view()["g"] / plan.n_leaves).astype(np.float32)
+    loss, dl, err = pkg.tree_weighted_nll(*(torch.from_numpy(x).to(DEV) for x in (logits, labels, w)))
+    _, _, tok = oracle.weighted_nll(logits, labels, w)
+    assert loss.item() == pytest.approx(oracle.per_path_loss(op, tok), rel=1e-5)
+    labels[3] = 999                         # outside [0, V): flagged, contributes 0
+    loss2, dl2, err2 = pkg.tree_weighted_nll(*(torch.from_numpy(x).to(DEV) for x in (logits, labels, w)))
+    assert int(err2.item()) == 1
+    assert not dl2[3].any()
+    labels[3] = -100
+    loss3, _, err3 = pkg.tree_weighted_nll(*(torch.from_numpy(x).to(DEV) for x in (logits, labels, w)))
+    assert loss3.item() == pytest.approx(loss2.item(), rel=1e-6) and int(err3.item()) == 0
+    l4, d4, _ = pkg.tree_weighted_nll(*(torch.from_numpy(x).to(DEV) for x in (logits, labels, w)), need_grad=False)
+    assert d4 is None and l4.item() == pytest.approx(loss3.item(), rel=1e-6)
+
+
+def _decode_case(lens, Hq, Hkv, n_splits, seed, multi_span=False, gap=3):
+    print(f"[decode] lens={lens} Hq={Hq} Hkv={Hkv} splits={n_splits}", flush=True)
+    B, d = len(lens), 128
+    if multi_span:   # each item reads two or three disjoint spans (a leaf's ancestor chain)
+        rng = np.random.default_rng(seed)
+        ptr, sp, off = [0], [], 0
+        for n in lens:
+            cuts = np.sort(rng.choice(np.arange(1, n), size=min(2, n - 1), replace=False)) if n > 2 else []
+            bounds = [0, *cuts, n]
+            for a, b in zip(bounds[:-1], bounds[1:]):
+                sp.append((off + a + 5 * len(sp), b - a))
+            ptr.append(len(sp))
+            off += n + 5 * len(sp) + gap
+        span_ptr, spans, L = np.array(ptr, np.int32), np.array(sp, np.int32), off + 16
+    else:
+        span_ptr, spans, L = W.decode_spans(lens, gap=gap)
+    q = W.normal(seed, (B, Hq, d))
+    k = W.normal(seed + 1, (L, Hkv, d))
+    v = W.normal(seed + 2, (L, Hkv, d))
+    Q, K, V = (torch.from_numpy(x).to(DEV).bfloat16() for x in (q, k, v))
+    o, lse = pkg.tree_decode_splitkv(Q, K, V, torch.from_numpy(span_ptr).to(DEV),
+                                     torch.from_numpy(spans).to(DEV), max(lens), n_splits=n_splits)
+    ro, rl = oracle.decode_attention(*(t.float().cpu().double().numpy() for t in (Q, K, V)), span_ptr, spans)
+    err = np.abs(o.float().cpu().numpy() - ro)
+    assert (err <= 2e-2 + 1e-2 * np.abs(ro)).all(), float(err.max())
+    assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("n_splits", [0, 1, 3, 7, 64])
+def test_decode_small(n_splits):
+    _decode_case([1, 37, 200, 1000], 32, 8, n_splits, 0)
+
+
+def test_decode_multi_span_and_gqa_shapes():
+    _decode_case([5, 300, 64, 2], 8, 2, 0, 1, multi_span=True)
+    _decode_case([100, 3], 16, 2, 5, 2)        # 8 query heads per KV head: two head groups
+    _decode_case([77], 2, 2, 2, 3)             # one query head per KV head
+
+
+@pytest.mark.timeout(600)
+def test_decode_32k_full_batch():
+    """One of the decode workloads at full size: B = 8 items of 32K keys,
+    32 query / 8 KV heads; checks every (item, head) against the oracle."""
+    _decode_case([32768] * 8, 32, 8, 0, 4, gap=0)

@@ -1,0 +1,165 @@
+"""The C++ planner (through the C ABI, host only) against the oracle plan:
+DFS order, positions, g_t, K, DFS intervals, ancestor chains, visible-key
+sets and full flags of the forward tiles, and the backward key tiles must be
+bit-exact.  Error paths return status codes."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import prefix_shared_masked_amd as pkg
+from prefix_shared_masked_amd import TA_BLOCK_M, TA_BLOCK_N, TA_BLOCK_KV
+import workloads as W
+
+
+def expand_chunks(view, tile):
+    """Keys of a query tile from the gathered chunk table, with each chunk's
+    full flag repeated per key and the DFS-interval end of each key."""
+    keys, full, kend = [], [], []
+    for c in range(view["fq_ptr"][tile], view["fq_ptr"][tile + 1]):
+        ch = view["fq_chunk"][c]
+        nseg, nkeys, fl = int(ch[0]), int(ch[1]), int(ch[2])
+        assert 1 <= nseg <= 4 and 1 <= nkeys <= TA_BLOCK_N
+        for v in range(nkeys):
+            s = max(x for x in range(4) if ch[8 + x] <= v)
+            assert s < nseg
+            keys.append(int(ch[4 + s] + v - ch[8 + s]))
+            kend.append(int(ch[12 + s]))
+            full.append(fl)
+        if fl:
+            assert nkeys == TA_BLOCK_N
+    return np.array(keys, np.int64), np.array(full, bool), np.array(kend, np.int64)
+
+
+def compare(tree):
+    p = pkg.tree_plan(tree.parent, tree.seg_len)
+    v = p.view()
+    o = oracle.oracle_plan(tree.parent, tree.seg_len)
+    assert p.n_tokens == o.n_tokens and p.n_leaves == o.n_leaves
+    assert p.n_flat == o.n_flat and p.visible_pairs == o.visible_pairs
+    assert v["dfs_order"].tolist() == o.dfs_order.tolist()
+    assert v["node_start"].tolist() == o.node_start.tolist()
+    assert v["node_sub_end"].tolist() == o.node_sub_end.tolist()
+    for name in ("pos", "g", "node_of", "sub_end"):
+        assert v[name].tolist() == getattr(o, name).tolist(), name
+    assert p.max_pos == (int(o.pos.max()) if o.n_tokens else -1)
+    for i in range(o.n_nodes):
+        assert v["anc"][v["anc_ptr"][i]:v["anc_ptr"][i + 1]].tolist() == o.anc[i]
+    # forward tiles: same visible keys; a chunk flagged full only if the
+    # oracle says every row reads every one of its keys
+    otiles = oracle.fwd_tile_keys(o, TA_BLOCK_M)
+    assert p.n_qtiles == len(otiles)
+    for t, (okeys, ofull) in enumerate(otiles):
+        keys, full, kend = expand_chunks(v, t)
+        order = np.argsort(keys, kind="stable")
+        assert keys[order].tolist() == okeys.tolist(), t
+        assert not (full[order] & ~ofull).any(), t
+        assert kend.tolist() == o.sub_end[keys].tolist()
+        # a chunk of all-full keys that is itself complete must be flagged
+        for c in range(v["fq_ptr"][t], v["fq_ptr"][t + 1]):
+            ch = v["fq_chunk"][c]
+            ks = [int(ch[4 + s] + x) for s in range(ch[0]) for x in range(
+                (ch[8 + s + 1] if s + 1 < ch[0] else ch[1]) - ch[8 + s])]
+            allfull = all(ofull[np.searchsorted(okeys, kk)] for kk in ks)
+            assert bool(ch[2]) == (allfull and ch[1] == TA_BLOCK_N)
+    # longest chunk lists first
+    counts = np.diff(v["fq_ptr"])
+    assert sorted(v["fq_order"].tolist()) == list(range(p.n_qtiles))
+    assert (np.diff(counts[v["fq_order"]]) <= 0).all()
+    # backward key tiles
+    bk = [tuple(int(x) for x in row[:3]) for row in v["bk"]]
+    assert sorted(bk) == oracle.bwd_tiles(o, TA_BLOCK_KV)
+    work = [kl * (qe - k0) for k0, kl, qe in bk]
+    assert all(a >= b for a, b in zip(work, work[1:]))
+    for row in v["bk"]:
+        assert o.node_of[row[0]] == row[3]
+    return p, o
+
+
+def test_six_node():
+    p, _ = compare(W.six_node_tree(16))
+    assert p.view()["dfs_order"].tolist() == [0, 1, 3, 4, 2, 5]
+    assert p.visible_pairs == 2864
+
+
+def test_spine_full_size():
+    p, o = compare(W.spine_tree())
+    assert (p.n_tokens, p.n_flat, p.n_leaves) == (16352, 129184, 44)
+
+
+def test_random_agentic_tree():
+    compare(W.random_agentic_tree(0))
+
+
+def test_varlen_forest():
+    p, o = compare(W.varlen_forest(0))
+    assert p.n_leaves == 64 and p.n_flat == p.n_tokens
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_small_trees(seed):
+    rng = np.random.default_rng(100 + seed)
+    for c in range(40):
+        shape = ["random", "chain", "star"][c % 3]
+        tree = W.random_tree(rng, int(rng.integers(1, 60)), max_len=int(rng.integers(1, 140)),
+                             p_zero=0.15, n_roots=int(rng.integers(1, 4)), shape=shape)
+        if tree.n_tokens == 0:
+            continue
+        compare(tree)
+
+
+def test_node_lengths_around_tile_edges():
+    for L in (1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129):
+        compare(W.Tree(np.array([-1, 0, 0, 1], np.int32), np.array([L, L, 3, L], np.int32)))
+
+
+def test_star_with_64_children_and_deep_chain():
+    compare(W.Tree(np.array([-1] + [0] * 64, np.int32), np.array([40] + [7] * 64, np.int32)))
+    n = 300
+    compare(W.Tree(np.array([-1] + list(range(n - 1)), np.int32), np.array([3] * n, np.int32)))
+
+
+def test_determinism():
+    t = W.random_agentic_tree(1)
+    a, b = pkg.tree_plan(t.parent, t.seg_len).view(), pkg.tree_plan(t.parent, t.seg_len).view()
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def _status(parent, seg_len, n=None, bm=0, bn=0):
+    L = pkg.load_library()
+    out = ctypes.c_void_p(123)
+    pI32 = ctypes.POINTER(ctypes.c_int32)
+    par = np.ascontiguousarray(parent, np.int32)
+    sl = np.ascontiguousarray(seg_len, np.int32)
+    st = L.tree_plan(par.ctypes.data_as(pI32), sl.ctypes.data_as(pI32), len(par) if n is None else n, bm, bn,
+                     ctypes.byref(out))
+    if st == 0:
+        L.tree_plan_free(out)
+    else:
+        assert not out.value          # *out is NULL on error
+    return st
+
+
+def test_error_codes():
+    assert _status([-1, 0], [1, 1]) == 0
+    assert _status([1, 0], [1, 1]) == 2              # cycle without a root
+    assert _status([-1, 0, 3, 2], [1, 1, 1, 1]) == 2
+    assert _status([-1, 1], [1, 1]) == 2             # self-parent
+    assert _status([-1, 5], [1, 1]) == 1             # parent out of range
+    assert _status([-1, -2], [1, 1]) == 1
+    assert _status([-1, 0], [1, -1]) == 1            # negative length
+    assert _status([-1], [1], n=0) == 1
+    assert _status([-1], [1], bm=16) == 5            # block sizes the kernels are not built for
+    assert _status([-1], [1], bn=128) == 5
+    assert _status([-1, 0], [2 ** 30, 2 ** 30]) == 3  # N overflows int32
+    L = pkg.load_library()
+    assert L.tree_plan(None, None, 1, 0, 0, None) == 1
+    L.tree_plan_free(None)                           # NULL-safe
+    with pytest.raises(pkg.TreeAttnError):
+        pkg.tree_plan([0], [1])
+
+
+def test_zero_token_nodes_only_between():
+    compare(W.Tree(np.array([-1, 0, 1, 0, 3], np.int32), np.array([0, 5, 0, 0, 2], np.int32)))
