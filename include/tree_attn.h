@@ -70,7 +70,8 @@ typedef enum ta_dtype { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
  * exactly these values. */
 #define TA_BLOCK_M 32   /* query rows per forward tile */
 #define TA_BLOCK_N 64   /* key slots per gathered key chunk */
-#define TA_BLOCK_KV 32  /* keys per backward key tile (never crosses a node) */
+#define TA_BLOCK_KV 128 /* keys per backward key tile (never crosses a node) */
+#define TA_KV_SUB 32    /* backward sub-tile: 32 keys against 32-row query blocks */
 #define TA_CHUNK_INTS 16
 #define TA_CHUNK_MAX_SEG 4
 
@@ -111,7 +112,8 @@ typedef struct ta_plan_view {
   const int32_t* fq_ptr;     /* [n_qtiles + 1] chunk range of each query tile */
   const int32_t* fq_chunk;   /* [n_chunks * TA_CHUNK_INTS] gathered key chunks (layout above) */
   const int32_t* fq_order;   /* [n_qtiles] query tiles, most chunks first */
-  const int32_t* bk;         /* [n_ktiles * 4] (k0, klen, q_end, node), most work first */
+  const int32_t* bk;         /* [n_ktiles * 4] (k0, klen, q_end, node), most work first; every
+                                query in [k0, q_end) lies in the node's subtree */
 } ta_plan_view;
 
 /* Build the plan of a prefix tree (host only, synchronous, deterministic).

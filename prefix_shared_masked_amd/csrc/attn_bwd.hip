@@ -15,15 +15,17 @@
 //     chunks.  P is recomputed from LSE; S^T, dP^T and dQ^T are MFMA tiles
 //     with the query on the lane, K^T read with the LDS transpose read.  It
 //     also writes D and an fp16 copy of the rotated Q for step 3;
-//  3. dK/dV, key-stationary: one workgroup per (node-aligned key tile of at
-//     most 32 keys, KV head).  Every query in [k0, kend) of the node's DFS
-//     interval reads every key of the tile (only the diagonal block needs
-//     the causal compare), so Q and dO stream as contiguous row blocks with
-//     no gather.  Scores use the fp16 copies of rotated Q and K (finer
+//  3. dK/dV, key-stationary: one workgroup per (node-aligned tile of at most
+//     128 keys, KV head), one wavefront per 32 keys.  Every query in
+//     [k0, kend) of the node's DFS interval reads every key of the tile
+//     (only a wavefront's diagonal block needs the causal compare), so Q and
+//     dO stream as contiguous 32-row blocks with no gather; each block is
+//     staged in LDS once and shared by the four wavefronts, and the loop runs
+//     over every query head of the GQA group, so the group's sum stays in
+//     registers.  Scores use the fp16 copies of rotated Q and K (finer
 //     rounding than bf16 for rotated values; same MFMA rate), so P matches
 //     the forward's.  K and V stay in registers; dV += P^T dO and
-//     dK += dS^T Q use the LDS transpose read of the streamed blocks.  The
-//     query heads of the GQA group are summed inside the workgroup.
+//     dK += dS^T Q use the LDS transpose read of the staged blocks.
 #include "common.h"
 #include "plan_internal.h"
 
@@ -33,7 +35,6 @@ namespace bwd {
 constexpr int D = 128;
 constexpr int BM = TA_BLOCK_M;
 constexpr int BN = TA_BLOCK_N;
-constexpr int BK = TA_BLOCK_KV;
 constexpr int PK = D + 8;   // row-read friendly pitch
 constexpr int PT = D + 16;  // transpose-read friendly pitch
 
@@ -280,32 +281,51 @@ struct KVParams {
   float scale, scale_log2, rope_base;
 };
 
+constexpr int SUB = TA_KV_SUB;  // keys per wavefront = rows per query block
+
+// One staged query block in LDS: fp16 Q rows (scores), bf16 Q and dO rows
+// (transpose-read operands of dK and dV), and the rows' LSE and D.
+struct KVStageLayout {
+  static constexpr int Q16 = 0;                                 // f16 [SUB][PK]
+  static constexpr int QB = Q16 + SUB * PK * 2;                 // bf16 [SUB][PT]
+  static constexpr int DO = QB + SUB * PT * 2;                  // bf16 [SUB][PT]
+  static constexpr int LS = DO + SUB * PT * 2;                  // float [SUB]
+  static constexpr int DD = LS + SUB * 4;                       // float [SUB]
+  static constexpr int BYTES = DD + SUB * 4;
+};
+
+struct KVLoad {
+  uint4 q[2], d[2];
+  float x;
+};
+
 __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
-  constexpr int WAVE_LDS = 2 * BK * PT;  // Q block + dO block per wavefront
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * WAVE_LDS];
-  static_assert(sizeof(smem) >= 4 * BK * D * sizeof(float), "reduction buffer must fit");
+  using L = KVStageLayout;
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::BYTES];
 
   const int kvh = blockIdx.x % P.Hkv;
   const int32_t* tl = P.bk + (size_t)(blockIdx.x / P.Hkv) * 4;
   const int k0 = tl[0], klen = tl[1], qe = tl[2];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int col = lane & 31, half = lane >> 5;
-  const bool kvalid = col < klen;
-  bf16* sQ = smem + wave * WAVE_LDS;
-  bf16* sDO = sQ + BK * PT;
+  const int kw = k0 + SUB * wave;                 // this wavefront's first key
+  const int wkeys = max(0, min(SUB, klen - SUB * wave));
+  const bool kvalid = col < wkeys;
+  const int key = kw + col;
 
+  // K (fp16) and V as B operands: lane = key column, k-slots s*16 + half*8 + e
   f16x8 kf[8];
   bf16x8 vf[8];
   {
-    const size_t off = ((size_t)(kvalid ? k0 + col : k0) * P.Hkv + kvh) * D + half * 8;
+    const size_t off = ((size_t)(kvalid ? key : k0) * P.Hkv + kvh) * D + half * 8;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const f16x8 a = *(const f16x8*)(P.k + off + s * 16);
-      const bf16x8 b = *(const bf16x8*)(P.v + off + s * 16);
+      const bf16x8 c = *(const bf16x8*)(P.v + off + s * 16);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         kf[s][e] = kvalid ? a[e] : (f16)0.f;
-        vf[s][e] = kvalid ? b[e] : (bf16)0.f;
+        vf[s][e] = kvalid ? c[e] : (bf16)0.f;
       }
     }
   }
@@ -317,54 +337,94 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   }
   const int trow = half * 4 + ((lane & 15) >> 2);
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  const int key = k0 + col;
 
-  for (int hs = wave; hs < P.G; hs += 4) {
-    const int h = kvh * P.G + hs;
-    const float* lse_h = P.lse + (size_t)h * P.N;
-    const float* D_h = P.Dd + (size_t)h * P.N;
-    for (int qb = k0; qb < qe; qb += BK) {
-      const int qrow = qb + col;
-      const bool rvalid = qrow < qe;
-      const size_t roff = ((size_t)(rvalid ? qrow : qb) * P.Hq + h) * D + half * 8;
-      f16x8 qa[8];
-      bf16x8 da[8];
+  // Items are (query head, 32-row block); all four wavefronts share each
+  // staged block.  Thread t loads 32 bytes of Q and of dO of row t/8 and, for
+  // t < 64, one LSE (t < 32) or D value.  Rows past the query range stage as
+  // zeros (LSE = D = 0), so they contribute exactly nothing.
+  const int nblk = (qe - k0 + SUB - 1) / SUB;
+  const int nitem = P.G * nblk;
+  const int lrow = t >> 3, lpart = (t & 7) * 16;
+  auto fetch = [&](int it, KVLoad& ld) {
+    const int h = kvh * P.G + it / nblk;
+    const int qb = k0 + SUB * (it % nblk);
+    const int row = qb + lrow;
+    const bool rv = row < qe;
+    const size_t roff = ((size_t)(rv ? row : qb) * P.Hq + h) * D + lpart;
+    const uint4 z = {0u, 0u, 0u, 0u};
+    ld.q[0] = rv ? *(const uint4*)(P.q + roff) : z;
+    ld.q[1] = rv ? *(const uint4*)(P.q + roff + 8) : z;
+    ld.d[0] = rv ? *(const uint4*)(P.dO + roff) : z;
+    ld.d[1] = rv ? *(const uint4*)(P.dO + roff + 8) : z;
+    ld.x = 0.f;
+    if (t < 2 * SUB) {
+      const int r = qb + (t & (SUB - 1));
+      if (r < qe) ld.x = t < SUB ? P.lse[(size_t)h * P.N + r] * TA_LOG2E : P.Dd[(size_t)h * P.N + r];
+    }
+  };
+  auto stage = [&](const KVLoad& ld, char* base) {
+    f16* q16 = (f16*)(base + L::Q16);
+    bf16* qbf = (bf16*)(base + L::QB);
+    bf16* dob = (bf16*)(base + L::DO);
+    *(uint4*)(q16 + lrow * PK + lpart) = ld.q[0];
+    *(uint4*)(q16 + lrow * PK + lpart + 8) = ld.q[1];
+    *(uint4*)(dob + lrow * PT + lpart) = ld.d[0];
+    *(uint4*)(dob + lrow * PT + lpart + 8) = ld.d[1];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 a = *(const f16x8*)(P.q + roff + s * 16);
-        const bf16x8 b = *(const bf16x8*)(P.dO + roff + s * 16);
+    for (int u = 0; u < 2; ++u) {
+      const f16x8 h8 = *(const f16x8*)&ld.q[u];
+      bf16x8 b8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qa[s][e] = rvalid ? a[e] : (f16)0.f;
-          da[s][e] = rvalid ? b[e] : (bf16)0.f;
-        }
-      }
-      wave_lds_sync();  // previous block's transpose reads are done
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        bf16x8 qb;  // bf16 copy of Q for dK = dS^T Q
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qb[e] = (bf16)(float)qa[s][e];
-        *(bf16x8*)(sQ + col * PT + s * 16 + half * 8) = qb;
-        *(bf16x8*)(sDO + col * PT + s * 16 + half * 8) = da[s];
-      }
+      for (int e = 0; e < 8; ++e) b8[e] = (bf16)(float)h8[e];
+      *(bf16x8*)(qbf + lrow * PT + lpart + 8 * u) = b8;
+    }
+    if (t < 2 * SUB) ((float*)(base + (t < SUB ? L::LS : L::DD)))[t & (SUB - 1)] = ld.x;
+  };
+
+  KVLoad ld;
+  if (nitem > 0) {
+    fetch(0, ld);
+    stage(ld, smem);
+  }
+  __syncthreads();
+  for (int it = 0; it < nitem; ++it) {
+    const int buf = it & 1;
+    const int qb = k0 + SUB * (it % nblk);
+    if (it + 1 < nitem) fetch(it + 1, ld);
+    char* base = smem + buf * L::BYTES;
+    // blocks that end before this wavefront's first key see none of its keys
+    if (wkeys > 0 && qb + SUB > kw) {
+      const f16* q16 = (const f16*)(base + L::Q16);
+      const bf16* qbf = (const bf16*)(base + L::QB);
+      const bf16* dob = (const bf16*)(base + L::DO);
+      const float* ls = (const float*)(base + L::LS);
+      const float* dd = (const float*)(base + L::DD);
       f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        S = mfma32h(qa[s], kf[s], S);
-        dP = mfma32(da[s], vf[s], dP);
+        const f16x8 a = *(const f16x8*)(q16 + col * PK + s * 16 + half * 8);
+        const bf16x8 c = *(const bf16x8*)(dob + col * PT + s * 16 + half * 8);
+        S = mfma32h(a, kf[s], S);
+        dP = mfma32(c, vf[s], dP);
       }
-      // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key k0 + col
+      // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col
+      float lr[16], dr[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = qb + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = kvalid && row < qe && key <= row;
-        const float lr = vis ? lse_h[row] : 0.f;
-        const float dr = vis ? D_h[row] : 0.f;
-        const float p = vis ? exp2f_fast(S[r] * P.scale_log2 - lr * TA_LOG2E) : 0.f;
-        S[r] = p;
-        dP[r] = p * (dP[r] - dr);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 a = *(const float4*)(ls + 8 * r4 + 4 * half);
+        const float4 c = *(const float4*)(dd + 8 * r4 + 4 * half);
+        lr[4 * r4] = a.x, lr[4 * r4 + 1] = a.y, lr[4 * r4 + 2] = a.z, lr[4 * r4 + 3] = a.w;
+        dr[4 * r4] = c.x, dr[4 * r4 + 1] = c.y, dr[4 * r4 + 2] = c.z, dr[4 * r4 + 3] = c.w;
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = exp2f_fast(S[r] * P.scale_log2 - lr[r]);
+      if (qb == kw) {  // diagonal block: key <= row
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key > qb + 8 * (r >> 2) + 4 * half + (r & 3)) S[r] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dP[r] = S[r] * (dP[r] - dr[r]);
       bf16x8 pa[2], sa[2];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -373,60 +433,47 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
         sa[0][e] = (bf16)dP[e];
         sa[1][e] = (bf16)dP[8 + e];
       }
-      wave_lds_sync();  // this block's rows are in LDS
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
-          const bf16x4 d0 = lds_read_tr(sDO + (qs * 16 + trow) * PT + dt * 32 + tcol);
-          const bf16x4 d1 = lds_read_tr(sDO + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol);
+          const bf16x4 d0 = lds_read_tr(dob + (qs * 16 + trow) * PT + dt * 32 + tcol);
+          const bf16x4 d1 = lds_read_tr(dob + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol);
           dv[dt] = mfma32(pa[qs], cat(d0, d1), dv[dt]);
-          const bf16x4 q0 = lds_read_tr(sQ + (qs * 16 + trow) * PT + dt * 32 + tcol);
-          const bf16x4 q1 = lds_read_tr(sQ + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol);
+          const bf16x4 q0 = lds_read_tr(qbf + (qs * 16 + trow) * PT + dt * 32 + tcol);
+          const bf16x4 q1 = lds_read_tr(qbf + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol);
           dk[dt] = mfma32(sa[qs], cat(q0, q1), dk[dt]);
         }
     }
+    if (it + 1 < nitem) stage(ld, smem + (buf ^ 1) * L::BYTES);
+    __syncthreads();
   }
 
-  // Sum the wavefronts' partials (the GQA heads) through LDS, then rotate dK
-  // back and store.  Accumulator register r of tile dt <-> key 8*(r/4) +
-  // 4*half + r%4, d = dt*32 + col.
-  float* red = (float*)smem;
-  for (int pass = 0; pass < 2; ++pass) {
-    __syncthreads();
-    f32x16* src = pass == 0 ? dk : dv;
+  // Each wavefront owns its keys: scale and rotate dK back, store dK and dV.
+  // Accumulator register r of tile dt <-> key kw + 8*(r/4) + 4*half + r%4,
+  // d = dt*32 + col; the rotate-half partner d + 64 is tile dt + 2.
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int r = 0; r < 16; ++r) {
+    const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
+    if (kr >= wkeys) continue;
+    const size_t o = ((size_t)(kw + kr) * P.Hkv + kvh) * D;
+    float g[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
-        red[(wave * BK + kr) * D + dt * 32 + col] = src[dt][r];
-      }
-    __syncthreads();
-    bf16* out = pass == 0 ? P.dk : P.dv;
-    for (int idx = threadIdx.x; idx < BK * (D / 2); idx += 256) {
-      const int kr = idx / (D / 2), i = idx % (D / 2);
-      if (kr >= klen) continue;
-      float a = 0.f, b = 0.f;
+    for (int dt = 0; dt < 4; ++dt) g[dt] = dk[dt][r] * P.scale;
+    if (P.rope_base > 0.f) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        a += red[(w * BK + kr) * D + i];
-        b += red[(w * BK + kr) * D + i + D / 2];
+      for (int dt = 0; dt < 2; ++dt) {
+        float sn, cs;
+        rope_sincos(P.pos[kw + kr], dt * 32 + col, D, P.rope_base, &sn, &cs);
+        const float y1 = g[dt], y2 = g[dt + 2];
+        g[dt] = y1 * cs + y2 * sn;
+        g[dt + 2] = y2 * cs - y1 * sn;
       }
-      if (pass == 0) {
-        a *= P.scale;
-        b *= P.scale;
-        if (P.rope_base > 0.f) {
-          float sn, cs;
-          rope_sincos(P.pos[k0 + kr], i, D, P.rope_base, &sn, &cs);
-          const float y1 = a, y2 = b;
-          a = y1 * cs + y2 * sn;
-          b = y2 * cs - y1 * sn;
-        }
-      }
-      const size_t o = ((size_t)(k0 + kr) * P.Hkv + kvh) * D;
-      out[o + i] = (bf16)a;
-      out[o + i + D / 2] = (bf16)b;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      P.dk[o + dt * 32 + col] = (bf16)g[dt];
+      P.dv[o + dt * 32 + col] = (bf16)dv[dt][r];
     }
   }
 }

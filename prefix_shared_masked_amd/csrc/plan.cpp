@@ -224,8 +224,10 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_pla
     return (p->fq_ptr[x + 1] - p->fq_ptr[x]) > (p->fq_ptr[y + 1] - p->fq_ptr[y]);
   });
 
-  // backward key tiles, most work first
-  const int32_t BK = p->block_kv;
+  // backward key tiles, most work first.  A tile holds up to TA_BLOCK_KV keys
+  // of one node; the kernel splits it into 32-key sub-tiles, sub-tile s
+  // reading the 32-row query blocks from its own diagonal block onwards.
+  const int32_t BK = p->block_kv, SUB = TA_KV_SUB;
   struct KT {
     int32_t k0, klen, qe, node;
     int64_t work;
@@ -236,9 +238,11 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_pla
     const int32_t s = p->node_start[node], e = s + seg_len[node], qe = p->node_sub_end[node];
     for (int32_t k0 = s; k0 < e; k0 += BK) {
       const int32_t kl = std::min(BK, e - k0);
-      const int64_t rows = qe - k0;
-      kts.push_back({k0, kl, qe, node, int64_t(kl) * rows});
-      comp_bwd += int64_t(BK) * ((rows + BK - 1) / BK) * BK;
+      const int64_t nblk = (int64_t(qe - k0) + SUB - 1) / SUB;
+      int64_t blocks = 0;
+      for (int32_t sub = 0; sub * SUB < kl; ++sub) blocks += nblk - sub;
+      kts.push_back({k0, kl, qe, node, blocks});
+      comp_bwd += blocks * SUB * SUB;
     }
   }
   std::stable_sort(kts.begin(), kts.end(), [](const KT& x, const KT& y) { return x.work > y.work; });

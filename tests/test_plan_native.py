@@ -70,8 +70,16 @@ def compare(tree):
     # backward key tiles
     bk = [tuple(int(x) for x in row[:3]) for row in v["bk"]]
     assert sorted(bk) == oracle.bwd_tiles(o, TA_BLOCK_KV)
-    work = [kl * (qe - k0) for k0, kl, qe in bk]
+    # most work first: 32-key sub-tile s reads the 32-row blocks from its own
+    # diagonal block to the end of the query range
+    sub = pkg.TA_KV_SUB
+
+    def blocks(k0, kl, qe):
+        nblk = -(-(qe - k0) // sub)
+        return sum(nblk - s for s in range(-(-kl // sub)))
+    work = [blocks(*x) for x in bk]
     assert all(a >= b for a, b in zip(work, work[1:]))
+    assert p.computed_pairs_bwd == sub * sub * sum(work)
     for row in v["bk"]:
         assert o.node_of[row[0]] == row[3]
     return p, o
