@@ -15,6 +15,10 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in arch VGPRs: the softmax reads them with VALU
+    # ops, and the AGPR form made the register allocator copy the
+    # loop-carried accumulators in and out of AGPRs every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -299,9 +299,16 @@ struct KVLoad {
   float x;
 };
 
+constexpr int KV_KEYS = TA_BLOCK_KV;
+constexpr int KV_TILE_BYTES = KV_KEYS * PK * 2;  // one of K (fp16) / V (bf16), padded rows
+
 __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   using L = KVStageLayout;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::BYTES];
+  // [K tile | V tile | stage 0 | stage 1]
+  __shared__ __attribute__((aligned(16))) char smem[2 * KV_TILE_BYTES + 2 * L::BYTES];
+  f16* sK = (f16*)smem;
+  bf16* sV = (bf16*)(smem + KV_TILE_BYTES);
+  char* stages = smem + 2 * KV_TILE_BYTES;
 
   const int kvh = blockIdx.x % P.Hkv;
   const int32_t* tl = P.bk + (size_t)(blockIdx.x / P.Hkv) * 4;
@@ -310,25 +317,21 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   const int col = lane & 31, half = lane >> 5;
   const int kw = k0 + SUB * wave;                 // this wavefront's first key
   const int wkeys = max(0, min(SUB, klen - SUB * wave));
-  const bool kvalid = col < wkeys;
   const int key = kw + col;
 
-  // K (fp16) and V as B operands: lane = key column, k-slots s*16 + half*8 + e
-  f16x8 kf[8];
-  bf16x8 vf[8];
+  // The tile's K (fp16) and V rows go to LDS once; keys past klen are zero.
   {
-    const size_t off = ((size_t)(kvalid ? key : k0) * P.Hkv + kvh) * D + half * 8;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8 a = *(const f16x8*)(P.k + off + s * 16);
-      const bf16x8 c = *(const bf16x8*)(P.v + off + s * 16);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kf[s][e] = kvalid ? a[e] : (f16)0.f;
-        vf[s][e] = kvalid ? c[e] : (bf16)0.f;
-      }
+    const uint4 z = {0u, 0u, 0u, 0u};
+    for (int idx = t; idx < KV_KEYS * (D / 8); idx += 256) {
+      const int r = idx >> 4, c = (idx & 15) * 8;
+      const bool ok = r < klen;
+      const size_t off = ((size_t)(ok ? k0 + r : k0) * P.Hkv + kvh) * D + c;
+      *(uint4*)(sK + r * PK + c) = ok ? *(const uint4*)(P.k + off) : z;
+      *(uint4*)(sV + r * PK + c) = ok ? *(const uint4*)(P.v + off) : z;
     }
   }
+  const f16* kw16 = sK + (SUB * wave) * PK;   // this wavefront's 32 K rows
+  const bf16* vwb = sV + (SUB * wave) * PK;   // and V rows
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
@@ -384,14 +387,14 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   KVLoad ld;
   if (nitem > 0) {
     fetch(0, ld);
-    stage(ld, smem);
+    stage(ld, stages);
   }
   __syncthreads();
   for (int it = 0; it < nitem; ++it) {
     const int buf = it & 1;
     const int qb = k0 + SUB * (it % nblk);
     if (it + 1 < nitem) fetch(it + 1, ld);
-    char* base = smem + buf * L::BYTES;
+    char* base = stages + buf * L::BYTES;
     // blocks that end before this wavefront's first key see none of its keys
     if (wkeys > 0 && qb + SUB > kw) {
       const f16* q16 = (const f16*)(base + L::Q16);
@@ -403,35 +406,29 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const f16x8 a = *(const f16x8*)(q16 + col * PK + s * 16 + half * 8);
+        const f16x8 kb = *(const f16x8*)(kw16 + col * PK + s * 16 + half * 8);
         const bf16x8 c = *(const bf16x8*)(dob + col * PT + s * 16 + half * 8);
-        S = mfma32h(a, kf[s], S);
-        dP = mfma32(c, vf[s], dP);
+        const bf16x8 vb = *(const bf16x8*)(vwb + col * PK + s * 16 + half * 8);
+        S = mfma32h(a, kb, S);
+        dP = mfma32(c, vb, dP);
       }
-      // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col
-      float lr[16], dr[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 a = *(const float4*)(ls + 8 * r4 + 4 * half);
-        const float4 c = *(const float4*)(dd + 8 * r4 + 4 * half);
-        lr[4 * r4] = a.x, lr[4 * r4 + 1] = a.y, lr[4 * r4 + 2] = a.z, lr[4 * r4 + 3] = a.w;
-        dr[4 * r4] = c.x, dr[4 * r4 + 1] = c.y, dr[4 * r4 + 2] = c.z, dr[4 * r4 + 3] = c.w;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = exp2f_fast(S[r] * P.scale_log2 - lr[r]);
-      if (qb == kw) {  // diagonal block: key <= row
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key > qb + 8 * (r >> 2) + 4 * half + (r & 3)) S[r] = 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dP[r] = S[r] * (dP[r] - dr[r]);
+      // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col;
+      // each group of four rows takes its LSE and D as one float4 from LDS
+      const bool diag = qb == kw;
       bf16x8 pa[2], sa[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pa[0][e] = (bf16)S[e];
-        pa[1][e] = (bf16)S[8 + e];
-        sa[0][e] = (bf16)dP[e];
-        sa[1][e] = (bf16)dP[8 + e];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 l4 = *(const float4*)(ls + 8 * r4 + 4 * half);
+        const float4 d4 = *(const float4*)(dd + 8 * r4 + 4 * half);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * r4 + u;
+          float p = exp2f_fast(S[r] * P.scale_log2 - lv[u]);
+          if (diag && key > qb + 8 * r4 + 4 * half + u) p = 0.f;
+          pa[r >> 3][r & 7] = (bf16)p;
+          sa[r >> 3][r & 7] = (bf16)(p * (dP[r] - dv4[u]));
+        }
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -445,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
           dk[dt] = mfma32(sa[qs], cat(q0, q1), dk[dt]);
         }
     }
-    if (it + 1 < nitem) stage(ld, smem + (buf ^ 1) * L::BYTES);
+    if (it + 1 < nitem) stage(ld, stages + (buf ^ 1) * L::BYTES);
     __syncthreads();
   }
 
