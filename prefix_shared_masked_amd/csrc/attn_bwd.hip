@@ -299,16 +299,9 @@ struct KVLoad {
   float x;
 };
 
-constexpr int KV_KEYS = TA_BLOCK_KV;
-constexpr int KV_TILE_BYTES = KV_KEYS * PK * 2;  // one of K (fp16) / V (bf16), padded rows
-
 __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   using L = KVStageLayout;
-  // [K tile | V tile | stage 0 | stage 1]
-  __shared__ __attribute__((aligned(16))) char smem[2 * KV_TILE_BYTES + 2 * L::BYTES];
-  f16* sK = (f16*)smem;
-  bf16* sV = (bf16*)(smem + KV_TILE_BYTES);
-  char* stages = smem + 2 * KV_TILE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::BYTES];
 
   const int kvh = blockIdx.x % P.Hkv;
   const int32_t* tl = P.bk + (size_t)(blockIdx.x / P.Hkv) * 4;
@@ -317,27 +310,32 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   const int col = lane & 31, half = lane >> 5;
   const int kw = k0 + SUB * wave;                 // this wavefront's first key
   const int wkeys = max(0, min(SUB, klen - SUB * wave));
+  const bool kvalid = col < wkeys;
   const int key = kw + col;
 
-  // The tile's K (fp16) and V rows go to LDS once; keys past klen are zero.
+  // K (fp16) and V as B operands held in registers: lane = key column,
+  // k-slots s*16 + half*8 + e; keys past the tile are zero.
+  f16x8 kf[8];
+  bf16x8 vf[8];
   {
+    const size_t off = ((size_t)(kvalid ? key : k0) * P.Hkv + kvh) * D + half * 8;
     const uint4 z = {0u, 0u, 0u, 0u};
-    for (int idx = t; idx < KV_KEYS * (D / 8); idx += 256) {
-      const int r = idx >> 4, c = (idx & 15) * 8;
-      const bool ok = r < klen;
-      const size_t off = ((size_t)(ok ? k0 + r : k0) * P.Hkv + kvh) * D + c;
-      *(uint4*)(sK + r * PK + c) = ok ? *(const uint4*)(P.k + off) : z;
-      *(uint4*)(sV + r * PK + c) = ok ? *(const uint4*)(P.v + off) : z;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint4 a = kvalid ? *(const uint4*)(P.k + off + s * 16) : z;
+      const uint4 c = kvalid ? *(const uint4*)(P.v + off + s * 16) : z;
+      kf[s] = *(const f16x8*)&a;
+      vf[s] = *(const bf16x8*)&c;
     }
   }
-  const f16* kw16 = sK + (SUB * wave) * PK;   // this wavefront's 32 K rows
-  const bf16* vwb = sV + (SUB * wave) * PK;   // and V rows
+  // dK and dV accumulate in AGPRs for the whole loop
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
+  agpr_fence8(dk, dv);
   const int trow = half * 4 + ((lane & 15) >> 2);
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
 
@@ -387,16 +385,19 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   KVLoad ld;
   if (nitem > 0) {
     fetch(0, ld);
-    stage(ld, stages);
+    stage(ld, smem);
   }
   __syncthreads();
   for (int it = 0; it < nitem; ++it) {
     const int buf = it & 1;
     const int qb = k0 + SUB * (it % nblk);
     if (it + 1 < nitem) fetch(it + 1, ld);
-    char* base = stages + buf * L::BYTES;
-    // blocks that end before this wavefront's first key see none of its keys
-    if (wkeys > 0 && qb + SUB > kw) {
+    char* base = smem + buf * L::BYTES;
+    // Every wavefront runs every block: blocks that end before its first key
+    // are fully masked by the causal compare, and keys past the tile are
+    // never stored.  (Keeping the accumulating MFMAs unconditional lets the
+    // accumulators stay in AGPRs across iterations.)
+    {
       const f16* q16 = (const f16*)(base + L::Q16);
       const bf16* qbf = (const bf16*)(base + L::QB);
       const bf16* dob = (const bf16*)(base + L::DO);
@@ -406,15 +407,13 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const f16x8 a = *(const f16x8*)(q16 + col * PK + s * 16 + half * 8);
-        const f16x8 kb = *(const f16x8*)(kw16 + col * PK + s * 16 + half * 8);
         const bf16x8 c = *(const bf16x8*)(dob + col * PT + s * 16 + half * 8);
-        const bf16x8 vb = *(const bf16x8*)(vwb + col * PK + s * 16 + half * 8);
-        S = mfma32h(a, kb, S);
-        dP = mfma32(c, vb, dP);
+        S = mfma32h(a, kf[s], S);
+        dP = mfma32(c, vf[s], dP);
       }
       // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col;
       // each group of four rows takes its LSE and D as one float4 from LDS
-      const bool diag = qb == kw;
+      const bool diag = qb <= kw;  // diagonal or earlier: key <= row needed
       bf16x8 pa[2], sa[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -430,22 +429,30 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
           sa[r >> 3][r & 7] = (bf16)(p * (dP[r] - dv4[u]));
         }
       }
+      // dV += P^T dO and dK += dS^T Q: all transpose reads of a d-tile are
+      // issued before its four MFMAs
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt) {
+        bf16x8 od[2], oq[2];
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
-          const bf16x4 d0 = lds_read_tr(dob + (qs * 16 + trow) * PT + dt * 32 + tcol);
-          const bf16x4 d1 = lds_read_tr(dob + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol);
-          dv[dt] = mfma32(pa[qs], cat(d0, d1), dv[dt]);
-          const bf16x4 q0 = lds_read_tr(qbf + (qs * 16 + trow) * PT + dt * 32 + tcol);
-          const bf16x4 q1 = lds_read_tr(qbf + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol);
-          dk[dt] = mfma32(sa[qs], cat(q0, q1), dk[dt]);
+          od[qs] = cat(lds_read_tr(dob + (qs * 16 + trow) * PT + dt * 32 + tcol),
+                       lds_read_tr(dob + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol));
+          oq[qs] = cat(lds_read_tr(qbf + (qs * 16 + trow) * PT + dt * 32 + tcol),
+                       lds_read_tr(qbf + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol));
         }
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          mfma32_acc(dv[dt], pa[qs], od[qs]);
+          mfma32_acc(dk[dt], sa[qs], oq[qs]);
+        }
+      }
     }
-    if (it + 1 < nitem) stage(ld, stages + (buf ^ 1) * L::BYTES);
+    if (it + 1 < nitem) stage(ld, smem + (buf ^ 1) * L::BYTES);
     __syncthreads();
   }
 
+  agpr_fence8(dk, dv);
   // Each wavefront owns its keys: scale and rotate dK back, store dK and dV.
   // Accumulator register r of tile dt <-> key kw + 8*(r/4) + 4*half + r%4,
   // d = dt*32 + col; the rotate-half partner d + 64 is tile dt + 2.

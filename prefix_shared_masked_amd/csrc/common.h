@@ -29,6 +29,25 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Accumulating 32x32x16 bf16 MFMA whose accumulator lives in AGPRs, for
+// loop-carried accumulators that nothing but these MFMAs touches between
+// agpr_fence8() points.  The compiler's hazard recognizer does not look inside
+// inline asm, so the asm carries its own wait states: a VALU write of a VGPR
+// needs two wait states before an MFMA may read it as A or B (the compiler
+// itself spaces builtin MFMAs that way), and s_nop 2 gives three.  Chained
+// MFMAs into the same accumulator need none.
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the accumulators' MFMA writes and any other access (an
+// XDL 16-pass result needs at most 18; this gives 24), and between VALU
+// writes (zero init) and the first MFMA.  The accumulators are operands, so
+// their initialisation and epilogue reads cannot move across the fence.
+__device__ __forceinline__ void agpr_fence8(f32x16 (&x)[4], f32x16 (&y)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
+}
+
 // Same shape with fp16 operands (same rate; 10 stored mantissa bits).
 __device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
