@@ -283,19 +283,19 @@ struct KVParams {
 
 constexpr int SUB = TA_KV_SUB;  // keys per wavefront = rows per query block
 
-// One staged query block in LDS: fp16 Q rows (scores), bf16 Q and dO rows
-// (transpose-read operands of dK and dV), and the rows' LSE and D.
+// One staged query block in LDS: fp16 Q rows (scores, and the transpose-read
+// operand of dK), bf16 dO rows (dP, and the transpose-read operand of dV),
+// and the rows' LSE and D.
 struct KVStageLayout {
   static constexpr int Q16 = 0;                                 // f16 [SUB][PK]
-  static constexpr int QB = Q16 + SUB * PK * 2;                 // bf16 [SUB][PT]
-  static constexpr int DO = QB + SUB * PT * 2;                  // bf16 [SUB][PT]
+  static constexpr int DO = Q16 + SUB * PK * 2;                 // bf16 [SUB][PT]
   static constexpr int LS = DO + SUB * PT * 2;                  // float [SUB]
   static constexpr int DD = LS + SUB * 4;                       // float [SUB]
   static constexpr int BYTES = DD + SUB * 4;
 };
 
 struct KVLoad {
-  uint4 q[2], d[2];
+  u32x4 q[2], d[2];
   float x;
 };
 
@@ -319,13 +319,13 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   bf16x8 vf[8];
   {
     const size_t off = ((size_t)(kvalid ? key : k0) * P.Hkv + kvh) * D + half * 8;
-    const uint4 z = {0u, 0u, 0u, 0u};
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint4 a = kvalid ? *(const uint4*)(P.k + off + s * 16) : z;
-      const uint4 c = kvalid ? *(const uint4*)(P.v + off + s * 16) : z;
-      kf[s] = *(const f16x8*)&a;
-      vf[s] = *(const bf16x8*)&c;
+      const u32x4 a0 = *(const u32x4*)(P.k + off + s * 16), c0 = *(const u32x4*)(P.v + off + s * 16);
+      const u32x4 a = kvalid ? a0 : z, c = kvalid ? c0 : z;
+      kf[s] = __builtin_bit_cast(f16x8, a);
+      vf[s] = __builtin_bit_cast(bf16x8, c);
     }
   }
   // dK and dV accumulate in AGPRs for the whole loop
@@ -352,11 +352,14 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     const int row = qb + lrow;
     const bool rv = row < qe;
     const size_t roff = ((size_t)(rv ? row : qb) * P.Hq + h) * D + lpart;
-    const uint4 z = {0u, 0u, 0u, 0u};
-    ld.q[0] = rv ? *(const uint4*)(P.q + roff) : z;
-    ld.q[1] = rv ? *(const uint4*)(P.q + roff + 8) : z;
-    ld.d[0] = rv ? *(const uint4*)(P.dO + roff) : z;
-    ld.d[1] = rv ? *(const uint4*)(P.dO + roff + 8) : z;
+    // the address is always a valid row; rows past the range select zeros
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 q0 = *(const u32x4*)(P.q + roff), q1 = *(const u32x4*)(P.q + roff + 8);
+    const u32x4 d0 = *(const u32x4*)(P.dO + roff), d1 = *(const u32x4*)(P.dO + roff + 8);
+    ld.q[0] = rv ? q0 : z;
+    ld.q[1] = rv ? q1 : z;
+    ld.d[0] = rv ? d0 : z;
+    ld.d[1] = rv ? d1 : z;
     ld.x = 0.f;
     if (t < 2 * SUB) {
       const int r = qb + (t & (SUB - 1));
@@ -365,90 +368,94 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   };
   auto stage = [&](const KVLoad& ld, char* base) {
     f16* q16 = (f16*)(base + L::Q16);
-    bf16* qbf = (bf16*)(base + L::QB);
     bf16* dob = (bf16*)(base + L::DO);
-    *(uint4*)(q16 + lrow * PK + lpart) = ld.q[0];
-    *(uint4*)(q16 + lrow * PK + lpart + 8) = ld.q[1];
-    *(uint4*)(dob + lrow * PT + lpart) = ld.d[0];
-    *(uint4*)(dob + lrow * PT + lpart + 8) = ld.d[1];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const f16x8 h8 = *(const f16x8*)&ld.q[u];
-      bf16x8 b8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b8[e] = (bf16)(float)h8[e];
-      *(bf16x8*)(qbf + lrow * PT + lpart + 8 * u) = b8;
-    }
+    *(u32x4*)(q16 + lrow * PK + lpart) = ld.q[0];
+    *(u32x4*)(q16 + lrow * PK + lpart + 8) = ld.q[1];
+    *(u32x4*)(dob + lrow * PT + lpart) = ld.d[0];
+    *(u32x4*)(dob + lrow * PT + lpart + 8) = ld.d[1];
     if (t < 2 * SUB) ((float*)(base + (t < SUB ? L::LS : L::DD)))[t & (SUB - 1)] = ld.x;
   };
-
-  KVLoad ld;
-  if (nitem > 0) {
-    fetch(0, ld);
-    stage(ld, smem);
-  }
-  __syncthreads();
-  for (int it = 0; it < nitem; ++it) {
-    const int buf = it & 1;
+  // One staged block: S and dP, then P and dS in registers, then
+  // dV += P^T dO (bf16) and dK += dS^T Q (fp16).  Every wavefront runs every
+  // block: blocks that end before its first key are fully masked by the
+  // causal compare, and keys past the tile are never stored.  (Keeping the
+  // accumulating MFMAs unconditional lets the accumulators stay in AGPRs.)
+  auto compute = [&](int it, const char* base) {
     const int qb = k0 + SUB * (it % nblk);
-    if (it + 1 < nitem) fetch(it + 1, ld);
-    char* base = smem + buf * L::BYTES;
-    // Every wavefront runs every block: blocks that end before its first key
-    // are fully masked by the causal compare, and keys past the tile are
-    // never stored.  (Keeping the accumulating MFMAs unconditional lets the
-    // accumulators stay in AGPRs across iterations.)
-    {
-      const f16* q16 = (const f16*)(base + L::Q16);
-      const bf16* qbf = (const bf16*)(base + L::QB);
-      const bf16* dob = (const bf16*)(base + L::DO);
-      const float* ls = (const float*)(base + L::LS);
-      const float* dd = (const float*)(base + L::DD);
-      f32x16 S = f32x16{}, dP = f32x16{};
+    const f16* q16 = (const f16*)(base + L::Q16);
+    const bf16* dob = (const bf16*)(base + L::DO);
+    const float* ls = (const float*)(base + L::LS);
+    const float* dd = (const float*)(base + L::DD);
+    f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 a = *(const f16x8*)(q16 + col * PK + s * 16 + half * 8);
-        const bf16x8 c = *(const bf16x8*)(dob + col * PT + s * 16 + half * 8);
-        S = mfma32h(a, kf[s], S);
-        dP = mfma32(c, vf[s], dP);
-      }
-      // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col;
-      // each group of four rows takes its LSE and D as one float4 from LDS
-      const bool diag = qb <= kw;  // diagonal or earlier: key <= row needed
-      bf16x8 pa[2], sa[2];
+    for (int s = 0; s < 8; ++s) {
+      const f16x8 a = *(const f16x8*)(q16 + col * PK + s * 16 + half * 8);
+      const bf16x8 c = *(const bf16x8*)(dob + col * PT + s * 16 + half * 8);
+      S = mfma32h(a, kf[s], S);
+      dP = mfma32(c, vf[s], dP);
+    }
+    // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col;
+    // each group of four rows takes its LSE and D as one float4 from LDS
+    const bool diag = qb <= kw;  // diagonal or earlier: key <= row needed
+    bf16x8 pa[2];
+    float ds[16];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 l4 = *(const float4*)(ls + 8 * r4 + 4 * half);
-        const float4 d4 = *(const float4*)(dd + 8 * r4 + 4 * half);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 l4 = *(const float4*)(ls + 8 * r4 + 4 * half);
+      const float4 d4 = *(const float4*)(dd + 8 * r4 + 4 * half);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * r4 + u;
-          float p = exp2f_fast(S[r] * P.scale_log2 - lv[u]);
-          if (diag && key > qb + 8 * r4 + 4 * half + u) p = 0.f;
-          pa[r >> 3][r & 7] = (bf16)p;
-          sa[r >> 3][r & 7] = (bf16)(p * (dP[r] - dv4[u]));
-        }
-      }
-      // dV += P^T dO and dK += dS^T Q: all transpose reads of a d-tile are
-      // issued before its four MFMAs
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        bf16x8 od[2], oq[2];
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          od[qs] = cat(lds_read_tr(dob + (qs * 16 + trow) * PT + dt * 32 + tcol),
-                       lds_read_tr(dob + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol));
-          oq[qs] = cat(lds_read_tr(qbf + (qs * 16 + trow) * PT + dt * 32 + tcol),
-                       lds_read_tr(qbf + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol));
-        }
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          mfma32_acc(dv[dt], pa[qs], od[qs]);
-          mfma32_acc(dk[dt], sa[qs], oq[qs]);
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * r4 + u;
+        float p = exp2f_fast(S[r] * P.scale_log2 - lv[u]);
+        if (diag && key > qb + 8 * r4 + 4 * half + u) p = 0.f;
+        pa[r >> 3][r & 7] = (bf16)p;
+        ds[r] = p * (dP[r] - dv4[u]);
       }
     }
-    if (it + 1 < nitem) stage(ld, smem + (buf ^ 1) * L::BYTES);
+    const f16x8 sa[2] = {pack_f16_rtz(ds), pack_f16_rtz(ds + 8)};
+    // all transpose reads of a d-tile are issued before its four MFMAs
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      bf16x8 od[2];
+      f16x8 oq[2];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        od[qs] = cat(lds_read_tr(dob + (qs * 16 + trow) * PT + dt * 32 + tcol),
+                     lds_read_tr(dob + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol));
+        oq[qs] = cat(lds_read_tr(q16 + (qs * 16 + trow) * PK + dt * 32 + tcol),
+                     lds_read_tr(q16 + (qs * 16 + 8 + trow) * PK + dt * 32 + tcol));
+      }
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        mfma32_acc(dv[dt], pa[qs], od[qs]);
+        mfma32h_acc(dk[dt], sa[qs], oq[qs]);
+      }
+    }
+  };
+
+  // Block b sits in LDS buffer b & 1.  Its global loads are issued two
+  // blocks ahead (two register sets, alternating), so their latency hides
+  // behind two blocks of compute.  Fetches and stages run unconditionally
+  // (past the last item they reload it and fill a buffer nobody reads), which
+  // keeps the staging registers free of control flow.  nitem >= 1: a tile's
+  // query range holds at least its own first key.
+  const int last = nitem - 1;
+  KVLoad la, lb;
+  fetch(0, la);
+  stage(la, smem);
+  fetch(min(1, last), la);
+  fetch(min(2, last), lb);
+  __syncthreads();
+  for (int it = 0; it < nitem; it += 2) {
+    compute(it, smem);
+    stage(la, smem + L::BYTES);
+    fetch(min(it + 3, last), la);
+    __syncthreads();
+    if (it + 1 >= nitem) break;
+    compute(it + 1, smem + L::BYTES);
+    stage(lb, smem);
+    fetch(min(it + 4, last), lb);
     __syncthreads();
   }
 

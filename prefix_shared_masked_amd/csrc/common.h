@@ -13,8 +13,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16-byte load/store unit (a native vector: selects stay in registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define TA_LOG2E 1.4426950408889634f
 #define TA_LN2 0.6931471805599453f
@@ -38,6 +41,9 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // MFMAs into the same accumulator need none.
 __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32h_acc(f32x16& acc, const f16x8& a, const f16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // Wait states between the accumulators' MFMA writes and any other access (an
 // XDL 16-pass result needs at most 18; this gives 24), and between VALU
@@ -65,8 +71,40 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
+// The transpose read moves 16-bit elements whatever their type.
+__device__ __forceinline__ f16x4 lds_read_tr(const f16* p) {
+  return __builtin_bit_cast(f16x4, lds_read_tr((const bf16*)p));
+}
+// Eight floats to fp16, rounding toward zero: out-of-range values clamp to
+// +-65504 instead of becoming infinities.
+__device__ __forceinline__ f16x8 pack_f16_rtz(const float* x) {
+  uint4 w;
+  w.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[0], x[1]));
+  w.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[2], x[3]));
+  w.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[4], x[5]));
+  w.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[6], x[7]));
+  return __builtin_bit_cast(f16x8, w);
+}
+
 __device__ __forceinline__ bf16x8 cat(const bf16x4& a, const bf16x4& b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f16x8 cat(const f16x4& a, const f16x4& b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// MFMA operand rows in LDS are read as two 8-byte halves (ds_read_b64 runs
+// at about twice the bytes per clock of ds_read_b128 on gfx950).  Lane half h
+// then holds the k-slots {4h..4h+3} and {8+4h..8+4h+3} of each group of 16;
+// the other operand uses the same order, so the contraction is unchanged.
+__device__ __forceinline__ f16x8 row_frag(const f16* row, int s, int half) {
+  return cat(*(const f16x4*)(row + s * 16 + 4 * half), *(const f16x4*)(row + s * 16 + 8 + 4 * half));
+}
+__device__ __forceinline__ bf16x8 row_frag(const bf16* row, int s, int half) {
+  return cat(*(const bf16x4*)(row + s * 16 + 4 * half), *(const bf16x4*)(row + s * 16 + 8 + 4 * half));
+}
+// d index of element e (0..7) of k-group s for lane half h in that order
+__device__ __forceinline__ constexpr int frag_d(int s, int half, int e) {
+  return s * 16 + (e >> 2) * 8 + 4 * half + (e & 3);
 }
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
