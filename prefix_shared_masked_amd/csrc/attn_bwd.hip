@@ -63,7 +63,7 @@ struct Stage {
 };
 
 __device__ __forceinline__ void load_stage(const DQParams& P, int c, int kvh, Stage& s) {
-  const int32_t* ch = P.fq_chunk + (size_t)c * TA_CHUNK_INTS;
+  const cint_ptr ch = as_const(P.fq_chunk) + (size_t)c * TA_CHUNK_INTS;
   const int t = threadIdx.x, piece = t & 15;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
   __shared__ __attribute__((aligned(16))) int sE[2][BN];
 
   const int kvh = blockIdx.x % P.Hkv;
-  const int tile = P.fq_order[blockIdx.x / P.Hkv];
+  const int tile = as_const(P.fq_order)[blockIdx.x / P.Hkv];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int hsub = blockIdx.y * 4 + wave;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-  const int c0 = P.fq_ptr[tile], c1 = P.fq_ptr[tile + 1];
+  const int c0 = as_const(P.fq_ptr)[tile], c1 = as_const(P.fq_ptr)[tile + 1];
   Stage st;
   load_stage(P, c0, kvh, st);
   store_stage(st, sK[0], sV[0], sJ[0], sE[0]);
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
         p0 = mfma32(b0, df[s], p0);
         p1 = mfma32(b1, df[s], p1);
       }
-      const int full = P.fq_chunk[(size_t)c * TA_CHUNK_INTS + 2];
+      const int full = as_const(P.fq_chunk)[(size_t)c * TA_CHUNK_INTS + 2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s0[r] = exp2f_fast(s0[r] * P.scale_log2 - lse_i);
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   __shared__ __attribute__((aligned(16))) char smem[2 * L::BYTES];
 
   const int kvh = blockIdx.x % P.Hkv;
-  const int32_t* tl = P.bk + (size_t)(blockIdx.x / P.Hkv) * 4;
+  const cint_ptr tl = as_const(P.bk) + (size_t)(blockIdx.x / P.Hkv) * 4;
   const int k0 = tl[0], klen = tl[1], qe = tl[2];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int col = lane & 31, half = lane >> 5;
@@ -346,34 +346,34 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   const int nblk = (qe - k0 + SUB - 1) / SUB;
   const int nitem = P.G * nblk;
   const int lrow = t >> 3, lpart = (t & 7) * 16;
+  // fetch() only issues loads (from always-valid rows); everything that
+  // consumes the loaded values, the zero-select for rows past the range
+  // included, happens in stage(), so the loads stay in flight until then.
   auto fetch = [&](int it, KVLoad& ld) {
     const int h = kvh * P.G + it / nblk;
     const int qb = k0 + SUB * (it % nblk);
-    const int row = qb + lrow;
-    const bool rv = row < qe;
-    const size_t roff = ((size_t)(rv ? row : qb) * P.Hq + h) * D + lpart;
-    // the address is always a valid row; rows past the range select zeros
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 q0 = *(const u32x4*)(P.q + roff), q1 = *(const u32x4*)(P.q + roff + 8);
-    const u32x4 d0 = *(const u32x4*)(P.dO + roff), d1 = *(const u32x4*)(P.dO + roff + 8);
-    ld.q[0] = rv ? q0 : z;
-    ld.q[1] = rv ? q1 : z;
-    ld.d[0] = rv ? d0 : z;
-    ld.d[1] = rv ? d1 : z;
+    const int row = min(qb + lrow, qe - 1);
+    const size_t roff = ((size_t)row * P.Hq + h) * D + lpart;
+    ld.q[0] = *(const u32x4*)(P.q + roff);
+    ld.q[1] = *(const u32x4*)(P.q + roff + 8);
+    ld.d[0] = *(const u32x4*)(P.dO + roff);
+    ld.d[1] = *(const u32x4*)(P.dO + roff + 8);
     ld.x = 0.f;
     if (t < 2 * SUB) {
       const int r = qb + (t & (SUB - 1));
-      if (r < qe) ld.x = t < SUB ? P.lse[(size_t)h * P.N + r] * TA_LOG2E : P.Dd[(size_t)h * P.N + r];
+      if (r < qe) ld.x = t < SUB ? P.lse[(size_t)h * P.N + r] : P.Dd[(size_t)h * P.N + r];
     }
   };
-  auto stage = [&](const KVLoad& ld, char* base) {
+  auto stage = [&](int it, const KVLoad& ld, char* base) {
+    const bool rv = k0 + SUB * (it % nblk) + lrow < qe;
+    const u32x4 z = {0u, 0u, 0u, 0u};
     f16* q16 = (f16*)(base + L::Q16);
     bf16* dob = (bf16*)(base + L::DO);
-    *(u32x4*)(q16 + lrow * PK + lpart) = ld.q[0];
-    *(u32x4*)(q16 + lrow * PK + lpart + 8) = ld.q[1];
-    *(u32x4*)(dob + lrow * PT + lpart) = ld.d[0];
-    *(u32x4*)(dob + lrow * PT + lpart + 8) = ld.d[1];
-    if (t < 2 * SUB) ((float*)(base + (t < SUB ? L::LS : L::DD)))[t & (SUB - 1)] = ld.x;
+    *(u32x4*)(q16 + lrow * PK + lpart) = rv ? ld.q[0] : z;
+    *(u32x4*)(q16 + lrow * PK + lpart + 8) = rv ? ld.q[1] : z;
+    *(u32x4*)(dob + lrow * PT + lpart) = rv ? ld.d[0] : z;
+    *(u32x4*)(dob + lrow * PT + lpart + 8) = rv ? ld.d[1] : z;
+    if (t < 2 * SUB) ((float*)(base + (t < SUB ? L::LS : L::DD)))[t & (SUB - 1)] = t < SUB ? ld.x * TA_LOG2E : ld.x;
   };
   // One staged block: S and dP, then P and dS in registers, then
   // dV += P^T dO (bf16) and dK += dS^T Q (fp16).  Every wavefront runs every
@@ -443,18 +443,18 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   const int last = nitem - 1;
   KVLoad la, lb;
   fetch(0, la);
-  stage(la, smem);
+  stage(0, la, smem);
   fetch(min(1, last), la);
   fetch(min(2, last), lb);
   __syncthreads();
   for (int it = 0; it < nitem; it += 2) {
     compute(it, smem);
-    stage(la, smem + L::BYTES);
+    stage(min(it + 1, last), la, smem + L::BYTES);
     fetch(min(it + 3, last), la);
     __syncthreads();
     if (it + 1 >= nitem) break;
     compute(it + 1, smem + L::BYTES);
-    stage(lb, smem);
+    stage(min(it + 2, last), lb, smem);
     fetch(min(it + 4, last), lb);
     __syncthreads();
   }

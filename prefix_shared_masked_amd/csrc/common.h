@@ -129,16 +129,72 @@ __device__ __forceinline__ void rope_sincos(int pos, int i, int d, float base, f
 
 // Gathered key chunk of the plan: slot v -> packed key index and the end of
 // the DFS interval of the key's node (row i reads the key iff key <= i < kend).
-__device__ __forceinline__ void chunk_slot(const int32_t* __restrict__ ch, int v, int& phys, int& kend) {
-  int s = 0;
+// K/V tiles staged by direct global-to-LDS copies use rows of 128 16-bit
+// elements (256 bytes) with no padding; the 16-byte piece p of row r is
+// stored at piece p ^ swz(r).  swz permutes the row's low four bits
+// (b3 b2 b1 b0 -> b3 b1 b0 b2), so the 16 rows that one 16-byte row read
+// touches land on 16 distinct pieces, and the 4 rows x 2 pieces of a
+// transpose read's 16-lane group land on 8 distinct pieces.
+__device__ __forceinline__ constexpr int swz(int r) { return (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// One 16-byte global-to-LDS copy per lane (global_load_lds_dwordx4): lane i
+// writes lds_base + 16 i, where lds_base (taken from M0; one wait state after
+// writing it) is the same for the whole wavefront.  The copy bypasses VGPRs
+// and counts on the vector-memory counter.  It is issued from inline asm
+// because the compiler cannot tell that the copies target the buffer nobody
+// is reading and would wait for them before every LDS read; the cost is that
+// the copies are invisible to its wait-count bookkeeping, so whoever reads the
+// data must first run lds_copies_wait() (then a workgroup barrier).
+__device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds_base) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copies_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Plan tables are read-only for a kernel's lifetime.  Reading them through
+// the constant address space lets uniform reads become scalar loads, which
+// issue early and never make the vector-memory counter wait on them.
+typedef const int32_t __attribute__((address_space(4)))* cint_ptr;
+__device__ __forceinline__ cint_ptr as_const(const int32_t* p) { return (cint_ptr)p; }
+
+// A chunk record held in registers: [nseg nkeys full -], kstart[4],
+// vstart[4], kend[4].  Loaded with four uniform 16-byte reads before any use,
+// so slot lookups below are register selects only.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef const i32x4 __attribute__((address_space(4)))* ci32x4_ptr;
+struct ChunkRec {
+  i32x4 h, ks, ko, ke;
+};
+__device__ __forceinline__ ChunkRec load_chunk(cint_ptr ch) {
+  const ci32x4_ptr p = (ci32x4_ptr)ch;
+  return ChunkRec{p[0], p[1], p[2], p[3]};
+}
+__device__ __forceinline__ void chunk_slot(const ChunkRec& c, int v, int& phys, int& kend) {
+  int j = c.ks[0] + (v - c.ko[0]), e = c.ke[0];
 #pragma unroll
-  for (int x = 1; x < TA_CHUNK_MAX_SEG; ++x) s = (ch[8 + x] <= v) ? x : s;
-  phys = ch[4 + s] + (v - ch[8 + s]);
-  kend = ch[12 + s];
-  if (v >= ch[1]) {  // padding slot: a valid row, never visible
-    phys = ch[4];
-    kend = 0;
+  for (int x = 1; x < TA_CHUNK_MAX_SEG; ++x) {
+    const bool in = c.ko[x] <= v;
+    j = in ? c.ks[x] + (v - c.ko[x]) : j;
+    e = in ? c.ke[x] : e;
   }
+  phys = v < c.h[1] ? j : c.ks[0];  // padding slot: a valid row, never visible
+  kend = v < c.h[1] ? e : 0;
+}
+
+// Key index and DFS-interval end of slot v of a gathered chunk.  All fields
+// are read with uniform indices (scalar loads) and the segment is picked per
+// lane with selects; unused segments carry offsets past the last slot.
+template <class Ptr>
+__device__ __forceinline__ void chunk_slot(Ptr ch, int v, int& phys, int& kend) {
+  int j = ch[4] + (v - ch[8]), e = ch[12];
+#pragma unroll
+  for (int x = 1; x < TA_CHUNK_MAX_SEG; ++x) {
+    const int ks = ch[4 + x], ko = ch[8 + x], ke = ch[12 + x];
+    j = ko <= v ? ks + (v - ko) : j;
+    e = ko <= v ? ke : e;
+  }
+  phys = v < ch[1] ? j : ch[4];  // padding slot: a valid row, never visible
+  kend = v < ch[1] ? e : 0;
 }
 
 // Order LDS traffic of one wavefront: earlier LDS writes complete before any
