@@ -57,41 +57,36 @@ struct DQParams {
   float scale, scale_log2, rope_base;
 };
 
-struct Stage {
-  uint4 k[4], v[4];
-  int j[4], e[4];
-};
-
-__device__ __forceinline__ void load_stage(const DQParams& P, int c, int kvh, Stage& s) {
-  const cint_ptr ch = as_const(P.fq_chunk) + (size_t)c * TA_CHUNK_INTS;
-  const int t = threadIdx.x, piece = t & 15;
+// Copies chunk c's 64 K and V rows into one LDS buffer (swizzled 256-byte
+// rows, see swz) and its key indices / DFS-interval ends into sJ / sE.  Copy
+// instruction i of a tile fills rows 4i..4i+3; wavefront w issues i = w + 4k.
+__device__ __forceinline__ void stage_chunk(const DQParams& P, int c, int kvh, bf16* sKb, bf16* sVb, int* sJb,
+                                            int* sEb) {
+  const ChunkRec ch = load_chunk(as_const(P.fq_chunk) + (size_t)c * TA_CHUNK_INTS);
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int v = (t >> 4) + 16 * r;
-    chunk_slot(ch, v, s.j[r], s.e[r]);
-    const size_t off = ((size_t)s.j[r] * P.Hkv + kvh) * D + piece * 8;
-    s.k[r] = *(const uint4*)(P.k + off);
-    s.v[r] = *(const uint4*)(P.v + off);
+  for (int k = 0; k < 4; ++k) {
+    const int i = w + 4 * k;
+    const int row = 4 * i + (l >> 4);
+    int j, e;
+    chunk_slot(ch, row, j, e);
+    const int piece = (l & 15) ^ swz(row & 15);
+    const size_t off = ((size_t)j * P.Hkv + kvh) * D + piece * 8;
+    copy16_to_lds(P.k + off, sKb + 4 * i * D);
+    copy16_to_lds(P.v + off, sVb + 4 * i * D);
   }
-}
-
-__device__ __forceinline__ void store_stage(const Stage& s, bf16* sK, bf16* sV, int* sJ, int* sE) {
-  const int t = threadIdx.x, piece = t & 15;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int v = (t >> 4) + 16 * r;
-    *(uint4*)(sK + v * PT + piece * 8) = s.k[r];
-    *(uint4*)(sV + v * PK + piece * 8) = s.v[r];
-    if (piece == 0) {
-      sJ[v] = s.j[r];
-      sE[v] = s.e[r];
-    }
+  int j, e;
+  chunk_slot(ch, l, j, e);
+  if (t < BN) {
+    sJb[t] = j;
+    sEb[t] = e;
   }
 }
 
 __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][BN * PT];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][BN * PK];
+  __shared__ __attribute__((aligned(1024))) bf16 sK[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[2][BN * D];
   __shared__ __attribute__((aligned(16))) int sJ[2][BN];
   __shared__ __attribute__((aligned(16))) int sE[2][BN];
 
@@ -161,31 +156,44 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
   const int c0 = as_const(P.fq_ptr)[tile], c1 = as_const(P.fq_ptr)[tile + 1];
-  Stage st;
-  load_stage(P, c0, kvh, st);
-  store_stage(st, sK[0], sV[0], sJ[0], sE[0]);
+  stage_chunk(P, c0, kvh, sK[0], sV[0], sJ[0], sE[0]);
+  lds_copies_wait();
   __syncthreads();
 
+  // Swizzled LDS offsets (in elements), fixed per lane: koff[s] for the
+  // 16-byte row reads of k-group s (K for S^T, V for dP^T; rows col and
+  // col + 32 share them), toff[dt][x] for the K transpose read of d-tile dt,
+  // rows trow + 8x of each 16-row group.
   const int trow = half * 4 + ((lane & 15) >> 2);
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  int koff[8], toff[4][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = col * D + (((2 * s + half) ^ swz(col & 15)) << 3);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = trow + 8 * x;
+      toff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
+    }
 
   for (int c = c0; c < c1; ++c) {
     const int buf = (c - c0) & 1;
-    // prefetch the next chunk (the last iteration reloads its own chunk,
-    // which keeps the staging registers free of control flow)
-    load_stage(P, c + 1 < c1 ? c + 1 : c, kvh, st);
+    // copy the next chunk into the other buffer (the last iteration copies
+    // its own chunk again, into the buffer nobody reads)
+    stage_chunk(P, c + 1 < c1 ? c + 1 : c, kvh, sK[buf ^ 1], sV[buf ^ 1], sJ[buf ^ 1], sE[buf ^ 1]);
     if (active) {
       const bf16* kb = sK[buf];
       const bf16* vb = sV[buf];
       f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 a0 = *(const bf16x8*)(kb + col * PT + s * 16 + half * 8);
-        const bf16x8 a1 = *(const bf16x8*)(kb + (32 + col) * PT + s * 16 + half * 8);
+        const bf16x8 a0 = *(const bf16x8*)(kb + koff[s]);
+        const bf16x8 a1 = *(const bf16x8*)(kb + 32 * D + koff[s]);
         s0 = mfma32(a0, qf[s], s0);
         s1 = mfma32(a1, qf[s], s1);
-        const bf16x8 b0 = *(const bf16x8*)(vb + col * PK + s * 16 + half * 8);
-        const bf16x8 b1 = *(const bf16x8*)(vb + (32 + col) * PK + s * 16 + half * 8);
+        const bf16x8 b0 = *(const bf16x8*)(vb + koff[s]);
+        const bf16x8 b1 = *(const bf16x8*)(vb + 32 * D + koff[s]);
         p0 = mfma32(b0, df[s], p0);
         p1 = mfma32(b1, df[s], p1);
       }
@@ -222,12 +230,12 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x4 t0 = lds_read_tr(kb + (kk * 16 + trow) * PT + dt * 32 + tcol);
-          const bf16x4 t1 = lds_read_tr(kb + (kk * 16 + 8 + trow) * PT + dt * 32 + tcol);
+          const bf16x4 t0 = lds_read_tr(kb + kk * 16 * D + toff[dt][0]);
+          const bf16x4 t1 = lds_read_tr(kb + kk * 16 * D + toff[dt][1]);
           acc[dt] = mfma32(cat(t0, t1), db[kk], acc[dt]);
         }
     }
-    store_stage(st, sK[buf ^ 1], sV[buf ^ 1], sJ[buf ^ 1], sE[buf ^ 1]);
+    lds_copies_wait();
     __syncthreads();
   }
 
