@@ -48,6 +48,7 @@ struct DQParams {
   const float* lse;
   bf16* dq;
   float* Dd;    // [Hq, N] out
+  float* l2;    // [Hq, N] out: LSE * log2(e)
   f16* qs;      // [N, Hq, d] out: fp16 copy of Q (rotated when RoPE is on)
   const int32_t* pos;
   const int32_t* fq_ptr;
@@ -84,7 +85,7 @@ __device__ __forceinline__ void stage_chunk(const DQParams& P, int c, int kvh, b
   }
 }
 
-__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
+__global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
   __shared__ __attribute__((aligned(1024))) bf16 sK[2][BN * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV[2][BN * D];
   __shared__ __attribute__((aligned(16))) int sJ[2][BN];
@@ -147,7 +148,10 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
     if (!qvalid) Di = 0.f;
     lse_i = qvalid ? P.lse[(size_t)h * P.N + qi] * TA_LOG2E : 0.f;
     if (active && qvalid) {
-      if (half == 0) P.Dd[(size_t)h * P.N + qi] = Di;
+      if (half == 0) {
+        P.Dd[(size_t)h * P.N + qi] = Di;
+        P.l2[(size_t)h * P.N + qi] = lse_i;
+      }
     }
   }
 
@@ -182,58 +186,51 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(DQParams P) {
     // copy the next chunk into the other buffer (the last iteration copies
     // its own chunk again, into the buffer nobody reads)
     stage_chunk(P, c + 1 < c1 ? c + 1 : c, kvh, sK[buf ^ 1], sV[buf ^ 1], sJ[buf ^ 1], sE[buf ^ 1]);
-    if (active) {
-      const bf16* kb = sK[buf];
-      const bf16* vb = sV[buf];
-      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 a0 = *(const bf16x8*)(kb + koff[s]);
-        const bf16x8 a1 = *(const bf16x8*)(kb + 32 * D + koff[s]);
-        s0 = mfma32(a0, qf[s], s0);
-        s1 = mfma32(a1, qf[s], s1);
-        const bf16x8 b0 = *(const bf16x8*)(vb + koff[s]);
-        const bf16x8 b1 = *(const bf16x8*)(vb + 32 * D + koff[s]);
-        p0 = mfma32(b0, df[s], p0);
-        p1 = mfma32(b1, df[s], p1);
-      }
+    // The chunk is processed as two halves of 32 keys, which keeps S^T and
+    // dP^T at 16 registers each (the kernel fits two workgroups per CU).
+    // Wavefronts without a head (fewer than four heads per KV head) compute
+    // too and never store.
+    {
       const int full = as_const(P.fq_chunk)[(size_t)c * TA_CHUNK_INTS + 2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = exp2f_fast(s0[r] * P.scale_log2 - lse_i);
-        s1[r] = exp2f_fast(s1[r] * P.scale_log2 - lse_i);
-      }
-      if (!full) {
+      for (int kh = 0; kh < 2; ++kh) {
+        const bf16* kb = sK[buf] + kh * 32 * D;
+        const bf16* vb = sV[buf] + kh * 32 * D;
+        f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int v0 = r4 * 8 + half * 4;
-          const int4 J0 = *(const int4*)&sJ[buf][v0], E0 = *(const int4*)&sE[buf][v0];
-          const int4 J1 = *(const int4*)&sJ[buf][32 + v0], E1 = *(const int4*)&sE[buf][32 + v0];
-          const int j0[4] = {J0.x, J0.y, J0.z, J0.w}, e0[4] = {E0.x, E0.y, E0.z, E0.w};
-          const int j1[4] = {J1.x, J1.y, J1.z, J1.w}, e1[4] = {E1.x, E1.y, E1.z, E1.w};
+        for (int s = 0; s < 8; ++s) {
+          sc = mfma32(*(const bf16x8*)(kb + koff[s]), qf[s], sc);
+          dp = mfma32(*(const bf16x8*)(vb + koff[s]), df[s], dp);
+        }
+        // S^T register r <-> key slot kh*32 + 8*(r/4) + 4*half + r%4
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (!(j0[u] <= qi && qi < e0[u])) s0[r4 * 4 + u] = 0.f;
-            if (!(j1[u] <= qi && qi < e1[u])) s1[r4 * 4 + u] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[r] = exp2f_fast(sc[r] * P.scale_log2 - lse_i);
+        if (!full) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int v0 = kh * 32 + r4 * 8 + half * 4;
+            const int4 J = *(const int4*)&sJ[buf][v0], E = *(const int4*)&sE[buf][v0];
+            const int jj[4] = {J.x, J.y, J.z, J.w}, ee[4] = {E.x, E.y, E.z, E.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (!(jj[u] <= qi && qi < ee[u])) sc[r4 * 4 + u] = 0.f;
           }
         }
-      }
-      bf16x8 db[4];
+        bf16x8 db[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        db[0][e] = (bf16)(s0[e] * (p0[e] - Di));
-        db[1][e] = (bf16)(s0[8 + e] * (p0[8 + e] - Di));
-        db[2][e] = (bf16)(s1[e] * (p1[e] - Di));
-        db[3][e] = (bf16)(s1[8 + e] * (p1[8 + e] - Di));
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x4 t0 = lds_read_tr(kb + kk * 16 * D + toff[dt][0]);
-          const bf16x4 t1 = lds_read_tr(kb + kk * 16 * D + toff[dt][1]);
-          acc[dt] = mfma32(cat(t0, t1), db[kk], acc[dt]);
+        for (int e = 0; e < 8; ++e) {
+          db[0][e] = (bf16)(sc[e] * (dp[e] - Di));
+          db[1][e] = (bf16)(sc[8 + e] * (dp[8 + e] - Di));
         }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const bf16x4 t0 = lds_read_tr(kb + kk * 16 * D + toff[dt][0]);
+            const bf16x4 t1 = lds_read_tr(kb + kk * 16 * D + toff[dt][1]);
+            acc[dt] = mfma32(cat(t0, t1), db[kk], acc[dt]);
+          }
+      }
     }
     lds_copies_wait();
     __syncthreads();
@@ -279,7 +276,7 @@ struct KVParams {
   const f16* k;   // fp16 copy of K (rotated when RoPE is on)
   const bf16* v;
   const bf16* dO;
-  const float* lse;
+  const float* l2;  // LSE * log2(e), [Hq, N]
   const float* Dd;
   bf16* dk;
   bf16* dv;
@@ -293,23 +290,19 @@ constexpr int SUB = TA_KV_SUB;  // keys per wavefront = rows per query block
 
 // One staged query block in LDS: fp16 Q rows (scores, and the transpose-read
 // operand of dK), bf16 dO rows (dP, and the transpose-read operand of dV),
-// and the rows' LSE and D.
+// both as swizzled 256-byte rows (see swz), and the rows' LSE * log2(e) and D.
 struct KVStageLayout {
-  static constexpr int Q16 = 0;                                 // f16 [SUB][PK]
-  static constexpr int DO = Q16 + SUB * PK * 2;                 // bf16 [SUB][PT]
-  static constexpr int LS = DO + SUB * PT * 2;                  // float [SUB]
-  static constexpr int DD = LS + SUB * 4;                       // float [SUB]
+  static constexpr int Q16 = 0;                  // f16 [SUB][D]
+  static constexpr int DO = Q16 + SUB * D * 2;   // bf16 [SUB][D]
+  static constexpr int LS = DO + SUB * D * 2;    // float [SUB]
+  static constexpr int DD = LS + SUB * 4;        // float [SUB]
   static constexpr int BYTES = DD + SUB * 4;
 };
-
-struct KVLoad {
-  u32x4 q[2], d[2];
-  float x;
-};
+static_assert(KVStageLayout::BYTES % 16 == 0, "stage buffers stay 16-byte aligned");
 
 __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   using L = KVStageLayout;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[3 * L::BYTES];
 
   const int kvh = blockIdx.x % P.Hkv;
   const cint_ptr tl = as_const(P.bk) + (size_t)(blockIdx.x / P.Hkv) * 4;
@@ -344,44 +337,47 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     dv[dt] = f32x16{};
   }
   agpr_fence8(dk, dv);
+
+  // Swizzled LDS offsets (in elements), fixed per lane: koff[s] for the
+  // 16-byte row reads of k-group s (Q for S, dO for dP), toff[dt][x] for the
+  // transpose reads of d-tile dt, rows trow + 8x of each 16-row group.
   const int trow = half * 4 + ((lane & 15) >> 2);
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  int koff[8], toff[4][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff[s] = col * D + (((2 * s + half) ^ swz(col & 15)) << 3);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = trow + 8 * x;
+      toff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
+    }
 
   // Items are (query head, 32-row block); all four wavefronts share each
-  // staged block.  Thread t loads 32 bytes of Q and of dO of row t/8 and, for
-  // t < 64, one LSE (t < 32) or D value.  Rows past the query range stage as
-  // zeros (LSE = D = 0), so they contribute exactly nothing.
+  // staged block.  Each wavefront issues exactly five copies per block: two
+  // 1 KiB copies of Q rows, two of dO rows (rows 4i..4i+3 for i = w, w + 4),
+  // and sixteen LSE or D values (wavefront w: LSE rows 16w.. for w < 2, D rows
+  // 16(w-2).. otherwise).  Rows past the query range copy the last valid row
+  // and are masked to P = 0 below, so they contribute nothing.
   const int nblk = (qe - k0 + SUB - 1) / SUB;
   const int nitem = P.G * nblk;
-  const int lrow = t >> 3, lpart = (t & 7) * 16;
-  // fetch() only issues loads (from always-valid rows); everything that
-  // consumes the loaded values, the zero-select for rows past the range
-  // included, happens in stage(), so the loads stay in flight until then.
-  auto fetch = [&](int it, KVLoad& ld) {
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  auto stage = [&](int it, char* base) {
     const int h = kvh * P.G + it / nblk;
     const int qb = k0 + SUB * (it % nblk);
-    const int row = min(qb + lrow, qe - 1);
-    const size_t roff = ((size_t)row * P.Hq + h) * D + lpart;
-    ld.q[0] = *(const u32x4*)(P.q + roff);
-    ld.q[1] = *(const u32x4*)(P.q + roff + 8);
-    ld.d[0] = *(const u32x4*)(P.dO + roff);
-    ld.d[1] = *(const u32x4*)(P.dO + roff + 8);
-    ld.x = 0.f;
-    if (t < 2 * SUB) {
-      const int r = qb + (t & (SUB - 1));
-      if (r < qe) ld.x = t < SUB ? P.lse[(size_t)h * P.N + r] : P.Dd[(size_t)h * P.N + r];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = w + 4 * k;
+      const int row = 4 * i + (lane >> 4);
+      const size_t off = ((size_t)min(qb + row, qe - 1) * P.Hq + h) * D + (((lane & 15) ^ swz(row & 15)) << 3);
+      copy16_to_lds(P.q + off, base + L::Q16 + 4 * i * D * 2);
+      copy16_to_lds(P.dO + off, base + L::DO + 4 * i * D * 2);
     }
-  };
-  auto stage = [&](int it, const KVLoad& ld, char* base) {
-    const bool rv = k0 + SUB * (it % nblk) + lrow < qe;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    f16* q16 = (f16*)(base + L::Q16);
-    bf16* dob = (bf16*)(base + L::DO);
-    *(u32x4*)(q16 + lrow * PK + lpart) = rv ? ld.q[0] : z;
-    *(u32x4*)(q16 + lrow * PK + lpart + 8) = rv ? ld.q[1] : z;
-    *(u32x4*)(dob + lrow * PT + lpart) = rv ? ld.d[0] : z;
-    *(u32x4*)(dob + lrow * PT + lpart + 8) = rv ? ld.d[1] : z;
-    if (t < 2 * SUB) ((float*)(base + (t < SUB ? L::LS : L::DD)))[t & (SUB - 1)] = t < SUB ? ld.x * TA_LOG2E : ld.x;
+    if (lane < 16) {
+      const int r = min(qb + 16 * (w & 1) + lane, qe - 1);
+      copy4_to_lds((w < 2 ? P.l2 : P.Dd) + (size_t)h * P.N + r, base + L::LS + 64 * w);
+    }
   };
   // One staged block: S and dP, then P and dS in registers, then
   // dV += P^T dO (bf16) and dK += dS^T Q (fp16).  Every wavefront runs every
@@ -397,14 +393,14 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const f16x8 a = *(const f16x8*)(q16 + col * PK + s * 16 + half * 8);
-      const bf16x8 c = *(const bf16x8*)(dob + col * PT + s * 16 + half * 8);
-      S = mfma32h(a, kf[s], S);
-      dP = mfma32(c, vf[s], dP);
+      S = mfma32h(*(const f16x8*)(q16 + koff[s]), kf[s], S);
+      dP = mfma32(*(const bf16x8*)(dob + koff[s]), vf[s], dP);
     }
     // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col;
-    // each group of four rows takes its LSE and D as one float4 from LDS
-    const bool diag = qb <= kw;  // diagonal or earlier: key <= row needed
+    // each group of four rows takes its LSE and D as one float4 from LDS.
+    // Only the diagonal-or-earlier block and the range's last block need
+    // the element mask (key <= row < qe).
+    const bool edge = qb <= kw || qb + SUB > qe;
     bf16x8 pa[2];
     float ds[16];
 #pragma unroll
@@ -415,8 +411,9 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * r4 + u;
+        const int row = qb + 8 * r4 + 4 * half + u;
         float p = exp2f_fast(S[r] * P.scale_log2 - lv[u]);
-        if (diag && key > qb + 8 * r4 + 4 * half + u) p = 0.f;
+        if (edge && (key > row || row >= qe)) p = 0.f;
         pa[r >> 3][r & 7] = (bf16)p;
         ds[r] = p * (dP[r] - dv4[u]);
       }
@@ -429,10 +426,8 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
       f16x8 oq[2];
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
-        od[qs] = cat(lds_read_tr(dob + (qs * 16 + trow) * PT + dt * 32 + tcol),
-                     lds_read_tr(dob + (qs * 16 + 8 + trow) * PT + dt * 32 + tcol));
-        oq[qs] = cat(lds_read_tr(q16 + (qs * 16 + trow) * PK + dt * 32 + tcol),
-                     lds_read_tr(q16 + (qs * 16 + 8 + trow) * PK + dt * 32 + tcol));
+        od[qs] = cat(lds_read_tr(dob + qs * 16 * D + toff[dt][0]), lds_read_tr(dob + qs * 16 * D + toff[dt][1]));
+        oq[qs] = cat(lds_read_tr(q16 + qs * 16 * D + toff[dt][0]), lds_read_tr(q16 + qs * 16 * D + toff[dt][1]));
       }
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
@@ -442,30 +437,37 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     }
   };
 
-  // Block b sits in LDS buffer b & 1.  Its global loads are issued two
-  // blocks ahead (two register sets, alternating), so their latency hides
-  // behind two blocks of compute.  Fetches and stages run unconditionally
-  // (past the last item they reload it and fill a buffer nobody reads), which
-  // keeps the staging registers free of control flow.  nitem >= 1: a tile's
-  // query range holds at least its own first key.
+  // Three LDS buffers: block b sits in buffer b % 3, and its copies are
+  // issued two blocks ahead.  Staging runs unconditionally (past the last
+  // item it copies the last item again into a buffer nobody reads), so every
+  // wavefront always has exactly five copies per block in flight and
+  // "at most five outstanding" means the next block has landed.  nitem >= 1:
+  // a tile's query range holds at least its own first key.
   const int last = nitem - 1;
-  KVLoad la, lb;
-  fetch(0, la);
-  stage(0, la, smem);
-  fetch(min(1, last), la);
-  fetch(min(2, last), lb);
+  char* const b0 = smem;
+  char* const b1 = smem + L::BYTES;
+  char* const b2 = smem + 2 * L::BYTES;
+  stage(0, b0);
+  stage(min(1, last), b1);
+  asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   __syncthreads();
-  for (int it = 0; it < nitem; it += 2) {
-    compute(it, smem);
-    stage(min(it + 1, last), la, smem + L::BYTES);
-    fetch(min(it + 3, last), la);
+  for (int it = 0; it < nitem; it += 3) {
+    stage(min(it + 2, last), b2);
+    compute(it, b0);
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     __syncthreads();
     if (it + 1 >= nitem) break;
-    compute(it + 1, smem + L::BYTES);
-    stage(min(it + 2, last), lb, smem);
-    fetch(min(it + 4, last), lb);
+    stage(min(it + 3, last), b0);
+    compute(it + 1, b1);
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    __syncthreads();
+    if (it + 2 >= nitem) break;
+    stage(min(it + 4, last), b1);
+    compute(it + 2, b2);
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     __syncthreads();
   }
+  lds_copies_wait();
 
   agpr_fence8(dk, dv);
   // Each wavefront owns its keys: scale and rotate dK back, store dK and dV.
@@ -584,6 +586,7 @@ size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t
   const size_t N = p->n_tokens;
   size_t b = align256(N * Hq * sizeof(float));  // D
   if (dt == TA_BF16) {
+    b += align256(N * Hq * sizeof(float));                                             // LSE * log2(e)
     b += align256(N * Hq * d * sizeof(f16)) + align256(N * Hkv * d * sizeof(f16));  // fp16 Q, K
     if (rope_base > 0.f) b += align256(N * Hkv * d * sizeof(bf16));                 // rotated bf16 K
   } else if (rope_base > 0.f) {
@@ -626,6 +629,8 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   w += align256((size_t)N * Hq * sizeof(float));
 
   if (dt == TA_BF16) {
+    float* l2 = (float*)w;
+    w += align256((size_t)N * Hq * sizeof(float));
     f16* qs = (f16*)w;
     w += align256((size_t)N * Hq * d * sizeof(f16));
     f16* ks = (f16*)w;
@@ -649,6 +654,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     A.lse = lse;
     A.dq = (bf16*)dq;
     A.Dd = Dd;
+    A.l2 = l2;
     A.qs = qs;
     A.pos = pos;
     A.fq_ptr = fq_ptr;
@@ -670,7 +676,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.k = ks;
     B.v = (const bf16*)v;
     B.dO = (const bf16*)dO;
-    B.lse = lse;
+    B.l2 = l2;
     B.Dd = Dd;
     B.dk = (bf16*)dk;
     B.dv = (bf16*)dv;

@@ -49,6 +49,9 @@ __device__ __forceinline__ void mfma32h_acc(f32x16& acc, const f16x8& a, const f
 // XDL 16-pass result needs at most 18; this gives 24), and between VALU
 // writes (zero init) and the first MFMA.  The accumulators are operands, so
 // their initialisation and epilogue reads cannot move across the fence.
+__device__ __forceinline__ void agpr_fence4(f32x16 (&x)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]));
+}
 __device__ __forceinline__ void agpr_fence8(f32x16 (&x)[4], f32x16 (&y)[4]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
@@ -148,6 +151,11 @@ __device__ __forceinline__ constexpr int swz(int r) { return (r & 8) | ((r & 3) 
 __device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds_base) {
   const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory", "m0");
+}
+// 4-byte variant (global_load_lds_dword): lane i writes lds_base + 4 i.
+__device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds_base) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(a) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_copies_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
