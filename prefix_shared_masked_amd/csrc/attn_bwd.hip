@@ -47,8 +47,8 @@ struct DQParams {
   const bf16* dO;
   const float* lse;
   bf16* dq;
-  float* Dd;    // [Hq, N] out
-  float* l2;    // [Hq, N] out: LSE * log2(e)
+  float* nd;    // [Hq, N] out: -D
+  float* nl2;   // [Hq, N] out: -LSE * log2(e)
   f16* qs;      // [N, Hq, d] out: fp16 copy of Q (rotated when RoPE is on)
   const int32_t* pos;
   const int32_t* fq_ptr;
@@ -149,8 +149,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
     lse_i = qvalid ? P.lse[(size_t)h * P.N + qi] * TA_LOG2E : 0.f;
     if (active && qvalid) {
       if (half == 0) {
-        P.Dd[(size_t)h * P.N + qi] = Di;
-        P.l2[(size_t)h * P.N + qi] = lse_i;
+        P.nd[(size_t)h * P.N + qi] = -Di;
+        P.nl2[(size_t)h * P.N + qi] = -lse_i;
       }
     }
   }
@@ -273,11 +273,11 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
 // ---------------------------------------------------------------------------
 struct KVParams {
   const f16* q;   // fp16 copy of Q (rotated when RoPE is on)
-  const f16* k;   // fp16 copy of K (rotated when RoPE is on)
+  const f16* k;   // fp16 copy of K (rotated when RoPE is on) times scale * log2(e)
   const bf16* v;
   const bf16* dO;
-  const float* l2;  // LSE * log2(e), [Hq, N]
-  const float* Dd;
+  const float* nl2;  // -LSE * log2(e), [Hq, N]
+  const float* nd;   // -D, [Hq, N]
   bf16* dk;
   bf16* dv;
   const int32_t* pos;
@@ -290,7 +290,8 @@ constexpr int SUB = TA_KV_SUB;  // keys per wavefront = rows per query block
 
 // One staged query block in LDS: fp16 Q rows (scores, and the transpose-read
 // operand of dK), bf16 dO rows (dP, and the transpose-read operand of dV),
-// both as swizzled 256-byte rows (see swz), and the rows' LSE * log2(e) and D.
+// both as swizzled 256-byte rows (see swz), and the rows' -LSE * log2(e) and
+// -D, which seed the S and dP accumulators.
 struct KVStageLayout {
   static constexpr int Q16 = 0;                  // f16 [SUB][D]
   static constexpr int DO = Q16 + SUB * D * 2;   // bf16 [SUB][D]
@@ -302,7 +303,7 @@ static_assert(KVStageLayout::BYTES % 16 == 0, "stage buffers stay 16-byte aligne
 
 __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   using L = KVStageLayout;
-  __shared__ __attribute__((aligned(1024))) char smem[3 * L::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * L::BYTES];
 
   const int kvh = blockIdx.x % P.Hkv;
   const cint_ptr tl = as_const(P.bk) + (size_t)(blockIdx.x / P.Hkv) * 4;
@@ -376,96 +377,121 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     }
     if (lane < 16) {
       const int r = min(qb + 16 * (w & 1) + lane, qe - 1);
-      copy4_to_lds((w < 2 ? P.l2 : P.Dd) + (size_t)h * P.N + r, base + L::LS + 64 * w);
+      copy4_to_lds((w < 2 ? P.nl2 : P.nd) + (size_t)h * P.N + r, base + L::LS + 64 * w);
     }
   };
-  // One staged block: S and dP, then P and dS in registers, then
-  // dV += P^T dO (bf16) and dK += dS^T Q (fp16).  Every wavefront runs every
-  // block: blocks that end before its first key are fully masked by the
-  // causal compare, and keys past the tile are never stored.  (Keeping the
-  // accumulating MFMAs unconditional lets the accumulators stay in AGPRs.)
-  auto compute = [&](int it, const char* base) {
-    const int qb = k0 + SUB * (it % nblk);
+  // scores(): S = Q K^T - LSE (fp16 MFMA, in log2 units: the K copy carries
+  // scale * log2(e)) and dP = dO V^T - D of one staged block; the
+  // accumulators start from the staged -LSE and -D, so P = exp2(S) and
+  // dS = P dP need no further per-element terms.
+  // grads(): P and dS in registers, then dV += P^T dO (bf16) and
+  // dK += dS^T Q (fp16).  Every wavefront runs every block: blocks that end
+  // before its first key are fully masked by the causal compare, and keys
+  // past the tile are never stored.  (Keeping the accumulating MFMAs
+  // unconditional lets the accumulators stay in AGPRs.)
+  auto scores = [&](const char* base, f32x16& S, f32x16& dP) {
     const f16* q16 = (const f16*)(base + L::Q16);
     const bf16* dob = (const bf16*)(base + L::DO);
     const float* ls = (const float*)(base + L::LS);
     const float* dd = (const float*)(base + L::DD);
-    f32x16 S = f32x16{}, dP = f32x16{};
+    // register r <-> query row 8*(r/4) + 4*half + r%4 of the block
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 l4 = *(const float4*)(ls + 8 * r4 + 4 * half);
+      const float4 d4 = *(const float4*)(dd + 8 * r4 + 4 * half);
+      S[4 * r4 + 0] = l4.x;
+      S[4 * r4 + 1] = l4.y;
+      S[4 * r4 + 2] = l4.z;
+      S[4 * r4 + 3] = l4.w;
+      dP[4 * r4 + 0] = d4.x;
+      dP[4 * r4 + 1] = d4.y;
+      dP[4 * r4 + 2] = d4.z;
+      dP[4 * r4 + 3] = d4.w;
+    }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       S = mfma32h(*(const f16x8*)(q16 + koff[s]), kf[s], S);
       dP = mfma32(*(const bf16x8*)(dob + koff[s]), vf[s], dP);
     }
-    // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col;
-    // each group of four rows takes its LSE and D as one float4 from LDS.
-    // Only the diagonal-or-earlier block and the range's last block need
-    // the element mask (key <= row < qe).
-    const bool edge = qb <= kw || qb + SUB > qe;
+  };
+  auto grads = [&](int it, const char* base, const f32x16& S, const f32x16& dP) {
+    const int qb = k0 + SUB * (it % nblk);
+    const f16* q16 = (const f16*)(base + L::Q16);
+    const bf16* dob = (const bf16*)(base + L::DO);
+    // transpose reads first: their latency hides behind the exponentials
+    bf16x8 od[4][2];
+    f16x8 oq[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        od[dt][qs] = cat(lds_read_tr(dob + qs * 16 * D + toff[dt][0]), lds_read_tr(dob + qs * 16 * D + toff[dt][1]));
+        oq[dt][qs] = cat(lds_read_tr(q16 + qs * 16 * D + toff[dt][0]), lds_read_tr(q16 + qs * 16 * D + toff[dt][1]));
+      }
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = exp2f_fast(S[r]);
+    // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col.
+    // Only the diagonal-or-earlier block and the range's last block need the
+    // element mask key <= row < qe, one unsigned compare: (row - key) <
+    // (qe - key).
+    if (qb <= kw || qb + SUB > qe) {
+      const int d0 = qb + 4 * half - key;
+      const unsigned lim = (unsigned)(qe - key);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((unsigned)(d0 + 8 * (r >> 2) + (r & 3)) >= lim) p[r] = 0.f;
+    }
     bf16x8 pa[2];
     float ds[16];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 l4 = *(const float4*)(ls + 8 * r4 + 4 * half);
-      const float4 d4 = *(const float4*)(dd + 8 * r4 + 4 * half);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * r4 + u;
-        const int row = qb + 8 * r4 + 4 * half + u;
-        float p = exp2f_fast(S[r] * P.scale_log2 - lv[u]);
-        if (edge && (key > row || row >= qe)) p = 0.f;
-        pa[r >> 3][r & 7] = (bf16)p;
-        ds[r] = p * (dP[r] - dv4[u]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      pa[r >> 3][r & 7] = (bf16)p[r];
+      ds[r] = p[r] * dP[r];
     }
     const f16x8 sa[2] = {pack_f16_rtz(ds), pack_f16_rtz(ds + 8)};
-    // all transpose reads of a d-tile are issued before its four MFMAs
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      bf16x8 od[2];
-      f16x8 oq[2];
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
-        od[qs] = cat(lds_read_tr(dob + qs * 16 * D + toff[dt][0]), lds_read_tr(dob + qs * 16 * D + toff[dt][1]));
-        oq[qs] = cat(lds_read_tr(q16 + qs * 16 * D + toff[dt][0]), lds_read_tr(q16 + qs * 16 * D + toff[dt][1]));
+        mfma32_acc(dv[dt], pa[qs], od[dt][qs]);
+        mfma32h_acc(dk[dt], sa[qs], oq[dt][qs]);
       }
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        mfma32_acc(dv[dt], pa[qs], od[qs]);
-        mfma32h_acc(dk[dt], sa[qs], oq[qs]);
-      }
-    }
   };
 
-  // Three LDS buffers: block b sits in buffer b % 3, and its copies are
-  // issued two blocks ahead.  Staging runs unconditionally (past the last
-  // item it copies the last item again into a buffer nobody reads), so every
-  // wavefront always has exactly five copies per block in flight and
-  // "at most five outstanding" means the next block has landed.  nitem >= 1:
-  // a tile's query range holds at least its own first key.
+  // Four LDS buffers: block b sits in buffer b % 4 and its copies are issued
+  // three blocks ahead.  Step `it` issues the copies of block it + 3, the
+  // score MFMAs of block it + 1 and the softmax / gradient work of block it,
+  // so the matrix unit has independent work while the VALU computes P and
+  // dS.  Staging and scores run unconditionally (past the last item they
+  // repeat the last item, into a buffer / registers nobody uses), so every
+  // wavefront always has exactly five copies per block in flight and "at
+  // most five outstanding" after a step means block it + 2 has landed.
+  // nitem >= 1: a tile's query range holds at least its own first key.
   const int last = nitem - 1;
-  char* const b0 = smem;
-  char* const b1 = smem + L::BYTES;
-  char* const b2 = smem + 2 * L::BYTES;
-  stage(0, b0);
-  stage(min(1, last), b1);
-  asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  char* const bb[4] = {smem, smem + L::BYTES, smem + 2 * L::BYTES, smem + 3 * L::BYTES};
+  stage(0, bb[0]);
+  stage(min(1, last), bb[1]);
+  stage(min(2, last), bb[2]);
+  asm volatile("s_waitcnt vmcnt(5)" ::: "memory");  // blocks 0 and 1 landed
   __syncthreads();
-  for (int it = 0; it < nitem; it += 3) {
-    stage(min(it + 2, last), b2);
-    compute(it, b0);
-    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    __syncthreads();
-    if (it + 1 >= nitem) break;
-    stage(min(it + 3, last), b0);
-    compute(it + 1, b1);
-    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    __syncthreads();
-    if (it + 2 >= nitem) break;
-    stage(min(it + 4, last), b1);
-    compute(it + 2, b2);
-    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    __syncthreads();
+  f32x16 Sa, dPa, Sb, dPb;
+  scores(bb[0], Sa, dPa);
+  for (int it = 0; it < nitem; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u > 0 && it + u >= nitem) break;
+      stage(min(it + u + 3, last), bb[(u + 3) & 3]);
+      if (u & 1) {
+        scores(bb[(u + 1) & 3], Sa, dPa);
+        grads(it + u, bb[u], Sb, dPb);
+      } else {
+        scores(bb[(u + 1) & 3], Sb, dPb);
+        grads(it + u, bb[u], Sa, dPa);
+      }
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      __syncthreads();
+    }
   }
   lds_copies_wait();
 
@@ -637,7 +663,8 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     w += align256((size_t)N * Hkv * d * sizeof(f16));
     mark(ev, nev, 0, stream);
     const bf16* kb = (const bf16*)k;
-    if (launch_rope<bf16, f16>((const bf16*)k, ks, pos, N, Hkv, d, rope_base, 0, stream) != hipSuccess)
+    if (launch_rope<bf16, f16>((const bf16*)k, ks, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E) !=
+        hipSuccess)
       return TA_EHIP;
     if (rope) {
       if (launch_rope<bf16, bf16>((const bf16*)k, (bf16*)w, pos, N, Hkv, d, rope_base, 0, stream) != hipSuccess)
@@ -653,8 +680,8 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     A.dO = (const bf16*)dO;
     A.lse = lse;
     A.dq = (bf16*)dq;
-    A.Dd = Dd;
-    A.l2 = l2;
+    A.nd = Dd;
+    A.nl2 = l2;
     A.qs = qs;
     A.pos = pos;
     A.fq_ptr = fq_ptr;
@@ -676,8 +703,8 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.k = ks;
     B.v = (const bf16*)v;
     B.dO = (const bf16*)dO;
-    B.l2 = l2;
-    B.Dd = Dd;
+    B.nl2 = l2;
+    B.nd = Dd;
     B.dk = (bf16*)dk;
     B.dv = (bf16*)dv;
     B.pos = pos;

@@ -33,7 +33,7 @@
 namespace ta {
 
 // ---------------------------------------------------------------------------
-// RoPE by depth position and/or dtype conversion: y[t, h, :] = R(pos[t])
+// RoPE by depth position and/or dtype conversion: y[t, h, :] = mul R(pos[t])
 // x[t, h, :] (transpose=1 gives R^T; base <= 0 converts only).  Rotate-half
 // pairs (i, i + d/2), angle pos * base^(-2i/d), arithmetic in fp32.
 template <typename T>
@@ -43,7 +43,7 @@ __device__ __forceinline__ f16 cvt_out<f16>(float x) { return to_f16_sat(x); }
 
 template <typename Ti, typename To>
 __global__ void rope_kernel(const Ti* x, To* y, const int32_t* __restrict__ pos,  // x may alias y
-                            int N, int H, int d, float base, int transpose) {
+                            int N, int H, int d, float base, int transpose, float mul) {
   const int half = d / 2;
   const size_t total = (size_t)N * H * half;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -54,6 +54,8 @@ __global__ void rope_kernel(const Ti* x, To* y, const int32_t* __restrict__ pos,
     float s = 0.f, c = 1.f;
     if (base > 0.f) rope_sincos(pos[t], i, d, base, &s, &c);
     if (transpose) s = -s;
+    s *= mul;
+    c *= mul;
     const size_t row = th * d;
     const float x1 = (float)x[row + i], x2 = (float)x[row + i + half];
     y[row + i] = cvt_out<To>(x1 * c - x2 * s);
@@ -63,20 +65,21 @@ __global__ void rope_kernel(const Ti* x, To* y, const int32_t* __restrict__ pos,
 
 template <typename Ti, typename To>
 hipError_t launch_rope(const Ti* x, To* y, const int32_t* pos, int N, int H, int d, float base, int transpose,
-                       hipStream_t st) {
+                       hipStream_t st, float mul) {
   const size_t total = (size_t)N * H * (d / 2);
   if (total == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL((rope_kernel<Ti, To>), dim3(blocks), dim3(256), 0, st, x, y, pos, N, H, d, base, transpose);
+  hipLaunchKernelGGL((rope_kernel<Ti, To>), dim3(blocks), dim3(256), 0, st, x, y, pos, N, H, d, base, transpose,
+                     mul);
   return hipGetLastError();
 }
 
 template hipError_t launch_rope<float, float>(const float*, float*, const int32_t*, int, int, int, float, int,
-                                              hipStream_t);
+                                              hipStream_t, float);
 template hipError_t launch_rope<bf16, bf16>(const bf16*, bf16*, const int32_t*, int, int, int, float, int,
-                                            hipStream_t);
+                                            hipStream_t, float);
 template hipError_t launch_rope<bf16, f16>(const bf16*, f16*, const int32_t*, int, int, int, float, int,
-                                           hipStream_t);
+                                           hipStream_t, float);
 
 namespace fwd {
 
@@ -86,7 +89,7 @@ constexpr int BN = TA_BLOCK_N;
 
 struct Params {
   const bf16* q;
-  const f16* k;   // fp16 copy of K (rotated when RoPE is on) for the scores
+  const f16* k;   // fp16 copy of K (rotated when RoPE is on) times scale * log2(e)
   const bf16* v;
   bf16* o;
   float* lse;
@@ -95,7 +98,6 @@ struct Params {
   const int32_t* fq_chunk;
   const int32_t* fq_order;
   int N, Hq, Hkv, G;
-  float scale_log2;  // softmax scale * log2(e)
   float rope_base;
 };
 
@@ -211,12 +213,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
         s0 = mfma32h(a0, qf[s], s0);
         s1 = mfma32h(a1, qf[s], s1);
       }
-      // S^T register r of tile kt <-> key slot kt*32 + 8*(r/4) + 4*half + r%4
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] *= P.scale_log2;
-        s1[r] *= P.scale_log2;
-      }
+      // S^T register r of tile kt <-> key slot kt*32 + 8*(r/4) + 4*half + r%4;
+      // the fp16 K copy carries the factor scale * log2(e), so S^T is
+      // already in log2 units
       const int full = as_const(P.fq_chunk)[(size_t)c * TA_CHUNK_INTS + 2];
       if (!full) {
 #pragma unroll
@@ -423,7 +422,8 @@ extern "C" ta_status tree_attn_fwd_ex(const ta_plan* p, const void* dplan, ta_dt
   mark(ev, nev, 0, stream);
   if (dt == TA_BF16) {
     f16* kk = (f16*)ws;
-    if (launch_rope<bf16, f16>((const bf16*)k, kk, pos, N, Hkv, d, rope_base, 0, stream) != hipSuccess)
+    if (launch_rope<bf16, f16>((const bf16*)k, kk, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E) !=
+        hipSuccess)
       return TA_EHIP;
     mark(ev, nev, 1, stream);
     fwd::Params P;
@@ -440,7 +440,6 @@ extern "C" ta_status tree_attn_fwd_ex(const ta_plan* p, const void* dplan, ta_dt
     P.Hq = Hq;
     P.Hkv = Hkv;
     P.G = Hq / Hkv;
-    P.scale_log2 = scale * TA_LOG2E;
     P.rope_base = rope_base;
     dim3 grid(p->n_qtiles * Hkv, (P.G + 3) / 4);
     hipLaunchKernelGGL(fwd::fwd_bf16_kernel, grid, dim3(256), 0, stream, P);
