@@ -662,15 +662,12 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     f16* ks = (f16*)w;
     w += align256((size_t)N * Hkv * d * sizeof(f16));
     mark(ev, nev, 0, stream);
-    const bf16* kb = (const bf16*)k;
-    if (launch_rope<bf16, f16>((const bf16*)k, ks, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E) !=
-        hipSuccess)
+    // one pass: fp16 K * scale * log2(e) for dK/dV's scores and, with RoPE,
+    // the rotated bf16 K for dQ
+    const bf16* kb = rope ? (const bf16*)w : (const bf16*)k;
+    if (launch_rope<bf16, f16>((const bf16*)k, ks, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E,
+                               rope ? (bf16*)w : nullptr) != hipSuccess)
       return TA_EHIP;
-    if (rope) {
-      if (launch_rope<bf16, bf16>((const bf16*)k, (bf16*)w, pos, N, Hkv, d, rope_base, 0, stream) != hipSuccess)
-        return TA_EHIP;
-      kb = (const bf16*)w;
-    }
     mark(ev, nev, 1, stream);
     bwd::DQParams A;
     A.q = (const bf16*)q;

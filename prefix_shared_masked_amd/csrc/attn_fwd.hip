@@ -34,52 +34,57 @@ namespace ta {
 
 // ---------------------------------------------------------------------------
 // RoPE by depth position and/or dtype conversion: y[t, h, :] = mul R(pos[t])
-// x[t, h, :] (transpose=1 gives R^T; base <= 0 converts only).  Rotate-half
-// pairs (i, i + d/2), angle pos * base^(-2i/d), arithmetic in fp32.
+// x[t, h, :] (transpose=1 gives R^T; base <= 0 converts only), and when y2 is
+// given also y2[t, h, :] = R(pos[t]) x[t, h, :] in bf16.  Rotate-half pairs
+// (i, i + d/2), angle pos * base^(-2i/d); the sine and cosine of a (t, i)
+// pair are computed once and applied to all H heads (consecutive lanes take
+// consecutive i, so every access is coalesced).
 template <typename T>
 __device__ __forceinline__ T cvt_out(float x) { return (T)x; }
 template <>
 __device__ __forceinline__ f16 cvt_out<f16>(float x) { return to_f16_sat(x); }
 
 template <typename Ti, typename To>
-__global__ void rope_kernel(const Ti* x, To* y, const int32_t* __restrict__ pos,  // x may alias y
+__global__ void rope_kernel(const Ti* x, To* y, bf16* y2, const int32_t* __restrict__ pos,  // x may alias y
                             int N, int H, int d, float base, int transpose, float mul) {
   const int half = d / 2;
-  const size_t total = (size_t)N * H * half;
+  const size_t total = (size_t)N * half;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int i = (int)(idx % half);
-    const size_t th = idx / half;
-    const int t = (int)(th / H);
+    const int t = (int)(idx / half);
     float s = 0.f, c = 1.f;
     if (base > 0.f) rope_sincos(pos[t], i, d, base, &s, &c);
     if (transpose) s = -s;
-    s *= mul;
-    c *= mul;
-    const size_t row = th * d;
-    const float x1 = (float)x[row + i], x2 = (float)x[row + i + half];
-    y[row + i] = cvt_out<To>(x1 * c - x2 * s);
-    y[row + i + half] = cvt_out<To>(x2 * c + x1 * s);
+    for (int h = 0; h < H; ++h) {
+      const size_t row = ((size_t)t * H + h) * d;
+      const float x1 = (float)x[row + i], x2 = (float)x[row + i + half];
+      const float r1 = x1 * c - x2 * s, r2 = x2 * c + x1 * s;
+      y[row + i] = cvt_out<To>(mul * r1);
+      y[row + i + half] = cvt_out<To>(mul * r2);
+      if (y2) {
+        y2[row + i] = (bf16)r1;
+        y2[row + i + half] = (bf16)r2;
+      }
+    }
   }
 }
 
 template <typename Ti, typename To>
 hipError_t launch_rope(const Ti* x, To* y, const int32_t* pos, int N, int H, int d, float base, int transpose,
-                       hipStream_t st, float mul) {
-  const size_t total = (size_t)N * H * (d / 2);
+                       hipStream_t st, float mul, bf16* y2) {
+  const size_t total = (size_t)N * (d / 2);
   if (total == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL((rope_kernel<Ti, To>), dim3(blocks), dim3(256), 0, st, x, y, pos, N, H, d, base, transpose,
+  hipLaunchKernelGGL((rope_kernel<Ti, To>), dim3(blocks), dim3(256), 0, st, x, y, y2, pos, N, H, d, base, transpose,
                      mul);
   return hipGetLastError();
 }
 
 template hipError_t launch_rope<float, float>(const float*, float*, const int32_t*, int, int, int, float, int,
-                                              hipStream_t, float);
-template hipError_t launch_rope<bf16, bf16>(const bf16*, bf16*, const int32_t*, int, int, int, float, int,
-                                            hipStream_t, float);
+                                              hipStream_t, float, bf16*);
 template hipError_t launch_rope<bf16, f16>(const bf16*, f16*, const int32_t*, int, int, int, float, int,
-                                           hipStream_t, float);
+                                           hipStream_t, float, bf16*);
 
 namespace fwd {
 

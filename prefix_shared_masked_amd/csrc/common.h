@@ -213,10 +213,11 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // RoPE / conversion pass over a [N, H, d] tensor (attn_fwd.hip); the result
-// is multiplied by mul before the conversion to To.
+// is multiplied by mul before the conversion to To.  A non-null y2 also
+// receives the rotated values (without mul) in bf16.
 template <typename Ti, typename To>
 hipError_t launch_rope(const Ti* x, To* y, const int32_t* pos, int N, int H, int d, float base, int transpose,
-                       hipStream_t st, float mul = 1.f);
+                       hipStream_t st, float mul = 1.f, bf16* y2 = nullptr);
 
 }  // namespace ta
 
