@@ -49,9 +49,6 @@ __device__ __forceinline__ void mfma32h_acc(f32x16& acc, const f16x8& a, const f
 // XDL 16-pass result needs at most 18; this gives 24), and between VALU
 // writes (zero init) and the first MFMA.  The accumulators are operands, so
 // their initialisation and epilogue reads cannot move across the fence.
-__device__ __forceinline__ void agpr_fence4(f32x16 (&x)[4]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]));
-}
 __device__ __forceinline__ void agpr_fence8(f32x16 (&x)[4], f32x16 (&y)[4]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
@@ -94,20 +91,6 @@ __device__ __forceinline__ bf16x8 cat(const bf16x4& a, const bf16x4& b) {
 }
 __device__ __forceinline__ f16x8 cat(const f16x4& a, const f16x4& b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-// MFMA operand rows in LDS are read as two 8-byte halves (ds_read_b64 runs
-// at about twice the bytes per clock of ds_read_b128 on gfx950).  Lane half h
-// then holds the k-slots {4h..4h+3} and {8+4h..8+4h+3} of each group of 16;
-// the other operand uses the same order, so the contraction is unchanged.
-__device__ __forceinline__ f16x8 row_frag(const f16* row, int s, int half) {
-  return cat(*(const f16x4*)(row + s * 16 + 4 * half), *(const f16x4*)(row + s * 16 + 8 + 4 * half));
-}
-__device__ __forceinline__ bf16x8 row_frag(const bf16* row, int s, int half) {
-  return cat(*(const bf16x4*)(row + s * 16 + 4 * half), *(const bf16x4*)(row + s * 16 + 8 + 4 * half));
-}
-// d index of element e (0..7) of k-group s for lane half h in that order
-__device__ __forceinline__ constexpr int frag_d(int s, int half, int e) {
-  return s * 16 + (e >> 2) * 8 + 4 * half + (e & 3);
 }
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -204,11 +187,6 @@ __device__ __forceinline__ void chunk_slot(Ptr ch, int v, int& phys, int& kend) 
   phys = v < ch[1] ? j : ch[4];  // padding slot: a valid row, never visible
   kend = v < ch[1] ? e : 0;
 }
-
-// Order LDS traffic of one wavefront: earlier LDS writes complete before any
-// later LDS access is issued, and the compiler may not move memory accesses
-// across this point.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
