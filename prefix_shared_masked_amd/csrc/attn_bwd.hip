@@ -355,8 +355,12 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
       toff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
     }
 
-  // Items are (query head, 32-row block); all four wavefronts share each
-  // staged block.  Each wavefront issues exactly five copies per block: two
+  // Items are (32-row block, query head), blocks from the end of the query
+  // range down and the heads of the group innermost: the workgroups resident
+  // on an XCD share a KV head and (for nested subtrees) the tail of their
+  // query ranges, so they stream the same rows at about the same time and
+  // one fetch serves them from L2.  All four wavefronts share each staged
+  // block.  Each wavefront issues exactly five copies per block: two
   // 1 KiB copies of Q rows, two of dO rows (rows 4i..4i+3 for i = w, w + 4),
   // and sixteen LSE or D values (wavefront w: LSE rows 16w.. for w < 2, D rows
   // 16(w-2).. otherwise).  Rows past the query range copy the last valid row
@@ -365,8 +369,8 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   const int nitem = P.G * nblk;
   const int w = __builtin_amdgcn_readfirstlane(wave);
   auto stage = [&](int it, char* base) {
-    const int h = kvh * P.G + it / nblk;
-    const int qb = k0 + SUB * (it % nblk);
+    const int h = kvh * P.G + it % P.G;
+    const int qb = k0 + SUB * (nblk - 1 - it / P.G);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = w + 4 * k;
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     }
   };
   auto grads = [&](int it, const char* base, const f32x16& S, const f32x16& dP) {
-    const int qb = k0 + SUB * (it % nblk);
+    const int qb = k0 + SUB * (nblk - 1 - it / P.G);
     const f16* q16 = (const f16*)(base + L::Q16);
     const bf16* dob = (const bf16*)(base + L::DO);
     // transpose reads first: their latency hides behind the exponentials
