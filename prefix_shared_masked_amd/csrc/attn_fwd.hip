@@ -237,13 +237,29 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
           }
         }
       }
+      // Row max of the chunk with the NaN-propagating maximum (v_maximum3):
+      // unlike fmaxf it needs no canonicalising instruction per MFMA result.
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f_fast(m - muse);
+      for (int r = 0; r < 16; ++r)
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
+      mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+      // Lazy rescaling: the reference m moves (and O, l are rescaled) only when
+      // some lane's chunk max exceeds it by more than 8 (log2 units).  Otherwise
+      // the exponentials use the stale m, so P <= 2^8, and O / l and
+      // LSE = m + log2(l) are unchanged: the softmax does not depend on the
+      // reference as long as O, l and m agree.
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.f)) {
+        const float mnew = __builtin_elementwise_maximum(m, mx);
+        const float alpha = exp2f_fast(m - ((mnew == -INFINITY) ? 0.f : mnew));
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        m = mnew;
+      }
+      const float muse = (m == -INFINITY) ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -251,12 +267,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
         s1[r] = exp2f_fast(s1[r] - muse);
         rs += s0[r] + s1[r];
       }
-      l = l * alpha + rs;  // per-lane partial over this lane's key rows
-      m = mnew;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      l += rs;  // per-lane partial over this lane's key rows
       bf16x8 pb[4];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
