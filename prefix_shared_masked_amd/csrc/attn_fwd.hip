@@ -114,22 +114,40 @@ __device__ __forceinline__ void stage_chunk(const Params& P, int c, int kvh, f16
   const ChunkRec ch = load_chunk(as_const(P.fq_chunk) + (size_t)c * TA_CHUNK_INTS);
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  // this lane's row within each 4-row copy and its swizzled 16-byte piece
+  // (rows 4i + l/16 with i = w + 4k share their low four bits)
+  const int sub = l >> 4;
+  const int poff = ((l & 15) ^ swz((4 * w + sub) & 15)) << 3;
+  if (ch.h[0] == 1 && ch.h[1] == BN) {
+    // one segment filling all 64 slots: slot v holds key v + delta
+    const int delta = ch.ks[0] - ch.ko[0];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = w + 4 * k;
-    const int row = 4 * i + (l >> 4);
+    for (int k = 0; k < 4; ++k) {
+      const int i = w + 4 * k;
+      const size_t off = ((size_t)(4 * i + sub + delta) * P.Hkv + kvh) * D + poff;
+      copy16_to_lds(P.k + off, sKb + 4 * i * D);
+      copy16_to_lds(P.v + off, sVb + 4 * i * D);
+    }
+    if (t < BN) {
+      sJb[t] = t + delta;
+      sEb[t] = ch.ke[0];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = w + 4 * k;
+      int j, e;
+      chunk_slot(ch, 4 * i + sub, j, e);
+      const size_t off = ((size_t)j * P.Hkv + kvh) * D + poff;
+      copy16_to_lds(P.k + off, sKb + 4 * i * D);
+      copy16_to_lds(P.v + off, sVb + 4 * i * D);
+    }
     int j, e;
-    chunk_slot(ch, row, j, e);
-    const int piece = (l & 15) ^ swz(row & 15);
-    const size_t off = ((size_t)j * P.Hkv + kvh) * D + piece * 8;
-    copy16_to_lds(P.k + off, sKb + 4 * i * D);
-    copy16_to_lds(P.v + off, sVb + 4 * i * D);
-  }
-  int j, e;
-  chunk_slot(ch, l, j, e);
-  if (t < BN) {
-    sJb[t] = j;
-    sEb[t] = e;
+    chunk_slot(ch, l, j, e);
+    if (t < BN) {
+      sJb[t] = j;
+      sEb[t] = e;
+    }
   }
 }
 
