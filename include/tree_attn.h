@@ -97,7 +97,8 @@ typedef struct ta_plan_view {
   int32_t block_m, block_n, block_kv;
   int32_t n_qtiles, n_chunks, n_ktiles;
   int64_t n_flat;            /* sum over paths of the path length = sum_t g_t */
-  int64_t visible_pairs;     /* sum_t (pos(t) + 1): (i, j) pairs the mask allows, per head */
+  int64_t visible_pairs;     /* sum over query rows t >= q_start of (pos(t) + 1): (i, j) pairs the
+                                mask allows, per head */
   int64_t computed_pairs_fwd;/* pairs the forward tiles compute, per head (>= visible_pairs) */
   int64_t computed_pairs_bwd;/* pairs the backward key tiles compute, per head */
   const int32_t* dfs_order;  /* [n_nodes] node ids in visiting order */
@@ -113,7 +114,9 @@ typedef struct ta_plan_view {
   const int32_t* fq_chunk;   /* [n_chunks * TA_CHUNK_INTS] gathered key chunks (layout above) */
   const int32_t* fq_order;   /* [n_qtiles] query tiles, most chunks first */
   const int32_t* bk;         /* [n_ktiles * 4] (k0, klen, q_end, node), most work first; every
-                                query in [k0, q_end) lies in the node's subtree */
+                                query in [max(k0, q_start), q_end) lies in the node's subtree */
+  int32_t n_prefix_nodes;    /* key-only chain prefix (tree_plan_ex), 0 for tree_plan */
+  int32_t q_start;           /* its tokens [0, q_start) are keys only: no query tiles, no outputs */
 } ta_plan_view;
 
 /* Build the plan of a prefix tree (host only, synchronous, deterministic).
@@ -127,6 +130,22 @@ typedef struct ta_plan_view {
  * set to NULL. */
 ta_status tree_plan(const int32_t* parent, const int32_t* seg_len, int32_t n_nodes,
                     int32_t block_m, int32_t block_n, ta_plan** out);
+
+/* tree_plan with a key-only prefix: the subtree of one partition of a tree
+ * too large for one device, planned below the ancestor chain of its root
+ * (the "gateway" of the Tree Training post, sections 8.1-8.2: a child
+ * partition reads its ancestors' K/V instead of recomputing them).  Nodes
+ * 0..n_prefix_nodes-1 are that chain: node 0 is the only root, node i's
+ * parent is i - 1, and each chain node has exactly one child (the next chain
+ * node; for the last one, the partition's root).  The chain's tokens
+ * [0, q_start) serve as keys only: the forward and dQ kernels form no query
+ * tiles for them and leave their O, LSE and dQ rows untouched, and dK/dV of
+ * a chain key sums over the partition's queries only (the gradient the
+ * partition relays to its parent).  Depth positions count the chain, so they
+ * equal the positions in the whole tree.  n_prefix_nodes = 0 is tree_plan.
+ * Errors as tree_plan, plus TA_EINVAL when the chain rules do not hold. */
+ta_status tree_plan_ex(const int32_t* parent, const int32_t* seg_len, int32_t n_nodes,
+                       int32_t n_prefix_nodes, int32_t block_m, int32_t block_n, ta_plan** out);
 
 ta_status tree_plan_view(const ta_plan* plan, ta_plan_view* view);
 
@@ -244,6 +263,90 @@ ta_status tree_decode_splitkv_ex(ta_dtype dt, const void* q, const void* k, cons
                                  int32_t Hq, int32_t Hkv, int32_t d, int32_t max_len, float scale,
                                  int32_t n_splits, void* o, float* lse, void* ws, size_t ws_bytes,
                                  hipEvent_t* events, int32_t n_events, hipStream_t stream);
+
+/* ---- Partitioning a tree too large for one device (Tree Training post,
+ * section 8) ----------------------------------------------------------------
+ * tree_partition cuts a tree (or forest) along node boundaries into connected
+ * subtrees whose own tokens fit `capacity` (section 8.3: each partition is a
+ * connected subtree, so the partitions form a tree and each has one parent
+ * partition).  Every token belongs to exactly one partition, so the unique
+ * work stays N (section 8.1).  A partition's local tree is the ancestor chain
+ * of its root (key-only, as in tree_plan_ex: the gateway K/V its parent
+ * partitions export, section 8.2) followed by its own nodes in ascending
+ * global id; the chain and the own nodes keep their depth positions.
+ * Cut rule (the post fixes only the constraints): a post-order pass keeps at
+ * each node its own tokens plus the open subtrees of its children and, while
+ * that exceeds capacity, cuts off the largest open child subtree (ties: the
+ * smaller node id).  Partitions are numbered in preorder of their roots, so a
+ * parent partition precedes its children.
+ * parent / seg_len as for tree_plan; capacity >= every seg_len (a node is
+ * never split); block_m / block_n as for tree_plan (used for the local plans).
+ * Errors: TA_EINVAL (null pointer, n_nodes <= 0, capacity < 1, a node longer
+ * than capacity, bad parent), TA_ECYCLE, TA_ERANGE, TA_EUNSUPPORTED,
+ * TA_ENOMEM.  On error *out is NULL. */
+typedef struct ta_partition ta_partition;
+
+typedef struct ta_partition_view {
+  int32_t n_nodes, n_parts;
+  int32_t max_local_tokens;     /* largest chain + own row count of a partition */
+  int32_t reserved;
+  int64_t n_tokens;             /* N = sum of own tokens over the partitions */
+  int64_t naive_tokens;         /* sum of (chain + own) tokens: the rows a partition
+                                   scheme that re-runs the ancestors would compute */
+  const int32_t* part_of;       /* [n_nodes] partition of each node */
+  const int32_t* part_root;     /* [n_parts] global node id of each partition's root */
+  const int32_t* part_parent;   /* [n_parts] parent partition, -1 for a tree's root */
+  const int32_t* n_prefix;      /* [n_parts] chain nodes of the local tree */
+  const int64_t* own_tokens;    /* [n_parts] */
+  const int32_t* local_ptr;     /* [n_parts + 1] CSR over local nodes */
+  const int32_t* local_node;    /* global node id of each local node */
+  const int32_t* local_parent;  /* local parent id (-1 for local node 0) */
+  const int32_t* local_len;     /* seg_len of each local node */
+  const int32_t* tok_ptr;       /* [n_parts + 1] CSR over local rows */
+  const int32_t* tok_idx;       /* global packed row of each local row, in the
+                                   local plan's packed order */
+} ta_partition_view;
+
+ta_status tree_partition(const int32_t* parent, const int32_t* seg_len, int32_t n_nodes,
+                         int64_t capacity, int32_t block_m, int32_t block_n, ta_partition** out);
+ta_status tree_partition_view(const ta_partition* part, ta_partition_view* view);
+/* The local plan of partition i (owned by the partition object). */
+ta_status tree_partition_plan(const ta_partition* part, int32_t i, const ta_plan** plan);
+/* Device image of every local plan and row map, as tree_plan_device_bytes /
+ * tree_plan_upload (the partition must outlive the asynchronous copy). */
+ta_status tree_partition_device_bytes(const ta_partition* part, size_t* bytes);
+ta_status tree_partition_upload(const ta_partition* part, void* dpart, size_t bytes,
+                                hipStream_t stream);
+/* NULL-safe. */
+void tree_partition_free(ta_partition* part);
+
+/* Workspace bytes of tree_partition_fwd (op = 0) / tree_partition_bwd (op = 1). */
+ta_status tree_partition_ws_bytes(const ta_partition* part, int32_t op, ta_dtype dt, int32_t Hq,
+                                  int32_t Hkv, int32_t d, float rope_base, size_t* bytes);
+
+/* Tree attention run one partition at a time through the gateway (section
+ * 8.2), with the whole tree's tensors in the layouts of tree_attn_fwd/bwd.
+ * Each partition gathers its rows (the chain's K/V are the gateway leaves it
+ * reads from its ancestors; the chain's Q, O and dO rows are zero-filled and
+ * never read), runs tree_attn_fwd/bwd on its local plan and writes back its
+ * own rows of O, LSE and dQ.  The backward relays every local dK/dV row,
+ * chain rows included, into an fp32 accumulator per global row (the fp32
+ * accumulator of section 8.2 for cut nodes shared by several children;
+ * partitions are visited in a fixed order, so results are deterministic),
+ * which is finally written to dk/dv in dt.  On one device the partitions run
+ * in sequence; each one is the work a separate device would do.  The results
+ * equal tree_attn_fwd/bwd on the whole tree up to rounding order (in bf16,
+ * each partition's dK/dV is rounded to bf16 once before the fp32 sum).
+ * Errors as tree_attn_fwd/bwd. */
+ta_status tree_partition_fwd(const ta_partition* part, const void* dpart, ta_dtype dt,
+                             const void* q, const void* k, const void* v, int32_t Hq, int32_t Hkv,
+                             int32_t d, float scale, float rope_base, void* o, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+ta_status tree_partition_bwd(const ta_partition* part, const void* dpart, ta_dtype dt,
+                             const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dO, int32_t Hq, int32_t Hkv, int32_t d,
+                             float scale, float rope_base, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* ta_status_string(ta_status s);

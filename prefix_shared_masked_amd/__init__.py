@@ -21,7 +21,8 @@ import os
 
 import numpy as np
 
-__all__ = ["TreeAttnError", "Plan", "HipEvents", "tree_plan", "tree_attn_fwd", "tree_attn_bwd", "tree_weighted_nll",
+__all__ = ["TreeAttnError", "Plan", "Partition", "HipEvents", "tree_plan", "tree_partition", "tree_attn_fwd",
+           "tree_attn_bwd", "tree_partition_fwd", "tree_partition_bwd", "tree_weighted_nll",
            "tree_decode_splitkv", "library_path", "load_library", "TA_BLOCK_M", "TA_BLOCK_N", "TA_BLOCK_KV"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,7 +47,18 @@ class _View(ctypes.Structure):
         [(n, ctypes.c_int64) for n in ("n_flat", "visible_pairs", "computed_pairs_fwd", "computed_pairs_bwd")] + \
         [(n, ctypes.POINTER(ctypes.c_int32)) for n in (
             "dfs_order", "node_start", "node_sub_end", "pos", "g", "node_of", "sub_end", "anc_ptr", "anc",
-            "fq_ptr", "fq_chunk", "fq_order", "bk")]
+            "fq_ptr", "fq_chunk", "fq_order", "bk")] + \
+        [(n, ctypes.c_int32) for n in ("n_prefix_nodes", "q_start")]
+
+
+class _PartView(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_nodes", "n_parts", "max_local_tokens", "reserved")] + \
+        [(n, ctypes.c_int64) for n in ("n_tokens", "naive_tokens")] + \
+        [("part_of", ctypes.POINTER(ctypes.c_int32)), ("part_root", ctypes.POINTER(ctypes.c_int32)),
+         ("part_parent", ctypes.POINTER(ctypes.c_int32)), ("n_prefix", ctypes.POINTER(ctypes.c_int32)),
+         ("own_tokens", ctypes.POINTER(ctypes.c_int64))] + \
+        [(n, ctypes.POINTER(ctypes.c_int32)) for n in (
+            "local_ptr", "local_node", "local_parent", "local_len", "tok_ptr", "tok_idx")]
 
 
 _lib = None
@@ -69,6 +81,7 @@ def load_library():
     pI32 = ctypes.POINTER(ctypes.c_int32)
     sigs = {
         "tree_plan": (I32, [pI32, pI32, I32, I32, I32, ctypes.POINTER(P)]),
+        "tree_plan_ex": (I32, [pI32, pI32, I32, I32, I32, I32, ctypes.POINTER(P)]),
         "tree_plan_view": (I32, [P, ctypes.POINTER(_View)]),
         "tree_plan_device_bytes": (I32, [P, ctypes.POINTER(SZ)]),
         "tree_plan_upload": (I32, [P, P, SZ, P]),
@@ -85,6 +98,15 @@ def load_library():
                                    P]),
         "tree_decode_splitkv_ex": (I32, [I32, P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P, P, P, SZ, P, I32,
                                          P]),
+        "tree_partition": (I32, [pI32, pI32, I32, I64, I32, I32, ctypes.POINTER(P)]),
+        "tree_partition_view": (I32, [P, ctypes.POINTER(_PartView)]),
+        "tree_partition_plan": (I32, [P, I32, ctypes.POINTER(P)]),
+        "tree_partition_device_bytes": (I32, [P, ctypes.POINTER(SZ)]),
+        "tree_partition_upload": (I32, [P, P, SZ, P]),
+        "tree_partition_free": (None, [P]),
+        "tree_partition_ws_bytes": (I32, [P, I32, I32, I32, I32, I32, F32, ctypes.POINTER(SZ)]),
+        "tree_partition_fwd": (I32, [P, P, I32, P, P, P, I32, I32, I32, F32, F32, P, P, P, SZ, P]),
+        "tree_partition_bwd": (I32, [P, P, I32, P, P, P, P, P, P, I32, I32, I32, F32, F32, P, P, P, P, SZ, P]),
         "ta_status_string": (ctypes.c_char_p, [I32]),
     }
     for name, (res, args) in sigs.items():
@@ -107,7 +129,7 @@ def _i32(a) -> np.ndarray:
 class Plan:
     """Host plan of a prefix tree (owned by the library; freed on deletion)."""
 
-    def __init__(self, parent, seg_len, block_m: int = 0, block_n: int = 0):
+    def __init__(self, parent, seg_len, block_m: int = 0, block_n: int = 0, n_prefix_nodes: int = 0):
         L = load_library()
         parent, seg_len = _i32(parent), _i32(seg_len)
         if parent.ndim != 1 or parent.shape != seg_len.shape:
@@ -115,15 +137,31 @@ class Plan:
         self._lib = L
         self._ptr = ctypes.c_void_p()
         pI32 = ctypes.POINTER(ctypes.c_int32)
-        _check("tree_plan", L.tree_plan(parent.ctypes.data_as(pI32), seg_len.ctypes.data_as(pI32),
-                                        int(parent.shape[0]), block_m, block_n, ctypes.byref(self._ptr)))
+        _check("tree_plan", L.tree_plan_ex(parent.ctypes.data_as(pI32), seg_len.ctypes.data_as(pI32),
+                                           int(parent.shape[0]), int(n_prefix_nodes), block_m, block_n,
+                                           ctypes.byref(self._ptr)))
+        self._owner = None
+        self._load_view()
+
+    @classmethod
+    def _borrowed(cls, ptr, owner):
+        """A view of a plan owned by another library object (kept alive by `owner`)."""
+        self = cls.__new__(cls)
+        self._lib = load_library()
+        self._ptr = ctypes.c_void_p(ptr)
+        self._owner = owner
+        self._load_view()
+        return self
+
+    def _load_view(self):
+        L = self._lib
         v = _View()
         _check("tree_plan_view", L.tree_plan_view(self._ptr, ctypes.byref(v)))
         self._v = v
         self._dev = {}
         for name in ("n_nodes", "n_tokens", "n_leaves", "max_pos", "block_m", "block_n", "block_kv",
                      "n_qtiles", "n_chunks", "n_ktiles", "n_flat", "visible_pairs",
-                     "computed_pairs_fwd", "computed_pairs_bwd"):
+                     "computed_pairs_fwd", "computed_pairs_bwd", "n_prefix_nodes", "q_start"):
             setattr(self, name, int(getattr(v, name)))
 
     def _arr(self, name, n):
@@ -167,13 +205,97 @@ class Plan:
 
     def __del__(self):
         ptr = getattr(self, "_ptr", None)
-        if ptr is not None and ptr.value:
+        if ptr is not None and ptr.value and getattr(self, "_owner", None) is None:
             self._lib.tree_plan_free(ptr)
             self._ptr = None
 
 
-def tree_plan(parent, seg_len, block_m: int = 0, block_n: int = 0) -> Plan:
-    return Plan(parent, seg_len, block_m, block_n)
+def tree_plan(parent, seg_len, block_m: int = 0, block_n: int = 0, n_prefix_nodes: int = 0) -> Plan:
+    """Plan of a prefix tree; n_prefix_nodes > 0 plans nodes 0..n-1 as a key-only ancestor chain
+    (tree_plan_ex)."""
+    return Plan(parent, seg_len, block_m, block_n, n_prefix_nodes)
+
+
+class Partition:
+    """Connected-subtree partition of a tree under a token capacity (tree_partition), with each
+    partition's local plan (its root's ancestor chain as a key-only prefix)."""
+
+    def __init__(self, parent, seg_len, capacity: int, block_m: int = 0, block_n: int = 0):
+        L = load_library()
+        parent, seg_len = _i32(parent), _i32(seg_len)
+        if parent.ndim != 1 or parent.shape != seg_len.shape:
+            raise ValueError("parent and seg_len must be 1-D arrays of equal length")
+        self._lib = L
+        self._ptr = ctypes.c_void_p()
+        pI32 = ctypes.POINTER(ctypes.c_int32)
+        _check("tree_partition", L.tree_partition(parent.ctypes.data_as(pI32), seg_len.ctypes.data_as(pI32),
+                                                  int(parent.shape[0]), int(capacity), block_m, block_n,
+                                                  ctypes.byref(self._ptr)))
+        v = _PartView()
+        _check("tree_partition_view", L.tree_partition_view(self._ptr, ctypes.byref(v)))
+        self._v = v
+        self._dev = {}
+        for name in ("n_nodes", "n_parts", "max_local_tokens", "n_tokens", "naive_tokens"):
+            setattr(self, name, int(getattr(v, name)))
+        self.plans = []
+        for i in range(self.n_parts):
+            pp = ctypes.c_void_p()
+            _check("tree_partition_plan", L.tree_partition_plan(self._ptr, i, ctypes.byref(pp)))
+            self.plans.append(Plan._borrowed(pp.value, self) if pp.value else None)
+
+    def _arr(self, name, n):
+        if n == 0:
+            return np.zeros(0, getattr(self._v, name)._type_)
+        return np.ctypeslib.as_array(getattr(self._v, name), shape=(n,)).copy()
+
+    def view(self) -> dict:
+        """Copies of the partition tables as numpy arrays."""
+        n, P = self.n_nodes, self.n_parts
+        local_ptr = self._arr("local_ptr", P + 1)
+        tok_ptr = self._arr("tok_ptr", P + 1)
+        return dict(
+            part_of=self._arr("part_of", n), part_root=self._arr("part_root", P),
+            part_parent=self._arr("part_parent", P), n_prefix=self._arr("n_prefix", P),
+            own_tokens=self._arr("own_tokens", P), local_ptr=local_ptr,
+            local_node=self._arr("local_node", int(local_ptr[-1])),
+            local_parent=self._arr("local_parent", int(local_ptr[-1])),
+            local_len=self._arr("local_len", int(local_ptr[-1])), tok_ptr=tok_ptr,
+            tok_idx=self._arr("tok_idx", int(tok_ptr[-1])))
+
+    @property
+    def handle(self):
+        return self._ptr
+
+    def device(self, device=None):
+        """Every local plan and row map uploaded to device memory (a torch uint8 tensor, cached)."""
+        import torch
+        dev = torch.device(device if device is not None else "cuda")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        key = str(dev)
+        if key not in self._dev:
+            n = ctypes.c_size_t()
+            _check("tree_partition_device_bytes",
+                   self._lib.tree_partition_device_bytes(self._ptr, ctypes.byref(n)))
+            buf = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+            st = torch.cuda.current_stream(dev)
+            _check("tree_partition_upload", self._lib.tree_partition_upload(
+                self._ptr, ctypes.c_void_p(buf.data_ptr()), int(n.value), ctypes.c_void_p(st.cuda_stream)))
+            st.synchronize()  # the host tables are pageable: finish the copy before returning
+            self._dev[key] = buf
+        return self._dev[key]
+
+    def __del__(self):
+        ptr = getattr(self, "_ptr", None)
+        if ptr is not None and ptr.value:
+            self.plans = []
+            self._lib.tree_partition_free(ptr)
+            self._ptr = None
+
+
+def tree_partition(parent, seg_len, capacity: int, block_m: int = 0, block_n: int = 0) -> Partition:
+    """Cut a tree into connected subtrees of at most `capacity` own tokens (tree_partition)."""
+    return Partition(parent, seg_len, capacity, block_m, block_n)
 
 
 def _dt(t):
@@ -316,6 +438,61 @@ def tree_attn_bwd(plan: Plan, q, k, v, o, lse, dO, scale: float = 0.0, rope_base
         plan.handle, _ptr(plan.device(dev)), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
         Hq, Hkv, d, float(scale), float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsn, ev, nev,
         _stream(q)))
+    return dq, dk, dv
+
+
+def partition_ws_bytes(part: Partition, op: int, dtype_code: int, Hq: int, Hkv: int, d: int,
+                       rope_base: float) -> int:
+    n = ctypes.c_size_t()
+    _check("tree_partition_ws_bytes", load_library().tree_partition_ws_bytes(
+        part.handle, op, dtype_code, Hq, Hkv, d, float(rope_base), ctypes.byref(n)))
+    return int(n.value)
+
+
+def tree_partition_fwd(part: Partition, q, k, v, scale: float = 0.0, rope_base: float = 0.0, o=None, lse=None,
+                       ws=None):
+    """tree_attn_fwd run one partition at a time through the gateway.  Same layouts as tree_attn_fwd."""
+    import torch
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if N != part.n_tokens:
+        raise ValueError(f"q has {N} tokens, the partition {part.n_tokens}")
+    for name, t, shp in (("q", q, (N, Hq, d)), ("k", k, (N, Hkv, d)), ("v", v, (N, Hkv, d))):
+        _need(t, name, shp, q.dtype, dev)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(Hq, N, dtype=torch.float32, device=dev) if lse is None else lse
+    _need(o, "o", (N, Hq, d), q.dtype, dev)
+    _need(lse, "lse", (Hq, N), torch.float32, dev)
+    dt = _dt(q)
+    ws, wsn = _workspace(partition_ws_bytes(part, 0, dt, Hq, Hkv, d, rope_base), dev, ws)
+    _check("tree_partition_fwd", load_library().tree_partition_fwd(
+        part.handle, _ptr(part.device(dev)), dt, _ptr(q), _ptr(k), _ptr(v), Hq, Hkv, d, float(scale),
+        float(rope_base), _ptr(o), _ptr(lse), _ptr(ws), wsn, _stream(q)))
+    return o, lse
+
+
+def tree_partition_bwd(part: Partition, q, k, v, o, lse, dO, scale: float = 0.0, rope_base: float = 0.0,
+                       dq=None, dk=None, dv=None, ws=None):
+    """Backward of tree_partition_fwd -> (dq, dk, dv), with the gateway gradients relayed in fp32."""
+    import torch
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if N != part.n_tokens:
+        raise ValueError(f"q has {N} tokens, the partition {part.n_tokens}")
+    for name, t, shp in (("q", q, (N, Hq, d)), ("k", k, (N, Hkv, d)), ("v", v, (N, Hkv, d)),
+                         ("o", o, (N, Hq, d)), ("dO", dO, (N, Hq, d))):
+        _need(t, name, shp, q.dtype, dev)
+    _need(lse, "lse", (Hq, N), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dt = _dt(q)
+    ws, wsn = _workspace(partition_ws_bytes(part, 1, dt, Hq, Hkv, d, rope_base), dev, ws)
+    _check("tree_partition_bwd", load_library().tree_partition_bwd(
+        part.handle, _ptr(part.device(dev)), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+        Hq, Hkv, d, float(scale), float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsn, _stream(q)))
     return dq, dk, dv
 
 

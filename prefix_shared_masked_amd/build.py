@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtree_attn.so")
-SOURCES = ["plan.cpp", "attn_fwd.hip", "attn_bwd.hip", "nll.hip", "decode.hip"]
+SOURCES = ["plan.cpp", "partition.cpp", "gateway.hip", "attn_fwd.hip", "attn_bwd.hip", "nll.hip", "decode.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

@@ -55,6 +55,7 @@ struct DQParams {
   const int32_t* fq_chunk;
   const int32_t* fq_order;
   int N, Hq, Hkv, G;
+  int q0;  // first query row (rows below are a key-only prefix)
   float scale, scale_log2, rope_base;
 };
 
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
   const int hsub = blockIdx.y * 4 + wave;
   const bool active = hsub < P.G;
   const int h = kvh * P.G + (active ? hsub : 0);
-  const int qi = tile * BM + col;
+  const int qi = P.q0 + tile * BM + col;
   const bool qvalid = qi < P.N;
   const size_t rowoff = ((size_t)(qvalid ? qi : 0) * P.Hq + h) * D;
 
@@ -301,6 +302,7 @@ struct KVParams {
   const int32_t* pos;
   const int32_t* bk;
   int N, Hq, Hkv, G;
+  int q0;  // first query row (rows below are a key-only prefix)
   float scale, scale_log2, rope_base;
 };
 
@@ -326,6 +328,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   const int kvh = blockIdx.x % P.Hkv;
   const cint_ptr tl = as_const(P.bk) + (size_t)(blockIdx.x / P.Hkv) * 4;
   const int k0 = tl[0], klen = tl[1], qe = tl[2];
+  const int qs = max(k0, P.q0);                   // first query row of the tile
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int col = lane & 31, half = lane >> 5;
   const int kw = k0 + SUB * wave;                 // this wavefront's first key
@@ -383,12 +386,12 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   // and sixteen LSE or D values (wavefront w: LSE rows 16w.. for w < 2, D rows
   // 16(w-2).. otherwise).  Rows past the query range copy the last valid row
   // and are masked to P = 0 below, so they contribute nothing.
-  const int nblk = (qe - k0 + SUB - 1) / SUB;
+  const int nblk = qe > qs ? (qe - qs + SUB - 1) / SUB : 0;
   const int nitem = P.G * nblk;
   const int w = __builtin_amdgcn_readfirstlane(wave);
   auto stage = [&](int it, char* base) {
     const int h = kvh * P.G + it % P.G;
-    const int qb = k0 + SUB * (nblk - 1 - it / P.G);
+    const int qb = qs + SUB * (nblk - 1 - it / P.G);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = w + 4 * k;
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     }
   };
   auto grads = [&](int it, const char* base, const f32x16& S, const f32x16& dP) {
-    const int qb = k0 + SUB * (nblk - 1 - it / P.G);
+    const int qb = qs + SUB * (nblk - 1 - it / P.G);
     const f16* q16 = (const f16*)(base + L::Q16);
     const bf16* dob = (const bf16*)(base + L::DO);
     // transpose reads first: their latency hides behind the exponentials
@@ -492,6 +495,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   // nitem >= 1: a tile's query range holds at least its own first key.
   const int last = nitem - 1;
   char* const bb[4] = {smem, smem + L::BYTES, smem + 2 * L::BYTES, smem + 3 * L::BYTES};
+  if (nitem > 0) {  // uniform; a tile with no query rows writes zero gradients
   stage(0, bb[0]);
   stage(min(1, last), bb[1]);
   stage(min(2, last), bb[2]);
@@ -516,6 +520,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     }
   }
   lds_copies_wait();
+  }
 
   agpr_fence8(dk, dv);
   // Each wavefront owns its keys: scale and rotate dK back, store dK and dV.
@@ -556,9 +561,9 @@ __global__ __launch_bounds__(TA_BLOCK_M) void dq_f32_kernel(const float* __restr
                                                              float* __restrict__ dq, float* __restrict__ Dd,
                                                              const int32_t* __restrict__ fq_ptr,
                                                              const int32_t* __restrict__ fq_chunk, int N, int Hq,
-                                                             int Hkv, float scale) {
+                                                             int Hkv, float scale, int q0) {
   const int tile = blockIdx.x, h = blockIdx.y, G = Hq / Hkv, kvh = h / G;
-  const int i = tile * TA_BLOCK_M + threadIdx.x;
+  const int i = q0 + tile * TA_BLOCK_M + threadIdx.x;
   if (i >= N) return;
   const size_t ro = ((size_t)i * Hq + h) * D_;
   float Di = 0.f;
@@ -594,7 +599,7 @@ __global__ __launch_bounds__(TA_BLOCK_KV) void dkv_f32_kernel(const float* __res
                                                                const float* __restrict__ lse, const float* __restrict__ Dd,
                                                                float* __restrict__ dk, float* __restrict__ dv,
                                                                const int32_t* __restrict__ bk, int N, int Hq, int Hkv,
-                                                               float scale) {
+                                                               float scale, int q0) {
   const int32_t* tl = bk + (size_t)blockIdx.x * 4;
   const int kvh = blockIdx.y, G = Hq / Hkv;
   if ((int)threadIdx.x >= tl[1]) return;
@@ -604,7 +609,7 @@ __global__ __launch_bounds__(TA_BLOCK_KV) void dkv_f32_kernel(const float* __res
   for (int x = 0; x < D_; ++x) gk[x] = gv[x] = 0.f;
   for (int hs = 0; hs < G; ++hs) {
     const int h = kvh * G + hs;
-    for (int i = j; i < qe; ++i) {
+    for (int i = max(j, q0); i < qe; ++i) {
       const size_t ro = ((size_t)i * Hq + h) * D_;
       float s = 0.f, dp = 0.f;
       for (int x = 0; x < D_; ++x) {
@@ -710,6 +715,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     A.Hq = Hq;
     A.Hkv = Hkv;
     A.G = Hq / Hkv;
+    A.q0 = p->q_start;
     A.scale = scale;
     A.scale_log2 = scale * TA_LOG2E;
     A.rope_base = rope_base;
@@ -732,6 +738,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.Hq = Hq;
     B.Hkv = Hkv;
     B.G = Hq / Hkv;
+    B.q0 = p->q_start;
     B.scale = scale;
     B.scale_log2 = scale * TA_LOG2E;
     B.rope_base = rope_base;
@@ -755,18 +762,24 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   dim3 g1(p->n_qtiles, Hq), g2(p->n_ktiles, Hkv);
   if (d == 64) {
     hipLaunchKernelGGL(bwd::dq_f32_kernel<64>, g1, dim3(TA_BLOCK_M), 0, stream, qq, kk, (const float*)v,
-                       (const float*)o, (const float*)dO, lse, (float*)dq, Dd, fq_ptr, fq_chunk, N, Hq, Hkv, scale);
+                       (const float*)o, (const float*)dO, lse, (float*)dq, Dd, fq_ptr, fq_chunk, N, Hq, Hkv, scale,
+                       p->q_start);
     hipLaunchKernelGGL(bwd::dkv_f32_kernel<64>, g2, dim3(TA_BLOCK_KV), 0, stream, qq, kk, (const float*)v,
-                       (const float*)dO, lse, Dd, (float*)dk, (float*)dv, bk, N, Hq, Hkv, scale);
+                       (const float*)dO, lse, Dd, (float*)dk, (float*)dv, bk, N, Hq, Hkv, scale,
+                       p->q_start);
   } else {
     hipLaunchKernelGGL(bwd::dq_f32_kernel<128>, g1, dim3(TA_BLOCK_M), 0, stream, qq, kk, (const float*)v,
-                       (const float*)o, (const float*)dO, lse, (float*)dq, Dd, fq_ptr, fq_chunk, N, Hq, Hkv, scale);
+                       (const float*)o, (const float*)dO, lse, (float*)dq, Dd, fq_ptr, fq_chunk, N, Hq, Hkv, scale,
+                       p->q_start);
     hipLaunchKernelGGL(bwd::dkv_f32_kernel<128>, g2, dim3(TA_BLOCK_KV), 0, stream, qq, kk, (const float*)v,
-                       (const float*)dO, lse, Dd, (float*)dk, (float*)dv, bk, N, Hq, Hkv, scale);
+                       (const float*)dO, lse, Dd, (float*)dk, (float*)dv, bk, N, Hq, Hkv, scale,
+                       p->q_start);
   }
   TA_LAUNCH_CHECK();
   if (rope) {
-    if (launch_rope<float, float>((const float*)dq, (float*)dq, pos, N, Hq, d, rope_base, 1, stream) != hipSuccess)
+    const int q0 = p->q_start;  // prefix rows of dQ are not outputs: leave them untouched
+    if (launch_rope<float, float>((const float*)dq + (size_t)q0 * Hq * d, (float*)dq + (size_t)q0 * Hq * d,
+                                  pos + q0, N - q0, Hq, d, rope_base, 1, stream) != hipSuccess)
       return TA_EHIP;
     if (launch_rope<float, float>((const float*)dk, (float*)dk, pos, N, Hkv, d, rope_base, 1, stream) != hipSuccess)
       return TA_EHIP;

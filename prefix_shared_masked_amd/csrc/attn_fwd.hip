@@ -103,6 +103,7 @@ struct Params {
   const int32_t* fq_chunk;
   const int32_t* fq_order;
   int N, Hq, Hkv, G;
+  int q0;  // first query row (rows below are a key-only prefix)
   float rope_base;
 };
 
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
   const int hsub = blockIdx.y * 4 + wave;
   const bool active = hsub < P.G;
   const int h = kvh * P.G + (active ? hsub : 0);
-  const int qi = tile * BM + col;
+  const int qi = P.q0 + tile * BM + col;
   const bool qvalid = qi < P.N;
 
   // Q (rotated by depth position, fp16) as the B operand: lane = query
@@ -335,9 +336,9 @@ __global__ __launch_bounds__(TA_BLOCK_M) void fwd_f32_kernel(const float* __rest
                                                               const float* __restrict__ v, float* __restrict__ o,
                                                               float* __restrict__ lse, const int32_t* __restrict__ fq_ptr,
                                                               const int32_t* __restrict__ fq_chunk, int N, int Hq, int Hkv,
-                                                              float scale) {
+                                                              float scale, int q0) {
   const int tile = blockIdx.x, h = blockIdx.y, G = Hq / Hkv, kvh = h / G;
-  const int i = tile * TA_BLOCK_M + threadIdx.x;
+  const int i = q0 + tile * TA_BLOCK_M + threadIdx.x;
   if (i >= N) return;
   float qv[D], acc[D];
   for (int x = 0; x < D; ++x) {
@@ -474,6 +475,7 @@ extern "C" ta_status tree_attn_fwd_ex(const ta_plan* p, const void* dplan, ta_dt
     P.Hq = Hq;
     P.Hkv = Hkv;
     P.G = Hq / Hkv;
+    P.q0 = p->q_start;
     P.rope_base = rope_base;
     dim3 grid(p->n_qtiles * Hkv, (P.G + 3) / 4);
     hipLaunchKernelGGL(fwd::fwd_bf16_kernel, grid, dim3(256), 0, stream, P);
@@ -496,10 +498,10 @@ extern "C" ta_status tree_attn_fwd_ex(const ta_plan* p, const void* dplan, ta_dt
   dim3 grid(p->n_qtiles, Hq);
   if (d == 64)
     hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(TA_BLOCK_M), 0, stream, qq, kk, (const float*)v, (float*)o, lse,
-                       fq_ptr, fq_chunk, N, Hq, Hkv, scale);
+                       fq_ptr, fq_chunk, N, Hq, Hkv, scale, p->q_start);
   else
     hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(TA_BLOCK_M), 0, stream, qq, kk, (const float*)v, (float*)o,
-                       lse, fq_ptr, fq_chunk, N, Hq, Hkv, scale);
+                       lse, fq_ptr, fq_chunk, N, Hq, Hkv, scale, p->q_start);
   TA_LAUNCH_CHECK();
   mark(ev, nev, 2, stream);
   return TA_OK;

@@ -132,14 +132,19 @@ __device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 2) | ((
 // because the compiler cannot tell that the copies target the buffer nobody
 // is reading and would wait for them before every LDS read; the cost is that
 // the copies are invisible to its wait-count bookkeeping, so whoever reads the
-// data must first run lds_copies_wait() (then a workgroup barrier).
+// data must first run lds_copies_wait() (then a workgroup barrier).  M0 is
+// listed as clobbered for the reader; the compiler reserves M0 and emits no
+// other M0 use in these kernels (checked in the generated code), so nothing
+// it keeps there is lost.
 __device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds_base) {
-  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory", "m0");
 }
 // 4-byte variant (global_load_lds_dword): lane i writes lds_base + 4 i.
 __device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds_base) {
-  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(a) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_copies_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -38,8 +38,9 @@ struct Segment {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_plan* p) {
+ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_t n_prefix, ta_plan* p) {
   p->n_nodes = n;
+  p->n_prefix_nodes = n_prefix;
   p->block_m = TA_BLOCK_M;
   p->block_n = TA_BLOCK_N;
   p->block_kv = TA_BLOCK_KV;
@@ -79,6 +80,23 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_pla
   const int32_t N = static_cast<int32_t>(cursor);
   p->n_tokens = N;
 
+  // Key-only prefix: nodes 0..n_prefix-1 form a chain from the only root (node
+  // i's parent is i - 1, and each has exactly one child, the next chain node
+  // or, for the last one, the root of everything else).  The chain is then
+  // visited first, so its tokens are [0, q_start).
+  if (n_prefix > 0) {
+    if (roots.size() != 1 || roots[0] != 0) return TA_EINVAL;
+    for (int32_t i = 0; i < n_prefix; ++i) {
+      if (i > 0 && parent[i] != i - 1) return TA_EINVAL;
+      if (i + 1 < n_prefix && (child_ptr[i + 1] - child_ptr[i] != 1 || child[child_ptr[i]] != i + 1))
+        return TA_EINVAL;
+      if (i + 1 == n_prefix && child_ptr[i + 1] - child_ptr[i] > 1) return TA_EINVAL;
+    }
+    p->q_start = p->node_start[n_prefix - 1] + seg_len[n_prefix - 1];
+    if (p->q_start == N) return TA_EINVAL;  // the nodes below the chain hold no token
+  }
+  const int32_t Q0 = p->q_start;
+
   // bottom-up: subtree token counts and leaf counts
   std::vector<int64_t> sub_tok(n, 0), leaves(n, 0);
   for (int32_t r = n - 1; r >= 0; --r) {
@@ -113,7 +131,7 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_pla
       p->node_of[s + j] = node;
       p->sub_end[s + j] = p->node_sub_end[node];
       n_flat += leaves[node];
-      pairs += ps + 1;
+      if (s + j >= Q0) pairs += ps + 1;  // pairs whose query is a real (non-prefix) row
       max_pos = std::max(max_pos, ps);
     }
   }
@@ -138,14 +156,14 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_pla
 
   // forward tiles: union of visible node segments, packed into key chunks
   const int32_t BM = p->block_m, BN = p->block_n;
-  const int32_t n_qt = (N + BM - 1) / BM;
+  const int32_t n_qt = (N - Q0 + BM - 1) / BM;  // query tiles cover rows [q_start, N)
   p->n_qtiles = n_qt;
   p->fq_ptr.assign(n_qt + 1, 0);
   std::vector<int32_t> stamp(n, -1);
   std::vector<Segment> segs;
   int64_t comp_fwd = 0;
   for (int32_t t = 0; t < n_qt; ++t) {
-    const int32_t q0 = t * BM, q1 = std::min(N, q0 + BM);
+    const int32_t q0 = Q0 + t * BM, q1 = std::min(N, q0 + BM);
     segs.clear();
     for (int32_t i = q0; i < q1;) {
       const int32_t b = p->node_of[i];
@@ -225,8 +243,9 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_pla
   });
 
   // backward key tiles, most work first.  A tile holds up to TA_BLOCK_KV keys
-  // of one node; the kernel splits it into 32-key sub-tiles, sub-tile s
-  // reading the 32-row query blocks from its own diagonal block onwards.
+  // of one node; its queries are the rows [max(k0, q_start), q_end) (the key-
+  // only prefix has no query rows); the kernel runs 32-key sub-tiles against
+  // 32-row query blocks.
   const int32_t BK = p->block_kv, SUB = TA_KV_SUB;
   struct KT {
     int32_t k0, klen, qe, node;
@@ -237,10 +256,10 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_pla
   for (int32_t node : p->dfs_order) {
     const int32_t s = p->node_start[node], e = s + seg_len[node], qe = p->node_sub_end[node];
     for (int32_t k0 = s; k0 < e; k0 += BK) {
-      const int32_t kl = std::min(BK, e - k0);
-      const int64_t nblk = (int64_t(qe - k0) + SUB - 1) / SUB;
+      const int32_t kl = std::min(BK, e - k0), qs = std::max(k0, Q0);
+      const int64_t nblk = (int64_t(std::max(qe - qs, 0)) + SUB - 1) / SUB;
       int64_t blocks = 0;
-      for (int32_t sub = 0; sub * SUB < kl; ++sub) blocks += nblk - sub;
+      for (int32_t sub = 0; sub * SUB < kl; ++sub) blocks += std::max<int64_t>(nblk - (qs == k0 ? sub : 0), 0);
       kts.push_back({k0, kl, qe, node, blocks});
       comp_bwd += blocks * SUB * SUB;
     }
@@ -277,9 +296,14 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, ta_pla
 
 extern "C" ta_status tree_plan(const int32_t* parent, const int32_t* seg_len, int32_t n_nodes,
                                int32_t block_m, int32_t block_n, ta_plan** out) {
+  return tree_plan_ex(parent, seg_len, n_nodes, 0, block_m, block_n, out);
+}
+
+extern "C" ta_status tree_plan_ex(const int32_t* parent, const int32_t* seg_len, int32_t n_nodes,
+                                  int32_t n_prefix_nodes, int32_t block_m, int32_t block_n, ta_plan** out) {
   if (!out) return TA_EINVAL;
   *out = nullptr;
-  if (!parent || !seg_len || n_nodes <= 0) return TA_EINVAL;
+  if (!parent || !seg_len || n_nodes <= 0 || n_prefix_nodes < 0 || n_prefix_nodes > n_nodes) return TA_EINVAL;
   if ((block_m != 0 && block_m != TA_BLOCK_M) || (block_n != 0 && block_n != TA_BLOCK_N))
     return TA_EUNSUPPORTED;
   for (int32_t i = 0; i < n_nodes; ++i) {
@@ -290,7 +314,7 @@ extern "C" ta_status tree_plan(const int32_t* parent, const int32_t* seg_len, in
   if (!p) return TA_ENOMEM;
   ta_status st;
   try {
-    st = build(parent, seg_len, n_nodes, p);
+    st = build(parent, seg_len, n_nodes, n_prefix_nodes, p);
   } catch (const std::bad_alloc&) {
     st = TA_ENOMEM;
   }
@@ -332,6 +356,8 @@ extern "C" ta_status tree_plan_view(const ta_plan* p, ta_plan_view* v) {
   v->fq_chunk = p->fq_chunk.data();
   v->fq_order = p->fq_order.data();
   v->bk = p->bk.data();
+  v->n_prefix_nodes = p->n_prefix_nodes;
+  v->q_start = p->q_start;
   return TA_OK;
 }
 

@@ -6,6 +6,7 @@
 
 struct ta_plan {
   int32_t n_nodes = 0, n_tokens = 0, n_leaves = 0, max_pos = -1;
+  int32_t n_prefix_nodes = 0, q_start = 0;  // key-only chain prefix: tokens [0, q_start)
   int32_t block_m = 0, block_n = 0, block_kv = 0;
   int32_t n_qtiles = 0, n_chunks = 0, n_ktiles = 0;
   int64_t n_flat = 0, visible_pairs = 0, computed_pairs_fwd = 0, computed_pairs_bwd = 0;

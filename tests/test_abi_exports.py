@@ -24,7 +24,10 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("tree_plan", "tree_plan_view", "tree_plan_device_bytes", "tree_plan_upload", "tree_plan_free",
               "tree_attn_ws_bytes", "tree_attn_fwd", "tree_attn_bwd", "tree_nll_ws_bytes", "tree_weighted_nll",
-              "tree_decode_ws_bytes", "tree_decode_splitkv", "ta_status_string"):
+              "tree_decode_ws_bytes", "tree_decode_splitkv", "ta_status_string", "tree_plan_ex",
+              "tree_partition", "tree_partition_view", "tree_partition_plan", "tree_partition_device_bytes",
+              "tree_partition_upload", "tree_partition_free", "tree_partition_ws_bytes", "tree_partition_fwd",
+              "tree_partition_bwd"):
         assert n in names
 
 
