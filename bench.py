@@ -98,6 +98,52 @@ def time_tree(pkg, tree, steps, warmup, dev, seed=0, Hq=32, Hkv=8, d=128, rope=1
     return res
 
 
+def time_partitioned(pkg, tree, capacity, steps, warmup, dev, seed=0, Hq=32, Hkv=8, d=128, rope=10000.0):
+    """fwd+bwd through tree_partition_fwd/bwd (partition at a time, gateway
+    gathers and the fp32 relay of chain dK/dV).  Returns averages (ms)."""
+    import torch
+    part = pkg.tree_partition(tree.parent, tree.seg_len, capacity)
+    part.device(dev)
+    whole = pkg.tree_plan(tree.parent, tree.seg_len)
+    q, k, v, do = make_inputs(part.n_tokens, Hq, Hkv, d, seed, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(Hq, part.n_tokens, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wf = torch.empty(max(1, pkg.partition_ws_bytes(part, 0, 1, Hq, Hkv, d, rope)), dtype=torch.uint8, device=dev)
+    wb = torch.empty(max(1, pkg.partition_ws_bytes(part, 1, 1, Hq, Hkv, d, rope)), dtype=torch.uint8, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def step(i=None):
+        if i is not None:
+            evs[i][0].record()
+        pkg.tree_partition_fwd(part, q, k, v, rope_base=rope, o=o, lse=lse, ws=wf)
+        if i is not None:
+            evs[i][1].record()
+        pkg.tree_partition_bwd(part, q, k, v, o, lse, do, rope_base=rope, dq=dq, dk=dk, dv=dv, ws=wb)
+        if i is not None:
+            evs[i][2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    fwd = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    bwd = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+    P = whole.visible_pairs
+    local_pairs = sum(pl.visible_pairs for pl in part.plans if pl is not None)
+    assert local_pairs == P  # every visible (query, key) pair is computed exactly once
+    ms = fwd + bwd
+    res = dict(capacity=capacity, n_parts=part.n_parts, n_tokens=part.n_tokens, naive_tokens=part.naive_tokens,
+               max_local_tokens=part.max_local_tokens, ms_per_step=ms, fwd_ms=fwd, bwd_ms=bwd,
+               tflops=14 * d * Hq * P / (ms * 1e-3) / 1e12)
+    del q, k, v, do, o, dq, dk, dv, wf, wb
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_decode(pkg, L, steps, warmup, dev, B=8, Hq=32, Hkv=8, d=128, seed=5):
     import torch
     g = torch.Generator(device=dev).manual_seed(seed)
@@ -203,6 +249,12 @@ def main():
             print(f"[bench] {name} fwd+bwd", flush=True)
             r = time_tree(pkg, tree, max(3, args.steps // 2), args.warmup, dev)
             extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "flops_alg"}
+        for cap in (4096,):
+            print(f"[bench] spine tree partitioned at {cap} tokens, fwd+bwd", flush=True)
+            r = time_partitioned(pkg, spine, cap, max(3, args.steps // 2), args.warmup, dev)
+            r["vs_whole_tree"] = round(head["ms_per_step"] / r["ms_per_step"], 4)
+            extra[f"spine_partitioned_{cap}"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                                 for k, v in r.items()}
         extra["decode"] = []
         for L in (32768, 65536, 131072, 262144):
             print(f"[bench] decode L={L}", flush=True)

@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   // and sixteen LSE or D values (wavefront w: LSE rows 16w.. for w < 2, D rows
   // 16(w-2).. otherwise).  Rows past the query range copy the last valid row
   // and are masked to P = 0 below, so they contribute nothing.
-  const int nblk = qe > qs ? (qe - qs + SUB - 1) / SUB : 0;
+  const int nblk = (qe - qs + SUB - 1) / SUB;     // >= 1: the plan gives every tile a query row
   const int nitem = P.G * nblk;
   const int w = __builtin_amdgcn_readfirstlane(wave);
   auto stage = [&](int it, char* base) {
@@ -492,10 +492,9 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   // repeat the last item, into a buffer / registers nobody uses), so every
   // wavefront always has exactly five copies per block in flight and "at
   // most five outstanding" after a step means block it + 2 has landed.
-  // nitem >= 1: a tile's query range holds at least its own first key.
+  // nitem >= 1: every tile's query range holds at least one row.
   const int last = nitem - 1;
   char* const bb[4] = {smem, smem + L::BYTES, smem + 2 * L::BYTES, smem + 3 * L::BYTES};
-  if (nitem > 0) {  // uniform; a tile with no query rows writes zero gradients
   stage(0, bb[0]);
   stage(min(1, last), bb[1]);
   stage(min(2, last), bb[2]);
@@ -520,7 +519,6 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     }
   }
   lds_copies_wait();
-  }
 
   agpr_fence8(dk, dv);
   // Each wavefront owns its keys: scale and rotate dK back, store dK and dV.

@@ -136,15 +136,20 @@ __device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 2) | ((
 // listed as clobbered for the reader; the compiler reserves M0 and emits no
 // other M0 use in these kernels (checked in the generated code), so nothing
 // it keeps there is lost.
+// The LDS address of a generic pointer into shared memory: a flat address in
+// the LDS aperture holds the LDS offset in its low 32 bits (the aperture base
+// is the high half), so truncation gives it without the null check an
+// address-space cast carries.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
 __device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds_base) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base);
+  const uint32_t a = lds_addr(lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory", "m0");
 }
 // 4-byte variant (global_load_lds_dword): lane i writes lds_base + 4 i.
 __device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds_base) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base);
+  const uint32_t a = lds_addr(lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(a) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_copies_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -257,6 +257,10 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
     const int32_t s = p->node_start[node], e = s + seg_len[node], qe = p->node_sub_end[node];
     for (int32_t k0 = s; k0 < e; k0 += BK) {
       const int32_t kl = std::min(BK, e - k0), qs = std::max(k0, Q0);
+      // every tile has a query row: its own first key, or (a chain key) the
+      // rows below the chain, whose DFS interval it spans; the dK/dV kernel
+      // relies on it
+      if (qe <= qs) return TA_EINVAL;
       const int64_t nblk = (int64_t(std::max(qe - qs, 0)) + SUB - 1) / SUB;
       int64_t blocks = 0;
       for (int32_t sub = 0; sub * SUB < kl; ++sub) blocks += std::max<int64_t>(nblk - (qs == k0 ? sub : 0), 0);
