@@ -227,6 +227,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--secondary", default="random_agentic_tree,varlen_forest,spine_partitioned_4096,decode",
+                    help="comma-separated secondary workloads to run after the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: tree attention here runs on a single device "
@@ -244,19 +246,26 @@ def main():
     print("[bench] spine tree fwd+bwd", flush=True)
     head = time_tree(pkg, spine, args.steps, args.warmup, dev)
     extra = {}
-    if not args.headline_only:
-        for name, tree in (("random_agentic_tree", W.random_agentic_tree(0)), ("varlen_forest", W.varlen_forest(0))):
+    chosen = set() if args.headline_only else {x for x in args.secondary.split(",") if x}
+    if chosen:
+        for name, mk in (("random_agentic_tree", lambda: W.random_agentic_tree(0)),
+                         ("varlen_forest", lambda: W.varlen_forest(0))):
+            if name not in chosen:
+                continue
+            tree = mk()
             print(f"[bench] {name} fwd+bwd", flush=True)
             r = time_tree(pkg, tree, max(3, args.steps // 2), args.warmup, dev)
             extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "flops_alg"}
         for cap in (4096,):
+            if f"spine_partitioned_{cap}" not in chosen:
+                continue
             print(f"[bench] spine tree partitioned at {cap} tokens, fwd+bwd", flush=True)
             r = time_partitioned(pkg, spine, cap, max(3, args.steps // 2), args.warmup, dev)
             r["vs_whole_tree"] = round(head["ms_per_step"] / r["ms_per_step"], 4)
             extra[f"spine_partitioned_{cap}"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                                  for k, v in r.items()}
-        extra["decode"] = []
-        for L in (32768, 65536, 131072, 262144):
+        for L in (32768, 65536, 131072, 262144) if "decode" in chosen else ():
+            extra.setdefault("decode", [])
             print(f"[bench] decode L={L}", flush=True)
             r = time_decode(pkg, L, args.steps, args.warmup, dev)
             extra["decode"].append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()})
@@ -302,7 +311,8 @@ def main():
     }
     if extra:
         out["secondary"] = extra
-        dec = extra["decode"]
+    dec = extra.get("decode")
+    if dec:
         out["decode_GBps"] = {str(r["L"]): r["GBps"] for r in dec}
         out["decode_frac_hbm_peak"] = {str(r["L"]): round(r["GBps"] / PEAK_HBM_GBS, 4) for r in dec}
     if not args.no_cpu_baseline:
