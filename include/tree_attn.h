@@ -251,6 +251,9 @@ ta_status tree_decode_ws_bytes(int32_t B, int32_t Hq, int32_t d, int32_t max_len
  * spans[s] = (start, len) for s in [span_ptr[b], span_ptr[b+1]) in order
  * (plain decode: one span; tree decode: the ancestor chain of a leaf).
  * max_len bounds every item's total length.  dt: TA_BF16, d = 128.
+ * Precision: q.k products of bf16 values accumulate exactly in fp32; the
+ * probabilities are rounded to bf16 for the P V product (fp32 accumulation);
+ * the softmax sums and the merge are fp32.
  * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_ENOMEM, TA_EHIP. */
 ta_status tree_decode_splitkv(ta_dtype dt, const void* q, const void* k, const void* v,
                               const int32_t* span_ptr, const int32_t* spans, int32_t B,

@@ -5,12 +5,10 @@
 // handled by different workgroups, and the "AllReduce" is a pairwise merge
 // tree of depth ceil(log2 S) over the S slices.
 //
-// Partial kernel: one workgroup per (slice, KV head x group of <= 4 query
-// heads, batch item).  Decode is HBM-bound (each KV byte is used for a
-// handful of FLOPs), so the kernel is a streaming loop: eight lanes cover a
-// 256-byte K or V row with 32-byte loads, a wavefront walks 32 rows per
-// step, scores are reduced across the eight lanes and the running
-// (m, l, o) is updated once per block of four keys per lane group.
+// Decode is HBM-bound: each K/V byte feeds a few FLOPs per query head.  The
+// partial kernel therefore keeps as many bytes in flight as the LDS holds
+// (direct global-to-LDS copies into a per-wavefront ring) and leaves the
+// arithmetic to the matrix cores, so the vector ALU does only the softmax.
 // Merge kernel: one workgroup per (batch item, query head); round r merges
 // slice pairs (i, i + 2^r) in parallel over the head dimension.
 #include "common.h"
@@ -19,18 +17,8 @@ namespace ta {
 namespace dec {
 
 constexpr int D = 128;
-constexpr int HG = 4;   // query heads per workgroup
-constexpr int KB = 4;   // keys per lane group per step
 constexpr int MAX_SPLITS = 120;  // merge keeps S x (2 + D) floats in 64 KB of LDS
-
-__device__ __forceinline__ void bf16x16_to_f32(const uint4& a, const uint4& b, float* f) {
-  const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    f[2 * i] = __uint_as_float(u[i] << 16);
-    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-  }
-}
+constexpr int AUTO_SPLITS = 64;  // default cap: 64 slices measured best at 256K keys per item
 
 struct Params {
   const bf16* q;
@@ -43,156 +31,232 @@ struct Params {
   float scale_log2;
 };
 
-__global__ __launch_bounds__(256) void partial_kernel(Params P) {
-  __shared__ float sh_m[4][HG], sh_l[4][HG], sh_o[4][HG][D];
+// ---------------------------------------------------------------------------
+// Matrix-core partial kernel.  One workgroup per (slice, KV head x group of
+// up to 32 query heads, batch item); the slice is cut into four contiguous
+// parts, one per wavefront, so each wavefront streams its own keys through a
+// private two-stage LDS ring with direct global-to-LDS copies (non-temporal:
+// every K/V byte is read once) and needs no workgroup barrier in its loop.
+// Per 32-key block: S^T = K q^T on 32x32x16 bf16 MFMA (keys on the rows, the
+// query heads on the 32 columns, so each lane owns one head and the running
+// max / sum stay in registers plus one exchange with the lane 32 away), then
+// O^T += V^T P^T with V^T from the LDS transpose read.  The products of bf16
+// values are exact in the fp32 accumulators, so no conversion work is left
+// on the vector ALU.  The four wavefronts' (m, l, o) are merged in LDS.
+constexpr int KS = 32;               // keys per block (one MFMA row tile)
+constexpr int WV = 4;                // wavefronts per workgroup
+constexpr int HC = 32;               // query heads per workgroup (MFMA columns)
+constexpr int STAGE = 2 * KS * D;    // bf16 elements per ring stage: K rows, then V rows
+
+struct Blk {
+  int row, n;  // physical first row, valid keys (1..KS)
+};
+
+// The KS-key blocks of the virtual range [pos, end) of one item's spans, in
+// order; wavefront-uniform (the span table is read with scalar loads).
+struct SpanWalk {
+  cint_ptr spans;
+  int s, s1, base, pos, end;
+  __device__ __forceinline__ bool next(Blk& out) {
+    while (s < s1 && pos < end) {
+      const int st = spans[2 * s], len = spans[2 * s + 1];
+      const int hi = min(end, base + len);
+      if (pos < hi) {
+        out.row = st + (pos - base);
+        out.n = min(KS, hi - pos);
+        pos += out.n;
+        return true;
+      }
+      base += len;
+      ++s;
+      pos = max(pos, base);
+    }
+    return false;
+  }
+};
+
+__device__ __forceinline__ void copy16_to_lds_nt(const void* g, const void* lds_base) {
+  const uint32_t a = lds_addr(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(a)
+               : "memory", "m0");
+}
+
+// Copies block b's K and V rows into one ring stage (swizzled 256-byte rows;
+// rows past the block's valid keys repeat its last key and are masked).
+// Copy i fills rows 4i..4i+3: lane l writes row 4i + l/16, piece l%16.
+__device__ __forceinline__ void stage_block(const Params& P, const Blk& b, int kvh, bf16* sb) {
+  const int l = threadIdx.x & 63, sub = l >> 4;
+#pragma unroll
+  for (int i = 0; i < KS / 4; ++i) {
+    const int r = 4 * i + sub;
+    const int poff = ((l & 15) ^ swz(r & 15)) << 3;
+    const size_t off = ((size_t)(b.row + min(r, b.n - 1)) * P.Hkv + kvh) * D + poff;
+    copy16_to_lds_nt(P.k + off, sb + 4 * i * D);
+    copy16_to_lds_nt(P.v + off, sb + KS * D + 4 * i * D);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void partial_kernel(Params P) {
+  __shared__ __attribute__((aligned(1024))) bf16 ring[WV][2][STAGE];
   const int split = blockIdx.x;
   const int kvh = blockIdx.y % P.Hkv, hgrp = blockIdx.y / P.Hkv;
   const int b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kl = lane >> 3, dp = lane & 7;
-  const int nh = min(HG, P.G - hgrp * HG);
-  const int h0 = kvh * P.G + hgrp * HG;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int nh = min(HC, P.G - hgrp * HC);
+  const bool hvalid = col < nh;
+  const int h = kvh * P.G + hgrp * HC + (hvalid ? col : 0);
 
-  // this item's total length and this workgroup's slice of it
-  const int sp0 = P.span_ptr[b], sp1 = P.span_ptr[b + 1];
+  // this item's length, this workgroup's slice and this wavefront's part
+  const cint_ptr sp = as_const(P.spans);
+  const int sp0 = as_const(P.span_ptr)[b], sp1 = as_const(P.span_ptr)[b + 1];
   int L = 0;
-  for (int s = sp0; s < sp1; ++s) L += P.spans[2 * s + 1];
-  const int per = (((L + P.S - 1) / P.S) + 31) & ~31;
+  for (int s = sp0; s < sp1; ++s) L += sp[2 * s + 1];
+  const int per = (((L + P.S - 1) / P.S) + KS - 1) & ~(KS - 1);
   const int vs = min(L, split * per), ve = min(L, vs + per);
+  const int wper = (((ve - vs + WV - 1) / WV) + KS - 1) & ~(KS - 1);
+  SpanWalk walk{sp, sp0, sp1, 0, min(ve, vs + w * wper), min(ve, vs + (w + 1) * wper)};
 
-  float qv[HG][16];
+  // q as the B operand: lane = head column, k-slots 16 s + 8 half + e
+  bf16x8 qf[8];
+  {
+    const bf16* qr = P.q + ((size_t)b * P.Hq + h) * D + half * 8;
 #pragma unroll
-  for (int hh = 0; hh < HG; ++hh) {
-    const int h = hh < nh ? h0 + hh : h0;
-    const bf16* qr = P.q + ((size_t)b * P.Hq + h) * D + dp * 16;
-    const uint4 a = *(const uint4*)qr, c = *(const uint4*)(qr + 8);
-    bf16x16_to_f32(a, c, qv[hh]);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) qv[hh][e] *= P.scale_log2;
+    for (int s = 0; s < 8; ++s) qf[s] = hvalid ? *(const bf16x8*)(qr + 16 * s) : bf16x8{};
   }
-  float m[HG], l[HG], o[HG][16];
-#pragma unroll
-  for (int hh = 0; hh < HG; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[hh][e] = 0.f;
-  }
+  // the q loads must land before the ring copies start counting on vmcnt
+  asm volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[7]) : "memory");
 
-  // walk the spans that overlap [vs, ve) in virtual order
-  int base = 0;
-  for (int s = sp0; s < sp1 && base < ve; ++s) {
-    const int st = P.spans[2 * s], len = P.spans[2 * s + 1];
-    const int lo = max(vs, base), hi = min(ve, base + len);
-    for (int v0 = lo + wave * (8 * KB); v0 < hi; v0 += 4 * 8 * KB) {
-      float sc[KB][HG];
-      int rows[KB];
+  int koff[8], voff[4][2];
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int vv = v0 + u * 8 + kl;
-        rows[u] = vv < hi ? st + (vv - base) : -1;
-        float kf[16];
-        if (rows[u] >= 0) {
-          const bf16* kr = P.k + ((size_t)rows[u] * P.Hkv + kvh) * D + dp * 16;
-          bf16x16_to_f32(*(const uint4*)kr, *(const uint4*)(kr + 8), kf);
-        } else {
+  for (int s = 0; s < 8; ++s) koff[s] = col * D + (((2 * s + half) ^ swz(col & 15)) << 3);
+  {
+    const int trow = half * 4 + ((lane & 15) >> 2);
+    const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) kf[e] = 0.f;
-        }
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-          float a = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) a = fmaf(qv[hh][e], kf[e], a);
-          sc[u][hh] = a;
-        }
+      for (int x = 0; x < 2; ++x) {
+        const int r = trow + 8 * x;
+        voff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
       }
-#pragma unroll
-      for (int u = 0; u < KB; ++u)
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-          float a = sc[u][hh];
-          a += __shfl_xor(a, 1);
-          a += __shfl_xor(a, 2);
-          a += __shfl_xor(a, 4);
-          sc[u][hh] = rows[u] >= 0 ? a : -INFINITY;
-        }
-#pragma unroll
-      for (int hh = 0; hh < HG; ++hh) {
-        float mx = m[hh];
-#pragma unroll
-        for (int u = 0; u < KB; ++u) mx = fmaxf(mx, sc[u][hh]);
-        const float muse = mx == -INFINITY ? 0.f : mx;
-        const float a = exp2f_fast(m[hh] - muse);
-        l[hh] *= a;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[hh][e] *= a;
-        m[hh] = mx;
-#pragma unroll
-        for (int u = 0; u < KB; ++u) sc[u][hh] = exp2f_fast(sc[u][hh] - muse);
-      }
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        if (rows[u] < 0) continue;
-        float vf[16];
-        const bf16* vr = P.v + ((size_t)rows[u] * P.Hkv + kvh) * D + dp * 16;
-        bf16x16_to_f32(*(const uint4*)vr, *(const uint4*)(vr + 8), vf);
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-          l[hh] += sc[u][hh];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[hh][e] = fmaf(sc[u][hh], vf[e], o[hh][e]);
-        }
-      }
-    }
-    base += len;
   }
 
-  // merge the eight lane groups of the wavefront (lanes with equal dp)
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[4];
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+  auto compute = [&](const bf16* sb, int n) {
+    f32x16 sc = f32x16{};
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      const float m2 = __shfl_xor(m[hh], off), l2 = __shfl_xor(l[hh], off);
-      const float M = fmaxf(m[hh], m2);
-      const float Mu = M == -INFINITY ? 0.f : M;
-      const float fa = exp2f_fast(m[hh] - Mu), fb = exp2f_fast(m2 - Mu);
-      l[hh] = l[hh] * fa + l2 * fb;
+    for (int s = 0; s < 8; ++s) sc = mfma32(*(const bf16x8*)(sb + koff[s]), qf[s], sc);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[hh][e] = o[hh][e] * fa + __shfl_xor(o[hh][e], off) * fb;
-      m[hh] = M;
+    for (int r = 0; r < 16; ++r) sc[r] *= P.scale_log2;
+    if (n < KS) {  // uniform: only a span's last block is ragged
+      // register r <-> key slot 8 (r / 4) + 4 half + r % 4
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * half + (r & 3) >= n) sc[r] = -INFINITY;
     }
-  }
-  if (kl == 0) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      if (dp == 0) {
-        sh_m[wave][hh] = m[hh];
-        sh_l[wave][hh] = l[hh];
+    for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[r]);
+    mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+    // lazy rescaling as in the forward kernel: the reference moves only when
+    // the block max exceeds it by more than 8 (log2 units)
+    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f)) {
+      const float mnew = __builtin_elementwise_maximum(m, mx);
+      const float alpha = exp2f_fast(m - ((mnew == -INFINITY) ? 0.f : mnew));
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      m = mnew;
+    }
+    const float muse = (m == -INFINITY) ? 0.f : m;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2f_fast(sc[r] - muse);
+      l += p;
+      pb[r >> 3][r & 7] = (bf16)p;
+    }
+    const bf16* vb = sb + KS * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x4 t0 = lds_read_tr(vb + kk * 16 * D + voff[dt][0]);
+        const bf16x4 t1 = lds_read_tr(vb + kk * 16 * D + voff[dt][1]);
+        acc[dt] = mfma32(cat(t0, t1), pb[kk], acc[dt]);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sh_o[wave][hh][dp * 16 + e] = o[hh][e];
+    // every LDS read of this stage has returned before it is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  bf16* const r0 = ring[w][0];
+  bf16* const r1 = ring[w][1];
+  Blk b0, b1;
+  bool h0 = walk.next(b0);
+  if (h0) stage_block(P, b0, kvh, r0);
+  bool h1 = h0 && walk.next(b1);
+  if (h1) stage_block(P, b1, kvh, r1);
+  while (h0) {
+    // a stage is 2 * KS / 4 = 16 copies; the other stage may still be in flight
+    if (h1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    compute(r0, b0.n);
+    h0 = h1 && walk.next(b0);
+    if (h0) stage_block(P, b0, kvh, r0);
+    if (!h1) break;
+    if (h0) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    compute(r1, b1.n);
+    h1 = h0 && walk.next(b1);
+    if (h1) stage_block(P, b1, kvh, r1);
+  }
+  lds_copies_wait();
+  __syncthreads();  // every wavefront is done with its ring: reuse it for the merge
+
+  // per wavefront: m (log2 units), l and o of each head
+  float* sm = (float*)&ring[0][0][0];      // [WV][HC]
+  float* sl = sm + WV * HC;                // [WV][HC]
+  float* so = sl + WV * HC;                // [WV][HC][D]
+  const float lt = l + __shfl_xor(l, 32);
+  if (hvalid) {
+    if (half == 0) {
+      sm[w * HC + col] = m;
+      sl[w * HC + col] = lt;
     }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        so[(w * HC + col) * D + dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = acc[dt][r];
   }
   __syncthreads();
-  // merge the four wavefronts: thread -> (head, d)
+  const int h0g = kvh * P.G + hgrp * HC;
   for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
     const int hh = idx / D, d = idx % D;
     float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sh_m[w][hh]);
+#pragma unroll
+    for (int x = 0; x < WV; ++x) M = __builtin_elementwise_maximum(M, sm[x * HC + hh]);
     const float Mu = M == -INFINITY ? 0.f : M;
-    float lt = 0.f, ot = 0.f;
-    for (int w = 0; w < 4; ++w) {
-      const float f = exp2f_fast(sh_m[w][hh] - Mu);
-      lt += sh_l[w][hh] * f;
-      ot += sh_o[w][hh][d] * f;
+    float ls = 0.f, os = 0.f;
+#pragma unroll
+    for (int x = 0; x < WV; ++x) {
+      const float f = exp2f_fast(sm[x * HC + hh] - Mu);
+      ls += sl[x * HC + hh] * f;
+      os += so[(x * HC + hh) * D + d] * f;
     }
-    float* dst = P.part + (((size_t)b * P.Hq + h0 + hh) * P.S + split) * (2 + D);
+    float* dst = P.part + (((size_t)b * P.Hq + h0g + hh) * P.S + split) * (2 + D);
     if (d == 0) {
       dst[0] = M;
-      dst[1] = lt;
+      dst[1] = ls;
     }
-    dst[2 + d] = ot;
+    dst[2 + d] = os;
   }
 }
 
@@ -248,8 +312,8 @@ using namespace ta;
 namespace {
 int32_t pick_splits(int32_t max_len, int32_t n_splits) {
   if (n_splits > 0) return n_splits;
-  int32_t s = (max_len + 2047) / 2048;
-  return s < 1 ? 1 : (s > dec::MAX_SPLITS ? dec::MAX_SPLITS : s);
+  int32_t s = (max_len + 2047) / 2048;  // about 2K keys (512 per wavefront) per workgroup
+  return s < 1 ? 1 : (s > dec::AUTO_SPLITS ? dec::AUTO_SPLITS : s);
 }
 }  // namespace
 
@@ -298,7 +362,7 @@ extern "C" ta_status tree_decode_splitkv_ex(ta_dtype dt, const void* q, const vo
   P.G = Hq / Hkv;
   P.S = S;
   P.scale_log2 = scale * TA_LOG2E;
-  const int hgroups = (P.G + dec::HG - 1) / dec::HG;
+  const int hgroups = (P.G + dec::HC - 1) / dec::HC;
   mark(ev, nev, 0, stream);
   hipLaunchKernelGGL(dec::partial_kernel, dim3(S, Hkv * hgroups, B), dim3(256), 0, stream, P);
   TA_LAUNCH_CHECK();

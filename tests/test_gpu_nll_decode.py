@@ -78,8 +78,10 @@ def test_decode_small(n_splits):
 
 def test_decode_multi_span_and_gqa_shapes():
     _decode_case([5, 300, 64, 2], 8, 2, 0, 1, multi_span=True)
-    _decode_case([100, 3], 16, 2, 5, 2)        # 8 query heads per KV head: two head groups
+    _decode_case([100, 3], 16, 2, 5, 2)        # 8 query heads per KV head
     _decode_case([77], 2, 2, 2, 3)             # one query head per KV head
+    _decode_case([90, 33], 32, 1, 3, 5)        # 32 query heads per KV head: every MFMA column
+    _decode_case([65, 1000], 40, 1, 4, 6)      # 40 per KV head: two head groups (32 + 8)
 
 
 @pytest.mark.timeout(600)
