@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "tree-attn fwd+bwd TFLOP/s on visible pairs (% bf16 MFMA peak); decode GB/s"
-KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "decode.hip", "common.h"]
+# the sources of the attention kernels (their traffic counts are keyed by this hash)
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "common.h", "plan.cpp", "plan_internal.h"]
 
 
 def source_hash() -> str:
@@ -307,7 +308,7 @@ def main():
         "plan_ms": head["plan_ms"], "plan_upload_ms": head["upload_ms"],
         "por": head["por"], "fwd_tile_efficiency": head["fwd_tile_efficiency"],
         "bwd_tile_efficiency": head["bwd_tile_efficiency"],
-        "kernel_source_hash": source_hash(),
+        "kernel_source_hash": source_hash(),  # attention kernels and planner
     }
     if extra:
         out["secondary"] = extra
