@@ -237,6 +237,33 @@ ta_status tree_weighted_nll(ta_dtype dt, const void* logits, const int32_t* labe
                             int32_t N, int32_t V, int32_t ignore_index, float* loss, void* dlogits,
                             int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Output layer fused with the weighted NLL (agent-rl chapter 14, section
+ * 14.3; Tree Training post, sections 6.2 and 6.3) ----------------------------
+ * loss = sum_t w_t [y_t valid] (logsumexp_v(h_t . W_v) - h_t . W_{y_t}) for
+ * hidden states h [N, Dm] and output weights W [V, Dm] (bf16, row-major),
+ * without ever holding the N x V logits: the forward reduces 256 x 256 logit
+ * tiles to per-token (max, sum) partials on the matrix cores; the backward
+ * recomputes the logits one vocabulary chunk at a time (section 14.3's
+ * recompute), forms dS = w [valid] (softmax - onehot(y)) in bf16 for that
+ * chunk only and accumulates dh += dS W_chunk (fp32) and dW_chunk = dS^T h.
+ * labels [N] int32 (ignore_index marks unsupervised tokens; another label
+ * outside [0, V) contributes 0 and sets *err_flag = 1 when err_flag is not
+ * NULL); w [N] fp32 (g_t/K for a tree).  loss: device fp32 scalar (a fixed-
+ * order sum: bitwise reproducible).  lse: optional [N] fp32 output (natural
+ * log).  dh [N, Dm] and dW [V, Dm] (bf16, overwritten): both NULL for the
+ * forward only, else both set.  vocab_chunk: vocabulary rows per backward
+ * chunk (0 picks about 256 MB of dS; rounded down to whole 256-row tiles).
+ * Dm must be a multiple of 32.  ws: tree_lmhead_nll_ws_bytes bytes.
+ * Precision: products of bf16 values accumulate in fp32; dS is rounded to
+ * bf16 for the two backward products.
+ * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_ERANGE, TA_ENOMEM, TA_EHIP. */
+ta_status tree_lmhead_nll_ws_bytes(int32_t N, int32_t V, int32_t Dm, int32_t need_grad,
+                                   int32_t vocab_chunk, size_t* bytes);
+ta_status tree_lmhead_nll(ta_dtype dt, const void* h, const void* W, const int32_t* labels,
+                          const float* w, int32_t N, int32_t V, int32_t Dm, int32_t ignore_index,
+                          int32_t vocab_chunk, float* loss, float* lse, void* dh, void* dW,
+                          int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes of tree_decode_splitkv; *n_splits_out receives the split
  * count it will use (n_splits = 0 picks one from the longest item). */
 ta_status tree_decode_ws_bytes(int32_t B, int32_t Hq, int32_t d, int32_t max_len, int32_t n_splits,

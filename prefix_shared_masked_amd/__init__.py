@@ -22,7 +22,7 @@ import os
 import numpy as np
 
 __all__ = ["TreeAttnError", "Plan", "Partition", "HipEvents", "tree_plan", "tree_partition", "tree_attn_fwd",
-           "tree_attn_bwd", "tree_partition_fwd", "tree_partition_bwd", "tree_weighted_nll",
+           "tree_attn_bwd", "tree_partition_fwd", "tree_partition_bwd", "tree_weighted_nll", "tree_lmhead_nll",
            "tree_decode_splitkv", "library_path", "load_library", "TA_BLOCK_M", "TA_BLOCK_N", "TA_BLOCK_KV"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -107,6 +107,8 @@ def load_library():
         "tree_partition_ws_bytes": (I32, [P, I32, I32, I32, I32, I32, F32, ctypes.POINTER(SZ)]),
         "tree_partition_fwd": (I32, [P, P, I32, P, P, P, I32, I32, I32, F32, F32, P, P, P, SZ, P]),
         "tree_partition_bwd": (I32, [P, P, I32, P, P, P, P, P, P, I32, I32, I32, F32, F32, P, P, P, P, SZ, P]),
+        "tree_lmhead_nll_ws_bytes": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
+        "tree_lmhead_nll": (I32, [I32, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
         "ta_status_string": (ctypes.c_char_p, [I32]),
     }
     for name, (res, args) in sigs.items():
@@ -494,6 +496,44 @@ def tree_partition_bwd(part: Partition, q, k, v, o, lse, dO, scale: float = 0.0,
         part.handle, _ptr(part.device(dev)), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
         Hq, Hkv, d, float(scale), float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsn, _stream(q)))
     return dq, dk, dv
+
+
+def lmhead_ws_bytes(N: int, V: int, Dm: int, need_grad: bool, vocab_chunk: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check("tree_lmhead_nll_ws_bytes", load_library().tree_lmhead_nll_ws_bytes(
+        int(N), int(V), int(Dm), int(bool(need_grad)), int(vocab_chunk), ctypes.byref(n)))
+    return int(n.value)
+
+
+def tree_lmhead_nll(h, W, labels, w, ignore_index: int = -100, need_grad: bool = True, vocab_chunk: int = 0,
+                    loss=None, lse=None, dh=None, dW=None, err_flag=None, ws=None):
+    """Output layer + weighted NLL without the N x V logits.  h [N,Dm] bf16, W [V,Dm] bf16,
+    labels [N] int32, w [N] fp32 -> (loss [1] fp32, lse [N] fp32, dh, dW (bf16, None without grad),
+    err_flag [1] int32)."""
+    import torch
+    N, Dm = h.shape
+    V = W.shape[0]
+    dev = h.device
+    _need(h, "h", (N, Dm), torch.bfloat16, dev)
+    _need(W, "W", (V, Dm), torch.bfloat16, dev)
+    _need(labels, "labels", (N,), torch.int32, dev)
+    _need(w, "w", (N,), torch.float32, dev)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev) if loss is None else loss
+    lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
+    err_flag = torch.zeros(1, dtype=torch.int32, device=dev) if err_flag is None else err_flag
+    if need_grad:
+        dh = torch.empty_like(h) if dh is None else dh
+        dW = torch.empty_like(W) if dW is None else dW
+        _need(dh, "dh", (N, Dm), torch.bfloat16, dev)
+        _need(dW, "dW", (V, Dm), torch.bfloat16, dev)
+    else:
+        dh = dW = None
+    ws, wsn = _workspace(lmhead_ws_bytes(N, V, Dm, need_grad, vocab_chunk), dev, ws)
+    _check("tree_lmhead_nll", load_library().tree_lmhead_nll(
+        TA_BF16, _ptr(h), _ptr(W), _ptr(labels), _ptr(w), N, V, Dm, int(ignore_index), int(vocab_chunk),
+        _ptr(loss), _ptr(lse), _ptr(dh) if dh is not None else None, _ptr(dW) if dW is not None else None,
+        _ptr(err_flag), _ptr(ws), wsn, _stream(h)))
+    return loss, lse, dh, dW, err_flag
 
 
 def tree_weighted_nll(logits, labels, w, ignore_index: int = -100, need_grad: bool = True,

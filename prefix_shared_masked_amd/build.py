@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtree_attn.so")
-SOURCES = ["plan.cpp", "partition.cpp", "gateway.hip", "attn_fwd.hip", "attn_bwd.hip", "nll.hip", "decode.hip"]
+SOURCES = ["plan.cpp", "partition.cpp", "gateway.hip", "attn_fwd.hip", "attn_bwd.hip", "nll.hip", "decode.hip",
+           "lmhead.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
@@ -26,7 +27,8 @@ FLAGS = [
 def build_library(verbose: bool = False, extra=()) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     cmd = [hipcc, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+           *[os.path.join(CSRC, s) for s in SOURCES], "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -83,6 +83,14 @@ __global__ __launch_bounds__(1024) void sum_kernel(const float* __restrict__ v, 
 }
 
 }  // namespace nll
+
+// Fixed-order sum of n floats into *out by one workgroup (shared with the
+// fused output-layer loss).
+hipError_t launch_sum(const float* v, int n, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(nll::sum_kernel, dim3(1), dim3(1024), 0, st, v, n, out);
+  return hipGetLastError();
+}
+
 }  // namespace ta
 
 using namespace ta;
