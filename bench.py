@@ -145,6 +145,49 @@ def time_partitioned(pkg, tree, capacity, steps, warmup, dev, seed=0, Hq=32, Hkv
     return res
 
 
+def time_lmhead(pkg, tree, steps, warmup, dev, V=151936, Dm=1024, seed=9):
+    """Output layer (Qwen3-0.6B shape: V = 151,936, Dm = 1,024) fused with the
+    g/K weighted NLL over the tree's tokens: forward alone and forward+backward."""
+    import torch
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    N = plan.n_tokens
+    g = torch.Generator(device=dev).manual_seed(seed)
+    h = torch.randn(N, Dm, generator=g, device=dev).bfloat16()
+    W = (torch.randn(V, Dm, generator=g, device=dev) / Dm ** 0.5).bfloat16()
+    labels = torch.randint(0, V, (N,), generator=g, device=dev, dtype=torch.int32)
+    w = torch.from_numpy((plan.view()["g"] / plan.n_leaves).astype("float32")).to(dev)
+    loss = torch.zeros(1, device=dev)
+    lse = torch.empty(N, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dh, dW = torch.empty_like(h), torch.empty_like(W)
+    ws = torch.empty(pkg.lmhead_ws_bytes(N, V, Dm, True), dtype=torch.uint8, device=dev)
+
+    def timed(grad):
+        for _ in range(warmup):
+            pkg.tree_lmhead_nll(h, W, labels, w, need_grad=grad, loss=loss, lse=lse, dh=dh, dW=dW,
+                                err_flag=err, ws=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            pkg.tree_lmhead_nll(h, W, labels, w, need_grad=grad, loss=loss, lse=lse, dh=dh, dW=dW,
+                                err_flag=err, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    fwd = timed(False)
+    total = timed(True)
+    gemm = 2.0 * N * V * Dm
+    res = dict(n_tokens=N, vocab=V, hidden=Dm, fwd_ms=fwd, fwd_bwd_ms=total, bwd_ms=total - fwd,
+               fwd_tflops=gemm / (fwd * 1e-3) / 1e12,
+               # forward, the backward's recompute, dh and dW: four products of 2 N V Dm
+               fwd_bwd_tflops=4 * gemm / (total * 1e-3) / 1e12,
+               logits_gb_never_held=N * V * 4 / 1e9)
+    del h, W, dh, dW, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_decode(pkg, L, steps, warmup, dev, B=8, Hq=32, Hkv=8, d=128, seed=5):
     import torch
     g = torch.Generator(device=dev).manual_seed(seed)
@@ -228,7 +271,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--secondary", default="random_agentic_tree,varlen_forest,spine_partitioned_4096,decode",
+    ap.add_argument("--secondary", default="random_agentic_tree,varlen_forest,spine_partitioned_4096,lmhead,decode",
                     help="comma-separated secondary workloads to run after the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -265,6 +308,10 @@ def main():
             r["vs_whole_tree"] = round(head["ms_per_step"] / r["ms_per_step"], 4)
             extra[f"spine_partitioned_{cap}"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                                  for k, v in r.items()}
+        if "lmhead" in chosen:
+            print("[bench] output layer + weighted NLL over the spine tree's tokens", flush=True)
+            r = time_lmhead(pkg, spine, max(3, args.steps // 2), args.warmup, dev)
+            extra["lmhead"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         for L in (32768, 65536, 131072, 262144) if "decode" in chosen else ():
             extra.setdefault("decode", [])
             print(f"[bench] decode L={L}", flush=True)
