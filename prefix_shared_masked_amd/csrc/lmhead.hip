@@ -14,7 +14,7 @@
 //    workgroup sums the token losses in a fixed order (bitwise reproducible).
 //  - ds_kernel (backward, per vocabulary chunk): the same tiles recomputed,
 //    epilogue dS = w [valid] (exp(S - LSE) - onehot(y)) in bf16, laid out
-//    [chunk rows, N]; then two plain GEMMs on the library's matrix kernels:
+//    [N, chunk rows]; then two plain GEMMs on the library's matrix kernels:
 //    dh += dS W_chunk (fp32 accumulator) and dW_chunk = dS^T h.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
@@ -73,7 +73,8 @@ struct Params {
   const float* w;
   const float* lse;     // [N] natural log (ds_kernel)
   float2* part;         // [n_parts][N] (m in log2 units, l) (lse_kernel)
-  bf16* ds;             // [chunk rows][N] (ds_kernel)
+  bf16* ds;             // [N][ld_ds] (ds_kernel): the chunk's dS, token-major
+  int ld_ds;            // row stride of ds (the chunk's row capacity)
   int N, V, Dm;
   int vt_per_wg;        // vocabulary tiles per workgroup
   int vt_first;         // first vocabulary tile of the launch
@@ -231,17 +232,25 @@ __global__ __launch_bounds__(256, 1) void ds_kernel(Params P) {
   const int vrow0 = P.vt_first * BV;  // first vocabulary row of this chunk
   tile_loop(P, ring, [&](int vt, f32x16 (&acc)[4][4]) {
     const int vb = vt * BV + 128 * wv;
+    const bool ragged = vb + 128 > P.V;  // uniform
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = blockIdx.x * BT + 128 * wt + 32 * j + rr;
+      bf16* row = P.ds + (size_t)(tv[j] ? t : 0) * P.ld_ds + (vb - vrow0) + 4 * half;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = vb + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float p = exp2f_fast(acc[i][j][r] * L2E - lse2[j]);
-          const float g = wt_[j] * (p - (v == y[j] ? 1.f : 0.f));
-          if (tv[j] && v < P.V) P.ds[(size_t)(v - vrow0) * P.N + t] = (bf16)g;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          // registers 4 r4 .. 4 r4 + 3: four consecutive vocabulary rows
+          const int v0 = vb + 32 * i + 8 * r4 + 4 * half;
+          bf16x4 o;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float p = exp2f_fast(acc[i][j][4 * r4 + u] * L2E - lse2[j]);
+            const float g = wt_[j] * (p - (v0 + u == y[j] ? 1.f : 0.f));
+            o[u] = (bf16)(v0 + u < P.V ? g : 0.f);
+          }
+          if (tv[j] && (!ragged || v0 < P.V)) *(bf16x4*)(row + 32 * i + 8 * r4) = o;
         }
     }
     // stores count on vmcnt too and may complete out of order with the ring
@@ -460,21 +469,25 @@ extern "C" ta_status tree_lmhead_nll(ta_dtype dt, const void* h, const void* W, 
   float* dh_acc = (float*)(wsb + S.off_dh);
   void* ltws = wsb + S.off_lt;
   P.ds = ds;
+  P.ld_ds = S.chunk_vt * lmh::BV;
   for (int c = 0; c < S.n_chunks; ++c) {
     const int vt_a = c * S.chunk_vt, vt_b = std::min(S.n_vt, vt_a + S.chunk_vt);
     const int v0 = vt_a * lmh::BV, cv = std::min(V, vt_b * lmh::BV) - v0;  // rows of this chunk
     P.vt_first = vt_a;
     P.vt_last = vt_b;
-    // one vocabulary tile per workgroup: chunk tiles x token tiles workgroups
-    P.vt_per_wg = 1;
-    hipLaunchKernelGGL(lmh::ds_kernel, dim3(S.n_tt, vt_b - vt_a), dim3(256), 0, stream, P);
+    // about four workgroups per CU, each walking a few vocabulary tiles
+    const int ntile = vt_b - vt_a;
+    P.vt_per_wg = std::max(1, std::min(ntile, ntile * S.n_tt / 1024));
+    hipLaunchKernelGGL(lmh::ds_kernel, dim3(S.n_tt, (ntile + P.vt_per_wg - 1) / P.vt_per_wg), dim3(256), 0, stream,
+                       P);
     TA_LAUNCH_CHECK();
-    // column-major views: dS is (N x cv) with ld N; W_chunk (Dm x cv), h (Dm x N), dh (Dm x N), dW_chunk (Dm x cv)
-    ta_status st = lmh::lt_gemm(false, true, Dm, N, cv, (const bf16*)W + (size_t)v0 * Dm, Dm, ds, N, dh_acc,
+    // column-major views: dS is (cv x N) with ld = ld_ds; W_chunk (Dm x cv), h (Dm x N), dh (Dm x N),
+    // dW_chunk (Dm x cv)
+    ta_status st = lmh::lt_gemm(false, false, Dm, N, cv, (const bf16*)W + (size_t)v0 * Dm, Dm, ds, P.ld_ds, dh_acc,
                                 HIP_R_32F, Dm, c == 0 ? 0.f : 1.f, ltws, lmh::LT_WS, stream);
     if (st != TA_OK) return st;
-    st = lmh::lt_gemm(false, false, Dm, cv, N, h, Dm, ds, N, (bf16*)dW + (size_t)v0 * Dm, HIP_R_16BF, Dm, 0.f, ltws,
-                      lmh::LT_WS, stream);
+    st = lmh::lt_gemm(false, true, Dm, cv, N, h, Dm, ds, P.ld_ds, (bf16*)dW + (size_t)v0 * Dm, HIP_R_16BF, Dm, 0.f,
+                      ltws, lmh::LT_WS, stream);
     if (st != TA_OK) return st;
   }
   const size_t nel = (size_t)N * Dm;
