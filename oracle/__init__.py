@@ -19,6 +19,8 @@ on the pages:
                    (max, numerator, denominator) merge algebra.
 * ``lmhead``    -- the output layer h W^T fused with the weighted NLL, in its
                    full form and in the chunk-and-recompute form.
+* ``ssm``       -- tree-routed linear recurrence and causal-conv context, by
+                   running every root-to-leaf path as its own sequence.
 
 Parity status of each function is stated in its docstring; the pins live in
 ``tests/test_oracle_*.py``.
@@ -28,6 +30,7 @@ from .plan import (oracle_plan, fwd_tile_keys, bwd_tiles, OraclePlan, dense_mask
 from .attention import (per_path_attention, dense_mask_attention, rope,  # noqa: F401
                         rope_transpose, rows_attention)
 from .nll import weighted_nll, per_path_loss  # noqa: F401
+from .ssm import tree_scan, tree_conv  # noqa: F401
 from .lmhead import lmhead_weighted_nll, chunked_lmhead_weighted_nll  # noqa: F401
 from .decode import (decode_attention, partial_triple, merge_triples,  # noqa: F401
                      finalize_triple, triple_from_lse, IDENTITY)
