@@ -378,6 +378,60 @@ ta_status tree_partition_bwd(const ta_partition* part, const void* dpart, ta_dty
                              float scale, float rope_base, void* dq, void* dk, void* dv, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
+/* ---- Recurrent layers over the packed tree (Tree Training post, section 9) --
+ * In DFS-packed order the token before a node's first token can belong to a
+ * sibling branch; recurrent layers must instead continue from the parent.
+ * tree_route builds, from a plan (tree_plan, no key-only prefix), the tables
+ * for: (9.1) a linear recurrence h_t = a_t * h_prev(t) + b_t per channel
+ * whose chunks start from their parent's end state -- every node is cut into
+ * chunks of up to `chunk` tokens, a chunk's parent being the previous chunk
+ * of its node or the last chunk of the nearest ancestor that holds tokens,
+ * zero state before a root -- and (9.2) a causal depthwise convolution of
+ * width conv_k (1..8) whose window runs back along the root-to-token path
+ * (the parent's last conv_k - 1 tokens, continuing into the grandparent when
+ * the parent is shorter; zero past the root).  chunks are in DFS order, so a
+ * parent chunk precedes its children.  Errors: TA_EINVAL, TA_EUNSUPPORTED
+ * (a plan with a key-only prefix), TA_ERANGE, TA_ENOMEM. */
+typedef struct ta_route ta_route;
+typedef struct ta_route_view {
+  int32_t n_tokens, n_chunks, chunk, conv_k;
+  const int32_t* chunks;    /* [n_chunks][4]: first token, length, parent chunk or -1, the token
+                               before the first one on the path or -1 */
+  const int32_t* cprev;     /* [N][conv_k - 1]: the j-th path predecessor of t (j = 1..), -1 past the root */
+  const int32_t* succ_ptr;  /* [N + 1] CSR: the (t, j) whose j-th predecessor is s, */
+  const int32_t* succ;      /* encoded t * conv_k + j, ascending t */
+} ta_route_view;
+ta_status tree_route(const ta_plan* plan, int32_t conv_k, ta_route** out);
+ta_status tree_route_view(const ta_route* route, ta_route_view* view);
+ta_status tree_route_device_bytes(const ta_route* route, size_t* bytes);
+ta_status tree_route_upload(const ta_route* route, void* droute, size_t bytes, hipStream_t stream);
+void tree_route_free(ta_route* route); /* NULL-safe */
+
+/* Tree-routed scan.  a, b, h: [N, C] fp32 (token-major, channels contiguous),
+ * h = the recurrence's states (the layer's output).  Backward: given the
+ * forward's h and the upstream gradient dh [N, C], writes da = dh_total *
+ * h_prev and db = dh_total, where dh_total of a node's last token sums the
+ * contributions of every child branch.  Deterministic (fixed-order sums, no
+ * atomics).  ws: tree_scan_ws_bytes.  Errors: TA_EINVAL, TA_ERANGE,
+ * TA_ENOMEM, TA_EHIP. */
+ta_status tree_scan_ws_bytes(const ta_route* route, int32_t C, size_t* bytes);
+ta_status tree_scan_fwd(const ta_route* route, const void* droute, const float* a, const float* b,
+                        int32_t C, float* h, void* ws, size_t ws_bytes, hipStream_t stream);
+ta_status tree_scan_bwd(const ta_route* route, const void* droute, const float* a, const float* h,
+                        const float* dh, int32_t C, float* da, float* db, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Tree-routed causal conv.  x, y, dy, dx: [N, C] fp32; w, dw: [C, conv_k]
+ * fp32, tap j multiplying the j-th path predecessor (j = 0: the token itself).
+ * dx and dw are overwritten; deterministic.  ws (backward only):
+ * tree_conv_ws_bytes.  Errors as tree_scan_fwd. */
+ta_status tree_conv_ws_bytes(const ta_route* route, int32_t C, size_t* bytes);
+ta_status tree_conv_fwd(const ta_route* route, const void* droute, const float* x, const float* w,
+                        int32_t C, float* y, hipStream_t stream);
+ta_status tree_conv_bwd(const ta_route* route, const void* droute, const float* x, const float* w,
+                        const float* dy, int32_t C, float* dx, float* dw, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
 /* Static text for a status code. */
 const char* ta_status_string(ta_status s);
 

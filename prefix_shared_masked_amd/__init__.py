@@ -23,6 +23,7 @@ import numpy as np
 
 __all__ = ["TreeAttnError", "Plan", "Partition", "HipEvents", "tree_plan", "tree_partition", "tree_attn_fwd",
            "tree_attn_bwd", "tree_partition_fwd", "tree_partition_bwd", "tree_weighted_nll", "tree_lmhead_nll",
+           "Route", "tree_route", "tree_scan_fwd", "tree_scan_bwd", "tree_conv_fwd", "tree_conv_bwd",
            "tree_decode_splitkv", "library_path", "load_library", "TA_BLOCK_M", "TA_BLOCK_N", "TA_BLOCK_KV"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +60,11 @@ class _PartView(ctypes.Structure):
          ("own_tokens", ctypes.POINTER(ctypes.c_int64))] + \
         [(n, ctypes.POINTER(ctypes.c_int32)) for n in (
             "local_ptr", "local_node", "local_parent", "local_len", "tok_ptr", "tok_idx")]
+
+
+class _RouteView(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_tokens", "n_chunks", "chunk", "conv_k")] + \
+        [(n, ctypes.POINTER(ctypes.c_int32)) for n in ("chunks", "cprev", "succ_ptr", "succ")]
 
 
 _lib = None
@@ -109,6 +115,17 @@ def load_library():
         "tree_partition_bwd": (I32, [P, P, I32, P, P, P, P, P, P, I32, I32, I32, F32, F32, P, P, P, P, SZ, P]),
         "tree_lmhead_nll_ws_bytes": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
         "tree_lmhead_nll": (I32, [I32, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]),
+        "tree_route": (I32, [P, I32, ctypes.POINTER(P)]),
+        "tree_route_view": (I32, [P, ctypes.POINTER(_RouteView)]),
+        "tree_route_device_bytes": (I32, [P, ctypes.POINTER(SZ)]),
+        "tree_route_upload": (I32, [P, P, SZ, P]),
+        "tree_route_free": (None, [P]),
+        "tree_scan_ws_bytes": (I32, [P, I32, ctypes.POINTER(SZ)]),
+        "tree_scan_fwd": (I32, [P, P, P, P, I32, P, P, SZ, P]),
+        "tree_scan_bwd": (I32, [P, P, P, P, P, I32, P, P, P, SZ, P]),
+        "tree_conv_ws_bytes": (I32, [P, I32, ctypes.POINTER(SZ)]),
+        "tree_conv_fwd": (I32, [P, P, P, P, I32, P, P]),
+        "tree_conv_bwd": (I32, [P, P, P, P, P, I32, P, P, P, SZ, P]),
         "ta_status_string": (ctypes.c_char_p, [I32]),
     }
     for name, (res, args) in sigs.items():
@@ -298,6 +315,62 @@ class Partition:
 def tree_partition(parent, seg_len, capacity: int, block_m: int = 0, block_n: int = 0) -> Partition:
     """Cut a tree into connected subtrees of at most `capacity` own tokens (tree_partition)."""
     return Partition(parent, seg_len, capacity, block_m, block_n)
+
+
+class Route:
+    """Routing tables of a plan for recurrent layers (tree_route): scan chunks and conv context."""
+
+    def __init__(self, plan: "Plan", conv_k: int = 4):
+        L = load_library()
+        self._lib = L
+        self._plan = plan
+        self._ptr = ctypes.c_void_p()
+        _check("tree_route", L.tree_route(plan.handle, int(conv_k), ctypes.byref(self._ptr)))
+        v = _RouteView()
+        _check("tree_route_view", L.tree_route_view(self._ptr, ctypes.byref(v)))
+        self._v = v
+        self._dev = {}
+        for name in ("n_tokens", "n_chunks", "chunk", "conv_k"):
+            setattr(self, name, int(getattr(v, name)))
+
+    def view(self) -> dict:
+        def arr(name, n):
+            return np.zeros(0, np.int32) if n == 0 else np.ctypeslib.as_array(getattr(self._v, name), shape=(n,)).copy()
+        sp = arr("succ_ptr", self.n_tokens + 1)
+        return dict(chunks=arr("chunks", 4 * self.n_chunks).reshape(-1, 4),
+                    cprev=arr("cprev", self.n_tokens * (self.conv_k - 1)).reshape(self.n_tokens, self.conv_k - 1),
+                    succ_ptr=sp, succ=arr("succ", int(sp[-1])))
+
+    @property
+    def handle(self):
+        return self._ptr
+
+    def device(self, device=None):
+        import torch
+        dev = torch.device(device if device is not None else "cuda")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        key = str(dev)
+        if key not in self._dev:
+            n = ctypes.c_size_t()
+            _check("tree_route_device_bytes", self._lib.tree_route_device_bytes(self._ptr, ctypes.byref(n)))
+            buf = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+            st = torch.cuda.current_stream(dev)
+            _check("tree_route_upload", self._lib.tree_route_upload(self._ptr, ctypes.c_void_p(buf.data_ptr()),
+                                                                     int(n.value), ctypes.c_void_p(st.cuda_stream)))
+            st.synchronize()
+            self._dev[key] = buf
+        return self._dev[key]
+
+    def __del__(self):
+        ptr = getattr(self, "_ptr", None)
+        if ptr is not None and ptr.value:
+            self._lib.tree_route_free(ptr)
+            self._ptr = None
+
+
+def tree_route(plan, conv_k: int = 4) -> Route:
+    return Route(plan, conv_k)
 
 
 def _dt(t):
@@ -534,6 +607,70 @@ def tree_lmhead_nll(h, W, labels, w, ignore_index: int = -100, need_grad: bool =
         _ptr(loss), _ptr(lse), _ptr(dh) if dh is not None else None, _ptr(dW) if dW is not None else None,
         _ptr(err_flag), _ptr(ws), wsn, _stream(h)))
     return loss, lse, dh, dW, err_flag
+
+
+def _route_ws(fn, route, C):
+    n = ctypes.c_size_t()
+    _check(fn, getattr(load_library(), fn)(route.handle, int(C), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _need_rows(route, name, t, C):
+    import torch
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (route.n_tokens, C):
+        raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor of shape ({route.n_tokens}, {C})")
+
+
+def tree_scan_fwd(route: Route, a, b, h=None, ws=None):
+    """h_t = a_t * h_prev(t) + b_t along the tree (chunks start from the parent's end state)."""
+    import torch
+    C = a.shape[1]
+    for name, t in (("a", a), ("b", b)):
+        _need_rows(route, name, t, C)
+    h = torch.empty_like(a) if h is None else h
+    ws, wsn = _workspace(_route_ws("tree_scan_ws_bytes", route, C), a.device, ws)
+    _check("tree_scan_fwd", load_library().tree_scan_fwd(route.handle, _ptr(route.device(a.device)), _ptr(a), _ptr(b),
+                                                         C, _ptr(h), _ptr(ws), wsn, _stream(a)))
+    return h
+
+
+def tree_scan_bwd(route: Route, a, h, dh, da=None, db=None, ws=None):
+    import torch
+    C = a.shape[1]
+    for name, t in (("a", a), ("h", h), ("dh", dh)):
+        _need_rows(route, name, t, C)
+    da = torch.empty_like(a) if da is None else da
+    db = torch.empty_like(a) if db is None else db
+    ws, wsn = _workspace(_route_ws("tree_scan_ws_bytes", route, C), a.device, ws)
+    _check("tree_scan_bwd", load_library().tree_scan_bwd(route.handle, _ptr(route.device(a.device)), _ptr(a), _ptr(h),
+                                                         _ptr(dh), C, _ptr(da), _ptr(db), _ptr(ws), wsn, _stream(a)))
+    return da, db
+
+
+def tree_conv_fwd(route: Route, x, w, y=None):
+    """y_t = sum_j w[:, j] * x_{prev^j(t)} along the tree path."""
+    import torch
+    C = x.shape[1]
+    _need_rows(route, "x", x, C)
+    _need(w, "w", (C, route.conv_k), torch.float32, x.device)
+    y = torch.empty_like(x) if y is None else y
+    _check("tree_conv_fwd", load_library().tree_conv_fwd(route.handle, _ptr(route.device(x.device)), _ptr(x), _ptr(w),
+                                                         C, _ptr(y), _stream(x)))
+    return y
+
+
+def tree_conv_bwd(route: Route, x, w, dy, dx=None, dw=None, ws=None):
+    import torch
+    C = x.shape[1]
+    for name, t in (("x", x), ("dy", dy)):
+        _need_rows(route, name, t, C)
+    _need(w, "w", (C, route.conv_k), torch.float32, x.device)
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w) if dw is None else dw
+    ws, wsn = _workspace(_route_ws("tree_conv_ws_bytes", route, C), x.device, ws)
+    _check("tree_conv_bwd", load_library().tree_conv_bwd(route.handle, _ptr(route.device(x.device)), _ptr(x), _ptr(w),
+                                                         _ptr(dy), C, _ptr(dx), _ptr(dw), _ptr(ws), wsn, _stream(x)))
+    return dx, dw
 
 
 def tree_weighted_nll(logits, labels, w, ignore_index: int = -100, need_grad: bool = True,

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtree_attn.so")
 SOURCES = ["plan.cpp", "partition.cpp", "gateway.hip", "attn_fwd.hip", "attn_bwd.hip", "nll.hip", "decode.hip",
-           "lmhead.hip"]
+           "lmhead.hip", "route.cpp", "ssm.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

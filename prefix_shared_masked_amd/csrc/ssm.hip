@@ -1,0 +1,363 @@
+// Tree-routed linear recurrence and causal convolution over DFS-packed tokens
+// (Tree Training post, section 9).  Rows are tokens, C channels per row, fp32.
+//
+// Scan h_t = a_t h_prev(t) + b_t, prev(t) following the root-to-token path
+// (section 9.1: a chunk starts from its parent's end state).  Chunks of up to
+// 256 tokens form a tree (parent = the previous chunk of the node, or the
+// last chunk of the nearest ancestor holding tokens).  Three passes, all with
+// consecutive lanes on consecutive channels, so every row access is
+// coalesced:
+//   reduce: per (chunk, channel) the chunk's decay A = prod a and its end
+//           state H from a zero start;
+//   walk:   per channel, chunks in DFS order: start = end of the parent chunk,
+//           end = A start + H (a few hundred dependent steps, their inputs
+//           fetched in batches ahead of the chain);
+//   apply:  per (chunk, channel) the scan again from its start, writing h.
+// The backward runs the mirror image: a reverse local scan per chunk, a walk
+// in reverse DFS order that adds every chunk's outgoing gradient a_first dh_first
+// into its parent (the sum over branches a shared prefix receives), and a
+// reverse scan per chunk writing da = dh h_prev and db = dh.
+//
+// Causal conv y_t = sum_j w[c][j] x_{prev^j(t)} (section 9.2: the window runs
+// back along the path into the parent's tail): a gather over the planner's
+// predecessor table; its backward gathers over the inverse table (dx) and
+// reduces over tokens in a fixed order (dw), so no atomics.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "route_internal.h"
+
+namespace ta {
+namespace ssm {
+
+constexpr int TH = 256;
+
+__global__ __launch_bounds__(TH) void scan_reduce(const int4* __restrict__ ch, const float* __restrict__ a,
+                                                  const float* __restrict__ b, int C, float* __restrict__ A,
+                                                  float* __restrict__ H) {
+  const int c = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
+  if (k >= C) return;
+  const int4 r = ch[c];
+  float da = 1.f, h = 0.f;
+  const float* ap = a + (size_t)r.x * C + k;
+  const float* bp = b + (size_t)r.x * C + k;
+#pragma unroll 8
+  for (int i = 0; i < r.y; ++i) {
+    const float x = ap[(size_t)i * C], y = bp[(size_t)i * C];
+    h = fmaf(x, h, y);
+    da *= x;
+  }
+  A[(size_t)c * C + k] = da;
+  H[(size_t)c * C + k] = h;
+}
+
+// Chunks in DFS order; a chunk's parent precedes it.  The end state of the
+// previous chunk is kept in a register (the parent of most chunks), others
+// come back from memory.  Inputs of 8 chunks are fetched before their chain.
+__global__ __launch_bounds__(TH) void scan_walk(const int4* __restrict__ ch, int n_chunks, const float* __restrict__ A,
+                                                const float* __restrict__ H, int C, float* __restrict__ hin,
+                                                float* __restrict__ hend) {
+  const int k = blockIdx.x * TH + threadIdx.x;
+  if (k >= C) return;
+  float prev_end = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+    float av[8], hv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = min(c0 + u, n_chunks - 1);
+      av[u] = A[(size_t)c * C + k];
+      hv[u] = H[(size_t)c * C + k];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u;
+      if (c >= n_chunks) break;
+      const int p = ch[c].z;
+      const float s = p < 0 ? 0.f : (p == c - 1 ? prev_end : hend[(size_t)p * C + k]);
+      prev_end = fmaf(av[u], s, hv[u]);
+      hin[(size_t)c * C + k] = s;
+      hend[(size_t)c * C + k] = prev_end;
+    }
+  }
+}
+
+__global__ __launch_bounds__(TH) void scan_apply(const int4* __restrict__ ch, const float* __restrict__ a,
+                                                 const float* __restrict__ b, int C, const float* __restrict__ hin,
+                                                 float* __restrict__ h) {
+  const int c = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
+  if (k >= C) return;
+  const int4 r = ch[c];
+  float s = hin[(size_t)c * C + k];
+  const size_t o = (size_t)r.x * C + k;
+#pragma unroll 8
+  for (int i = 0; i < r.y; ++i) {
+    s = fmaf(a[o + (size_t)i * C], s, b[o + (size_t)i * C]);
+    h[o + (size_t)i * C] = s;
+  }
+}
+
+// Backward, local pass: u = g_t + a_{t+1} u from the chunk's end with nothing
+// coming in; U = u at the first token, B = prod_{t > first} a_t.
+__global__ __launch_bounds__(TH) void scan_reduce_bwd(const int4* __restrict__ ch, const float* __restrict__ a,
+                                                      const float* __restrict__ g, int C, float* __restrict__ U,
+                                                      float* __restrict__ B) {
+  const int c = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
+  if (k >= C) return;
+  const int4 r = ch[c];
+  const size_t o = (size_t)r.x * C + k;
+  float u = 0.f, dec = 1.f, an = 0.f;  // an: a of the token after the current one
+#pragma unroll 8
+  for (int i = r.y - 1; i >= 0; --i) {
+    u = fmaf(an, u, g[o + (size_t)i * C]);
+    if (i + 1 < r.y) dec *= an;
+    an = a[o + (size_t)i * C];
+  }
+  U[(size_t)c * C + k] = u;
+  B[(size_t)c * C + k] = dec;
+}
+
+// Reverse DFS order: every successor of a chunk has a larger index, so a
+// chunk's incoming gradient is complete when the walk reaches it.
+__global__ __launch_bounds__(TH) void scan_walk_bwd(const int4* __restrict__ ch, int n_chunks, const float* __restrict__ a,
+                                                    const float* __restrict__ U, const float* __restrict__ B, int C,
+                                                    float* __restrict__ gin) {
+  const int k = blockIdx.x * TH + threadIdx.x;
+  if (k >= C) return;
+  for (int c = 0; c < n_chunks; ++c) gin[(size_t)c * C + k] = 0.f;
+  for (int c1 = n_chunks - 1; c1 >= 0; c1 -= 8) {
+    float uv[8], bv[8], af[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = max(c1 - u, 0);
+      uv[u] = U[(size_t)c * C + k];
+      bv[u] = B[(size_t)c * C + k];
+      af[u] = a[(size_t)ch[c].x * C + k];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c1 - u;
+      if (c < 0) break;
+      const int p = ch[c].z;
+      if (p < 0) continue;
+      const float dh0 = fmaf(bv[u], gin[(size_t)c * C + k], uv[u]);
+      gin[(size_t)p * C + k] += af[u] * dh0;
+    }
+  }
+}
+
+__global__ __launch_bounds__(TH) void scan_apply_bwd(const int4* __restrict__ ch, const float* __restrict__ a,
+                                                     const float* __restrict__ h, const float* __restrict__ g, int C,
+                                                     const float* __restrict__ gin, float* __restrict__ da,
+                                                     float* __restrict__ db) {
+  const int c = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
+  if (k >= C) return;
+  const int4 r = ch[c];
+  const size_t o = (size_t)r.x * C + k;
+  float u = gin[(size_t)c * C + k], an = 1.f;  // u carries a_{t+1} dh_{t+1} (the incoming sum at the end)
+#pragma unroll 4
+  for (int i = r.y - 1; i >= 0; --i) {
+    const float dh = g[o + (size_t)i * C] + an * u;
+    const float hp = i > 0 ? h[o + (size_t)(i - 1) * C] : (r.w >= 0 ? h[(size_t)r.w * C + k] : 0.f);
+    db[o + (size_t)i * C] = dh;
+    da[o + (size_t)i * C] = dh * hp;
+    u = dh;
+    an = a[o + (size_t)i * C];
+  }
+}
+
+// Causal conv over the path: y[t][k] = sum_j w[k][j] x[prev^j(t)][k].
+__global__ __launch_bounds__(TH) void conv_fwd(const int32_t* __restrict__ cprev, int N, int K, const float* __restrict__ x,
+                                               const float* __restrict__ w, int C, float* __restrict__ y) {
+  const int t = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
+  if (k >= C || t >= N) return;
+  float s = w[(size_t)k * K] * x[(size_t)t * C + k];
+  for (int j = 1; j < K; ++j) {
+    const int q = cprev[(size_t)t * (K - 1) + (j - 1)];
+    if (q >= 0) s = fmaf(w[(size_t)k * K + j], x[(size_t)q * C + k], s);
+  }
+  y[(size_t)t * C + k] = s;
+}
+
+// dx[s][k] = w[k][0] dy[s][k] + sum over (t, j) with prev^j(t) = s of w[k][j] dy[t][k].
+__global__ __launch_bounds__(TH) void conv_dx(const int32_t* __restrict__ sp, const int32_t* __restrict__ sc, int N, int K,
+                                              const float* __restrict__ dy, const float* __restrict__ w, int C,
+                                              float* __restrict__ dx) {
+  const int s = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
+  if (k >= C || s >= N) return;
+  float v = w[(size_t)k * K] * dy[(size_t)s * C + k];
+  for (int e = sp[s]; e < sp[s + 1]; ++e) {
+    const int code = sc[e], t = code / K, j = code - t * K;
+    v = fmaf(w[(size_t)k * K + j], dy[(size_t)t * C + k], v);
+  }
+  dx[(size_t)s * C + k] = v;
+}
+
+// dw partials: block (channel tile, token block) sums dy[t][k] x[prev^j(t)][k]
+// over its tokens for every tap j; a second pass adds the blocks in order.
+constexpr int TOKB = 64;
+__global__ __launch_bounds__(TH) void conv_dw_part(const int32_t* __restrict__ cprev, int N, int K,
+                                                   const float* __restrict__ x, const float* __restrict__ dy, int C,
+                                                   float* __restrict__ part) {
+  const int k = blockIdx.y * TH + threadIdx.x, tb = blockIdx.x;
+  if (k >= C) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int t1 = min(N, (tb + 1) * TOKB);
+  for (int t = tb * TOKB; t < t1; ++t) {
+    const float g = dy[(size_t)t * C + k];
+    acc[0] = fmaf(g, x[(size_t)t * C + k], acc[0]);
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      if (j >= K) break;
+      const int q = cprev[(size_t)t * (K - 1) + (j - 1)];
+      if (q >= 0) acc[j] = fmaf(g, x[(size_t)q * C + k], acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < K) part[((size_t)tb * C + k) * K + j] = acc[j];
+}
+
+__global__ __launch_bounds__(TH) void conv_dw_sum(const float* __restrict__ part, int nb, int C, int K,
+                                                  float* __restrict__ dw) {
+  const int i = blockIdx.x * TH + threadIdx.x;  // k * K + j
+  if (i >= C * K) return;
+  float s = 0.f;
+  for (int b = 0; b < nb; ++b) s += part[(size_t)b * C * K + i];
+  dw[i] = s;
+}
+
+}  // namespace ssm
+}  // namespace ta
+
+using namespace ta;
+
+namespace {
+struct RouteDev {
+  const int4* ch;
+  const int32_t *cprev, *succ_ptr, *succ;
+};
+RouteDev dev_tables(const ta_route* R, const void* d) {
+  const char* b = (const char*)d;
+  return {(const int4*)(b + R->off_chunks), (const int32_t*)(b + R->off_cprev), (const int32_t*)(b + R->off_succ_ptr),
+          (const int32_t*)(b + R->off_succ)};
+}
+size_t scan_ws(const ta_route* R, int C) { return align256((size_t)R->n_chunks * C * sizeof(float)) * 4; }
+size_t conv_ws(const ta_route* R, int C) {
+  return align256((size_t)((R->n_tokens + ssm::TOKB - 1) / ssm::TOKB) * C * R->conv_k * sizeof(float));
+}
+}  // namespace
+
+extern "C" ta_status tree_route_upload(const ta_route* R, void* droute, size_t bytes, hipStream_t stream) {
+  if (!R || !droute) return TA_EINVAL;
+  if (bytes < R->device_bytes) return TA_ENOMEM;
+  char* b = (char*)droute;
+  struct Part {
+    size_t off;
+    const std::vector<int32_t>* v;
+  } parts[] = {{R->off_chunks, &R->chunks}, {R->off_cprev, &R->cprev}, {R->off_succ_ptr, &R->succ_ptr},
+               {R->off_succ, &R->succ}};
+  for (const Part& x : parts) {
+    if (x.v->empty()) continue;
+    if (hipMemcpyAsync(b + x.off, x.v->data(), x.v->size() * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return TA_EHIP;
+  }
+  return TA_OK;
+}
+
+extern "C" ta_status tree_scan_ws_bytes(const ta_route* R, int32_t C, size_t* bytes) {
+  if (!R || !bytes || C <= 0) return TA_EINVAL;
+  *bytes = scan_ws(R, C);
+  return TA_OK;
+}
+
+extern "C" ta_status tree_conv_ws_bytes(const ta_route* R, int32_t C, size_t* bytes) {
+  if (!R || !bytes || C <= 0) return TA_EINVAL;
+  *bytes = conv_ws(R, C);
+  return TA_OK;
+}
+
+extern "C" ta_status tree_scan_fwd(const ta_route* R, const void* droute, const float* a, const float* b, int32_t C,
+                                   float* h, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!R || !droute || !a || !b || !h || C <= 0) return TA_EINVAL;
+  if ((int64_t)R->n_tokens * C > ((int64_t)1 << 40)) return TA_ERANGE;
+  if (R->n_chunks == 0) return TA_OK;
+  const size_t need = scan_ws(R, C);
+  if (!ws || ws_bytes < need) return TA_ENOMEM;
+  const RouteDev d = dev_tables(R, droute);
+  const size_t seg = need / 4;
+  float* A = (float*)ws;
+  float* H = (float*)((char*)ws + seg);
+  float* hin = (float*)((char*)ws + 2 * seg);
+  float* hend = (float*)((char*)ws + 3 * seg);
+  const int cb = (C + ssm::TH - 1) / ssm::TH;
+  hipLaunchKernelGGL(ssm::scan_reduce, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, b, C, A, H);
+  TA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(ssm::scan_walk, dim3(cb), dim3(ssm::TH), 0, stream, d.ch, R->n_chunks, (const float*)A,
+                     (const float*)H, C, hin, hend);
+  TA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(ssm::scan_apply, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, b, C,
+                     (const float*)hin, h);
+  TA_LAUNCH_CHECK();
+  return TA_OK;
+}
+
+extern "C" ta_status tree_scan_bwd(const ta_route* R, const void* droute, const float* a, const float* h,
+                                   const float* dh, int32_t C, float* da, float* db, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (!R || !droute || !a || !h || !dh || !da || !db || C <= 0) return TA_EINVAL;
+  if ((int64_t)R->n_tokens * C > ((int64_t)1 << 40)) return TA_ERANGE;
+  if (R->n_chunks == 0) return TA_OK;
+  const size_t need = scan_ws(R, C);
+  if (!ws || ws_bytes < need) return TA_ENOMEM;
+  const RouteDev d = dev_tables(R, droute);
+  const size_t seg = need / 4;
+  float* U = (float*)ws;
+  float* B = (float*)((char*)ws + seg);
+  float* gin = (float*)((char*)ws + 2 * seg);
+  const int cb = (C + ssm::TH - 1) / ssm::TH;
+  hipLaunchKernelGGL(ssm::scan_reduce_bwd, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, dh, C, U, B);
+  TA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(ssm::scan_walk_bwd, dim3(cb), dim3(ssm::TH), 0, stream, d.ch, R->n_chunks, a, (const float*)U,
+                     (const float*)B, C, gin);
+  TA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(ssm::scan_apply_bwd, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, h, dh, C,
+                     (const float*)gin, da, db);
+  TA_LAUNCH_CHECK();
+  return TA_OK;
+}
+
+extern "C" ta_status tree_conv_fwd(const ta_route* R, const void* droute, const float* x, const float* w, int32_t C,
+                                   float* y, hipStream_t stream) {
+  if (!R || !droute || !x || !w || !y || C <= 0) return TA_EINVAL;
+  if (R->n_tokens == 0) return TA_OK;
+  const RouteDev d = dev_tables(R, droute);
+  const int cb = (C + ssm::TH - 1) / ssm::TH;
+  hipLaunchKernelGGL(ssm::conv_fwd, dim3(R->n_tokens, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens, R->conv_k,
+                     x, w, C, y);
+  TA_LAUNCH_CHECK();
+  return TA_OK;
+}
+
+extern "C" ta_status tree_conv_bwd(const ta_route* R, const void* droute, const float* x, const float* w,
+                                   const float* dy, int32_t C, float* dx, float* dw, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (!R || !droute || !x || !w || !dy || !dx || !dw || C <= 0) return TA_EINVAL;
+  if (R->n_tokens == 0) return TA_OK;
+  const size_t need = conv_ws(R, C);
+  if (!ws || ws_bytes < need) return TA_ENOMEM;
+  const RouteDev d = dev_tables(R, droute);
+  const int cb = (C + ssm::TH - 1) / ssm::TH;
+  const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
+  hipLaunchKernelGGL(ssm::conv_dx, dim3(R->n_tokens, cb), dim3(ssm::TH), 0, stream, d.succ_ptr, d.succ, R->n_tokens,
+                     R->conv_k, dy, w, C, dx);
+  TA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(ssm::conv_dw_part, dim3(nb, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens, R->conv_k, x, dy,
+                     C, (float*)ws);
+  TA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(ssm::conv_dw_sum, dim3((C * R->conv_k + ssm::TH - 1) / ssm::TH), dim3(ssm::TH), 0, stream,
+                     (const float*)ws, nb, C, R->conv_k, dw);
+  TA_LAUNCH_CHECK();
+  return TA_OK;
+}

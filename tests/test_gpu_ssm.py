@@ -1,0 +1,90 @@
+"""GPU parity of the tree-routed scan and causal conv (Tree Training post,
+section 9) against the float64 per-path oracle (oracle/ssm.py).  fp32 on the
+GPU: |gpu - ref| <= 1e-4 |ref| + 1e-5 max|ref| elementwise."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import ssm
+import prefix_shared_masked_amd as pkg
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def close(name, got, ref):
+    got = got.cpu().double().numpy() if torch.is_tensor(got) else got
+    err = np.abs(got - ref)
+    bad = err > 1e-4 * np.abs(ref) + 1e-5 * np.abs(ref).max()
+    assert not bad.any(), f"{name}: {int(bad.sum())} of {bad.size} outside, max err {err.max():.3e}"
+
+
+def run(tree, C, K, seed, chans=None):
+    print(f"[ssm] {tree.name or 'tree'} N={tree.n_tokens} C={C} K={K}", flush=True)
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    route = pkg.tree_route(plan, K)
+    rng = np.random.default_rng(seed)
+    N = plan.n_tokens
+    a = rng.uniform(0.6, 1.0, (N, C)).astype(np.float32)
+    b = rng.standard_normal((N, C)).astype(np.float32)
+    x = rng.standard_normal((N, C)).astype(np.float32)
+    w = rng.standard_normal((C, K)).astype(np.float32)
+    g = rng.standard_normal((N, C)).astype(np.float32)
+    A, B, X, Wt, G = (torch.from_numpy(z).to(DEV) for z in (a, b, x, w, g))
+    h = pkg.tree_scan_fwd(route, A, B)
+    da, db = pkg.tree_scan_bwd(route, A, h, G)
+    y = pkg.tree_conv_fwd(route, X, Wt)
+    dx, dw = pkg.tree_conv_bwd(route, X, Wt, G)
+    torch.cuda.synchronize()
+    cs = np.arange(C) if chans is None else np.asarray(chans)
+    rs = ssm.tree_scan(op, a[:, cs], b[:, cs], g[:, cs])
+    rc = ssm.tree_conv(op, x[:, cs], w[cs], g[:, cs])
+    close("h", h[:, cs], rs["h"])
+    close("da", da[:, cs], rs["da"])
+    close("db", db[:, cs], rs["db"])
+    close("y", y[:, cs], rc["y"])
+    close("dx", dx[:, cs], rc["dx"])
+    if chans is None:
+        close("dw", dw, rc["dw"])
+    return route
+
+
+def test_six_node_and_short_parent():
+    run(W.six_node_tree(5), 37, 4, 0)
+    run(W.Tree(np.array([-1, 0, 1, 0]), np.array([4, 1, 3, 2]), "short_parent"), 64, 4, 1)
+
+
+@pytest.mark.parametrize("K", [1, 3, 8])
+def test_random_trees(K):
+    rng = np.random.default_rng(10 + K)
+    for c in range(3):
+        t = W.random_tree(rng, int(rng.integers(4, 30)), max_len=40, p_zero=0.15, n_roots=1 + c % 2)
+        run(t, 300, K, c)
+
+
+def test_long_nodes_several_chunks():
+    run(W.Tree(np.array([-1, 0, 0, 1]), np.array([700, 300, 256, 513]), "long"), 129, 4, 3)
+
+
+def test_deterministic():
+    t = W.spine_tree(64, 16, 24, 6)
+    plan = pkg.tree_plan(t.parent, t.seg_len)
+    route = pkg.tree_route(plan, 4)
+    g = torch.Generator(device=DEV).manual_seed(0)
+    a = torch.rand(plan.n_tokens, 256, generator=g, device=DEV) * 0.4 + 0.6
+    b, x, dy = (torch.randn(plan.n_tokens, 256, generator=g, device=DEV) for _ in range(3))
+    w = torch.randn(256, 4, generator=g, device=DEV)
+    r1 = (pkg.tree_scan_bwd(route, a, pkg.tree_scan_fwd(route, a, b), dy), pkg.tree_conv_bwd(route, x, w, dy))
+    r2 = (pkg.tree_scan_bwd(route, a, pkg.tree_scan_fwd(route, a, b), dy), pkg.tree_conv_bwd(route, x, w, dy))
+    for p, q in zip((*r1[0], *r1[1]), (*r2[0], *r2[1])):
+        assert torch.equal(p, q)
+
+
+@pytest.mark.timeout(600)
+def test_spine_full_size_sampled_channels():
+    """The spine workload (16,352 tokens) at 4,096 channels: every token of
+    eight sampled channels (the channels are independent) against the oracle."""
+    run(W.spine_tree(), 4096, 4, 7, chans=[0, 1, 255, 256, 1023, 2048, 4000, 4095])
