@@ -188,6 +188,46 @@ def time_lmhead(pkg, tree, steps, warmup, dev, V=151936, Dm=1024, seed=9):
     return res
 
 
+def time_ssm(pkg, tree, steps, warmup, dev, C=4096, K=4, seed=11):
+    """Tree-routed scan and causal conv (fp32, [N, C]) over the tree's tokens:
+    forward and backward of each, GB/s on the bytes each must move."""
+    import torch
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    route = pkg.tree_route(plan, K)
+    route.device(dev)
+    N = plan.n_tokens
+    g = torch.Generator(device=dev).manual_seed(seed)
+    a = torch.rand(N, C, generator=g, device=dev) * 0.4 + 0.6
+    b, x, dy = (torch.randn(N, C, generator=g, device=dev) for _ in range(3))
+    w = torch.randn(C, K, generator=g, device=dev)
+    h, da, db, y, dx = (torch.empty(N, C, device=dev) for _ in range(5))
+    dw = torch.empty(C, K, device=dev)
+    ws = torch.empty(max(pkg._route_ws("tree_scan_ws_bytes", route, C), pkg._route_ws("tree_conv_ws_bytes", route, C)),
+                     dtype=torch.uint8, device=dev)
+    calls = {
+        "scan_fwd": (lambda: pkg.tree_scan_fwd(route, a, b, h=h, ws=ws), 3 * 4),          # a, b in; h out
+        "scan_bwd": (lambda: pkg.tree_scan_bwd(route, a, h, dy, da=da, db=db, ws=ws), 5 * 4),  # a, h, dh in; da, db out
+        "conv_fwd": (lambda: pkg.tree_conv_fwd(route, x, w, y=y), 2 * 4),                 # x in; y out
+        "conv_bwd": (lambda: pkg.tree_conv_bwd(route, x, w, dy, dx=dx, dw=dw, ws=ws), 3 * 4),  # x, dy in; dx out
+    }
+    res = dict(n_tokens=N, channels=C, conv_k=K, n_chunks=route.n_chunks)
+    for name, (fn, bpe) in calls.items():
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name + "_us"] = ms * 1e3
+        res[name + "_GBps"] = N * C * bpe / (ms * 1e-3) / 1e9
+    del a, b, x, dy, h, da, db, y, dx, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_decode(pkg, L, steps, warmup, dev, B=8, Hq=32, Hkv=8, d=128, seed=5):
     import torch
     g = torch.Generator(device=dev).manual_seed(seed)
@@ -271,7 +311,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--secondary", default="random_agentic_tree,varlen_forest,spine_partitioned_4096,lmhead,decode",
+    ap.add_argument("--secondary", default="random_agentic_tree,varlen_forest,spine_partitioned_4096,lmhead,ssm,decode",
                     help="comma-separated secondary workloads to run after the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -312,6 +352,10 @@ def main():
             print("[bench] output layer + weighted NLL over the spine tree's tokens", flush=True)
             r = time_lmhead(pkg, spine, max(3, args.steps // 2), args.warmup, dev)
             extra["lmhead"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        if "ssm" in chosen:
+            print("[bench] tree-routed scan and causal conv over the spine tree's tokens", flush=True)
+            r = time_ssm(pkg, spine, args.steps, args.warmup, dev)
+            extra["ssm"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
         for L in (32768, 65536, 131072, 262144) if "decode" in chosen else ():
             extra.setdefault("decode", [])
             print(f"[bench] decode L={L}", flush=True)

@@ -167,56 +167,128 @@ __global__ __launch_bounds__(TH) void scan_apply_bwd(const int4* __restrict__ ch
   }
 }
 
-// Causal conv over the path: y[t][k] = sum_j w[k][j] x[prev^j(t)][k].
+// Causal conv over the path: y[t][k] = sum_j w[k][j] x[prev^j(t)][k].  VW
+// consecutive channels per lane (VW = 4: 16-byte accesses when C % 4 == 0).
+template <int VW>
+struct Vec;
+template <>
+struct Vec<1> {
+  typedef float T;
+  static __device__ __forceinline__ float get(const T& v, int) { return v; }
+  static __device__ __forceinline__ void set(T& v, int, float x) { v = x; }
+};
+template <>
+struct Vec<4> {
+  typedef f32x4 T;
+  static __device__ __forceinline__ float get(const T& v, int i) { return v[i]; }
+  static __device__ __forceinline__ void set(T& v, int i, float x) { v[i] = x; }
+};
+
+// A block covers TG tokens x (TH * VW) channels; each lane holds its
+// channels' taps in registers for all TG tokens.
+constexpr int TG = 8;
+template <int VW>
+__device__ __forceinline__ void load_taps(const float* __restrict__ w, int k, int K, float (&wr)[8][VW]) {
+#pragma unroll
+  for (int e = 0; e < VW; ++e)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wr[j][e] = j < K ? w[(size_t)(k + e) * K + j] : 0.f;
+}
+
+template <int VW>
 __global__ __launch_bounds__(TH) void conv_fwd(const int32_t* __restrict__ cprev, int N, int K, const float* __restrict__ x,
                                                const float* __restrict__ w, int C, float* __restrict__ y) {
-  const int t = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
-  if (k >= C || t >= N) return;
-  float s = w[(size_t)k * K] * x[(size_t)t * C + k];
-  for (int j = 1; j < K; ++j) {
-    const int q = cprev[(size_t)t * (K - 1) + (j - 1)];
-    if (q >= 0) s = fmaf(w[(size_t)k * K + j], x[(size_t)q * C + k], s);
+  typedef typename Vec<VW>::T V;
+  const int k = (blockIdx.y * TH + threadIdx.x) * VW;
+  if (k >= C) return;
+  float wr[8][VW];
+  load_taps<VW>(w, k, K, wr);
+  const int t1 = min(N, (int)(blockIdx.x + 1) * TG);
+  for (int t = blockIdx.x * TG; t < t1; ++t) {
+    const V x0 = *(const V*)(x + (size_t)t * C + k);
+    V s;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) Vec<VW>::set(s, e, wr[0][e] * Vec<VW>::get(x0, e));
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      if (j >= K) break;
+      // no branch on the table: a tap past the root loads the token's own row
+      // and contributes zero, so every load of the token can issue at once
+      const int q = cprev[(size_t)t * (K - 1) + (j - 1)];  // uniform over the block
+      const V xv = *(const V*)(x + (size_t)(q >= 0 ? q : t) * C + k);
+#pragma unroll
+      for (int e = 0; e < VW; ++e)
+        Vec<VW>::set(s, e, fmaf(wr[j][e], q >= 0 ? Vec<VW>::get(xv, e) : 0.f, Vec<VW>::get(s, e)));
+    }
+    *(V*)(y + (size_t)t * C + k) = s;
   }
-  y[(size_t)t * C + k] = s;
 }
 
 // dx[s][k] = w[k][0] dy[s][k] + sum over (t, j) with prev^j(t) = s of w[k][j] dy[t][k].
+template <int VW>
 __global__ __launch_bounds__(TH) void conv_dx(const int32_t* __restrict__ sp, const int32_t* __restrict__ sc, int N, int K,
                                               const float* __restrict__ dy, const float* __restrict__ w, int C,
                                               float* __restrict__ dx) {
-  const int s = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
-  if (k >= C || s >= N) return;
-  float v = w[(size_t)k * K] * dy[(size_t)s * C + k];
-  for (int e = sp[s]; e < sp[s + 1]; ++e) {
-    const int code = sc[e], t = code / K, j = code - t * K;
-    v = fmaf(w[(size_t)k * K + j], dy[(size_t)t * C + k], v);
+  typedef typename Vec<VW>::T V;
+  const int k = (blockIdx.y * TH + threadIdx.x) * VW;
+  if (k >= C) return;
+  float wr[8][VW];
+  load_taps<VW>(w, k, K, wr);
+  const int s1 = min(N, (int)(blockIdx.x + 1) * TG);
+  for (int s = blockIdx.x * TG; s < s1; ++s) {
+    const V g0 = *(const V*)(dy + (size_t)s * C + k);
+    V v;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) Vec<VW>::set(v, e, wr[0][e] * Vec<VW>::get(g0, e));
+    for (int i = sp[s]; i < sp[s + 1]; ++i) {
+      const int code = sc[i], t = code / K, j = code - t * K;
+      const V g = *(const V*)(dy + (size_t)t * C + k);
+#pragma unroll
+      for (int jj = 1; jj < 8; ++jj)
+        if (jj == j) {
+#pragma unroll
+          for (int e = 0; e < VW; ++e) Vec<VW>::set(v, e, fmaf(wr[jj][e], Vec<VW>::get(g, e), Vec<VW>::get(v, e)));
+        }
+    }
+    *(V*)(dx + (size_t)s * C + k) = v;
   }
-  dx[(size_t)s * C + k] = v;
 }
 
-// dw partials: block (channel tile, token block) sums dy[t][k] x[prev^j(t)][k]
+// dw partials: block (token block, channel tile) sums dy[t][k] x[prev^j(t)][k]
 // over its tokens for every tap j; a second pass adds the blocks in order.
-constexpr int TOKB = 64;
+constexpr int TOKB = 256;
+template <int VW>
 __global__ __launch_bounds__(TH) void conv_dw_part(const int32_t* __restrict__ cprev, int N, int K,
                                                    const float* __restrict__ x, const float* __restrict__ dy, int C,
                                                    float* __restrict__ part) {
-  const int k = blockIdx.y * TH + threadIdx.x, tb = blockIdx.x;
+  typedef typename Vec<VW>::T V;
+  const int k = (blockIdx.y * TH + threadIdx.x) * VW, tb = blockIdx.x;
   if (k >= C) return;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[8][VW];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[j][e] = 0.f;
   const int t1 = min(N, (tb + 1) * TOKB);
   for (int t = tb * TOKB; t < t1; ++t) {
-    const float g = dy[(size_t)t * C + k];
-    acc[0] = fmaf(g, x[(size_t)t * C + k], acc[0]);
+    const V g = *(const V*)(dy + (size_t)t * C + k);
+    const V x0 = *(const V*)(x + (size_t)t * C + k);
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[0][e] = fmaf(Vec<VW>::get(g, e), Vec<VW>::get(x0, e), acc[0][e]);
 #pragma unroll
     for (int j = 1; j < 8; ++j) {
       if (j >= K) break;
       const int q = cprev[(size_t)t * (K - 1) + (j - 1)];
-      if (q >= 0) acc[j] = fmaf(g, x[(size_t)q * C + k], acc[j]);
+      const V xq = *(const V*)(x + (size_t)(q >= 0 ? q : t) * C + k);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) acc[j][e] = fmaf(Vec<VW>::get(g, e), q >= 0 ? Vec<VW>::get(xq, e) : 0.f, acc[j][e]);
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < K) part[((size_t)tb * C + k) * K + j] = acc[j];
+  for (int e = 0; e < VW; ++e)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < K) part[((size_t)tb * C + k + e) * K + j] = acc[j][e];
 }
 
 __global__ __launch_bounds__(TH) void conv_dw_sum(const float* __restrict__ part, int nb, int C, int K,
@@ -333,9 +405,15 @@ extern "C" ta_status tree_conv_fwd(const ta_route* R, const void* droute, const 
   if (!R || !droute || !x || !w || !y || C <= 0) return TA_EINVAL;
   if (R->n_tokens == 0) return TA_OK;
   const RouteDev d = dev_tables(R, droute);
-  const int cb = (C + ssm::TH - 1) / ssm::TH;
-  hipLaunchKernelGGL(ssm::conv_fwd, dim3(R->n_tokens, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens, R->conv_k,
-                     x, w, C, y);
+  if (C % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0) {
+    const int cb = (C / 4 + ssm::TH - 1) / ssm::TH;
+    hipLaunchKernelGGL(ssm::conv_fwd<4>, dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens,
+                       R->conv_k, x, w, C, y);
+  } else {
+    const int cb = (C + ssm::TH - 1) / ssm::TH;
+    hipLaunchKernelGGL(ssm::conv_fwd<1>, dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens,
+                       R->conv_k, x, w, C, y);
+  }
   TA_LAUNCH_CHECK();
   return TA_OK;
 }
@@ -348,14 +426,24 @@ extern "C" ta_status tree_conv_bwd(const ta_route* R, const void* droute, const 
   const size_t need = conv_ws(R, C);
   if (!ws || ws_bytes < need) return TA_ENOMEM;
   const RouteDev d = dev_tables(R, droute);
-  const int cb = (C + ssm::TH - 1) / ssm::TH;
   const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
-  hipLaunchKernelGGL(ssm::conv_dx, dim3(R->n_tokens, cb), dim3(ssm::TH), 0, stream, d.succ_ptr, d.succ, R->n_tokens,
-                     R->conv_k, dy, w, C, dx);
-  TA_LAUNCH_CHECK();
-  hipLaunchKernelGGL(ssm::conv_dw_part, dim3(nb, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens, R->conv_k, x, dy,
-                     C, (float*)ws);
-  TA_LAUNCH_CHECK();
+  if (C % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)dy % 16 == 0 && (uintptr_t)dx % 16 == 0) {
+    const int cb = (C / 4 + ssm::TH - 1) / ssm::TH;
+    hipLaunchKernelGGL(ssm::conv_dx<4>, dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, stream, d.succ_ptr, d.succ,
+                       R->n_tokens, R->conv_k, dy, w, C, dx);
+    TA_LAUNCH_CHECK();
+    hipLaunchKernelGGL(ssm::conv_dw_part<4>, dim3(nb, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens, R->conv_k,
+                       x, dy, C, (float*)ws);
+    TA_LAUNCH_CHECK();
+  } else {
+    const int cb = (C + ssm::TH - 1) / ssm::TH;
+    hipLaunchKernelGGL(ssm::conv_dx<1>, dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, stream, d.succ_ptr, d.succ,
+                       R->n_tokens, R->conv_k, dy, w, C, dx);
+    TA_LAUNCH_CHECK();
+    hipLaunchKernelGGL(ssm::conv_dw_part<1>, dim3(nb, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens, R->conv_k,
+                       x, dy, C, (float*)ws);
+    TA_LAUNCH_CHECK();
+  }
   hipLaunchKernelGGL(ssm::conv_dw_sum, dim3((C * R->conv_k + ssm::TH - 1) / ssm::TH), dim3(ssm::TH), 0, stream,
                      (const float*)ws, nb, C, R->conv_k, dw);
   TA_LAUNCH_CHECK();
