@@ -263,3 +263,65 @@ def rows_attention(plan, q, k, v, rows, heads, scale=None, rope_base=0.0):
             o[ri, hi] = e @ vv / e.sum()
             lse[hi, ri] = mx + np.log(e.sum())
     return o, lse
+
+
+def _row_path(plan, i):
+    b = int(plan.node_of[i])
+    return np.concatenate([np.arange(plan.node_start[a], plan.node_start[a] + plan.seg_len[a])
+                           for a in plan.anc[b][:-1]] + [np.arange(plan.node_start[b], i + 1)]).astype(np.int64)
+
+
+def rows_attention_grads(plan, q, k, v, dO, rows, keys, scale=None, rope_base=0.0):
+    """Gradients of selected rows and keys only, from the definitions of the
+    dense backward (dP = dO V^T, D = rowsum(dO * O), dS = P (dP - D),
+    dQ = dS K s, dK = dS^T Q s, dV = P^T dO) restricted to what each output
+    needs: dq of query row i over i's own path; dk, dv of key j over every
+    query that reads j (the rows [j, sub_end(j)) of the packed order, each
+    with its own full-path softmax), all query heads of j's KV group summed.
+    For spot checks at sizes where whole-tree oracles are too slow.
+    Returns dq [len(rows), Hq, d], dk [len(keys), Hkv, d], dv [len(keys), Hkv, d]."""
+    q = np.asarray(q)
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(d) if not scale else float(scale)
+    cache = {}
+
+    def row(i, h):
+        """Everything of query row i, head h: path, rotated keys, P, D."""
+        if (i, h) in cache:
+            return cache[(i, h)]
+        idx = _row_path(plan, i)
+        p = np.arange(len(idx))
+        g = h // G
+        qi = rope(np.asarray(q[i:i + 1, h:h + 1], np.float64), p[-1:], rope_base)[0, 0]
+        kk = rope(np.asarray(k[idx][:, g:g + 1], np.float64), p, rope_base)[:, 0]
+        vv = np.asarray(v[idx][:, g], np.float64)
+        s = kk @ qi * scale
+        P = np.exp(s - s.max())
+        P /= P.sum()
+        o = P @ vv
+        do = np.asarray(dO[i, h], np.float64)
+        D = float(do @ o)
+        dS = P * (vv @ do - D)
+        cache[(i, h)] = (idx, qi, kk, P, dS, do)
+        return cache[(i, h)]
+
+    dq = np.zeros((len(rows), Hq, d))
+    for ri, i in enumerate(rows):
+        for h in range(Hq):
+            idx, qi, kk, P, dS, do = row(i, h)
+            g_rot = dS @ kk * scale                       # gradient w.r.t. the rotated q_i
+            dq[ri, h] = rope_transpose(g_rot[None, None, :], np.array([plan.pos[i]]), rope_base)[0, 0]
+    dk = np.zeros((len(keys), Hkv, d))
+    dv = np.zeros((len(keys), Hkv, d))
+    for kj, j in enumerate(keys):
+        for i in range(int(j), int(plan.sub_end[j])):
+            for h in range(Hq):
+                idx, qi, kk, P, dS, do = row(i, h)
+                at = int(np.flatnonzero(idx == j)[0])
+                g = h // G
+                dk[kj, g] += dS[at] * qi * scale
+                dv[kj, g] += P[at] * do
+        dk[kj] = rope_transpose(dk[kj][None], np.array([plan.pos[j]]), rope_base)[0]
+    return dq, dk, dv

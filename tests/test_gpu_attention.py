@@ -147,3 +147,36 @@ def test_spine_full_size():
 @pytest.mark.timeout(600)
 def test_random_agentic_full_size():
     _group_check(W.random_agentic_tree(0), 1)
+
+
+@pytest.mark.timeout(600)
+def test_varlen_forest_full_size_sampled():
+    """The varlen workload at full size (64 sequences, 133K tokens, up to 16K
+    each, bf16, RoPE): O and LSE of sampled (row, head) pairs, dQ of sampled
+    rows (all heads) and dK/dV of keys near sequence ends (all KV heads),
+    each from the per-row / per-key oracle."""
+    tree = W.varlen_forest(0)
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    N, Hq, Hkv, d = plan.n_tokens, 32, 8, 128
+    print(f"[full] varlen N={N}", flush=True)
+    q, k, v, do = W.attention_inputs(5, N, Hq, Hkv, d)
+    (Q, q64), (K, k64), (V, v64), (DO, do64) = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    o, lse = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=10000.0)
+    dq, dk, dv = pkg.tree_attn_bwd(plan, Q, K, V, o, lse, DO, rope_base=10000.0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    starts = plan.view()["node_start"]
+    lens = np.asarray(tree.seg_len)
+    longest = np.argsort(-lens)[:3]
+    rows = np.unique(np.concatenate([rng.integers(0, N, 6), starts[longest] + lens[longest] - 1]))
+    heads = [0, 9, 31]
+    ro, rl = oracle.rows_attention(op, q64, k64, v64, rows, heads, rope_base=10000.0)
+    close("o(sampled)", o[rows][:, heads], ro, torch.bfloat16)
+    close("lse(sampled)", lse[heads][:, rows], rl, torch.bfloat16)
+    keys = np.unique(np.concatenate([starts[longest] + lens[longest] - 1, starts[longest] + lens[longest] - 4,
+                                     starts[:2] + lens[:2] - 2]))
+    gq, gk, gv = oracle.rows_attention_grads(op, q64, k64, v64, do64, rows[:4], keys, rope_base=10000.0)
+    close("dq(sampled)", dq[rows[:4]], gq, torch.bfloat16)
+    close("dk(sampled)", dk[keys], gk, torch.bfloat16)
+    close("dv(sampled)", dv[keys], gv, torch.bfloat16)

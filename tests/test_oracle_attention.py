@@ -198,3 +198,19 @@ def test_rope_relative_position_property():
     for p0 in (0, 17, 3000):
         dots.append(float((rope(q, np.array([p0 + 9]), 10000.0) * rope(k, np.array([p0]), 10000.0)).sum()))
     assert dots[0] == pytest.approx(dots[1], rel=1e-10) and dots[0] == pytest.approx(dots[2], rel=1e-9)
+
+
+def test_rows_attention_grads_matches_dense():
+    """The per-row / per-key gradient oracle (for full-size spot checks)
+    against the dense-mask backward on a small tree with GQA and RoPE."""
+    rng = np.random.default_rng(21)
+    tree = W.random_tree(rng, 12, max_len=9, p_zero=0.1, n_roots=2)
+    op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    q, k, v, do = W.attention_inputs(8, op.n_tokens, 4, 2, 16)
+    ref = oracle.dense_mask_attention(op, q, k, v, rope_base=10000.0, dO=do)
+    rows = [0, op.n_tokens // 2, op.n_tokens - 1]
+    keys = [0, op.n_tokens // 3, op.n_tokens - 1]
+    dq, dk, dv = oracle.rows_attention_grads(op, q, k, v, do, rows, keys, rope_base=10000.0)
+    np.testing.assert_allclose(dq, ref["dq"][rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, ref["dk"][keys], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, ref["dv"][keys], rtol=1e-10, atol=1e-12)
