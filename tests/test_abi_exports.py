@@ -82,3 +82,38 @@ def test_validation_before_launch():
     assert L.tree_decode_ws_bytes(8, 32, 128, 262144, 0, ctypes.byref(n), ctypes.byref(s)) == 0
     assert 1 <= s.value <= 120 and n.value >= 8 * 32 * s.value * 130 * 4
     assert L.tree_attn_ws_bytes(plan.handle, 2, 1, 4, 2, 128, 0.0, ctypes.byref(n)) == 1
+
+
+def test_validation_before_launch_new_calls():
+    """The output layer, partition and recurrent-layer calls also fail before
+    any launch on arguments that are invalid on their face."""
+    L = pkg.load_library()
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    n = ctypes.c_size_t()
+    # output layer: fp32 unsupported, Dm not a multiple of 32, dh without dW, workspace too small
+    assert L.tree_lmhead_nll(0, fake, fake, fake, fake, 4, 100, 64, -100, 0, fake, None, None, None, None, fake,
+                             1 << 30, None) == 5
+    assert L.tree_lmhead_nll(1, fake, fake, fake, fake, 4, 100, 48, -100, 0, fake, None, None, None, None, fake,
+                             1 << 30, None) == 5
+    assert L.tree_lmhead_nll(1, fake, fake, fake, fake, 4, 100, 64, -100, 0, fake, None, fake, None, None, fake,
+                             1 << 30, None) == 1
+    assert L.tree_lmhead_nll(1, fake, fake, fake, fake, 4, 100, 64, -100, 0, fake, None, None, None, None, fake, 16,
+                             None) == 4
+    assert L.tree_lmhead_nll_ws_bytes(4, 100, 64, 1, 0, ctypes.byref(n)) == 0 and n.value > 0
+    assert L.tree_lmhead_nll_ws_bytes(0, 100, 64, 1, 0, ctypes.byref(n)) == 1
+    # partitioned attention: Hq not a multiple of Hkv; workspace too small
+    part = pkg.tree_partition([-1, 0, 0], [40, 30, 30], 50)
+    assert L.tree_partition_fwd(part.handle, fake, 1, fake, fake, fake, 3, 2, 128, 0.0, 0.0, fake, fake, fake,
+                                1 << 30, None) == 1
+    assert L.tree_partition_fwd(part.handle, fake, 1, fake, fake, fake, 4, 2, 128, 0.0, 0.0, fake, fake, fake, 16,
+                                None) == 4
+    assert L.tree_partition_ws_bytes(part.handle, 1, 1, 4, 2, 128, 0.0, ctypes.byref(n)) == 0 and n.value > 0
+    # recurrent layers: null device tables, workspace too small, C <= 0
+    plan = pkg.tree_plan([-1, 0], [300, 20])
+    route = pkg.tree_route(plan, 4)
+    assert L.tree_scan_fwd(route.handle, None, fake, fake, 8, fake, fake, 1 << 20, None) == 1
+    assert L.tree_scan_fwd(route.handle, fake, fake, fake, 8, fake, fake, 16, None) == 4
+    assert L.tree_scan_bwd(route.handle, fake, fake, fake, fake, 0, fake, fake, fake, 1 << 20, None) == 1
+    assert L.tree_conv_bwd(route.handle, fake, fake, fake, fake, 8, fake, fake, fake, 16, None) == 4
+    assert L.tree_scan_ws_bytes(route.handle, 8, ctypes.byref(n)) == 0 and n.value >= route.n_chunks * 8 * 4
