@@ -29,6 +29,7 @@ __all__ = ["TreeAttnError", "Plan", "Partition", "HipEvents", "tree_plan", "tree
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtree_attn.so")
 TA_BLOCK_M, TA_BLOCK_N, TA_BLOCK_KV, TA_KV_SUB, TA_CHUNK_INTS = 32, 64, 128, 32, 16
+TA_KPIECE_INTS, TA_KV_PIECE_MIN = 8, 32
 TA_F32, TA_BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "parent pointers contain a cycle",
            3: "size exceeds the int32 index range", 4: "out of memory or buffer too small",
@@ -49,7 +50,9 @@ class _View(ctypes.Structure):
         [(n, ctypes.POINTER(ctypes.c_int32)) for n in (
             "dfs_order", "node_start", "node_sub_end", "pos", "g", "node_of", "sub_end", "anc_ptr", "anc",
             "fq_ptr", "fq_chunk", "fq_order", "bk")] + \
-        [(n, ctypes.c_int32) for n in ("n_prefix_nodes", "q_start")]
+        [(n, ctypes.c_int32) for n in ("n_prefix_nodes", "q_start", "n_kpieces", "n_ksplit", "n_kslots",
+                                        "kv_piece_cap")] + \
+        [(n, ctypes.POINTER(ctypes.c_int32)) for n in ("kp", "kr")]
 
 
 class _PartView(ctypes.Structure):
@@ -180,7 +183,8 @@ class Plan:
         self._dev = {}
         for name in ("n_nodes", "n_tokens", "n_leaves", "max_pos", "block_m", "block_n", "block_kv",
                      "n_qtiles", "n_chunks", "n_ktiles", "n_flat", "visible_pairs",
-                     "computed_pairs_fwd", "computed_pairs_bwd", "n_prefix_nodes", "q_start"):
+                     "computed_pairs_fwd", "computed_pairs_bwd", "n_prefix_nodes", "q_start", "n_kpieces",
+                     "n_ksplit", "n_kslots", "kv_piece_cap"):
             setattr(self, name, int(getattr(v, name)))
 
     def _arr(self, name, n):
@@ -198,7 +202,9 @@ class Plan:
             node_of=self._arr("node_of", N), sub_end=self._arr("sub_end", N), anc_ptr=anc_ptr,
             anc=self._arr("anc", int(anc_ptr[-1])), fq_ptr=self._arr("fq_ptr", self.n_qtiles + 1),
             fq_chunk=self._arr("fq_chunk", self.n_chunks * TA_CHUNK_INTS).reshape(-1, TA_CHUNK_INTS),
-            fq_order=self._arr("fq_order", self.n_qtiles), bk=self._arr("bk", self.n_ktiles * 4).reshape(-1, 4))
+            fq_order=self._arr("fq_order", self.n_qtiles), bk=self._arr("bk", self.n_ktiles * 4).reshape(-1, 4),
+            kp=self._arr("kp", self.n_kpieces * TA_KPIECE_INTS).reshape(-1, TA_KPIECE_INTS),
+            kr=self._arr("kr", self.n_ksplit * 4).reshape(-1, 4))
 
     @property
     def handle(self):

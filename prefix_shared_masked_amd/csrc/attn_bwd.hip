@@ -300,13 +300,54 @@ struct KVParams {
   bf16* dk;
   bf16* dv;
   const int32_t* pos;
-  const int32_t* bk;
+  const int32_t* kp;  // work pieces, TA_KPIECE_INTS each
+  const int32_t* kr;  // cut tiles: (k0, klen, first slot, n_pieces)
+  float* part;        // partial dK/dV slots of cut tiles (PART_FLOATS per slot and KV head)
   int N, Hq, Hkv, G;
   int q0;  // first query row (rows below are a key-only prefix)
   float scale, scale_log2, rope_base;
 };
 
 constexpr int SUB = TA_KV_SUB;  // keys per wavefront = rows per query block
+
+// A partial slot holds one piece's raw dK and dV accumulators for one KV
+// head in register order: per wavefront w, [dK | dV] each [tile dt 4][r/4 4]
+// [lane 64][r%4 4] floats, so a wavefront writes and reads 1 KiB contiguous
+// runs (register r of tile dt of lane l <-> key 8*(r/4) + 4*(l/32) + r%4 of
+// the wavefront's 32, dimension dt*32 + l%32).
+constexpr int PART_WAVE = 2 * 4 * 16 * 64;
+constexpr int PART_FLOATS = 4 * PART_WAVE;
+
+// dK (scaled, rotated back by -pos) and dV of one wavefront's keys in bf16.
+// Accumulator register r of tile dt <-> key kw + 8*(r/4) + 4*half + r%4,
+// d = dt*32 + col; the rotate-half partner d + 64 is tile dt + 2.
+__device__ __forceinline__ void store_dkv(const KVParams& P, int kvh, int kw, int wkeys, int half, int col,
+                                          const f32x16 (&dk)[4], const f32x16 (&dv)[4]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
+    if (kr >= wkeys) continue;
+    const size_t o = ((size_t)(kw + kr) * P.Hkv + kvh) * D;
+    float g[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) g[dt] = dk[dt][r] * P.scale;
+    if (P.rope_base > 0.f) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        float sn, cs;
+        rope_sincos(P.pos[kw + kr], dt * 32 + col, D, P.rope_base, &sn, &cs);
+        const float y1 = g[dt], y2 = g[dt + 2];
+        g[dt] = y1 * cs + y2 * sn;
+        g[dt + 2] = y2 * cs - y1 * sn;
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      P.dk[o + dt * 32 + col] = (bf16)g[dt];
+      P.dv[o + dt * 32 + col] = (bf16)dv[dt][r];
+    }
+  }
+}
 
 // One staged query block in LDS: fp16 Q rows (scores, and the transpose-read
 // operand of dK), bf16 dO rows (dP, and the transpose-read operand of dV),
@@ -326,9 +367,9 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * L::BYTES];
 
   const int kvh = blockIdx.x % P.Hkv;
-  const cint_ptr tl = as_const(P.bk) + (size_t)(blockIdx.x / P.Hkv) * 4;
+  const cint_ptr tl = as_const(P.kp) + (size_t)(blockIdx.x / P.Hkv) * TA_KPIECE_INTS;
   const int k0 = tl[0], klen = tl[1], qe = tl[2];
-  const int qs = max(k0, P.q0);                   // first query row of the tile
+  const int qlo = tl[3], qhi = tl[4], slot = tl[5];  // this piece's query rows; its partial slot or -1
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int col = lane & 31, half = lane >> 5;
   const int kw = k0 + SUB * wave;                 // this wavefront's first key
@@ -376,8 +417,10 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
       toff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
     }
 
-  // Items are (32-row block, query head), blocks from the end of the query
-  // range down and the heads of the group innermost: the workgroups resident
+  // Items are (32-row block, query head) of the piece's rows [qlo, qhi)
+  // (blocks start at max(k0, q_start) + 32i, so a block past a wavefront's
+  // diagonal lies wholly below it), blocks from the end down and the heads of
+  // the group innermost: the workgroups resident
   // on an XCD share a KV head and (for nested subtrees) the tail of their
   // query ranges, so they stream the same rows at about the same time and
   // one fetch serves them from L2.  All four wavefronts share each staged
@@ -386,12 +429,12 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   // and sixteen LSE or D values (wavefront w: LSE rows 16w.. for w < 2, D rows
   // 16(w-2).. otherwise).  Rows past the query range copy the last valid row
   // and are masked to P = 0 below, so they contribute nothing.
-  const int nblk = (qe - qs + SUB - 1) / SUB;     // >= 1: the plan gives every tile a query row
+  const int nblk = (qhi - qlo + SUB - 1) / SUB;   // >= 1: the plan gives every piece a query row
   const int nitem = P.G * nblk;
   const int w = __builtin_amdgcn_readfirstlane(wave);
   auto stage = [&](int it, char* base) {
     const int h = kvh * P.G + it % P.G;
-    const int qb = qs + SUB * (nblk - 1 - it / P.G);
+    const int qb = qlo + SUB * (nblk - 1 - it / P.G);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = w + 4 * k;
@@ -440,7 +483,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     }
   };
   auto grads = [&](int it, const char* base, const f32x16& S, const f32x16& dP) {
-    const int qb = qs + SUB * (nblk - 1 - it / P.G);
+    const int qb = qlo + SUB * (nblk - 1 - it / P.G);
     const f16* q16 = (const f16*)(base + L::Q16);
     const bf16* dob = (const bf16*)(base + L::DO);
     // transpose reads first: their latency hides behind the exponentials
@@ -521,33 +564,60 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   lds_copies_wait();
 
   agpr_fence8(dk, dv);
-  // Each wavefront owns its keys: scale and rotate dK back, store dK and dV.
-  // Accumulator register r of tile dt <-> key kw + 8*(r/4) + 4*half + r%4,
-  // d = dt*32 + col; the rotate-half partner d + 64 is tile dt + 2.
+  // Each wavefront owns its keys: a whole tile stores them (scaled, rotated
+  // back, bf16); a piece of a cut tile writes its raw accumulators to its
+  // partial slot for dkv_sum_kernel.
+  if (slot < 0) {
+    store_dkv(P, kvh, kw, wkeys, half, col, dk, dv);
+  } else if (wkeys > 0) {
+    float* dst = P.part + ((size_t)slot * P.Hkv + kvh) * PART_FLOATS + wave * PART_WAVE + lane * 4;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
-    if (kr >= wkeys) continue;
-    const size_t o = ((size_t)(kw + kr) * P.Hkv + kvh) * D;
-    float g[4];
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) g[dt] = dk[dt][r] * P.scale;
-    if (P.rope_base > 0.f) {
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        float sn, cs;
-        rope_sincos(P.pos[kw + kr], dt * 32 + col, D, P.rope_base, &sn, &cs);
-        const float y1 = g[dt], y2 = g[dt + 2];
-        g[dt] = y1 * cs + y2 * sn;
-        g[dt + 2] = y2 * cs - y1 * sn;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int o = (dt * 4 + r4) * 256;
+        *(float4*)(dst + o) = float4{dk[dt][4 * r4], dk[dt][4 * r4 + 1], dk[dt][4 * r4 + 2], dk[dt][4 * r4 + 3]};
+        *(float4*)(dst + PART_WAVE / 2 + o) =
+            float4{dv[dt][4 * r4], dv[dt][4 * r4 + 1], dv[dt][4 * r4 + 2], dv[dt][4 * r4 + 3]};
       }
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      P.dk[o + dt * 32 + col] = (bf16)g[dt];
-      P.dv[o + dt * 32 + col] = (bf16)dv[dt][r];
-    }
   }
+}
+
+// Sums the partial slots of each cut tile in slot order (deterministic) and
+// stores dK / dV as the whole-tile epilogue does.  One workgroup per (cut
+// tile, KV head), one wavefront per 32 keys.
+__global__ __launch_bounds__(256) void dkv_sum_kernel(KVParams P) {
+  const int kvh = blockIdx.x % P.Hkv;
+  const int32_t* tl = P.kr + (size_t)(blockIdx.x / P.Hkv) * 4;
+  const int k0 = tl[0], klen = tl[1], slot0 = tl[2], np = tl[3];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kw = k0 + SUB * wave, wkeys = min(SUB, klen - SUB * wave);
+  if (wkeys <= 0) return;
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+  for (int s = 0; s < np; ++s) {
+    const float* src = P.part + ((size_t)(slot0 + s) * P.Hkv + kvh) * PART_FLOATS + wave * PART_WAVE + lane * 4;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int o = (dt * 4 + r4) * 256;
+        const float4 a = *(const float4*)(src + o), b = *(const float4*)(src + PART_WAVE / 2 + o);
+        dk[dt][4 * r4] += a.x;
+        dk[dt][4 * r4 + 1] += a.y;
+        dk[dt][4 * r4 + 2] += a.z;
+        dk[dt][4 * r4 + 3] += a.w;
+        dv[dt][4 * r4] += b.x;
+        dv[dt][4 * r4 + 1] += b.y;
+        dv[dt][4 * r4 + 2] += b.z;
+        dv[dt][4 * r4 + 3] += b.w;
+      }
+  }
+  store_dkv(P, kvh, kw, wkeys, lane >> 5, lane & 31, dk, dv);
 }
 
 // ---------------------------------------------------------------------------
@@ -640,6 +710,7 @@ size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t
     b += align256(N * Hq * sizeof(float));                                             // LSE * log2(e)
     b += align256(N * Hq * d * sizeof(f16)) + align256(N * Hkv * d * sizeof(f16));  // fp16 Q, K
     if (rope_base > 0.f) b += align256(N * Hkv * d * sizeof(bf16));                 // rotated bf16 K
+    b += align256((size_t)p->n_kslots * Hkv * bwd::PART_FLOATS * sizeof(float));     // dK/dV partials
   } else if (rope_base > 0.f) {
     b += align256(N * Hq * d * sizeof(float)) + align256(N * Hkv * d * sizeof(float));
   }
@@ -674,6 +745,8 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   const int32_t* fq_chunk = (const int32_t*)(base + p->off_fq_chunk);
   const int32_t* fq_order = (const int32_t*)(base + p->off_fq_order);
   const int32_t* bk = (const int32_t*)(base + p->off_bk);
+  const int32_t* kp = (const int32_t*)(base + p->off_kp);
+  const int32_t* kr = (const int32_t*)(base + p->off_kr);
   const bool rope = rope_base > 0.f;
   char* w = (char*)ws;
   float* Dd = (float*)w;
@@ -686,12 +759,15 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     w += align256((size_t)N * Hq * d * sizeof(f16));
     f16* ks = (f16*)w;
     w += align256((size_t)N * Hkv * d * sizeof(f16));
+    bf16* krot = rope ? (bf16*)w : nullptr;
+    if (rope) w += align256((size_t)N * Hkv * d * sizeof(bf16));
+    float* part = (float*)w;
     mark(ev, nev, 0, stream);
     // one pass: fp16 K * scale * log2(e) for dK/dV's scores and, with RoPE,
     // the rotated bf16 K for dQ
-    const bf16* kb = rope ? (const bf16*)w : (const bf16*)k;
+    const bf16* kb = rope ? krot : (const bf16*)k;
     if (launch_rope<bf16, f16>((const bf16*)k, ks, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E,
-                               rope ? (bf16*)w : nullptr) != hipSuccess)
+                               krot) != hipSuccess)
       return TA_EHIP;
     mark(ev, nev, 1, stream);
     bwd::DQParams A;
@@ -731,7 +807,9 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.dk = (bf16*)dk;
     B.dv = (bf16*)dv;
     B.pos = pos;
-    B.bk = bk;
+    B.kp = kp;
+    B.kr = kr;
+    B.part = part;
     B.N = N;
     B.Hq = Hq;
     B.Hkv = Hkv;
@@ -740,8 +818,12 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.scale = scale;
     B.scale_log2 = scale * TA_LOG2E;
     B.rope_base = rope_base;
-    hipLaunchKernelGGL(bwd::dkv_bf16_kernel, dim3(p->n_ktiles * Hkv), dim3(256), 0, stream, B);
+    hipLaunchKernelGGL(bwd::dkv_bf16_kernel, dim3(p->n_kpieces * Hkv), dim3(256), 0, stream, B);
     TA_LAUNCH_CHECK();
+    if (p->n_ksplit > 0) {
+      hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3(p->n_ksplit * Hkv), dim3(256), 0, stream, B);
+      TA_LAUNCH_CHECK();
+    }
     mark(ev, nev, 3, stream);
     return TA_OK;
   }

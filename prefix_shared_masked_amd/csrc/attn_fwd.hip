@@ -383,7 +383,9 @@ extern "C" ta_status tree_plan_upload(const ta_plan* p, void* dplan, size_t byte
                {p->off_fq_ptr, &p->fq_ptr},
                {p->off_fq_chunk, &p->fq_chunk},
                {p->off_fq_order, &p->fq_order},
-               {p->off_bk, &p->bk}};
+               {p->off_bk, &p->bk},
+               {p->off_kp, &p->kp},
+               {p->off_kr, &p->kr}};
   for (const Part& x : parts) {
     if (x.vec->empty()) continue;
     if (hipMemcpyAsync(base + x.off, x.vec->data(), x.vec->size() * sizeof(int32_t), hipMemcpyHostToDevice,

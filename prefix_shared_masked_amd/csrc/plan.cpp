@@ -280,7 +280,62 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
   }
   p->computed_pairs_bwd = comp_bwd;
 
-  // device image: pos | fq_ptr | fq_chunk | fq_order | bk, each 256-aligned
+  // dK/dV work pieces.  A workgroup of the dK/dV kernel runs every 32-row
+  // query block of its tile, and the root's keys are read by every query, so
+  // whole tiles leave one CU with far more than the average share.  A tile
+  // whose query range spans more than `cap` blocks is cut into equal runs of
+  // blocks (cap = max(TA_KV_PIECE_MIN, total blocks / 256): about 256 CUs'
+  // worth of pieces for any number of KV heads); the pieces of a cut tile
+  // write fp32 partial dK/dV to consecutive slots that a second pass sums in
+  // slot order.  Pieces are listed longest first.
+  {
+    int64_t total = 0;
+    std::vector<int32_t> tb(kts.size());
+    for (size_t i = 0; i < kts.size(); ++i) {
+      const int32_t qs = std::max(kts[i].k0, Q0);
+      tb[i] = (kts[i].qe - qs + SUB - 1) / SUB;
+      total += tb[i];
+    }
+    const int64_t cap = std::max<int64_t>(TA_KV_PIECE_MIN, (total + 255) / 256);
+    struct KP {
+      int32_t rec[TA_KPIECE_INTS];
+      int32_t blocks;
+    };
+    std::vector<KP> kps;
+    int32_t slots = 0;
+    for (size_t i = 0; i < kts.size(); ++i) {
+      const int32_t qs = std::max(kts[i].k0, Q0), nb = tb[i];
+      const int32_t np = static_cast<int32_t>((nb + cap - 1) / cap);
+      if (np > 1) {
+        p->kr.insert(p->kr.end(), {kts[i].k0, kts[i].klen, slots, np});
+      }
+      for (int32_t j = 0, b = 0; j < np; ++j) {
+        const int32_t len = nb / np + (j < nb % np ? 1 : 0);
+        KP x{};
+        x.rec[0] = kts[i].k0;
+        x.rec[1] = kts[i].klen;
+        x.rec[2] = kts[i].qe;
+        x.rec[3] = qs + SUB * b;
+        x.rec[4] = std::min(kts[i].qe, qs + SUB * (b + len));
+        x.rec[5] = np > 1 ? slots + j : -1;
+        x.rec[6] = static_cast<int32_t>(i);
+        x.blocks = len;
+        kps.push_back(x);
+        b += len;
+      }
+      if (np > 1) slots += np;
+    }
+    std::stable_sort(kps.begin(), kps.end(), [](const KP& x, const KP& y) { return x.blocks > y.blocks; });
+    if (int64_t(kps.size()) * TA_KPIECE_INTS > kI32Max) return TA_ERANGE;
+    p->kp.reserve(kps.size() * TA_KPIECE_INTS);
+    for (const KP& x : kps) p->kp.insert(p->kp.end(), x.rec, x.rec + TA_KPIECE_INTS);
+    p->n_kpieces = static_cast<int32_t>(kps.size());
+    p->n_ksplit = static_cast<int32_t>(p->kr.size() / 4);
+    p->n_kslots = slots;
+    p->kv_piece_cap = static_cast<int32_t>(cap);
+  }
+
+  // device image: pos | fq_ptr | fq_chunk | fq_order | bk | kp | kr, each 256-aligned
   size_t off = 0;
   p->off_pos = off;
   off = align256(off + sizeof(int32_t) * size_t(std::max(N, 1)));
@@ -292,6 +347,10 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
   off = align256(off + sizeof(int32_t) * std::max<size_t>(p->fq_order.size(), 1));
   p->off_bk = off;
   off = align256(off + sizeof(int32_t) * std::max<size_t>(p->bk.size(), 1));
+  p->off_kp = off;
+  off = align256(off + sizeof(int32_t) * std::max<size_t>(p->kp.size(), 1));
+  p->off_kr = off;
+  off = align256(off + sizeof(int32_t) * std::max<size_t>(p->kr.size(), 1));
   p->device_bytes = off;
   return TA_OK;
 }
@@ -362,6 +421,12 @@ extern "C" ta_status tree_plan_view(const ta_plan* p, ta_plan_view* v) {
   v->bk = p->bk.data();
   v->n_prefix_nodes = p->n_prefix_nodes;
   v->q_start = p->q_start;
+  v->n_kpieces = p->n_kpieces;
+  v->n_ksplit = p->n_ksplit;
+  v->n_kslots = p->n_kslots;
+  v->kv_piece_cap = p->kv_piece_cap;
+  v->kp = p->kp.data();
+  v->kr = p->kr.data();
   return TA_OK;
 }
 

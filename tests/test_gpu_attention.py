@@ -83,6 +83,42 @@ def test_bf16_small_trees(heads):
         run_case(t, Hq, Hkv, 128, torch.bfloat16, 10000.0 if i % 2 == 0 else 0.0, seed=i)
 
 
+def test_bf16_cut_key_tiles():
+    """Key tiles whose query rows are cut into pieces whose partial dK/dV a
+    second pass sums: a ragged 100-key root and three 300-key-node tiles over
+    2,000 rows (cap 32 blocks), all KV heads, with and without RoPE, bitwise
+    repeatable; then the root as a key-only prefix (pieces from q_start)."""
+    tree = W.Tree(np.array([-1, 0, 1, 1], np.int32), np.array([100, 300, 900, 700], np.int32), "cut")
+    for i, (Hq, Hkv) in enumerate(((8, 2), (4, 4))):
+        plan, res, _ = run_case(tree, Hq, Hkv, 128, torch.bfloat16, 10000.0 if i == 0 else 0.0, seed=11 + i)
+        assert plan.n_ksplit == 4
+    q, k, v, do = W.attention_inputs(12, tree.n_tokens, 8, 2, 128)
+    Q, K, V, DO = (torch.from_numpy(x).to(DEV).bfloat16() for x in (q, k, v, do))
+    o, l = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=10000.0)
+    g1 = pkg.tree_attn_bwd(plan, Q, K, V, o, l, DO, rope_base=10000.0)
+    g2 = pkg.tree_attn_bwd(plan, Q, K, V, o, l, DO, rope_base=10000.0)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+    pe = pkg.tree_plan(tree.parent, tree.seg_len, n_prefix_nodes=1)
+    q0, N = pe.q_start, pe.n_tokens
+    assert q0 == 100 and pe.n_ksplit >= 1
+    print(f"[case] cut prefix N={N} q0={q0}", flush=True)
+    q, k, v, do = W.attention_inputs(13, N, 4, 2, 128)
+    do[:q0] = 0.0
+    (Q, q64), (K, k64), (V, v64), (DO, do64) = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    o, lse = pkg.tree_attn_fwd(pe, Q, K, V, rope_base=10000.0)
+    o[:q0] = 0
+    dq, dk, dv = pkg.tree_attn_bwd(pe, Q, K, V, o, lse, DO, rope_base=10000.0)
+    torch.cuda.synchronize()
+    ref = oracle.dense_mask_attention(oracle.oracle_plan(tree.parent, tree.seg_len), q64, k64, v64,
+                                      rope_base=10000.0, dO=do64)
+    close("o", o[q0:], ref["o"][q0:], torch.bfloat16)
+    close("dq", dq[q0:], ref["dq"][q0:], torch.bfloat16)
+    close("dk", dk, ref["dk"], torch.bfloat16)
+    close("dv", dv, ref["dv"], torch.bfloat16)
+
+
 def test_bf16_deterministic_and_sibling_leak():
     """Same inputs -> bitwise-identical gradients; editing one branch leaves
     the other branch's outputs bit-for-bit unchanged (leak test of the Tree

@@ -82,7 +82,54 @@ def compare(tree):
     assert p.computed_pairs_bwd == sub * sub * sum(work)
     for row in v["bk"]:
         assert o.node_of[row[0]] == row[3]
+    check_pieces(p, v)
     return p, o
+
+
+def check_pieces(p, v):
+    """dK/dV work pieces: each tile's query rows [max(k0, q_start), q_end) are
+    covered once, in order, by runs that start on its 32-row block grid; a
+    tile is cut iff it spans more than the cap's blocks, into equal runs (to
+    one block) of at most the cap; cut tiles own consecutive slots; pieces
+    are listed longest first."""
+    sub = pkg.TA_KV_SUB
+    kp, kr, bk = v["kp"], v["kr"], v["bk"]
+    assert p.n_kpieces == len(kp) >= p.n_ktiles and p.n_ksplit == len(kr)
+    nb = [-(-(int(t[2]) - max(int(t[0]), p.q_start)) // sub) for t in bk]
+    cap = max(pkg.TA_KV_PIECE_MIN, -(-sum(nb) // 256))
+    assert p.kv_piece_cap == cap
+    by_tile = {}
+    for x in kp:
+        assert x[7] == 0 and 0 <= x[6] < p.n_ktiles
+        assert tuple(x[:3]) == tuple(bk[x[6]][:3])
+        by_tile.setdefault(int(x[6]), []).append(x)
+    assert sorted(by_tile) == list(range(p.n_ktiles))
+    slots = []
+    cut = {}
+    for t, ps in by_tile.items():
+        k0, kl, qe = (int(z) for z in bk[t][:3])
+        qs = max(k0, p.q_start)
+        ps = sorted(ps, key=lambda x: x[3])
+        assert ps[0][3] == qs and ps[-1][4] == qe
+        lens = []
+        for a, b in zip(ps, ps[1:]):
+            assert a[4] == b[3]
+        for x in ps:
+            assert x[3] < x[4] and (x[3] - qs) % sub == 0
+            lens.append(-(-(int(x[4]) - int(x[3])) // sub))
+        assert sum(lens) == nb[t] and max(lens) <= cap and max(lens) - min(lens) <= 1
+        if len(ps) == 1:
+            assert nb[t] <= cap and ps[0][5] == -1
+        else:
+            assert len(ps) == -(-nb[t] // cap)
+            ss = [int(x[5]) for x in ps]
+            assert ss == list(range(ss[0], ss[0] + len(ps)))
+            slots += ss
+            cut[(k0, kl)] = (ss[0], len(ps))
+    assert sorted(slots) == list(range(p.n_kslots))
+    assert {(int(r[0]), int(r[1])): (int(r[2]), int(r[3])) for r in kr} == cut and len(cut) == len(kr)
+    blocks = [-(-(int(x[4]) - int(x[3])) // sub) for x in kp]
+    assert all(a >= b for a, b in zip(blocks, blocks[1:]))
 
 
 def test_six_node():
@@ -120,6 +167,23 @@ def test_random_small_trees(seed):
 def test_node_lengths_around_tile_edges():
     for L in (1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129):
         compare(W.Tree(np.array([-1, 0, 0, 1], np.int32), np.array([L, L, 3, L], np.int32)))
+
+
+def test_cut_key_tiles():
+    """A 100-token root over a 300-token node with 900- and 700-token
+    children (2,000 rows): the tiles span 423 query blocks in all, so the cap
+    is 32; the root's tile (63 blocks) and node 1's three tiles (60, 56, 52)
+    are cut in two, the rest stay whole.  With the root as a key-only prefix
+    the pieces start at q_start."""
+    tree = W.Tree(np.array([-1, 0, 1, 1], np.int32), np.array([100, 300, 900, 700], np.int32))
+    p, _ = compare(tree)
+    v = p.view()
+    assert p.kv_piece_cap == 32 and p.n_ksplit == 4 and p.n_kslots == 8
+    root = sorted(-(-(int(x[4]) - int(x[3])) // 32) for x in v["kp"] if x[0] == 0)
+    assert root == [31, 32]
+    pe = pkg.tree_plan(tree.parent, tree.seg_len, n_prefix_nodes=1)
+    check_pieces(pe, pe.view())
+    assert pe.q_start == 100 and all(x[3] >= 100 for x in pe.view()["kp"])
 
 
 def test_star_with_64_children_and_deep_chain():
