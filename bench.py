@@ -291,16 +291,26 @@ def cpu_baseline(tree, budget_s=20.0, seed=0):
                        f"{t_total:.1f} s", seconds=round(t_total, 2))
 
 
+# kernels launched between the same two events as the named one (their HBM
+# bytes count toward its launch): dK/dV and the sum of its cut tiles' partials
+SPAN = {"dkv_bf16_kernel": ("dkv_bf16_kernel", "dkv_sum_kernel")}
+
+
 def load_traffic(kernel):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    e = t.get(kernel)
-    if not e or e.get("source_hash") != source_hash():
-        return None
-    return e.get("bytes_per_launch")
+    total = 0
+    for i, k in enumerate(SPAN.get(kernel, (kernel,))):
+        e = t.get(k)
+        if e is None and i > 0:
+            continue
+        if not e or e.get("source_hash") != source_hash():
+            return None
+        total += e.get("bytes_per_launch")
+    return total
 
 
 def main():

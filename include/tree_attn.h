@@ -122,16 +122,19 @@ typedef struct ta_plan_view {
   /* dK/dV work pieces (bf16 backward).  Every key tile of bk is one or more
    * pieces; a piece runs the tile's keys against a run of its query rows.  A
    * tile whose query range [max(k0, q_start), q_end) spans more than
-   * kv_piece_cap 32-row blocks is cut into equal runs of blocks; its pieces
-   * write fp32 partial dK/dV to n_pieces consecutive workspace slots, summed
-   * in slot order by a second pass, so the result stays deterministic. */
+   * kv_piece_cap 32-row blocks is cut into runs of exactly kv_piece_cap
+   * blocks counted back from q_end, the remainder at the front; its pieces
+   * write fp32 partial dK/dV to n_pieces consecutive workspace slots (slot
+   * first + e for the e-th run from the end), summed in slot order by a
+   * second pass, so the result stays deterministic. */
   int32_t n_kpieces;         /* pieces, >= n_ktiles */
   int32_t n_ksplit;          /* tiles that were cut */
   int32_t n_kslots;          /* partial slots: sum of n_pieces over cut tiles */
   int32_t kv_piece_cap;      /* max(TA_KV_PIECE_MIN, ceil(total query blocks of all tiles / 256)) */
   const int32_t* kp;         /* [n_kpieces * TA_KPIECE_INTS] (k0, klen, q_end, q_lo, q_hi, slot,
                                 tile, 0): rows [q_lo, q_hi); slot -1 = whole tile (writes dK/dV
-                                directly); longest first */
+                                directly); longest first, equal lengths by run
+                                from the end */
   const int32_t* kr;         /* [n_ksplit * 4] (k0, klen, first slot, n_pieces) of each cut tile */
 } ta_plan_view;
 

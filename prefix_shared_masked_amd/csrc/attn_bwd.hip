@@ -318,15 +318,17 @@ constexpr int SUB = TA_KV_SUB;  // keys per wavefront = rows per query block
 constexpr int PART_WAVE = 2 * 4 * 16 * 64;
 constexpr int PART_FLOATS = 4 * PART_WAVE;
 
-// dK (scaled, rotated back by -pos) and dV of one wavefront's keys in bf16.
-// Accumulator register r of tile dt <-> key kw + 8*(r/4) + 4*half + r%4,
-// d = dt*32 + col; the rotate-half partner d + 64 is tile dt + 2.
+// dK (scaled, rotated back by -pos) and dV of one wavefront's keys in bf16,
+// accumulator registers [rlo, rhi).  Register r of tile dt <-> key
+// kw + 8*(r/4) + 4*half + r%4, d = dt*32 + col; the rotate-half partner
+// d + 64 is tile dt + 2.
 __device__ __forceinline__ void store_dkv(const KVParams& P, int kvh, int kw, int wkeys, int half, int col,
-                                          const f32x16 (&dk)[4], const f32x16 (&dv)[4]) {
+                                          const f32x16 (&dk)[4], const f32x16 (&dv)[4], int rlo = 0,
+                                          int rhi = 16) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
-    if (kr >= wkeys) continue;
+    if (r < rlo || r >= rhi || kr >= wkeys) continue;
     const size_t o = ((size_t)(kw + kr) * P.Hkv + kvh) * D;
     float g[4];
 #pragma unroll
@@ -585,39 +587,60 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
 
 // Sums the partial slots of each cut tile in slot order (deterministic) and
 // stores dK / dV as the whole-tile epilogue does.  One workgroup per (cut
-// tile, KV head), one wavefront per 32 keys.
+// tile, KV head, register group g), one wavefront per 32 keys; group g holds
+// accumulator registers 4g..4g+3 of every tile (keys 8g + 4*half + 0..3).
 __global__ __launch_bounds__(256) void dkv_sum_kernel(KVParams P) {
-  const int kvh = blockIdx.x % P.Hkv;
-  const int32_t* tl = P.kr + (size_t)(blockIdx.x / P.Hkv) * 4;
+  const int g = blockIdx.x & 3, rest = blockIdx.x >> 2;
+  const int kvh = rest % P.Hkv;
+  const int32_t* tl = P.kr + (size_t)(rest / P.Hkv) * 4;
   const int k0 = tl[0], klen = tl[1], slot0 = tl[2], np = tl[3];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kw = k0 + SUB * wave, wkeys = min(SUB, klen - SUB * wave);
   if (wkeys <= 0) return;
+  float sk[4][4], sv[4][4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sk[dt][j] = sv[dt][j] = 0.f;
+  for (int s = 0; s < np; ++s) {
+    const float* src = P.part + ((size_t)(slot0 + s) * P.Hkv + kvh) * PART_FLOATS + wave * PART_WAVE + g * 256 +
+                       lane * 4;
+    float4 a[4], b[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      a[dt] = *(const float4*)(src + dt * 1024);
+      b[dt] = *(const float4*)(src + PART_WAVE / 2 + dt * 1024);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      sk[dt][0] += a[dt].x;
+      sk[dt][1] += a[dt].y;
+      sk[dt][2] += a[dt].z;
+      sk[dt][3] += a[dt].w;
+      sv[dt][0] += b[dt].x;
+      sv[dt][1] += b[dt].y;
+      sv[dt][2] += b[dt].z;
+      sv[dt][3] += b[dt].w;
+    }
+  }
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
-  for (int s = 0; s < np; ++s) {
-    const float* src = P.part + ((size_t)(slot0 + s) * P.Hkv + kvh) * PART_FLOATS + wave * PART_WAVE + lane * 4;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int gg = 0; gg < 4; ++gg)
+    if (gg == g) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int o = (dt * 4 + r4) * 256;
-        const float4 a = *(const float4*)(src + o), b = *(const float4*)(src + PART_WAVE / 2 + o);
-        dk[dt][4 * r4] += a.x;
-        dk[dt][4 * r4 + 1] += a.y;
-        dk[dt][4 * r4 + 2] += a.z;
-        dk[dt][4 * r4 + 3] += a.w;
-        dv[dt][4 * r4] += b.x;
-        dv[dt][4 * r4 + 1] += b.y;
-        dv[dt][4 * r4 + 2] += b.z;
-        dv[dt][4 * r4 + 3] += b.w;
-      }
-  }
-  store_dkv(P, kvh, kw, wkeys, lane >> 5, lane & 31, dk, dv);
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dk[dt][4 * gg + j] = sk[dt][j];
+          dv[dt][4 * gg + j] = sv[dt][j];
+        }
+    }
+  store_dkv(P, kvh, kw, wkeys, lane >> 5, lane & 31, dk, dv, 4 * g, 4 * g + 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -821,7 +844,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     hipLaunchKernelGGL(bwd::dkv_bf16_kernel, dim3(p->n_kpieces * Hkv), dim3(256), 0, stream, B);
     TA_LAUNCH_CHECK();
     if (p->n_ksplit > 0) {
-      hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3(p->n_ksplit * Hkv), dim3(256), 0, stream, B);
+      hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3(p->n_ksplit * Hkv * 4), dim3(256), 0, stream, B);
       TA_LAUNCH_CHECK();
     }
     mark(ev, nev, 3, stream);

@@ -283,11 +283,16 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
   // dK/dV work pieces.  A workgroup of the dK/dV kernel runs every 32-row
   // query block of its tile, and the root's keys are read by every query, so
   // whole tiles leave one CU with far more than the average share.  A tile
-  // whose query range spans more than `cap` blocks is cut into equal runs of
-  // blocks (cap = max(TA_KV_PIECE_MIN, total blocks / 256): about 256 CUs'
-  // worth of pieces for any number of KV heads); the pieces of a cut tile
-  // write fp32 partial dK/dV to consecutive slots that a second pass sums in
-  // slot order.  Pieces are listed longest first.
+  // whose query range spans more than `cap` blocks is cut into runs of
+  // exactly `cap` blocks counted back from the end of its range, the
+  // remainder (1..cap blocks) at the front (cap = max(TA_KV_PIECE_MIN,
+  // total blocks / 256): about 256 CUs' worth of pieces for any number of KV
+  // heads).  Nested subtrees often end on the same row, so the e-th run from
+  // the end of different tiles covers nearly the same rows; pieces are listed
+  // longest first and, among equal lengths, window by window from the end, so
+  // the workgroups resident at one time stream the same rows through L2, as
+  // whole tiles did.  The pieces of a cut tile write fp32 partial dK/dV to
+  // consecutive slots that a second pass sums in slot order.
   {
     int64_t total = 0;
     std::vector<int32_t> tb(kts.size());
@@ -296,43 +301,43 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
       tb[i] = (kts[i].qe - qs + SUB - 1) / SUB;
       total += tb[i];
     }
-    const int64_t cap = std::max<int64_t>(TA_KV_PIECE_MIN, (total + 255) / 256);
+    const int32_t cap = static_cast<int32_t>(std::max<int64_t>(TA_KV_PIECE_MIN, (total + 255) / 256));
     struct KP {
       int32_t rec[TA_KPIECE_INTS];
-      int32_t blocks;
+      int32_t blocks, from_end;
     };
     std::vector<KP> kps;
     int32_t slots = 0;
     for (size_t i = 0; i < kts.size(); ++i) {
       const int32_t qs = std::max(kts[i].k0, Q0), nb = tb[i];
-      const int32_t np = static_cast<int32_t>((nb + cap - 1) / cap);
-      if (np > 1) {
-        p->kr.insert(p->kr.end(), {kts[i].k0, kts[i].klen, slots, np});
-      }
-      for (int32_t j = 0, b = 0; j < np; ++j) {
-        const int32_t len = nb / np + (j < nb % np ? 1 : 0);
+      const int32_t np = (nb + cap - 1) / cap;
+      if (np > 1) p->kr.insert(p->kr.end(), {kts[i].k0, kts[i].klen, slots, np});
+      for (int32_t e = 0; e < np; ++e) {  // e-th run from the end: blocks [b0, b1)
+        const int32_t b1 = nb - e * cap, b0 = std::max(0, b1 - cap);
         KP x{};
         x.rec[0] = kts[i].k0;
         x.rec[1] = kts[i].klen;
         x.rec[2] = kts[i].qe;
-        x.rec[3] = qs + SUB * b;
-        x.rec[4] = std::min(kts[i].qe, qs + SUB * (b + len));
-        x.rec[5] = np > 1 ? slots + j : -1;
+        x.rec[3] = qs + SUB * b0;
+        x.rec[4] = std::min(kts[i].qe, qs + SUB * b1);
+        x.rec[5] = np > 1 ? slots + e : -1;
         x.rec[6] = static_cast<int32_t>(i);
-        x.blocks = len;
+        x.blocks = b1 - b0;
+        x.from_end = e;
         kps.push_back(x);
-        b += len;
       }
       if (np > 1) slots += np;
     }
-    std::stable_sort(kps.begin(), kps.end(), [](const KP& x, const KP& y) { return x.blocks > y.blocks; });
+    std::stable_sort(kps.begin(), kps.end(), [](const KP& x, const KP& y) {
+      return x.blocks != y.blocks ? x.blocks > y.blocks : x.from_end < y.from_end;
+    });
     if (int64_t(kps.size()) * TA_KPIECE_INTS > kI32Max) return TA_ERANGE;
     p->kp.reserve(kps.size() * TA_KPIECE_INTS);
     for (const KP& x : kps) p->kp.insert(p->kp.end(), x.rec, x.rec + TA_KPIECE_INTS);
     p->n_kpieces = static_cast<int32_t>(kps.size());
     p->n_ksplit = static_cast<int32_t>(p->kr.size() / 4);
     p->n_kslots = slots;
-    p->kv_piece_cap = static_cast<int32_t>(cap);
+    p->kv_piece_cap = cap;
   }
 
   // device image: pos | fq_ptr | fq_chunk | fq_order | bk | kp | kr, each 256-aligned

@@ -89,9 +89,10 @@ def compare(tree):
 def check_pieces(p, v):
     """dK/dV work pieces: each tile's query rows [max(k0, q_start), q_end) are
     covered once, in order, by runs that start on its 32-row block grid; a
-    tile is cut iff it spans more than the cap's blocks, into equal runs (to
-    one block) of at most the cap; cut tiles own consecutive slots; pieces
-    are listed longest first."""
+    tile is cut iff it spans more than the cap's blocks, into runs of exactly
+    the cap counted back from q_end with the remainder at the front; the e-th
+    run from the end owns slot first + e; pieces are listed longest first,
+    equal lengths by run from the end."""
     sub = pkg.TA_KV_SUB
     kp, kr, bk = v["kp"], v["kr"], v["bk"]
     assert p.n_kpieces == len(kp) >= p.n_ktiles and p.n_ksplit == len(kr)
@@ -104,20 +105,20 @@ def check_pieces(p, v):
         assert tuple(x[:3]) == tuple(bk[x[6]][:3])
         by_tile.setdefault(int(x[6]), []).append(x)
     assert sorted(by_tile) == list(range(p.n_ktiles))
-    slots = []
-    cut = {}
+    slots, cut, from_end = [], {}, {}
     for t, ps in by_tile.items():
         k0, kl, qe = (int(z) for z in bk[t][:3])
         qs = max(k0, p.q_start)
-        ps = sorted(ps, key=lambda x: x[3])
-        assert ps[0][3] == qs and ps[-1][4] == qe
-        lens = []
+        ps = sorted(ps, key=lambda x: -x[3])          # from the end of the range
+        assert ps[-1][3] == qs and ps[0][4] == qe
         for a, b in zip(ps, ps[1:]):
-            assert a[4] == b[3]
-        for x in ps:
+            assert b[4] == a[3]
+        lens = []
+        for e, x in enumerate(ps):
             assert x[3] < x[4] and (x[3] - qs) % sub == 0
             lens.append(-(-(int(x[4]) - int(x[3])) // sub))
-        assert sum(lens) == nb[t] and max(lens) <= cap and max(lens) - min(lens) <= 1
+            from_end[(t, int(x[3]))] = e
+        assert sum(lens) == nb[t] and all(n == cap for n in lens[:-1]) and 1 <= lens[-1] <= cap
         if len(ps) == 1:
             assert nb[t] <= cap and ps[0][5] == -1
         else:
@@ -128,8 +129,8 @@ def check_pieces(p, v):
             cut[(k0, kl)] = (ss[0], len(ps))
     assert sorted(slots) == list(range(p.n_kslots))
     assert {(int(r[0]), int(r[1])): (int(r[2]), int(r[3])) for r in kr} == cut and len(cut) == len(kr)
-    blocks = [-(-(int(x[4]) - int(x[3])) // sub) for x in kp]
-    assert all(a >= b for a, b in zip(blocks, blocks[1:]))
+    key = [(-(-(-(int(x[4]) - int(x[3])) // sub)), from_end[(int(x[6]), int(x[3]))]) for x in kp]
+    assert key == sorted(key)
 
 
 def test_six_node():
