@@ -73,7 +73,7 @@ typedef enum ta_dtype { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
 #define TA_BLOCK_KV 128 /* keys per backward key tile (never crosses a node) */
 #define TA_KV_SUB 32    /* backward sub-tile: 32 keys against 32-row query blocks */
 #define TA_KV_PIECE_MIN 32 /* dK/dV pieces span at least this many 32-row query blocks */
-#define TA_KPIECE_INTS 8
+#define TA_KPIECE_INTS 20
 #define TA_CHUNK_INTS 16
 #define TA_CHUNK_MAX_SEG 4
 
@@ -119,23 +119,25 @@ typedef struct ta_plan_view {
                                 query in [max(k0, q_start), q_end) lies in the node's subtree */
   int32_t n_prefix_nodes;    /* key-only chain prefix (tree_plan_ex), 0 for tree_plan */
   int32_t q_start;           /* its tokens [0, q_start) are keys only: no query tiles, no outputs */
-  /* dK/dV work pieces (bf16 backward).  Every key tile of bk is one or more
-   * pieces; a piece runs the tile's keys against a run of its query rows.  A
-   * tile whose query range [max(k0, q_start), q_end) spans more than
-   * kv_piece_cap 32-row blocks is cut into runs of exactly kv_piece_cap
-   * blocks counted back from q_end, the remainder at the front; its pieces
-   * write fp32 partial dK/dV to n_pieces consecutive workspace slots (slot
-   * first + e for the e-th run from the end), summed in slot order by a
-   * second pass, so the result stays deterministic. */
-  int32_t n_kpieces;         /* pieces, >= n_ktiles */
-  int32_t n_ksplit;          /* tiles that were cut */
-  int32_t n_kslots;          /* partial slots: sum of n_pieces over cut tiles */
+  /* dK/dV work pieces (bf16 backward).  A piece is one workgroup: four
+   * wavefronts, each owning the dK/dV of up to 32 keys of one node (a
+   * sub-tile), over a common run of query rows [q_lo, q_hi) staged once.  A
+   * full 128-key tile of bk whose query range [max(k0, q_start), q_end) spans
+   * at most kv_piece_cap 32-row blocks is one piece; the other tiles are cut
+   * into sub-tiles, each cut at the windows of kv_piece_cap blocks anchored
+   * at q_start, and the runs of one window are packed up to four to a piece.
+   * A sub-tile cut over several windows writes fp32 partial dK/dV to one
+   * workspace slot per window (consecutive, in window order), summed in slot
+   * order by a second pass, so the result stays deterministic. */
+  int32_t n_kpieces;         /* pieces */
+  int32_t n_ksplit;          /* sub-tiles cut over several windows */
+  int32_t n_kslots;          /* partial slots: sum of n_windows over cut sub-tiles */
   int32_t kv_piece_cap;      /* max(TA_KV_PIECE_MIN, ceil(total query blocks of all tiles / 256)) */
-  const int32_t* kp;         /* [n_kpieces * TA_KPIECE_INTS] (k0, klen, q_end, q_lo, q_hi, slot,
-                                tile, 0): rows [q_lo, q_hi); slot -1 = whole tile (writes dK/dV
-                                directly); longest first, equal lengths by run
-                                from the end */
-  const int32_t* kr;         /* [n_ksplit * 4] (k0, klen, first slot, n_pieces) of each cut tile */
+  const int32_t* kp;         /* [n_kpieces * TA_KPIECE_INTS] (q_lo, q_hi, 0, 0, then per wavefront
+                                (kw, wk, row_end, slot)): wavefront w owns keys [kw, kw + wk)
+                                (wk = 0: idle) and reads rows [max(key, q_lo), row_end),
+                                row_end <= q_hi; slot -1 stores dK/dV directly; longest first */
+  const int32_t* kr;         /* [n_ksplit * 4] (kw, wk, first slot, n_windows) of each cut sub-tile */
 } ta_plan_view;
 
 /* Build the plan of a prefix tree (host only, synchronous, deterministic).

@@ -29,7 +29,7 @@ __all__ = ["TreeAttnError", "Plan", "Partition", "HipEvents", "tree_plan", "tree
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtree_attn.so")
 TA_BLOCK_M, TA_BLOCK_N, TA_BLOCK_KV, TA_KV_SUB, TA_CHUNK_INTS = 32, 64, 128, 32, 16
-TA_KPIECE_INTS, TA_KV_PIECE_MIN = 8, 32
+TA_KPIECE_INTS, TA_KV_PIECE_MIN = 20, 32
 TA_F32, TA_BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "parent pointers contain a cycle",
            3: "size exceeds the int32 index range", 4: "out of memory or buffer too small",

@@ -301,8 +301,9 @@ struct KVParams {
   bf16* dv;
   const int32_t* pos;
   const int32_t* kp;  // work pieces, TA_KPIECE_INTS each
-  const int32_t* kr;  // cut tiles: (k0, klen, first slot, n_pieces)
-  float* part;        // partial dK/dV slots of cut tiles (PART_FLOATS per slot and KV head)
+  const int32_t* kr;  // cut sub-tiles: (kw, wk, first slot, n_windows)
+  float* part;        // partial dK/dV slots (PART_WAVE floats per slot and KV head)
+  int n_sum;          // cut sub-tiles
   int N, Hq, Hkv, G;
   int q0;  // first query row (rows below are a key-only prefix)
   float scale, scale_log2, rope_base;
@@ -310,44 +311,48 @@ struct KVParams {
 
 constexpr int SUB = TA_KV_SUB;  // keys per wavefront = rows per query block
 
-// A partial slot holds one piece's raw dK and dV accumulators for one KV
-// head in register order: per wavefront w, [dK | dV] each [tile dt 4][r/4 4]
-// [lane 64][r%4 4] floats, so a wavefront writes and reads 1 KiB contiguous
-// runs (register r of tile dt of lane l <-> key 8*(r/4) + 4*(l/32) + r%4 of
-// the wavefront's 32, dimension dt*32 + l%32).
+// A partial slot holds one wavefront's raw dK and dV accumulators for one
+// KV head in register order: [dK | dV] each [tile dt 4][r/4 4][lane 64]
+// [r%4 4] floats, so the wavefront writes and reads 1 KiB contiguous runs
+// (register r of tile dt of lane l <-> key 8*(r/4) + 4*(l/32) + r%4 of its
+// 32, dimension dt*32 + l%32).
 constexpr int PART_WAVE = 2 * 4 * 16 * 64;
-constexpr int PART_FLOATS = 4 * PART_WAVE;
 
-// dK (scaled, rotated back by -pos) and dV of one wavefront's keys in bf16,
-// accumulator registers [rlo, rhi).  Register r of tile dt <-> key
-// kw + 8*(r/4) + 4*half + r%4, d = dt*32 + col; the rotate-half partner
-// d + 64 is tile dt + 2.
+// dK (scaled, rotated back by -pos) and dV of one key in bf16, dimensions
+// dt*32 + col for dt = 0..3 (the rotate-half partner of d is tile dt + 2).
+__device__ __forceinline__ void store_key(const KVParams& P, int kvh, int key, int col, float (&g)[4],
+                                          const float (&v)[4]) {
+  const size_t o = ((size_t)key * P.Hkv + kvh) * D;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) g[dt] *= P.scale;
+  if (P.rope_base > 0.f) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      float sn, cs;
+      rope_sincos(P.pos[key], dt * 32 + col, D, P.rope_base, &sn, &cs);
+      const float y1 = g[dt], y2 = g[dt + 2];
+      g[dt] = y1 * cs + y2 * sn;
+      g[dt + 2] = y2 * cs - y1 * sn;
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    P.dk[o + dt * 32 + col] = (bf16)g[dt];
+    P.dv[o + dt * 32 + col] = (bf16)v[dt];
+  }
+}
+
+// dK and dV of one wavefront's keys [kw, kw + wkeys).  Accumulator register
+// r of tile dt <-> key kw + 8*(r/4) + 4*half + r%4, d = dt*32 + col.
 __device__ __forceinline__ void store_dkv(const KVParams& P, int kvh, int kw, int wkeys, int half, int col,
-                                          const f32x16 (&dk)[4], const f32x16 (&dv)[4], int rlo = 0,
-                                          int rhi = 16) {
+                                          const f32x16 (&dk)[4], const f32x16 (&dv)[4]) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
-    if (r < rlo || r >= rhi || kr >= wkeys) continue;
-    const size_t o = ((size_t)(kw + kr) * P.Hkv + kvh) * D;
-    float g[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) g[dt] = dk[dt][r] * P.scale;
-    if (P.rope_base > 0.f) {
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        float sn, cs;
-        rope_sincos(P.pos[kw + kr], dt * 32 + col, D, P.rope_base, &sn, &cs);
-        const float y1 = g[dt], y2 = g[dt + 2];
-        g[dt] = y1 * cs + y2 * sn;
-        g[dt + 2] = y2 * cs - y1 * sn;
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      P.dk[o + dt * 32 + col] = (bf16)g[dt];
-      P.dv[o + dt * 32 + col] = (bf16)dv[dt][r];
-    }
+    if (kr >= wkeys) continue;
+    float g[4] = {dk[0][r], dk[1][r], dk[2][r], dk[3][r]};
+    const float v[4] = {dv[0][r], dv[1][r], dv[2][r], dv[3][r]};
+    store_key(P, kvh, kw + kr, col, g, v);
   }
 }
 
@@ -370,12 +375,15 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
 
   const int kvh = blockIdx.x % P.Hkv;
   const cint_ptr tl = as_const(P.kp) + (size_t)(blockIdx.x / P.Hkv) * TA_KPIECE_INTS;
-  const int k0 = tl[0], klen = tl[1], qe = tl[2];
-  const int qlo = tl[3], qhi = tl[4], slot = tl[5];  // this piece's query rows; its partial slot or -1
+  const int qlo = tl[0], qhi = tl[1];             // the piece's query rows, staged for all four
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int col = lane & 31, half = lane >> 5;
-  const int kw = k0 + SUB * wave;                 // this wavefront's first key
-  const int wkeys = max(0, min(SUB, klen - SUB * wave));
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  // this wavefront's keys [kw, kw + wkeys) (0: idle), the end of the rows it
+  // reads (<= qhi; each key reads rows [max(key, qlo), rhi)), its partial
+  // slot or -1
+  const cint_ptr tw = tl + 4 + 4 * w;
+  const int kw = tw[0], wkeys = tw[1], rhi = tw[2], slot = tw[3];
   const bool kvalid = col < wkeys;
   const int key = kw + col;
 
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   f16x8 kf[8];
   bf16x8 vf[8];
   {
-    const size_t off = ((size_t)(kvalid ? key : k0) * P.Hkv + kvh) * D + half * 8;
+    const size_t off = ((size_t)(kvalid ? key : kw) * P.Hkv + kvh) * D + half * 8;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -419,21 +427,19 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
       toff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
     }
 
-  // Items are (32-row block, query head) of the piece's rows [qlo, qhi)
-  // (blocks start at max(k0, q_start) + 32i, so a block past a wavefront's
-  // diagonal lies wholly below it), blocks from the end down and the heads of
-  // the group innermost: the workgroups resident
-  // on an XCD share a KV head and (for nested subtrees) the tail of their
-  // query ranges, so they stream the same rows at about the same time and
-  // one fetch serves them from L2.  All four wavefronts share each staged
-  // block.  Each wavefront issues exactly five copies per block: two
-  // 1 KiB copies of Q rows, two of dO rows (rows 4i..4i+3 for i = w, w + 4),
-  // and sixteen LSE or D values (wavefront w: LSE rows 16w.. for w < 2, D rows
-  // 16(w-2).. otherwise).  Rows past the query range copy the last valid row
-  // and are masked to P = 0 below, so they contribute nothing.
+  // Items are (32-row block, query head) of the piece's rows [qlo, qhi),
+  // blocks qlo + 32i from the end down and the heads of the group innermost:
+  // the workgroups resident on an XCD share a KV head and mostly the same
+  // rows (pieces are listed by length and last row), so they stream the same
+  // rows at about the same time and one fetch serves them from L2.  All four
+  // wavefronts share each staged block.  Each wavefront issues exactly five
+  // copies per block: two 1 KiB copies of Q rows, two of dO rows (rows
+  // 4i..4i+3 for i = w, w + 4), and sixteen LSE or D values (wavefront w: LSE
+  // rows 16w.. for w < 2, D rows 16(w-2).. otherwise).  Rows past qhi copy
+  // the last row and, like every row outside a wavefront's [key, rhi), are
+  // masked to P = 0 below, so they contribute nothing.
   const int nblk = (qhi - qlo + SUB - 1) / SUB;   // >= 1: the plan gives every piece a query row
   const int nitem = P.G * nblk;
-  const int w = __builtin_amdgcn_readfirstlane(wave);
   auto stage = [&](int it, char* base) {
     const int h = kvh * P.G + it % P.G;
     const int qb = qlo + SUB * (nblk - 1 - it / P.G);
@@ -441,12 +447,12 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     for (int k = 0; k < 2; ++k) {
       const int i = w + 4 * k;
       const int row = 4 * i + (lane >> 4);
-      const size_t off = ((size_t)min(qb + row, qe - 1) * P.Hq + h) * D + (((lane & 15) ^ swz(row & 15)) << 3);
+      const size_t off = ((size_t)min(qb + row, qhi - 1) * P.Hq + h) * D + (((lane & 15) ^ swz(row & 15)) << 3);
       copy16_to_lds(P.q + off, base + L::Q16 + 4 * i * D * 2);
       copy16_to_lds(P.dO + off, base + L::DO + 4 * i * D * 2);
     }
     if (lane < 16) {
-      const int r = min(qb + 16 * (w & 1) + lane, qe - 1);
+      const int r = min(qb + 16 * (w & 1) + lane, qhi - 1);
       copy4_to_lds((w < 2 ? P.nl2 : P.nd) + (size_t)h * P.N + r, base + L::LS + 64 * w);
     }
   };
@@ -502,12 +508,13 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = exp2f_fast(S[r]);
     // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col.
-    // Only the diagonal-or-earlier block and the range's last block need the
-    // element mask key <= row < qe, one unsigned compare: (row - key) <
-    // (qe - key).
-    if (qb <= kw || qb + SUB > qe) {
+    // Only blocks that start before the wavefront's last key or end past its
+    // rows need the element mask key <= row < rhi, one unsigned compare:
+    // (row - key) < (rhi - key), with no rows at all for a key >= rhi (a
+    // window may end inside the wavefront's keys).
+    if (qb < kw + SUB || qb + SUB > rhi) {
       const int d0 = qb + 4 * half - key;
-      const unsigned lim = (unsigned)(qe - key);
+      const unsigned lim = (unsigned)max(rhi - key, 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if ((unsigned)(d0 + 8 * (r >> 2) + (r & 3)) >= lim) p[r] = 0.f;
@@ -572,7 +579,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   if (slot < 0) {
     store_dkv(P, kvh, kw, wkeys, half, col, dk, dv);
   } else if (wkeys > 0) {
-    float* dst = P.part + ((size_t)slot * P.Hkv + kvh) * PART_FLOATS + wave * PART_WAVE + lane * 4;
+    float* dst = P.part + ((size_t)slot * P.Hkv + kvh) * PART_WAVE + lane * 4;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -585,26 +592,26 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   }
 }
 
-// Sums the partial slots of each cut tile in slot order (deterministic) and
-// stores dK / dV as the whole-tile epilogue does.  One workgroup per (cut
-// tile, KV head, register group g), one wavefront per 32 keys; group g holds
-// accumulator registers 4g..4g+3 of every tile (keys 8g + 4*half + 0..3).
+// Sums the partial slots of each cut sub-tile in slot order (deterministic)
+// and stores its dK / dV as the whole-piece epilogue does.  One wavefront per
+// cut sub-tile, four per workgroup, and one workgroup per (four sub-tiles, KV
+// head, register group g); group g holds accumulator registers 4g..4g+3 of
+// every tile (keys 8g + 4*half + 0..3).
 __global__ __launch_bounds__(256) void dkv_sum_kernel(KVParams P) {
   const int g = blockIdx.x & 3, rest = blockIdx.x >> 2;
   const int kvh = rest % P.Hkv;
-  const int32_t* tl = P.kr + (size_t)(rest / P.Hkv) * 4;
-  const int k0 = tl[0], klen = tl[1], slot0 = tl[2], np = tl[3];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kw = k0 + SUB * wave, wkeys = min(SUB, klen - SUB * wave);
-  if (wkeys <= 0) return;
+  const int i = (rest / P.Hkv) * 4 + (threadIdx.x >> 6);
+  if (i >= P.n_sum) return;
+  const int32_t* tl = P.kr + (size_t)i * 4;
+  const int kw = tl[0], wkeys = tl[1], slot0 = tl[2], np = tl[3];
+  const int lane = threadIdx.x & 63;
   float sk[4][4], sv[4][4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) sk[dt][j] = sv[dt][j] = 0.f;
   for (int s = 0; s < np; ++s) {
-    const float* src = P.part + ((size_t)(slot0 + s) * P.Hkv + kvh) * PART_FLOATS + wave * PART_WAVE + g * 256 +
-                       lane * 4;
+    const float* src = P.part + ((size_t)(slot0 + s) * P.Hkv + kvh) * PART_WAVE + g * 256 + lane * 4;
     float4 a[4], b[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -623,24 +630,15 @@ __global__ __launch_bounds__(256) void dkv_sum_kernel(KVParams P) {
       sv[dt][3] += b[dt].w;
     }
   }
-  f32x16 dk[4], dv[4];
+  // register 4g + j of tile dt <-> key kw + 8g + 4*half + j
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
+  for (int j = 0; j < 4; ++j) {
+    const int kr = 8 * g + 4 * (lane >> 5) + j;
+    if (kr >= wkeys) continue;
+    float gk[4] = {sk[0][j], sk[1][j], sk[2][j], sk[3][j]};
+    const float gv[4] = {sv[0][j], sv[1][j], sv[2][j], sv[3][j]};
+    store_key(P, kvh, kw + kr, lane & 31, gk, gv);
   }
-#pragma unroll
-  for (int gg = 0; gg < 4; ++gg)
-    if (gg == g) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dk[dt][4 * gg + j] = sk[dt][j];
-          dv[dt][4 * gg + j] = sv[dt][j];
-        }
-    }
-  store_dkv(P, kvh, kw, wkeys, lane >> 5, lane & 31, dk, dv, 4 * g, 4 * g + 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,7 +731,7 @@ size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t
     b += align256(N * Hq * sizeof(float));                                             // LSE * log2(e)
     b += align256(N * Hq * d * sizeof(f16)) + align256(N * Hkv * d * sizeof(f16));  // fp16 Q, K
     if (rope_base > 0.f) b += align256(N * Hkv * d * sizeof(bf16));                 // rotated bf16 K
-    b += align256((size_t)p->n_kslots * Hkv * bwd::PART_FLOATS * sizeof(float));     // dK/dV partials
+    b += align256((size_t)p->n_kslots * Hkv * bwd::PART_WAVE * sizeof(float));       // dK/dV partials
   } else if (rope_base > 0.f) {
     b += align256(N * Hq * d * sizeof(float)) + align256(N * Hkv * d * sizeof(float));
   }
@@ -833,6 +831,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.kp = kp;
     B.kr = kr;
     B.part = part;
+    B.n_sum = p->n_ksplit;
     B.N = N;
     B.Hq = Hq;
     B.Hkv = Hkv;
@@ -844,7 +843,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     hipLaunchKernelGGL(bwd::dkv_bf16_kernel, dim3(p->n_kpieces * Hkv), dim3(256), 0, stream, B);
     TA_LAUNCH_CHECK();
     if (p->n_ksplit > 0) {
-      hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3(p->n_ksplit * Hkv * 4), dim3(256), 0, stream, B);
+      hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3((p->n_ksplit + 3) / 4 * Hkv * 4), dim3(256), 0, stream, B);
       TA_LAUNCH_CHECK();
     }
     mark(ev, nev, 3, stream);

@@ -280,56 +280,119 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
   }
   p->computed_pairs_bwd = comp_bwd;
 
-  // dK/dV work pieces.  A workgroup of the dK/dV kernel runs every 32-row
-  // query block of its tile, and the root's keys are read by every query, so
-  // whole tiles leave one CU with far more than the average share.  A tile
-  // whose query range spans more than `cap` blocks is cut into runs of
-  // exactly `cap` blocks counted back from the end of its range, the
-  // remainder (1..cap blocks) at the front (cap = max(TA_KV_PIECE_MIN,
-  // total blocks / 256): about 256 CUs' worth of pieces for any number of KV
-  // heads).  Nested subtrees often end on the same row, so the e-th run from
-  // the end of different tiles covers nearly the same rows; pieces are listed
-  // longest first and, among equal lengths, window by window from the end, so
-  // the workgroups resident at one time stream the same rows through L2, as
-  // whole tiles did.  The pieces of a cut tile write fp32 partial dK/dV to
-  // consecutive slots that a second pass sums in slot order.
+  // dK/dV work pieces.  A dK/dV workgroup has four wavefronts, each owning
+  // the dK/dV of up to 32 keys (a sub-tile) over a common run of 32-row query
+  // blocks [q_lo, q_hi) staged once in LDS.  Two things make whole tiles a
+  // poor unit: the root's keys are read by every query, so one workgroup can
+  // carry far more than an average CU's share, and a node shorter than 128
+  // keys leaves wavefronts idle (the 96-token history nodes of a navigation
+  // episode: a quarter of the work).  So a full 128-key tile whose range spans
+  // at most `cap` blocks stays one piece; every other tile is split into its
+  // 32-key sub-tiles, each cut at the windows of a grid of `cap` blocks
+  // anchored at q_start, and the sub-tile runs of one window are packed four
+  // to a piece when their row spans nest (a run joins only if the piece's span
+  // grows by at most one block over its longest run).  A sub-tile cut over
+  // several windows writes fp32 partial dK/dV to one slot per window
+  // (consecutive, in window order) that a second pass sums in slot order; one
+  // run in one window stores directly.  cap = max(TA_KV_PIECE_MIN,
+  // ceil(total blocks / 256)): about 256 CUs' worth for any number of KV
+  // heads.  Pieces are listed longest first, then by their last row (the
+  // workgroups resident at one time stream the same rows through L2).
   {
     int64_t total = 0;
     std::vector<int32_t> tb(kts.size());
     for (size_t i = 0; i < kts.size(); ++i) {
-      const int32_t qs = std::max(kts[i].k0, Q0);
-      tb[i] = (kts[i].qe - qs + SUB - 1) / SUB;
+      tb[i] = (kts[i].qe - std::max(kts[i].k0, Q0) + SUB - 1) / SUB;
       total += tb[i];
     }
     const int32_t cap = static_cast<int32_t>(std::max<int64_t>(TA_KV_PIECE_MIN, (total + 255) / 256));
+    const int64_t W = int64_t(SUB) * cap;  // rows per window
+    struct Run {
+      int32_t lo, hi, kw, wk, slot, seq;  // rows [lo, hi) of sub-tile kw.. (wk keys)
+    };
     struct KP {
       int32_t rec[TA_KPIECE_INTS];
-      int32_t blocks, from_end;
+      int32_t blocks, seq;
     };
     std::vector<KP> kps;
-    int32_t slots = 0;
+    std::vector<std::vector<Run>> win;  // runs by window
+    int32_t slots = 0, seq = 0;
     for (size_t i = 0; i < kts.size(); ++i) {
-      const int32_t qs = std::max(kts[i].k0, Q0), nb = tb[i];
-      const int32_t np = (nb + cap - 1) / cap;
-      if (np > 1) p->kr.insert(p->kr.end(), {kts[i].k0, kts[i].klen, slots, np});
-      for (int32_t e = 0; e < np; ++e) {  // e-th run from the end: blocks [b0, b1)
-        const int32_t b1 = nb - e * cap, b0 = std::max(0, b1 - cap);
+      const int32_t k0 = kts[i].k0, kl = kts[i].klen, qe = kts[i].qe, qs = std::max(k0, Q0);
+      if (kl == BK && tb[i] <= cap) {
         KP x{};
-        x.rec[0] = kts[i].k0;
-        x.rec[1] = kts[i].klen;
-        x.rec[2] = kts[i].qe;
-        x.rec[3] = qs + SUB * b0;
-        x.rec[4] = std::min(kts[i].qe, qs + SUB * b1);
-        x.rec[5] = np > 1 ? slots + e : -1;
-        x.rec[6] = static_cast<int32_t>(i);
-        x.blocks = b1 - b0;
-        x.from_end = e;
+        x.rec[0] = qs;
+        x.rec[1] = qe;
+        for (int w = 0; w < 4; ++w) {
+          int32_t* t = x.rec + 4 + 4 * w;
+          t[0] = k0 + SUB * w;
+          t[1] = SUB;
+          t[2] = qe;
+          t[3] = -1;
+        }
+        x.blocks = tb[i];
+        x.seq = seq++;
         kps.push_back(x);
+        continue;
       }
-      if (np > 1) slots += np;
+      for (int32_t kw = k0; kw < k0 + kl; kw += SUB) {
+        const int32_t wk = std::min(SUB, k0 + kl - kw), lo = std::max(kw, Q0);
+        const int64_t m0 = (lo - Q0) / W, m1 = (qe - 1 - Q0) / W;
+        const int32_t nw = static_cast<int32_t>(m1 - m0 + 1);
+        if (nw > 1) p->kr.insert(p->kr.end(), {kw, wk, slots, nw});
+        for (int64_t m = m0; m <= m1; ++m) {
+          if (win.size() <= size_t(m)) win.resize(m + 1);
+          const int32_t a = static_cast<int32_t>(std::max<int64_t>(lo, Q0 + m * W));
+          const int32_t b = static_cast<int32_t>(std::min<int64_t>(qe, Q0 + (m + 1) * W));
+          win[m].push_back({a, b, kw, wk, nw > 1 ? slots + static_cast<int32_t>(m - m0) : -1, seq++});
+        }
+        if (nw > 1) slots += nw;
+      }
+    }
+    for (std::vector<Run>& rs : win) {
+      std::stable_sort(rs.begin(), rs.end(),
+                       [](const Run& x, const Run& y) { return x.lo != y.lo ? x.lo < y.lo : x.hi < y.hi; });
+      size_t j = 0;
+      while (j < rs.size()) {
+        int32_t lo = rs[j].lo, hi = rs[j].hi, longest = hi - lo;
+        size_t e = j + 1;
+        while (e < rs.size() && e - j < 4) {
+          const int32_t l2 = std::min(lo, rs[e].lo), h2 = std::max(hi, rs[e].hi);
+          const int32_t m2 = std::max(longest, rs[e].hi - rs[e].lo);
+          if (h2 - l2 > m2 + SUB) break;
+          lo = l2;
+          hi = h2;
+          longest = m2;
+          ++e;
+        }
+        KP x{};
+        x.rec[0] = lo;
+        x.rec[1] = hi;
+        for (int w = 0; w < 4; ++w) {
+          int32_t* t = x.rec + 4 + 4 * w;
+          if (j + w < e) {
+            const Run& r = rs[j + w];
+            t[0] = r.kw;
+            t[1] = r.wk;
+            t[2] = r.hi;
+            t[3] = r.slot;
+          } else {  // idle wavefront: no keys (its loads read key 0, nothing is stored)
+            t[0] = 0;
+            t[1] = 0;
+            t[2] = lo;
+            t[3] = -1;
+          }
+        }
+        x.blocks = (hi - lo + SUB - 1) / SUB;
+        x.seq = rs[j].seq;
+        kps.push_back(x);
+        j = e;
+      }
     }
     std::stable_sort(kps.begin(), kps.end(), [](const KP& x, const KP& y) {
-      return x.blocks != y.blocks ? x.blocks > y.blocks : x.from_end < y.from_end;
+      if (x.blocks != y.blocks) return x.blocks > y.blocks;
+      if (x.rec[1] != y.rec[1]) return x.rec[1] > y.rec[1];
+      return x.seq < y.seq;
     });
     if (int64_t(kps.size()) * TA_KPIECE_INTS > kI32Max) return TA_ERANGE;
     p->kp.reserve(kps.size() * TA_KPIECE_INTS);

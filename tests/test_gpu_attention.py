@@ -84,14 +84,16 @@ def test_bf16_small_trees(heads):
 
 
 def test_bf16_cut_key_tiles():
-    """Key tiles whose query rows are cut into pieces whose partial dK/dV a
-    second pass sums: a ragged 100-key root and three 300-key-node tiles over
-    2,000 rows (cap 32 blocks), all KV heads, with and without RoPE, bitwise
-    repeatable; then the root as a key-only prefix (pieces from q_start)."""
+    """dK/dV work cut into 32-key sub-tiles over 1,024-row windows (cap 32
+    blocks) and packed four to a workgroup, with partial dK/dV summed by a
+    second pass: a ragged 100-key root and node 1's tiles over 2,000 rows
+    cross a window, node 2's full tiles stay whole; all KV heads, with and
+    without RoPE, bitwise repeatable; then the root as a key-only prefix
+    (windows from q_start)."""
     tree = W.Tree(np.array([-1, 0, 1, 1], np.int32), np.array([100, 300, 900, 700], np.int32), "cut")
     for i, (Hq, Hkv) in enumerate(((8, 2), (4, 4))):
         plan, res, _ = run_case(tree, Hq, Hkv, 128, torch.bfloat16, 10000.0 if i == 0 else 0.0, seed=11 + i)
-        assert plan.n_ksplit == 4
+        assert plan.n_ksplit >= 4 and plan.n_kslots >= 8
     q, k, v, do = W.attention_inputs(12, tree.n_tokens, 8, 2, 128)
     Q, K, V, DO = (torch.from_numpy(x).to(DEV).bfloat16() for x in (q, k, v, do))
     o, l = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=10000.0)

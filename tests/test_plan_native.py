@@ -87,49 +87,75 @@ def compare(tree):
 
 
 def check_pieces(p, v):
-    """dK/dV work pieces: each tile's query rows [max(k0, q_start), q_end) are
-    covered once, in order, by runs that start on its 32-row block grid; a
-    tile is cut iff it spans more than the cap's blocks, into runs of exactly
-    the cap counted back from q_end with the remainder at the front; the e-th
-    run from the end owns slot first + e; pieces are listed longest first,
-    equal lengths by run from the end."""
-    sub = pkg.TA_KV_SUB
+    """dK/dV work pieces (four wavefronts over common rows [q_lo, q_hi), each
+    owning a 32-key sub-tile and reading rows [max(key, q_lo), row_end)):
+    every sub-tile's rows [max(kw, q_start), q_end) are covered exactly once;
+    a full 128-key tile spanning at most the cap's blocks is one piece with its
+    four sub-tiles; every other run lies in one window of the cap's blocks
+    anchored at q_start, and runs are packed only when the piece's span is at
+    most one block longer than its longest run; a sub-tile over several
+    windows owns consecutive slots in window order and a sum record; pieces
+    are listed longest first, then by last row."""
+    sub, BK = pkg.TA_KV_SUB, pkg.TA_BLOCK_KV
     kp, kr, bk = v["kp"], v["kr"], v["bk"]
-    assert p.n_kpieces == len(kp) >= p.n_ktiles and p.n_ksplit == len(kr)
-    nb = [-(-(int(t[2]) - max(int(t[0]), p.q_start)) // sub) for t in bk]
+    q0 = p.q_start
+    assert p.n_kpieces == len(kp) and p.n_ksplit == len(kr) and kp.shape[1] == 20
+    nb = [-(-(int(t[2]) - max(int(t[0]), q0)) // sub) for t in bk]
     cap = max(pkg.TA_KV_PIECE_MIN, -(-sum(nb) // 256))
     assert p.kv_piece_cap == cap
-    by_tile = {}
+    W = sub * cap
+    whole = {int(t[0]): (int(t[2]), n) for t, n in zip(bk, nb) if t[1] == BK and n <= cap}
+    runs = {}          # kw -> list of (row_lo, row_hi, slot, wk)
     for x in kp:
-        assert x[7] == 0 and 0 <= x[6] < p.n_ktiles
-        assert tuple(x[:3]) == tuple(bk[x[6]][:3])
-        by_tile.setdefault(int(x[6]), []).append(x)
-    assert sorted(by_tile) == list(range(p.n_ktiles))
-    slots, cut, from_end = [], {}, {}
-    for t, ps in by_tile.items():
-        k0, kl, qe = (int(z) for z in bk[t][:3])
-        qs = max(k0, p.q_start)
-        ps = sorted(ps, key=lambda x: -x[3])          # from the end of the range
-        assert ps[-1][3] == qs and ps[0][4] == qe
-        for a, b in zip(ps, ps[1:]):
-            assert b[4] == a[3]
-        lens = []
-        for e, x in enumerate(ps):
-            assert x[3] < x[4] and (x[3] - qs) % sub == 0
-            lens.append(-(-(int(x[4]) - int(x[3])) // sub))
-            from_end[(t, int(x[3]))] = e
-        assert sum(lens) == nb[t] and all(n == cap for n in lens[:-1]) and 1 <= lens[-1] <= cap
-        if len(ps) == 1:
-            assert nb[t] <= cap and ps[0][5] == -1
+        qlo, qhi = int(x[0]), int(x[1])
+        assert x[2] == 0 and x[3] == 0 and q0 <= qlo < qhi <= p.n_tokens
+        waves = [tuple(int(z) for z in x[4 + 4 * w:8 + 4 * w]) for w in range(4)]
+        act = [t for t in waves if t[1] > 0]
+        assert act, "a piece with no keys"
+        if act[0][0] in whole and len(act) == 4 and act[0][3] == -1 and act[0][0] + 3 * sub == act[3][0]:
+            qe, n = whole.pop(act[0][0])
+            assert (qlo, qhi) == (max(act[0][0], q0), qe)
+            assert all(t == (act[0][0] + sub * w, sub, qe, -1) for w, t in enumerate(act))
+            for t in act:
+                runs.setdefault(t[0], []).append((max(t[0], qlo), qe, -1, sub))
+            continue
+        longest = 0
+        for kw, wk, rhi, slot in act:
+            assert 1 <= wk <= sub and rhi <= qhi
+            lo = max(kw, qlo)
+            assert lo < rhi
+            win = (rhi - 1 - q0) // W
+            a = max(kw, q0, q0 + win * W)
+            assert (a - q0) // W == win and a >= qlo
+            longest = max(longest, rhi - a)
+            runs.setdefault(kw, []).append((a, rhi, slot, wk))
+        assert qhi - qlo <= longest + sub
+        for kw, wk, rhi, slot in waves:
+            if wk == 0:
+                assert slot == -1
+    assert not whole, "a whole tile was not one piece"
+    node_of, sub_end = v["node_of"], v["sub_end"]
+    starts, seg = v["node_start"], None
+    slots, cut = [], {}
+    for kw, rs in runs.items():
+        qe = int(sub_end[kw])
+        rs.sort()
+        assert rs[0][0] == max(kw, q0) and rs[-1][1] == qe, kw
+        for (a0, b0, _, _), (a1, b1, _, _) in zip(rs, rs[1:]):
+            assert b0 == a1
+        assert len({r[3] for r in rs}) == 1 and all(node_of[kw + i] == node_of[kw] for i in range(rs[0][3]))
+        if len(rs) == 1:
+            assert rs[0][2] == -1
         else:
-            assert len(ps) == -(-nb[t] // cap)
-            ss = [int(x[5]) for x in ps]
-            assert ss == list(range(ss[0], ss[0] + len(ps)))
+            ss = [r[2] for r in rs]
+            assert ss == list(range(ss[0], ss[0] + len(rs)))
             slots += ss
-            cut[(k0, kl)] = (ss[0], len(ps))
+            cut[kw] = (rs[0][3], ss[0], len(rs))
     assert sorted(slots) == list(range(p.n_kslots))
-    assert {(int(r[0]), int(r[1])): (int(r[2]), int(r[3])) for r in kr} == cut and len(cut) == len(kr)
-    key = [(-(-(-(int(x[4]) - int(x[3])) // sub)), from_end[(int(x[6]), int(x[3]))]) for x in kp]
+    assert {int(r[0]): (int(r[1]), int(r[2]), int(r[3])) for r in kr} == cut and len(cut) == len(kr)
+    # every key of every node belongs to exactly one sub-tile
+    assert sum(r[0][3] for r in runs.values()) == p.n_tokens
+    key = [(-(-(-(int(x[1]) - int(x[0])) // sub)), -int(x[1])) for x in kp]
     assert key == sorted(key)
 
 
@@ -172,19 +198,21 @@ def test_node_lengths_around_tile_edges():
 
 def test_cut_key_tiles():
     """A 100-token root over a 300-token node with 900- and 700-token
-    children (2,000 rows): the tiles span 423 query blocks in all, so the cap
-    is 32; the root's tile (63 blocks) and node 1's three tiles (60, 56, 52)
-    are cut in two, the rest stay whole.  With the root as a key-only prefix
-    the pieces start at q_start."""
+    children (2,000 rows): the tiles span 423 query blocks, so the cap is 32
+    (windows of 1,024 rows); node 1's two full tiles (60 and 56 blocks) and
+    its 44-key tile, and the 100-key root, are cut into 32-key sub-tiles;
+    node 2's full tiles of at most 32 blocks stay whole.  With the root as a
+    key-only prefix the windows start at q_start."""
     tree = W.Tree(np.array([-1, 0, 1, 1], np.int32), np.array([100, 300, 900, 700], np.int32))
     p, _ = compare(tree)
     v = p.view()
-    assert p.kv_piece_cap == 32 and p.n_ksplit == 4 and p.n_kslots == 8
-    root = sorted(-(-(int(x[4]) - int(x[3])) // 32) for x in v["kp"] if x[0] == 0)
-    assert root == [31, 32]
+    assert p.kv_piece_cap == 32 and p.n_ksplit > 0
+    # the root's four sub-tiles (32, 32, 32, 4 keys) span rows [kw, 2000): two windows each
+    root = {int(r[0]): (int(r[1]), int(r[3])) for r in v["kr"] if r[0] < 100}
+    assert root == {0: (32, 2), 32: (32, 2), 64: (32, 2), 96: (4, 2)}
     pe = pkg.tree_plan(tree.parent, tree.seg_len, n_prefix_nodes=1)
     check_pieces(pe, pe.view())
-    assert pe.q_start == 100 and all(x[3] >= 100 for x in pe.view()["kp"])
+    assert pe.q_start == 100 and all(x[0] >= 100 for x in pe.view()["kp"])
 
 
 def test_star_with_64_children_and_deep_chain():
