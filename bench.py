@@ -90,9 +90,11 @@ def time_tree(pkg, tree, steps, warmup, dev, seed=0, Hq=32, Hkv=8, d=128, rope=1
         plan_ms=round(plan_ms, 3), upload_ms=round(upload_ms, 3),
         ms_per_step=avg(0, 6), wall_ms_per_step=wall,
         fwd_ms=avg(0, 2), bwd_ms=avg(3, 6),
-        k_fwd_prep_ms=avg(0, 1), k_fwd_ms=avg(1, 2), k_bwd_prep_ms=avg(3, 4), k_dq_ms=avg(4, 5), k_dkv_ms=avg(5, 6),
+        # backward events: [0] start, [1] after the preparation passes, [2] after dK/dV (and its
+        # partial sum), [3] after dQ, which reads the dS blocks dK/dV stored (one product)
+        k_fwd_prep_ms=avg(0, 1), k_fwd_ms=avg(1, 2), k_bwd_prep_ms=avg(3, 4), k_dkv_ms=avg(4, 5), k_dq_ms=avg(5, 6),
         flops_fwd=4 * flop_pair * P, flops_bwd=10 * flop_pair * P,
-        flops_alg=dict(fwd=4 * flop_pair * P, dq=6 * flop_pair * P, dkv=8 * flop_pair * P))
+        flops_alg=dict(fwd=4 * flop_pair * P, dq=2 * flop_pair * P, dkv=8 * flop_pair * P))
     res["tflops"] = (res["flops_fwd"] + res["flops_bwd"]) / (res["ms_per_step"] * 1e-3) / 1e12
     del q, k, v, do, o, dq, dk, dv, wf, wb
     torch.cuda.empty_cache()
@@ -374,7 +376,7 @@ def main():
 
     kernels = {"fwd": head["k_fwd_ms"], "dq": head["k_dq_ms"], "dkv": head["k_dkv_ms"]}
     dom = max(kernels, key=kernels.get)
-    names = {"fwd": "fwd_bf16_kernel", "dq": "dq_bf16_kernel", "dkv": "dkv_bf16_kernel"}
+    names = {"fwd": "fwd_bf16_kernel", "dq": "dq_ds_kernel", "dkv": "dkv_bf16_kernel"}
     achieved = head["flops_alg"][dom] / (kernels[dom] * 1e-3) / 1e12
     roofline = dict(bound="mfma", kernel=names[dom], achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=load_traffic(names[dom]),

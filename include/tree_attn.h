@@ -73,7 +73,8 @@ typedef enum ta_dtype { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
 #define TA_BLOCK_KV 128 /* keys per backward key tile (never crosses a node) */
 #define TA_KV_SUB 32    /* backward sub-tile: 32 keys against 32-row query blocks */
 #define TA_KV_PIECE_MIN 32 /* dK/dV pieces span at least this many 32-row query blocks */
-#define TA_KPIECE_INTS 20
+#define TA_KPIECE_INTS 32 /* (q_lo, q_hi, 0, 0) + 4 x TA_KWAVE_INTS */
+#define TA_KWAVE_INTS 7
 #define TA_CHUNK_INTS 16
 #define TA_CHUNK_MAX_SEG 4
 
@@ -121,11 +122,12 @@ typedef struct ta_plan_view {
   int32_t q_start;           /* its tokens [0, q_start) are keys only: no query tiles, no outputs */
   /* dK/dV work pieces (bf16 backward).  A piece is one workgroup: four
    * wavefronts, each owning the dK/dV of up to 32 keys of one node (a
-   * sub-tile), over a common run of query rows [q_lo, q_hi) staged once.  A
-   * full 128-key tile of bk whose query range [max(k0, q_start), q_end) spans
-   * at most kv_piece_cap 32-row blocks is one piece; the other tiles are cut
-   * into sub-tiles, each cut at the windows of kv_piece_cap blocks anchored
-   * at q_start, and the runs of one window are packed up to four to a piece.
+   * sub-tile), over a common run of query rows [q_lo, q_hi) staged once;
+   * q_lo lies on the query-tile grid q_start + 32t.  A full 128-key tile of
+   * bk whose query range [max(k0, q_start), q_end) spans at most
+   * kv_piece_cap 32-row blocks is one piece; the other tiles are cut into
+   * sub-tiles, each cut at the windows of kv_piece_cap blocks anchored at
+   * q_start, and the runs of one window are packed up to four to a piece.
    * A sub-tile cut over several windows writes fp32 partial dK/dV to one
    * workspace slot per window (consecutive, in window order), summed in slot
    * order by a second pass, so the result stays deterministic. */
@@ -134,10 +136,17 @@ typedef struct ta_plan_view {
   int32_t n_kslots;          /* partial slots: sum of n_windows over cut sub-tiles */
   int32_t kv_piece_cap;      /* max(TA_KV_PIECE_MIN, ceil(total query blocks of all tiles / 256)) */
   const int32_t* kp;         /* [n_kpieces * TA_KPIECE_INTS] (q_lo, q_hi, 0, 0, then per wavefront
-                                (kw, wk, row_end, slot)): wavefront w owns keys [kw, kw + wk)
-                                (wk = 0: idle) and reads rows [max(key, q_lo), row_end),
-                                row_end <= q_hi; slot -1 stores dK/dV directly; longest first */
+                                (kw, wk, r_lo, r_hi, slot, ds_off, 0)): wavefront w owns keys
+                                [kw, kw + wk) (wk = 0: idle) and reads rows [max(key, r_lo), r_hi),
+                                q_lo <= r_lo, r_hi <= q_hi; slot -1 stores dK/dV directly; its dS
+                                block of query tile t is ds_off + t; longest first */
   const int32_t* kr;         /* [n_ksplit * 4] (kw, wk, first slot, n_windows) of each cut sub-tile */
+  /* dS blocks: one per (query tile t, sub-tile) such that a row of t reads
+   * the sub-tile, numbered sub-tile by sub-tile; dq lists them per tile. */
+  int64_t n_dsblk;           /* dS blocks per query head */
+  const int32_t* dq_ptr;     /* [n_qtiles + 1] entry range of each query tile */
+  const int32_t* dq_ent;     /* [dq_ptr[n_qtiles] * 4] (kw, wk, dS block, 0), by first key */
+  const int32_t* dq_order;   /* [n_qtiles] query tiles, most entries first */
 } ta_plan_view;
 
 /* Build the plan of a prefix tree (host only, synchronous, deterministic).
@@ -181,8 +190,11 @@ ta_status tree_plan_upload(const ta_plan* plan, void* dplan, size_t bytes, hipSt
 /* NULL-safe. */
 void tree_plan_free(ta_plan* plan);
 
-/* Workspace bytes of tree_attn_fwd (op = 0) or tree_attn_bwd (op = 1) for
- * this plan and shape; 0 when none is needed. */
+/* Workspace bytes of tree_attn_fwd (op = 0) or tree_attn_bwd (op = 1: the
+ * full backward; op = 2: the smallest backward workspace) for this plan and
+ * shape; 0 when none is needed.  For TA_BF16, op 1 includes the dS blocks
+ * (2 * n_dsblk * 1024 bytes per query head) that let dQ read dS instead of
+ * recomputing S and dP; with op 2's size dQ recomputes them. */
 ta_status tree_attn_ws_bytes(const ta_plan* plan, int32_t op, ta_dtype dt, int32_t Hq, int32_t Hkv,
                              int32_t d, float rope_base, size_t* bytes);
 
@@ -210,7 +222,11 @@ ta_status tree_attn_fwd(const ta_plan* plan, const void* dplan, ta_dtype dt, con
  * is the sum over every descendant query that reads it (section 7: shared
  * prefixes receive the gradients of all branches).  Deterministic: the same
  * inputs give bitwise-identical outputs (no atomics).
- * ws: tree_attn_ws_bytes(op = 1) bytes.  Errors as tree_attn_fwd. */
+ * ws: tree_attn_ws_bytes(op = 1) bytes, or at least op = 2 bytes.  TA_BF16
+ * with the op-1 size: the dK/dV kernel stores the fp16 dS of every (query
+ * tile, 32-key sub-tile) block and dQ = scale * dS K reads it back (one
+ * product); with less: dQ recomputes S and dP (three products) before dK/dV.
+ * Errors as tree_attn_fwd (TA_ENOMEM below the op-2 size). */
 ta_status tree_attn_bwd(const ta_plan* plan, const void* dplan, ta_dtype dt, const void* q,
                         const void* k, const void* v, const void* o, const float* lse,
                         const void* dO, int32_t Hq, int32_t Hkv, int32_t d, float scale,
@@ -224,8 +240,11 @@ ta_status tree_attn_bwd(const ta_plan* plan, const void* dplan, ta_dtype dt, con
  * kernel with hipEventElapsedTime.
  *   tree_attn_fwd_ex:       [0] start, [1] after the K conversion/RoPE pass,
  *                           [2] after the attention kernel.
- *   tree_attn_bwd_ex:       [0] start, [1] after the K passes, [2] after the
- *                           dQ kernel, [3] after the dK/dV kernel.
+ *   tree_attn_bwd_ex:       [0] start, [1] after the preparation passes;
+ *                           bf16 with the dS workspace: [2] after the dK/dV
+ *                           kernel and its partial sum, [3] after the dQ
+ *                           kernel; otherwise [2] after the dQ kernel, [3]
+ *                           after dK/dV.
  *   tree_decode_splitkv_ex: [0] start, [1] after the partial kernel,
  *                           [2] after the merge kernel. */
 typedef struct ihipEvent_t* hipEvent_t;

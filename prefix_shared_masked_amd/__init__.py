@@ -29,7 +29,7 @@ __all__ = ["TreeAttnError", "Plan", "Partition", "HipEvents", "tree_plan", "tree
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtree_attn.so")
 TA_BLOCK_M, TA_BLOCK_N, TA_BLOCK_KV, TA_KV_SUB, TA_CHUNK_INTS = 32, 64, 128, 32, 16
-TA_KPIECE_INTS, TA_KV_PIECE_MIN = 20, 32
+TA_KPIECE_INTS, TA_KWAVE_INTS, TA_KV_PIECE_MIN = 32, 7, 32
 TA_F32, TA_BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "parent pointers contain a cycle",
            3: "size exceeds the int32 index range", 4: "out of memory or buffer too small",
@@ -52,7 +52,9 @@ class _View(ctypes.Structure):
             "fq_ptr", "fq_chunk", "fq_order", "bk")] + \
         [(n, ctypes.c_int32) for n in ("n_prefix_nodes", "q_start", "n_kpieces", "n_ksplit", "n_kslots",
                                         "kv_piece_cap")] + \
-        [(n, ctypes.POINTER(ctypes.c_int32)) for n in ("kp", "kr")]
+        [(n, ctypes.POINTER(ctypes.c_int32)) for n in ("kp", "kr")] + \
+        [("n_dsblk", ctypes.c_int64)] + \
+        [(n, ctypes.POINTER(ctypes.c_int32)) for n in ("dq_ptr", "dq_ent", "dq_order")]
 
 
 class _PartView(ctypes.Structure):
@@ -184,7 +186,7 @@ class Plan:
         for name in ("n_nodes", "n_tokens", "n_leaves", "max_pos", "block_m", "block_n", "block_kv",
                      "n_qtiles", "n_chunks", "n_ktiles", "n_flat", "visible_pairs",
                      "computed_pairs_fwd", "computed_pairs_bwd", "n_prefix_nodes", "q_start", "n_kpieces",
-                     "n_ksplit", "n_kslots", "kv_piece_cap"):
+                     "n_ksplit", "n_kslots", "kv_piece_cap", "n_dsblk"):
             setattr(self, name, int(getattr(v, name)))
 
     def _arr(self, name, n):
@@ -204,7 +206,10 @@ class Plan:
             fq_chunk=self._arr("fq_chunk", self.n_chunks * TA_CHUNK_INTS).reshape(-1, TA_CHUNK_INTS),
             fq_order=self._arr("fq_order", self.n_qtiles), bk=self._arr("bk", self.n_ktiles * 4).reshape(-1, 4),
             kp=self._arr("kp", self.n_kpieces * TA_KPIECE_INTS).reshape(-1, TA_KPIECE_INTS),
-            kr=self._arr("kr", self.n_ksplit * 4).reshape(-1, 4))
+            kr=self._arr("kr", self.n_ksplit * 4).reshape(-1, 4),
+            dq_ptr=self._arr("dq_ptr", self.n_qtiles + 1),
+            dq_ent=self._arr("dq_ent", int(self._arr("dq_ptr", self.n_qtiles + 1)[-1]) * 4).reshape(-1, 4),
+            dq_order=self._arr("dq_order", self.n_qtiles))
 
     @property
     def handle(self):
@@ -496,8 +501,10 @@ def tree_attn_fwd(plan: Plan, q, k, v, scale: float = 0.0, rope_base: float = 0.
 
 
 def tree_attn_bwd(plan: Plan, q, k, v, o, lse, dO, scale: float = 0.0, rope_base: float = 0.0,
-                  dq=None, dk=None, dv=None, ws=None, events=None):
-    """Backward of tree_attn_fwd -> (dq, dk, dv), overwritten, deterministic."""
+                  dq=None, dk=None, dv=None, ws=None, events=None, recompute_dq: bool = False):
+    """Backward of tree_attn_fwd -> (dq, dk, dv), overwritten, deterministic.
+    recompute_dq: use the smallest workspace, in which dQ recomputes S and dP
+    instead of reading the dS blocks the dK/dV kernel stores (bf16)."""
     import torch
     N, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -512,8 +519,10 @@ def tree_attn_bwd(plan: Plan, q, k, v, o, lse, dO, scale: float = 0.0, rope_base
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     dt = _dt(q)
-    wsb = attn_ws_bytes(plan, 1, dt, Hq, Hkv, d, rope_base)
+    wsb = attn_ws_bytes(plan, 2 if recompute_dq else 1, dt, Hq, Hkv, d, rope_base)
     ws, wsn = _workspace(wsb, dev, ws)
+    if recompute_dq:
+        wsn = min(wsn, wsb)
     ev, nev = _events(events)
     _check("tree_attn_bwd", load_library().tree_attn_bwd_ex(
         plan.handle, _ptr(plan.device(dev)), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),

@@ -303,7 +303,10 @@ struct KVParams {
   const int32_t* kp;  // work pieces, TA_KPIECE_INTS each
   const int32_t* kr;  // cut sub-tiles: (kw, wk, first slot, n_windows)
   float* part;        // partial dK/dV slots (PART_WAVE floats per slot and KV head)
+  f16* ds;            // dS blocks [Hkv][n_dsblk][G][32 keys][32 positions] (dS path only)
+  f16* ds_spare;      // a 32 x 32 block that absorbs the stores of blocks a wavefront does not own
   int n_sum;          // cut sub-tiles
+  int n_dsblk;
   int N, Hq, Hkv, G;
   int q0;  // first query row (rows below are a key-only prefix)
   float scale, scale_log2, rope_base;
@@ -369,6 +372,8 @@ struct KVStageLayout {
 };
 static_assert(KVStageLayout::BYTES % 16 == 0, "stage buffers stay 16-byte aligned");
 
+// DS: also store the fp16 dS blocks for the dQ pass (the dS path).
+template <bool DS>
 __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   using L = KVStageLayout;
   __shared__ __attribute__((aligned(1024))) char smem[4 * L::BYTES];
@@ -379,11 +384,11 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int col = lane & 31, half = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(wave);
-  // this wavefront's keys [kw, kw + wkeys) (0: idle), the end of the rows it
-  // reads (<= qhi; each key reads rows [max(key, qlo), rhi)), its partial
-  // slot or -1
-  const cint_ptr tw = tl + 4 + 4 * w;
-  const int kw = tw[0], wkeys = tw[1], rhi = tw[2], slot = tw[3];
+  // this wavefront's keys [kw, kw + wkeys) (0: idle), its rows [rlo, rhi)
+  // within [qlo, qhi) (each key reads rows [max(key, rlo), rhi)), its
+  // partial slot or -1, and the dS block of query tile t: dsoff + t
+  const cint_ptr tw = tl + 4 + TA_KWAVE_INTS * w;
+  const int kw = tw[0], wkeys = tw[1], rlo = tw[2], rhi = tw[3], slot = tw[4], dsoff = tw[5];
   const bool kvalid = col < wkeys;
   const int key = kw + col;
 
@@ -465,6 +470,15 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   // before its first key are fully masked by the causal compare, and keys
   // past the tile are never stored.  (Keeping the accumulating MFMAs
   // unconditional lets the accumulators stay in AGPRs.)
+  // dS path: the block computed in one step is stored at the start of the
+  // next, always (no branch in the loop), into the spare block when the
+  // wavefront does not own it; ds_blk is wave-uniform
+  f16* ds_blk = P.ds_spare;
+  f16x8 ds_val[2] = {f16x8{}, f16x8{}};
+  const int ds_lane = col * SUB + half * 16;  // this lane's 16 elements in a block
+  // element mask limit: key <= row < rhi is (row - key) < lim; keys past a
+  // short sub-tile read no rows, so their dS (and P) is exactly zero
+  const unsigned lim = kvalid ? (unsigned)max(rhi - key, 0) : 0u;
   auto scores = [&](const char* base, f32x16& S, f32x16& dP) {
     const f16* q16 = (const f16*)(base + L::Q16);
     const bf16* dob = (const bf16*)(base + L::DO);
@@ -512,9 +526,8 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     // rows need the element mask key <= row < rhi, one unsigned compare:
     // (row - key) < (rhi - key), with no rows at all for a key >= rhi (a
     // window may end inside the wavefront's keys).
-    if (qb < kw + SUB || qb + SUB > rhi) {
+    if (qb < kw + SUB || qb + SUB > rhi || wkeys < SUB) {
       const int d0 = qb + 4 * half - key;
-      const unsigned lim = (unsigned)max(rhi - key, 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if ((unsigned)(d0 + 8 * (r >> 2) + (r & 3)) >= lim) p[r] = 0.f;
@@ -527,6 +540,17 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
       ds[r] = p[r] * dP[r];
     }
     const f16x8 sa[2] = {pack_f16_rtz(ds), pack_f16_rtz(ds + 8)};
+    // dS of this block goes out at the start of the next step (see the
+    // loop): block qb is query tile (qb - q0) / 32; stored as [key][position]
+    // with position half*16 + r, so each lane writes 32 contiguous bytes
+    if (DS) {
+      const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
+      const int hg = it - (it / P.G) * P.G;
+      f16* const blk = P.ds + (((size_t)kvh * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * P.G + hg) * (SUB * SUB);
+      ds_blk = own ? blk : P.ds_spare;
+      ds_val[0] = sa[0];
+      ds_val[1] = sa[1];
+    }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -547,6 +571,16 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   // nitem >= 1: every tile's query range holds at least one row.
   const int last = nitem - 1;
   char* const bb[4] = {smem, smem + L::BYTES, smem + 2 * L::BYTES, smem + 3 * L::BYTES};
+  // The dS stores of a step are issued at the start of the next one, before
+  // its copies: the ring's "at most five outstanding" wait then still means
+  // the copies two blocks ahead have landed (loads complete in order, and the
+  // stores, older than the newest five copies, are complete as well).
+  auto flush_ds = [&]() {
+    if (DS) {  // non-temporal: dS is read once, by the dQ pass, and should not linger dirty in the caches
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ds_val[0]), (u32x4*)(ds_blk + ds_lane));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ds_val[1]), (u32x4*)(ds_blk + ds_lane + 8));
+    }
+  };
   stage(0, bb[0]);
   stage(min(1, last), bb[1]);
   stage(min(2, last), bb[2]);
@@ -558,6 +592,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (u > 0 && it + u >= nitem) break;
+      flush_ds();
       stage(min(it + u + 3, last), bb[(u + 3) & 3]);
       if (u & 1) {
         scores(bb[(u + 1) & 3], Sa, dPa);
@@ -570,6 +605,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
       __syncthreads();
     }
   }
+  flush_ds();
   lds_copies_wait();
 
   agpr_fence8(dk, dv);
@@ -643,6 +679,196 @@ __global__ __launch_bounds__(256) void dkv_sum_kernel(KVParams P) {
 
 // ---------------------------------------------------------------------------
 // fp32 path.
+// ---------------------------------------------------------------------------
+// The dS path.  The dK/dV kernel stores the fp16 dS of every (query tile,
+// 32-key sub-tile) block it computes, and dQ = scale * dS K becomes one
+// product instead of recomputing S and dP (three).  Before dK/dV, prep_kernel
+// writes what the recomputing dQ kernel otherwise produces for it: the fp16
+// copy of Q (rotated by position when RoPE is on), -D = -(dO . O) and
+// -LSE * log2(e), for query rows >= q_start.  Eight lanes per (row, head):
+// lane j takes dimensions 8j..8j+7 and their rotate-half partners 64 + 8j..,
+// and D is summed over the eight.
+struct PrepParams {
+  const bf16* q;
+  const bf16* o;
+  const bf16* dO;
+  const float* lse;
+  f16* qs;
+  float* nd;
+  float* nl2;
+  const int32_t* pos;
+  int N, Hq, q0;
+  float rope_base;
+};
+
+__global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t pr = gid >> 3;
+  const int j = (int)(gid & 7);
+  if (pr >= (size_t)(P.N - P.q0) * P.Hq) return;  // whole groups of eight lanes
+  const int row = P.q0 + (int)(pr / P.Hq), h = (int)(pr % P.Hq);
+  const size_t off = ((size_t)row * P.Hq + h) * D + 8 * j;
+  const bf16x8 q1 = *(const bf16x8*)(P.q + off), q2 = *(const bf16x8*)(P.q + off + D / 2);
+  const bf16x8 o1 = *(const bf16x8*)(P.o + off), o2 = *(const bf16x8*)(P.o + off + D / 2);
+  const bf16x8 d1 = *(const bf16x8*)(P.dO + off), d2 = *(const bf16x8*)(P.dO + off + D / 2);
+  const bool rot = P.rope_base > 0.f;
+  const int p = P.pos[row];
+  float dsum = 0.f;
+  f16x8 h1, h2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    dsum += (float)d1[e] * (float)o1[e] + (float)d2[e] * (float)o2[e];
+    float x1 = (float)q1[e], x2 = (float)q2[e];
+    if (rot) {
+      float sn, cs;
+      rope_sincos(p, 8 * j + e, D, P.rope_base, &sn, &cs);
+      const float y1 = x1 * cs - x2 * sn;
+      x2 = x2 * cs + x1 * sn;
+      x1 = y1;
+    }
+    h1[e] = to_f16_sat(x1);
+    h2[e] = to_f16_sat(x2);
+  }
+  *(f16x8*)(P.qs + off) = h1;
+  *(f16x8*)(P.qs + off + D / 2) = h2;
+  dsum += __shfl_xor(dsum, 1);
+  dsum += __shfl_xor(dsum, 2);
+  dsum += __shfl_xor(dsum, 4);
+  if (j == 0) {
+    P.nd[(size_t)h * P.N + row] = -dsum;
+    P.nl2[(size_t)h * P.N + row] = -P.lse[(size_t)h * P.N + row] * TA_LOG2E;
+  }
+}
+
+struct DSParams {
+  const f16* k;   // fp16 K * scale * log2(e) (rotated when RoPE is on)
+  const f16* ds;  // [Hkv][n_dsblk][G][32 keys][32 positions]
+  bf16* dq;
+  const int32_t* pos;
+  const int32_t* dq_ptr;
+  const int32_t* dq_ent;
+  const int32_t* dq_order;
+  int N, Hq, Hkv, G, q0, n_dsblk;
+  float rope_base;
+};
+
+// dQ from the stored dS: one workgroup per (query tile, KV head) and up to
+// four heads of its group, one wavefront per head.  For each 32-key sub-tile
+// some row of the tile reads (the plan's list, by first key) the sub-tile's
+// fp16 K rows and the heads' dS blocks are copied straight into a four-buffer
+// LDS ring three entries ahead (the dS blocks come from HBM); dQ^T += K^T dS^T
+// on 32x32x16 fp16 MFMA, both operands from transpose reads.  The K copy
+// carries scale * log2(e), so dQ = ln(2) * the accumulators; rotated back in
+// the epilogue.  A fixed order over the list: bitwise repeatable.
+constexpr int DS_COPIES = 4;  // copies per wavefront per entry: two of K rows, two of dS
+
+__global__ __launch_bounds__(256, 2) void dq_ds_kernel(DSParams P) {
+  __shared__ __attribute__((aligned(1024))) f16 sK[4][SUB * D];
+  __shared__ __attribute__((aligned(1024))) f16 sS[4][4][SUB * SUB];
+
+  const int kvh = blockIdx.x % P.Hkv;
+  const int tile = as_const(P.dq_order)[blockIdx.x / P.Hkv];
+  const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hsub = blockIdx.y * 4 + w;
+  const bool active = hsub < P.G;
+  const int g = active ? hsub : 0;  // wavefronts without a head copy head 0's blocks and never store
+  const int e0 = as_const(P.dq_ptr)[tile], e1 = as_const(P.dq_ptr)[tile + 1];  // e1 > e0: a row reads its own key
+  const int last = e1 - 1;
+
+  // copy instruction i of the K rows fills rows 4i..4i+3 (wavefront w: i = w, w + 4);
+  // the dS block of this wavefront's head is two 1 KiB copies
+  auto stage = [&](int e, int b) {
+    const cint_ptr en = as_const(P.dq_ent) + (size_t)e * 4;
+    const int kw = en[0], wk = en[1], blk = en[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = w + 4 * c;
+      const int row = 4 * i + (lane >> 4);
+      const size_t off = ((size_t)(kw + min(row, wk - 1)) * P.Hkv + kvh) * D + (((lane & 15) ^ swz(row & 15)) << 3);
+      copy16_to_lds(P.k + off, sK[b] + 4 * i * D);
+    }
+    const f16* src = P.ds + (((size_t)kvh * P.n_dsblk + blk) * P.G + g) * (SUB * SUB) + lane * 8;
+    copy16_to_lds_nt(src, sS[b][w]);
+    copy16_to_lds_nt(src + 512, sS[b][w] + 512);
+  };
+
+  // transpose-read offsets: K^T of d-tile dt (256-byte swizzled rows), dS^T
+  // (64-byte rows); rows trow + 8x of each 16-key group
+  const int trow = half * 4 + ((lane & 15) >> 2);
+  const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  int toff[4][2], soff[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int r = trow + 8 * x;
+    soff[x] = r * SUB + tcol;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) toff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+  stage(e0, 0);
+  stage(min(e0 + 1, last), 1);
+  stage(min(e0 + 2, last), 2);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // entry e0 landed
+  __syncthreads();
+  for (int e = e0; e < e1; ++e) {
+    const int b = (e - e0) & 3;
+    stage(min(e + 3, last), (e - e0 + 3) & 3);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const f16* sb = sS[b][w] + kk * 16 * SUB;
+      const f16x8 bs = cat(lds_read_tr(sb + soff[0]), lds_read_tr(sb + soff[1]));
+      const f16* kb = sK[b] + kk * 16 * D;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        acc[dt] = mfma32h(cat(lds_read_tr(kb + toff[dt][0]), lds_read_tr(kb + toff[dt][1])), bs, acc[dt]);
+    }
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // entry e + 1 landed
+    __syncthreads();
+  }
+  lds_copies_wait();
+
+  // dQ^T register r of tile dt <-> d = dt*32 + 8*(r/4) + 4*half + r%4; lane
+  // column `col` is dS position col, i.e. row 8*((col%16)/4) + 4*(col/16) +
+  // col%4 of the tile; the rotate-half partner d + 64 sits in tile dt + 2.
+  const int qi = P.q0 + tile * SUB + 8 * ((col & 15) >> 2) + 4 * (col >> 4) + (col & 3);
+  if (active && qi < P.N) {
+    constexpr float LN2 = 0.69314718055994530942f;
+    float gq[4][16];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gq[dt][r] = acc[dt][r] * LN2;
+    if (P.rope_base > 0.f) {
+      const int p = P.pos[qi];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float sn, cs;
+          rope_sincos(p, dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3), D, P.rope_base, &sn, &cs);
+          const float y1 = gq[dt][r], y2 = gq[dt + 2][r];
+          gq[dt][r] = y1 * cs + y2 * sn;
+          gq[dt + 2][r] = y2 * cs - y1 * sn;
+        }
+    }
+    bf16* out = P.dq + ((size_t)qi * P.Hq + kvh * P.G + hsub) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = (bf16)gq[dt][r4 * 4 + u];
+        *(bf16x4*)(out + dt * 32 + r4 * 8 + half * 4) = v;
+      }
+  }
+}
+
 template <int D_>
 __global__ __launch_bounds__(TA_BLOCK_M) void dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                              const float* __restrict__ v, const float* __restrict__ o,
@@ -724,7 +950,11 @@ __global__ __launch_bounds__(TA_BLOCK_KV) void dkv_f32_kernel(const float* __res
 
 using namespace ta;
 
-size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base) {
+constexpr size_t SUB_SQ = TA_KV_SUB * TA_KV_SUB;
+
+// Backward workspace.  with_ds: the dS path (bf16), which adds the dS blocks
+// (32 x 32 fp16 per (query tile, sub-tile) block and query head).
+size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base, bool with_ds) {
   const size_t N = p->n_tokens;
   size_t b = align256(N * Hq * sizeof(float));  // D
   if (dt == TA_BF16) {
@@ -732,6 +962,8 @@ size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t
     b += align256(N * Hq * d * sizeof(f16)) + align256(N * Hkv * d * sizeof(f16));  // fp16 Q, K
     if (rope_base > 0.f) b += align256(N * Hkv * d * sizeof(bf16));                 // rotated bf16 K
     b += align256((size_t)p->n_kslots * Hkv * bwd::PART_WAVE * sizeof(float));       // dK/dV partials
+    if (with_ds) b += align256((size_t)p->n_dsblk * Hq * SUB_SQ * sizeof(f16)) +     // dS blocks
+                      align256(SUB_SQ * sizeof(f16));                                // + a spare one
   } else if (rope_base > 0.f) {
     b += align256(N * Hq * d * sizeof(float)) + align256(N * Hkv * d * sizeof(float));
   }
@@ -755,8 +987,11 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return TA_EINVAL;
   if (dt == TA_BF16 ? d != 128 : (dt != TA_F32 || (d != 64 && d != 128))) return TA_EUNSUPPORTED;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return TA_EINVAL;
-  const size_t need = ta_bwd_ws(p, dt, Hq, Hkv, d, rope_base);
+  // bf16: the dS path when the workspace holds the dS blocks, else dQ
+  // recomputes S and dP
+  const size_t need = ta_bwd_ws(p, dt, Hq, Hkv, d, rope_base, false);
   if (!ws || ws_bytes < need) return TA_ENOMEM;
+  const bool ds_path = dt == TA_BF16 && ws_bytes >= ta_bwd_ws(p, dt, Hq, Hkv, d, rope_base, true);
   const int N = p->n_tokens;
   if (N == 0) return TA_OK;
   if (scale <= 0.f) scale = 1.f / sqrtf((float)d);
@@ -783,13 +1018,39 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     bf16* krot = rope ? (bf16*)w : nullptr;
     if (rope) w += align256((size_t)N * Hkv * d * sizeof(bf16));
     float* part = (float*)w;
+    w += align256((size_t)p->n_kslots * Hkv * bwd::PART_WAVE * sizeof(float));
+    f16* dsb = ds_path ? (f16*)w : nullptr;
+    f16* ds_spare = ds_path ? (f16*)(w + align256((size_t)p->n_dsblk * Hq * SUB_SQ * sizeof(f16))) : nullptr;
+    const int32_t* dq_ptr = (const int32_t*)(base + p->off_dq_ptr);
+    const int32_t* dq_ent = (const int32_t*)(base + p->off_dq_ent);
+    const int32_t* dq_order = (const int32_t*)(base + p->off_dq_order);
     mark(ev, nev, 0, stream);
     // one pass: fp16 K * scale * log2(e) for dK/dV's scores and, with RoPE,
     // the rotated bf16 K for dQ
     const bf16* kb = rope ? krot : (const bf16*)k;
     if (launch_rope<bf16, f16>((const bf16*)k, ks, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E,
-                               krot) != hipSuccess)
+                               ds_path ? nullptr : krot) != hipSuccess)
       return TA_EHIP;
+    if (ds_path) {
+      bwd::PrepParams R;
+      R.q = (const bf16*)q;
+      R.o = (const bf16*)o;
+      R.dO = (const bf16*)dO;
+      R.lse = lse;
+      R.qs = qs;
+      R.nd = Dd;
+      R.nl2 = l2;
+      R.pos = pos;
+      R.N = N;
+      R.Hq = Hq;
+      R.q0 = p->q_start;
+      R.rope_base = rope_base;
+      const size_t lanes = (size_t)(N - p->q_start) * Hq * 8;
+      if (lanes > 0) {
+        hipLaunchKernelGGL(bwd::prep_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, R);
+        TA_LAUNCH_CHECK();
+      }
+    }
     mark(ev, nev, 1, stream);
     bwd::DQParams A;
     A.q = (const bf16*)q;
@@ -814,9 +1075,11 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     A.scale = scale;
     A.scale_log2 = scale * TA_LOG2E;
     A.rope_base = rope_base;
-    hipLaunchKernelGGL(bwd::dq_bf16_kernel, dim3(p->n_qtiles * Hkv, (A.G + 3) / 4), dim3(256), 0, stream, A);
-    TA_LAUNCH_CHECK();
-    mark(ev, nev, 2, stream);
+    if (!ds_path) {
+      hipLaunchKernelGGL(bwd::dq_bf16_kernel, dim3(p->n_qtiles * Hkv, (A.G + 3) / 4), dim3(256), 0, stream, A);
+      TA_LAUNCH_CHECK();
+      mark(ev, nev, 2, stream);
+    }
 
     bwd::KVParams B;
     B.q = qs;
@@ -831,6 +1094,9 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.kp = kp;
     B.kr = kr;
     B.part = part;
+    B.ds = dsb;
+    B.ds_spare = ds_spare;
+    B.n_dsblk = (int)p->n_dsblk;
     B.n_sum = p->n_ksplit;
     B.N = N;
     B.Hq = Hq;
@@ -840,11 +1106,36 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.scale = scale;
     B.scale_log2 = scale * TA_LOG2E;
     B.rope_base = rope_base;
-    hipLaunchKernelGGL(bwd::dkv_bf16_kernel, dim3(p->n_kpieces * Hkv), dim3(256), 0, stream, B);
+    if (ds_path)
+      hipLaunchKernelGGL(bwd::dkv_bf16_kernel<true>, dim3(p->n_kpieces * Hkv), dim3(256), 0, stream, B);
+    else
+      hipLaunchKernelGGL(bwd::dkv_bf16_kernel<false>, dim3(p->n_kpieces * Hkv), dim3(256), 0, stream, B);
     TA_LAUNCH_CHECK();
     if (p->n_ksplit > 0) {
       hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3((p->n_ksplit + 3) / 4 * Hkv * 4), dim3(256), 0, stream, B);
       TA_LAUNCH_CHECK();
+    }
+    if (ds_path) {
+      mark(ev, nev, 2, stream);
+      bwd::DSParams Q;
+      Q.k = ks;
+      Q.ds = dsb;
+      Q.dq = (bf16*)dq;
+      Q.pos = pos;
+      Q.dq_ptr = dq_ptr;
+      Q.dq_ent = dq_ent;
+      Q.dq_order = dq_order;
+      Q.N = N;
+      Q.Hq = Hq;
+      Q.Hkv = Hkv;
+      Q.G = Hq / Hkv;
+      Q.q0 = p->q_start;
+      Q.n_dsblk = (int)p->n_dsblk;
+      Q.rope_base = rope_base;
+      if (p->n_qtiles > 0) {
+        hipLaunchKernelGGL(bwd::dq_ds_kernel, dim3(p->n_qtiles * Hkv, (Q.G + 3) / 4), dim3(256), 0, stream, Q);
+        TA_LAUNCH_CHECK();
+      }
     }
     mark(ev, nev, 3, stream);
     return TA_OK;

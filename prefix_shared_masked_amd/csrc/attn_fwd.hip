@@ -385,7 +385,10 @@ extern "C" ta_status tree_plan_upload(const ta_plan* p, void* dplan, size_t byte
                {p->off_fq_order, &p->fq_order},
                {p->off_bk, &p->bk},
                {p->off_kp, &p->kp},
-               {p->off_kr, &p->kr}};
+               {p->off_kr, &p->kr},
+               {p->off_dq_ptr, &p->dq_ptr},
+               {p->off_dq_ent, &p->dq_ent},
+               {p->off_dq_order, &p->dq_order}};
   for (const Part& x : parts) {
     if (x.vec->empty()) continue;
     if (hipMemcpyAsync(base + x.off, x.vec->data(), x.vec->size() * sizeof(int32_t), hipMemcpyHostToDevice,
@@ -421,13 +424,13 @@ size_t fwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d,
 }  // namespace
 
 // Backward workspace (defined in attn_bwd.hip).
-size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base);
+size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base, bool with_ds);
 
 extern "C" ta_status tree_attn_ws_bytes(const ta_plan* p, int32_t op, ta_dtype dt, int32_t Hq, int32_t Hkv,
                                         int32_t d, float rope_base, size_t* bytes) {
-  if (!p || !bytes || (op != 0 && op != 1)) return TA_EINVAL;
+  if (!p || !bytes || op < 0 || op > 2) return TA_EINVAL;
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return TA_EINVAL;
-  *bytes = op == 0 ? fwd_ws(p, dt, Hq, Hkv, d, rope_base) : ta_bwd_ws(p, dt, Hq, Hkv, d, rope_base);
+  *bytes = op == 0 ? fwd_ws(p, dt, Hq, Hkv, d, rope_base) : ta_bwd_ws(p, dt, Hq, Hkv, d, rope_base, op == 1);
   return TA_OK;
 }
 

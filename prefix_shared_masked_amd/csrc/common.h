@@ -147,6 +147,12 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, const void* lds_bas
   const uint32_t a = lds_addr(lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory", "m0");
 }
+// Non-temporal variant: the data streams past the caches.
+__device__ __forceinline__ void copy16_to_lds_nt(const void* g, const void* lds_base) {
+  const uint32_t a = lds_addr(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(a)
+               : "memory", "m0");
+}
 // 4-byte variant (global_load_lds_dword): lane i writes lds_base + 4 i.
 __device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds_base) {
   const uint32_t a = lds_addr(lds_base);

@@ -75,11 +75,6 @@ struct SpanWalk {
   }
 };
 
-__device__ __forceinline__ void copy16_to_lds_nt(const void* g, const void* lds_base) {
-  const uint32_t a = lds_addr(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(a)
-               : "memory", "m0");
-}
 
 // Copies block b's K and V rows into one ring stage (swizzled 256-byte rows;
 // rows past the block's valid keys repeat its last key and are masked).

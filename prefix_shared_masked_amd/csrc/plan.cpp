@@ -281,23 +281,25 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
   p->computed_pairs_bwd = comp_bwd;
 
   // dK/dV work pieces.  A dK/dV workgroup has four wavefronts, each owning
-  // the dK/dV of up to 32 keys (a sub-tile) over a common run of 32-row query
-  // blocks [q_lo, q_hi) staged once in LDS.  Two things make whole tiles a
-  // poor unit: the root's keys are read by every query, so one workgroup can
-  // carry far more than an average CU's share, and a node shorter than 128
-  // keys leaves wavefronts idle (the 96-token history nodes of a navigation
-  // episode: a quarter of the work).  So a full 128-key tile whose range spans
-  // at most `cap` blocks stays one piece; every other tile is split into its
-  // 32-key sub-tiles, each cut at the windows of a grid of `cap` blocks
-  // anchored at q_start, and the sub-tile runs of one window are packed four
-  // to a piece when their row spans nest (a run joins only if the piece's span
-  // grows by at most one block over its longest run).  A sub-tile cut over
-  // several windows writes fp32 partial dK/dV to one slot per window
-  // (consecutive, in window order) that a second pass sums in slot order; one
-  // run in one window stores directly.  cap = max(TA_KV_PIECE_MIN,
-  // ceil(total blocks / 256)): about 256 CUs' worth for any number of KV
-  // heads.  Pieces are listed longest first, then by their last row (the
-  // workgroups resident at one time stream the same rows through L2).
+  // the dK/dV of up to 32 keys of one node (a sub-tile) over a common run of
+  // 32-row query blocks [q_lo, q_hi) staged once in LDS; blocks lie on the
+  // query-tile grid q_start + 32t, so each (block, sub-tile) is one dS block
+  // the dQ pass reads back.  Two things make whole tiles a poor unit: the
+  // root's keys are read by every query, so one workgroup can carry far more
+  // than an average CU's share, and a node shorter than 128 keys leaves
+  // wavefronts idle (the 96-token history nodes of a navigation episode: a
+  // quarter of the work).  So a full 128-key tile whose range spans at most
+  // `cap` blocks stays one piece; every other tile is split into its 32-key
+  // sub-tiles, each cut at the windows of a grid of `cap` blocks anchored at
+  // q_start, and the sub-tile runs of one window are packed four to a piece
+  // when their row spans nest (a run joins only if the piece's span grows by
+  // at most one block over its longest run).  A sub-tile cut over several
+  // windows writes fp32 partial dK/dV to one slot per window (consecutive, in
+  // window order) that a second pass sums in slot order; one run in one
+  // window stores directly.  cap = max(TA_KV_PIECE_MIN, ceil(total blocks /
+  // 256)): about 256 CUs' worth for any number of KV heads.  Pieces are listed
+  // longest first, then by their last row (the workgroups resident at one
+  // time stream the same rows through L2).
   {
     int64_t total = 0;
     std::vector<int32_t> tb(kts.size());
@@ -307,44 +309,80 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
     }
     const int32_t cap = static_cast<int32_t>(std::max<int64_t>(TA_KV_PIECE_MIN, (total + 255) / 256));
     const int64_t W = int64_t(SUB) * cap;  // rows per window
+    auto grid_floor = [&](int32_t r) { return Q0 + SUB * ((r - Q0) / SUB); };
+
+    // sub-tiles: keys [kw, kw + wk) of one node, query tiles [t_lo, t_hi),
+    // dS blocks ds0 .. ds0 + t_hi - t_lo - 1
+    struct Sub {
+      int32_t kw, wk, qe, t_lo, t_hi;
+      int64_t ds0;
+    };
+    std::vector<Sub> subs;
+    std::vector<int32_t> first_sub(kts.size());
+    int64_t nds = 0;
+    for (size_t i = 0; i < kts.size(); ++i) {
+      first_sub[i] = static_cast<int32_t>(subs.size());
+      for (int32_t kw = kts[i].k0; kw < kts[i].k0 + kts[i].klen; kw += SUB) {
+        Sub x;
+        x.kw = kw;
+        x.wk = std::min(SUB, kts[i].k0 + kts[i].klen - kw);
+        x.qe = kts[i].qe;
+        x.t_lo = (std::max(kw, Q0) - Q0) / SUB;
+        x.t_hi = (x.qe - Q0 + SUB - 1) / SUB;
+        x.ds0 = nds;
+        nds += x.t_hi - x.t_lo;
+        subs.push_back(x);
+      }
+    }
+    if (nds > kI32Max) return TA_ERANGE;
+    p->n_dsblk = nds;
+
     struct Run {
-      int32_t lo, hi, kw, wk, slot, seq;  // rows [lo, hi) of sub-tile kw.. (wk keys)
+      int32_t lo, hi, sub, slot, seq;  // rows [lo, hi) of sub-tile `sub`
     };
     struct KP {
       int32_t rec[TA_KPIECE_INTS];
       int32_t blocks, seq;
     };
+    auto wave_rec = [&](int32_t* t, const Sub& x, int32_t lo, int32_t hi, int32_t slot) {
+      t[0] = x.kw;
+      t[1] = x.wk;
+      t[2] = lo;
+      t[3] = hi;
+      t[4] = slot;
+      t[5] = static_cast<int32_t>(x.ds0 - x.t_lo);
+      t[6] = 0;
+    };
     std::vector<KP> kps;
     std::vector<std::vector<Run>> win;  // runs by window
     int32_t slots = 0, seq = 0;
     for (size_t i = 0; i < kts.size(); ++i) {
-      const int32_t k0 = kts[i].k0, kl = kts[i].klen, qe = kts[i].qe, qs = std::max(k0, Q0);
+      const int32_t kl = kts[i].klen, qe = kts[i].qe, qs = std::max(kts[i].k0, Q0);
       if (kl == BK && tb[i] <= cap) {
         KP x{};
-        x.rec[0] = qs;
+        x.rec[0] = grid_floor(qs);
         x.rec[1] = qe;
         for (int w = 0; w < 4; ++w) {
-          int32_t* t = x.rec + 4 + 4 * w;
-          t[0] = k0 + SUB * w;
-          t[1] = SUB;
-          t[2] = qe;
-          t[3] = -1;
+          const Sub& su = subs[first_sub[i] + w];
+          wave_rec(x.rec + 4 + TA_KWAVE_INTS * w, su, std::max(su.kw, Q0), qe, -1);
         }
-        x.blocks = tb[i];
+        x.blocks = (qe - x.rec[0] + SUB - 1) / SUB;
         x.seq = seq++;
         kps.push_back(x);
         continue;
       }
-      for (int32_t kw = k0; kw < k0 + kl; kw += SUB) {
-        const int32_t wk = std::min(SUB, k0 + kl - kw), lo = std::max(kw, Q0);
+      const int32_t sub_end = i + 1 < kts.size() ? first_sub[i + 1] : static_cast<int32_t>(subs.size());
+      for (int32_t si = first_sub[i]; si < sub_end; ++si) {
+        const Sub& su = subs[si];
+        const int32_t lo = std::max(su.kw, Q0);
         const int64_t m0 = (lo - Q0) / W, m1 = (qe - 1 - Q0) / W;
         const int32_t nw = static_cast<int32_t>(m1 - m0 + 1);
-        if (nw > 1) p->kr.insert(p->kr.end(), {kw, wk, slots, nw});
+        if (nw > 1) p->kr.insert(p->kr.end(), {su.kw, su.wk, slots, nw});
         for (int64_t m = m0; m <= m1; ++m) {
           if (win.size() <= size_t(m)) win.resize(m + 1);
           const int32_t a = static_cast<int32_t>(std::max<int64_t>(lo, Q0 + m * W));
           const int32_t b = static_cast<int32_t>(std::min<int64_t>(qe, Q0 + (m + 1) * W));
-          win[m].push_back({a, b, kw, wk, nw > 1 ? slots + static_cast<int32_t>(m - m0) : -1, seq++});
+          win[m].push_back({a, b, si, nw > 1 ? slots + static_cast<int32_t>(m - m0) : -1, seq++});
         }
         if (nw > 1) slots += nw;
       }
@@ -366,24 +404,24 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
           ++e;
         }
         KP x{};
-        x.rec[0] = lo;
+        x.rec[0] = grid_floor(lo);
         x.rec[1] = hi;
         for (int w = 0; w < 4; ++w) {
-          int32_t* t = x.rec + 4 + 4 * w;
+          int32_t* t = x.rec + 4 + TA_KWAVE_INTS * w;
           if (j + w < e) {
             const Run& r = rs[j + w];
-            t[0] = r.kw;
-            t[1] = r.wk;
-            t[2] = r.hi;
-            t[3] = r.slot;
-          } else {  // idle wavefront: no keys (its loads read key 0, nothing is stored)
+            wave_rec(t, subs[r.sub], r.lo, r.hi, r.slot);
+          } else {  // idle wavefront: no keys, no rows (its loads read key 0, nothing is stored)
             t[0] = 0;
             t[1] = 0;
-            t[2] = lo;
-            t[3] = -1;
+            t[2] = x.rec[0];
+            t[3] = x.rec[0];
+            t[4] = -1;
+            t[5] = 0;
+            t[6] = 0;
           }
         }
-        x.blocks = (hi - lo + SUB - 1) / SUB;
+        x.blocks = (hi - x.rec[0] + SUB - 1) / SUB;
         x.seq = rs[j].seq;
         kps.push_back(x);
         j = e;
@@ -401,9 +439,39 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
     p->n_ksplit = static_cast<int32_t>(p->kr.size() / 4);
     p->n_kslots = slots;
     p->kv_piece_cap = cap;
+
+    // dQ lists: per query tile, the sub-tiles some of its rows read, by first
+    // key, each with its dS block (kw, wk, block, 0); tiles with the most
+    // entries first
+    std::vector<int32_t> cnt(n_qt + 1, 0);
+    for (const Sub& x : subs)
+      for (int32_t t = x.t_lo; t < x.t_hi; ++t) ++cnt[t + 1];
+    p->dq_ptr.assign(n_qt + 1, 0);
+    for (int32_t t = 0; t < n_qt; ++t) p->dq_ptr[t + 1] = p->dq_ptr[t] + cnt[t + 1];
+    if (int64_t(p->dq_ptr[n_qt]) * 4 > kI32Max) return TA_ERANGE;
+    std::vector<int32_t> order(subs.size());
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return subs[x].kw < subs[y].kw; });
+    std::vector<int32_t> fill(p->dq_ptr.begin(), p->dq_ptr.end() - 1);
+    p->dq_ent.assign(size_t(p->dq_ptr[n_qt]) * 4, 0);
+    for (int32_t si : order) {
+      const Sub& x = subs[si];
+      for (int32_t t = x.t_lo; t < x.t_hi; ++t) {
+        int32_t* e = p->dq_ent.data() + size_t(fill[t]++) * 4;
+        e[0] = x.kw;
+        e[1] = x.wk;
+        e[2] = static_cast<int32_t>(x.ds0 + t - x.t_lo);
+      }
+    }
+    p->dq_order.resize(n_qt);
+    std::iota(p->dq_order.begin(), p->dq_order.end(), 0);
+    std::stable_sort(p->dq_order.begin(), p->dq_order.end(), [&](int32_t x, int32_t y) {
+      return (p->dq_ptr[x + 1] - p->dq_ptr[x]) > (p->dq_ptr[y + 1] - p->dq_ptr[y]);
+    });
   }
 
-  // device image: pos | fq_ptr | fq_chunk | fq_order | bk | kp | kr, each 256-aligned
+  // device image: pos | fq_ptr | fq_chunk | fq_order | bk | kp | kr | dq_ptr | dq_ent | dq_order,
+  // each 256-aligned
   size_t off = 0;
   p->off_pos = off;
   off = align256(off + sizeof(int32_t) * size_t(std::max(N, 1)));
@@ -419,6 +487,12 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
   off = align256(off + sizeof(int32_t) * std::max<size_t>(p->kp.size(), 1));
   p->off_kr = off;
   off = align256(off + sizeof(int32_t) * std::max<size_t>(p->kr.size(), 1));
+  p->off_dq_ptr = off;
+  off = align256(off + sizeof(int32_t) * std::max<size_t>(p->dq_ptr.size(), 1));
+  p->off_dq_ent = off;
+  off = align256(off + sizeof(int32_t) * std::max<size_t>(p->dq_ent.size(), 1));
+  p->off_dq_order = off;
+  off = align256(off + sizeof(int32_t) * std::max<size_t>(p->dq_order.size(), 1));
   p->device_bytes = off;
   return TA_OK;
 }
@@ -495,6 +569,10 @@ extern "C" ta_status tree_plan_view(const ta_plan* p, ta_plan_view* v) {
   v->kv_piece_cap = p->kv_piece_cap;
   v->kp = p->kp.data();
   v->kr = p->kr.data();
+  v->n_dsblk = p->n_dsblk;
+  v->dq_ptr = p->dq_ptr.data();
+  v->dq_ent = p->dq_ent.data();
+  v->dq_order = p->dq_order.data();
   return TA_OK;
 }
 

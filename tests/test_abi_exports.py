@@ -81,7 +81,12 @@ def test_validation_before_launch():
     s = ctypes.c_int32()
     assert L.tree_decode_ws_bytes(8, 32, 128, 262144, 0, ctypes.byref(n), ctypes.byref(s)) == 0
     assert 1 <= s.value <= 120 and n.value >= 8 * 32 * s.value * 130 * 4
-    assert L.tree_attn_ws_bytes(plan.handle, 2, 1, 4, 2, 128, 0.0, ctypes.byref(n)) == 1
+    assert L.tree_attn_ws_bytes(plan.handle, 3, 1, 4, 2, 128, 0.0, ctypes.byref(n)) == 1
+    # the smallest backward workspace (op 2) is below the full one (op 1: plus the dS blocks)
+    small, full = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.tree_attn_ws_bytes(plan.handle, 2, 1, 4, 2, 128, 0.0, ctypes.byref(small)) == 0
+    assert L.tree_attn_ws_bytes(plan.handle, 1, 1, 4, 2, 128, 0.0, ctypes.byref(full)) == 0
+    assert full.value >= small.value + plan.n_dsblk * 4 * 2048
 
 
 def test_validation_before_launch_new_calls():

@@ -33,7 +33,7 @@ def close(name, got, ref, dtype, where=""):
                            f"max err {float(err.max()):.3e}")
 
 
-def run_case(tree, Hq, Hkv, d, dtype, rope, seed=0, grads=True, heads=None):
+def run_case(tree, Hq, Hkv, d, dtype, rope, seed=0, grads=True, heads=None, recompute_dq=False):
     print(f"[case] {tree.name or 'tree'} N={tree.n_tokens} Hq={Hq} Hkv={Hkv} d={d} {dtype} rope={rope}",
           flush=True)
     plan = pkg.tree_plan(tree.parent, tree.seg_len)
@@ -43,7 +43,7 @@ def run_case(tree, Hq, Hkv, d, dtype, rope, seed=0, grads=True, heads=None):
     o, lse = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=rope)
     res = dict(o=o, lse=lse)
     if grads:
-        dq, dk, dv = pkg.tree_attn_bwd(plan, Q, K, V, o, lse, DO, rope_base=rope)
+        dq, dk, dv = pkg.tree_attn_bwd(plan, Q, K, V, o, lse, DO, rope_base=rope, recompute_dq=recompute_dq)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     ref = oracle.per_path_attention(op, q64, k64, v64, rope_base=rope, dO=do64 if grads else None)
@@ -119,6 +119,15 @@ def test_bf16_cut_key_tiles():
     close("dq", dq[q0:], ref["dq"][q0:], torch.bfloat16)
     close("dk", dk, ref["dk"], torch.bfloat16)
     close("dv", dv, ref["dv"], torch.bfloat16)
+
+
+def test_bf16_recompute_dq_path():
+    """The smallest backward workspace: dQ recomputes S and dP (no stored dS)
+    before dK/dV; same oracle bar, on trees with short and cut key tiles."""
+    trees = [W.Tree(np.array([-1, 0, 1, 1], np.int32), np.array([100, 300, 900, 700], np.int32), "cut"),
+             W.spine_tree(64, 16, 24, 6), W.six_node_tree(48)]
+    for i, t in enumerate(trees):
+        run_case(t, 8, 2, 128, torch.bfloat16, 10000.0 if i != 1 else 0.0, seed=20 + i, recompute_dq=True)
 
 
 def test_bf16_deterministic_and_sibling_leak():

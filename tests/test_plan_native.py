@@ -87,55 +87,63 @@ def compare(tree):
 
 
 def check_pieces(p, v):
-    """dK/dV work pieces (four wavefronts over common rows [q_lo, q_hi), each
-    owning a 32-key sub-tile and reading rows [max(key, q_lo), row_end)):
-    every sub-tile's rows [max(kw, q_start), q_end) are covered exactly once;
-    a full 128-key tile spanning at most the cap's blocks is one piece with its
-    four sub-tiles; every other run lies in one window of the cap's blocks
-    anchored at q_start, and runs are packed only when the piece's span is at
-    most one block longer than its longest run; a sub-tile over several
-    windows owns consecutive slots in window order and a sum record; pieces
-    are listed longest first, then by last row."""
-    sub, BK = pkg.TA_KV_SUB, pkg.TA_BLOCK_KV
+    """dK/dV work pieces (four wavefronts over common rows [q_lo, q_hi) on the
+    query-tile grid, each owning a 32-key sub-tile and reading rows
+    [max(key, r_lo), r_hi)): every sub-tile's rows [max(kw, q_start), q_end)
+    are covered exactly once; a full 128-key tile spanning at most the cap's
+    blocks is one piece with its four sub-tiles; every other run lies in one
+    window of the cap's blocks anchored at q_start, and runs are packed only
+    when the piece's span is at most one block longer than its longest run; a
+    sub-tile over several windows owns consecutive slots in window order and
+    a sum record; pieces are listed longest first, then by last row.  The dS
+    blocks the wavefronts store are exactly the blocks the dQ lists read, each
+    once, numbered 0 .. n_dsblk - 1."""
+    sub, BK, KW = pkg.TA_KV_SUB, pkg.TA_BLOCK_KV, pkg.TA_KWAVE_INTS
     kp, kr, bk = v["kp"], v["kr"], v["bk"]
-    q0 = p.q_start
-    assert p.n_kpieces == len(kp) and p.n_ksplit == len(kr) and kp.shape[1] == 20
+    q0, N = p.q_start, p.n_tokens
+    assert p.n_kpieces == len(kp) and p.n_ksplit == len(kr) and kp.shape[1] == pkg.TA_KPIECE_INTS
     nb = [-(-(int(t[2]) - max(int(t[0]), q0)) // sub) for t in bk]
     cap = max(pkg.TA_KV_PIECE_MIN, -(-sum(nb) // 256))
     assert p.kv_piece_cap == cap
     W = sub * cap
-    whole = {int(t[0]): (int(t[2]), n) for t, n in zip(bk, nb) if t[1] == BK and n <= cap}
-    runs = {}          # kw -> list of (row_lo, row_hi, slot, wk)
+    floor = lambda r: q0 + sub * ((r - q0) // sub)
+    whole = {int(t[0]): int(t[2]) for t, n in zip(bk, nb) if t[1] == BK and n <= cap}
+    runs, written = {}, {}
     for x in kp:
-        qlo, qhi = int(x[0]), int(x[1])
-        assert x[2] == 0 and x[3] == 0 and q0 <= qlo < qhi <= p.n_tokens
-        waves = [tuple(int(z) for z in x[4 + 4 * w:8 + 4 * w]) for w in range(4)]
+        x = [int(z) for z in x]
+        qlo, qhi = x[0], x[1]
+        assert x[2] == 0 and x[3] == 0 and q0 <= qlo < qhi <= N and (qlo - q0) % sub == 0
+        waves = [x[4 + KW * w:4 + KW * (w + 1)] for w in range(4)]
         act = [t for t in waves if t[1] > 0]
         assert act, "a piece with no keys"
-        if act[0][0] in whole and len(act) == 4 and act[0][3] == -1 and act[0][0] + 3 * sub == act[3][0]:
-            qe, n = whole.pop(act[0][0])
-            assert (qlo, qhi) == (max(act[0][0], q0), qe)
-            assert all(t == (act[0][0] + sub * w, sub, qe, -1) for w, t in enumerate(act))
+        k0 = act[0][0]
+        is_whole = (k0 in whole and len(act) == 4 and all(t[4] == -1 for t in act)
+                    and [t[0] for t in act] == [k0 + sub * w for w in range(4)] and act[0][3] == whole[k0]
+                    and qlo == floor(max(k0, q0)))
+        if is_whole:
+            qe = whole.pop(k0)
+            assert qhi == qe
             for t in act:
-                runs.setdefault(t[0], []).append((max(t[0], qlo), qe, -1, sub))
-            continue
-        longest = 0
-        for kw, wk, rhi, slot in act:
-            assert 1 <= wk <= sub and rhi <= qhi
-            lo = max(kw, qlo)
-            assert lo < rhi
-            win = (rhi - 1 - q0) // W
-            a = max(kw, q0, q0 + win * W)
-            assert (a - q0) // W == win and a >= qlo
-            longest = max(longest, rhi - a)
-            runs.setdefault(kw, []).append((a, rhi, slot, wk))
-        assert qhi - qlo <= longest + sub
-        for kw, wk, rhi, slot in waves:
+                assert t[1:5] == [sub, max(t[0], q0), qe, -1] and t[6] == 0
+        else:
+            lo_min, longest = min(t[2] for t in act), 0
+            assert qlo == floor(lo_min)
+            for kw, wk, rlo, rhi, slot, dso, z in act:
+                assert 1 <= wk <= sub and qlo <= rlo < rhi <= qhi and z == 0
+                win = (rhi - 1 - q0) // W
+                assert (rlo - q0) // W == win and rlo == max(kw, q0, q0 + win * W)
+                longest = max(longest, rhi - rlo)
+            assert qhi - lo_min <= longest + sub
+        for kw, wk, rlo, rhi, slot, dso, z in waves:
             if wk == 0:
-                assert slot == -1
+                assert (rlo, rhi, slot) == (qlo, qlo, -1)
+                continue
+            runs.setdefault(kw, []).append((rlo, rhi, slot, wk))
+            for t in range((rlo - q0) // sub, -(-(rhi - q0) // sub)):
+                assert (kw, t) not in written, "a dS block stored twice"
+                written[(kw, t)] = dso + t
     assert not whole, "a whole tile was not one piece"
     node_of, sub_end = v["node_of"], v["sub_end"]
-    starts, seg = v["node_start"], None
     slots, cut = [], {}
     for kw, rs in runs.items():
         qe = int(sub_end[kw])
@@ -153,10 +161,23 @@ def check_pieces(p, v):
             cut[kw] = (rs[0][3], ss[0], len(rs))
     assert sorted(slots) == list(range(p.n_kslots))
     assert {int(r[0]): (int(r[1]), int(r[2]), int(r[3])) for r in kr} == cut and len(cut) == len(kr)
-    # every key of every node belongs to exactly one sub-tile
-    assert sum(r[0][3] for r in runs.values()) == p.n_tokens
+    assert sum(r[0][3] for r in runs.values()) == N     # every key in exactly one sub-tile
     key = [(-(-(-(int(x[1]) - int(x[0])) // sub)), -int(x[1])) for x in kp]
     assert key == sorted(key)
+    # dS blocks: stored once each, numbered densely, and exactly the dQ lists
+    assert p.n_dsblk == len(written) and sorted(written.values()) == list(range(p.n_dsblk))
+    dptr, dent, dord = v["dq_ptr"], v["dq_ent"], v["dq_order"]
+    assert len(dptr) == p.n_qtiles + 1 and (np.diff(dptr) >= 1).all() and dptr[-1] == len(dent) == p.n_dsblk
+    seen = {}
+    for t in range(p.n_qtiles):
+        ent = dent[dptr[t]:dptr[t + 1]]
+        assert list(ent[:, 0]) == sorted(ent[:, 0]) and (ent[:, 3] == 0).all()
+        for kw, wk, blk, _ in ent:
+            seen[(int(kw), t)] = int(blk)
+            assert runs[int(kw)][0][3] == wk
+    assert seen == written
+    cnt = np.diff(dptr)
+    assert sorted(dord.tolist()) == list(range(p.n_qtiles)) and (np.diff(cnt[dord]) <= 0).all()
 
 
 def test_six_node():
