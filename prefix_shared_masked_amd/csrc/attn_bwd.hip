@@ -755,16 +755,17 @@ struct DSParams {
 // dQ from the stored dS: one workgroup per (query tile, KV head) and up to
 // four heads of its group, one wavefront per head.  For each 32-key sub-tile
 // some row of the tile reads (the plan's list, by first key) the sub-tile's
-// fp16 K rows and the heads' dS blocks are copied straight into a four-buffer
-// LDS ring three entries ahead (the dS blocks come from HBM); dQ^T += K^T dS^T
+// fp16 K rows and the heads' dS blocks are copied straight into a three-buffer
+// LDS ring two entries ahead (48 KB, three workgroups per CU: the dS blocks
+// come from HBM and the latency wants many in flight); dQ^T += K^T dS^T
 // on 32x32x16 fp16 MFMA, both operands from transpose reads.  The K copy
 // carries scale * log2(e), so dQ = ln(2) * the accumulators; rotated back in
 // the epilogue.  A fixed order over the list: bitwise repeatable.
 constexpr int DS_COPIES = 4;  // copies per wavefront per entry: two of K rows, two of dS
 
-__global__ __launch_bounds__(256, 2) void dq_ds_kernel(DSParams P) {
-  __shared__ __attribute__((aligned(1024))) f16 sK[4][SUB * D];
-  __shared__ __attribute__((aligned(1024))) f16 sS[4][4][SUB * SUB];
+__global__ __launch_bounds__(256, 3) void dq_ds_kernel(DSParams P) {
+  __shared__ __attribute__((aligned(1024))) f16 sK[3][SUB * D];
+  __shared__ __attribute__((aligned(1024))) f16 sS[3][4][SUB * SUB];
 
   const int kvh = blockIdx.x % P.Hkv;
   const int tile = as_const(P.dq_order)[blockIdx.x / P.Hkv];
@@ -812,12 +813,12 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(DSParams P) {
 
   stage(e0, 0);
   stage(min(e0 + 1, last), 1);
-  stage(min(e0 + 2, last), 2);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // entry e0 landed
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // entry e0 landed
   __syncthreads();
   for (int e = e0; e < e1; ++e) {
-    const int b = (e - e0) & 3;
-    stage(min(e + 3, last), (e - e0 + 3) & 3);
+    const int b = (e - e0) % 3;
+    // the buffer refilled here was last read in the previous iteration, before its barrier
+    stage(min(e + 2, last), (e - e0 + 2) % 3);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const f16* sb = sS[b][w] + kk * 16 * SUB;
@@ -827,7 +828,7 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(DSParams P) {
       for (int dt = 0; dt < 4; ++dt)
         acc[dt] = mfma32h(cat(lds_read_tr(kb + toff[dt][0]), lds_read_tr(kb + toff[dt][1])), bs, acc[dt]);
     }
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // entry e + 1 landed
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // entry e + 1 landed
     __syncthreads();
   }
   lds_copies_wait();
