@@ -195,16 +195,56 @@ __device__ __forceinline__ void load_taps(const float* __restrict__ w, int k, in
     for (int j = 0; j < 8; ++j) wr[j][e] = j < K ? w[(size_t)(k + e) * K + j] : 0.f;
 }
 
-template <int VW>
+// Within a node (and from a parent into its first child, which follows it in
+// DFS order) the j-th path predecessor of token t is the packed row t - j.
+// A group of TG tokens whose taps all follow that pattern -- checked on the
+// table by the lanes of each wavefront, the same answer in every wavefront
+// of the block -- reads its TG + K - 1 rows once into registers; other groups
+// gather through the table.  KT: the compile-time width for the register
+// window (2..4), or 0: gather only.  Lanes past the channels clamp their
+// loads and skip their stores, so every lane takes part in the vote.
+template <int KT>
+__device__ __forceinline__ bool window_prev(const int32_t* __restrict__ cprev, int N, int t0) {
+  const int lane = threadIdx.x & 63;
+  bool ok = t0 + TG <= N;
+  if (lane < TG * (KT - 1) && ok) {
+    const int t = t0 + lane / (KT - 1), j = lane % (KT - 1) + 1;
+    // (t - j >= 0: the table marks a missing predecessor with -1, which t - j = -1 would match)
+    ok = t - j >= 0 && cprev[(size_t)t0 * (KT - 1) + lane] == t - j;
+  }
+  return __all(ok);
+}
+
+template <int VW, int KT>
 __global__ __launch_bounds__(TH) void conv_fwd(const int32_t* __restrict__ cprev, int N, int K, const float* __restrict__ x,
                                                const float* __restrict__ w, int C, float* __restrict__ y) {
   typedef typename Vec<VW>::T V;
-  const int k = (blockIdx.y * TH + threadIdx.x) * VW;
-  if (k >= C) return;
+  const int k0 = (blockIdx.y * TH + threadIdx.x) * VW;
+  const bool live = k0 < C;
+  const int k = live ? k0 : C - VW;
   float wr[8][VW];
   load_taps<VW>(w, k, K, wr);
-  const int t1 = min(N, (int)(blockIdx.x + 1) * TG);
-  for (int t = blockIdx.x * TG; t < t1; ++t) {
+  const int t0 = blockIdx.x * TG;
+  if (KT > 1 && window_prev<KT>(cprev, N, t0)) {
+    V r[TG + KT - 1];  // rows t0 - KT + 1 .. t0 + TG - 1 (all >= 0: every tap has a predecessor)
+#pragma unroll
+    for (int i = 0; i < TG + KT - 1; ++i) r[i] = *(const V*)(x + (size_t)(t0 - (KT - 1) + i) * C + k);
+#pragma unroll
+    for (int tt = 0; tt < TG; ++tt) {
+      V s;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        float acc = wr[0][e] * Vec<VW>::get(r[tt + KT - 1], e);
+#pragma unroll
+        for (int j = 1; j < KT; ++j) acc = fmaf(wr[j][e], Vec<VW>::get(r[tt + KT - 1 - j], e), acc);
+        Vec<VW>::set(s, e, acc);
+      }
+      if (live) *(V*)(y + (size_t)(t0 + tt) * C + k) = s;
+    }
+    return;
+  }
+  const int t1 = min(N, t0 + TG);
+  for (int t = t0; t < t1; ++t) {
     const V x0 = *(const V*)(x + (size_t)t * C + k);
     V s;
 #pragma unroll
@@ -220,22 +260,58 @@ __global__ __launch_bounds__(TH) void conv_fwd(const int32_t* __restrict__ cprev
       for (int e = 0; e < VW; ++e)
         Vec<VW>::set(s, e, fmaf(wr[j][e], q >= 0 ? Vec<VW>::get(xv, e) : 0.f, Vec<VW>::get(s, e)));
     }
-    *(V*)(y + (size_t)t * C + k) = s;
+    if (live) *(V*)(y + (size_t)t * C + k) = s;
   }
 }
 
-// dx[s][k] = w[k][0] dy[s][k] + sum over (t, j) with prev^j(t) = s of w[k][j] dy[t][k].
-template <int VW>
-__global__ __launch_bounds__(TH) void conv_dx(const int32_t* __restrict__ sp, const int32_t* __restrict__ sc, int N, int K,
-                                              const float* __restrict__ dy, const float* __restrict__ w, int C,
-                                              float* __restrict__ dx) {
+// dx[s] = sum_j w[j] dy[t] over the (t, j) with prev^j(t) = s (the inverse
+// table: sp / sc, codes t*K + j ordered by t).  Window: every token s of the
+// group has exactly the K - 1 successors s + 1 .. s + K - 1 (prev^j(s + j)
+// = s and no other), so dx[s] = sum_j w[j] dy[s + j] from TG + K - 1 rows.
+template <int KT>
+__device__ __forceinline__ bool window_succ(const int32_t* __restrict__ cprev, const int32_t* __restrict__ sp, int N,
+                                            int s0) {
+  const int lane = threadIdx.x & 63;
+  bool ok = s0 + TG + KT - 1 <= N;
+  if (ok && lane < TG * (KT - 1)) {
+    const int s = s0 + lane / (KT - 1), j = lane % (KT - 1) + 1;
+    ok = cprev[(size_t)(s + j) * (KT - 1) + (j - 1)] == s;
+  }
+  if (ok && lane < TG) ok = sp[s0 + lane + 1] - sp[s0 + lane] == KT - 1;
+  return __all(ok);
+}
+
+template <int VW, int KT>
+__global__ __launch_bounds__(TH) void conv_dx(const int32_t* __restrict__ cprev, const int32_t* __restrict__ sp,
+                                              const int32_t* __restrict__ sc, int N, int K, const float* __restrict__ dy,
+                                              const float* __restrict__ w, int C, float* __restrict__ dx) {
   typedef typename Vec<VW>::T V;
-  const int k = (blockIdx.y * TH + threadIdx.x) * VW;
-  if (k >= C) return;
+  const int k0 = (blockIdx.y * TH + threadIdx.x) * VW;
+  const bool live = k0 < C;
+  const int k = live ? k0 : C - VW;
   float wr[8][VW];
   load_taps<VW>(w, k, K, wr);
-  const int s1 = min(N, (int)(blockIdx.x + 1) * TG);
-  for (int s = blockIdx.x * TG; s < s1; ++s) {
+  const int s0 = blockIdx.x * TG;
+  if (KT > 1 && window_succ<KT>(cprev, sp, N, s0)) {
+    V r[TG + KT - 1];  // rows s0 .. s0 + TG + KT - 2
+#pragma unroll
+    for (int i = 0; i < TG + KT - 1; ++i) r[i] = *(const V*)(dy + (size_t)(s0 + i) * C + k);
+#pragma unroll
+    for (int tt = 0; tt < TG; ++tt) {
+      V v;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        float acc = wr[0][e] * Vec<VW>::get(r[tt], e);
+#pragma unroll
+        for (int j = 1; j < KT; ++j) acc = fmaf(wr[j][e], Vec<VW>::get(r[tt + j], e), acc);
+        Vec<VW>::set(v, e, acc);
+      }
+      if (live) *(V*)(dx + (size_t)(s0 + tt) * C + k) = v;
+    }
+    return;
+  }
+  const int s1 = min(N, s0 + TG);
+  for (int s = s0; s < s1; ++s) {
     const V g0 = *(const V*)(dy + (size_t)s * C + k);
     V v;
 #pragma unroll
@@ -250,40 +326,62 @@ __global__ __launch_bounds__(TH) void conv_dx(const int32_t* __restrict__ sp, co
           for (int e = 0; e < VW; ++e) Vec<VW>::set(v, e, fmaf(wr[jj][e], Vec<VW>::get(g, e), Vec<VW>::get(v, e)));
         }
     }
-    *(V*)(dx + (size_t)s * C + k) = v;
+    if (live) *(V*)(dx + (size_t)s * C + k) = v;
   }
 }
 
-// dw partials: block (token block, channel tile) sums dy[t][k] x[prev^j(t)][k]
-// over its tokens for every tap j; a second pass adds the blocks in order.
+// dw partials: per block of TOKB tokens and channel, sum_t dy[t] x[prev^j(t)]
+// in token order (fixed); each group of TG tokens takes the register window
+// when its taps allow.
 constexpr int TOKB = 256;
-template <int VW>
+template <int VW, int KT>
 __global__ __launch_bounds__(TH) void conv_dw_part(const int32_t* __restrict__ cprev, int N, int K,
                                                    const float* __restrict__ x, const float* __restrict__ dy, int C,
                                                    float* __restrict__ part) {
   typedef typename Vec<VW>::T V;
-  const int k = (blockIdx.y * TH + threadIdx.x) * VW, tb = blockIdx.x;
-  if (k >= C) return;
+  const int k0 = (blockIdx.y * TH + threadIdx.x) * VW, tb = blockIdx.x;
+  const bool live = k0 < C;
+  const int k = live ? k0 : C - VW;
   float acc[8][VW];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int e = 0; e < VW; ++e) acc[j][e] = 0.f;
-  const int t1 = min(N, (tb + 1) * TOKB);
-  for (int t = tb * TOKB; t < t1; ++t) {
-    const V g = *(const V*)(dy + (size_t)t * C + k);
-    const V x0 = *(const V*)(x + (size_t)t * C + k);
+  const int tend = min(N, (tb + 1) * TOKB);
+  for (int t0 = tb * TOKB; t0 < tend; t0 += TG) {
+    if (KT > 1 && t0 + TG <= tend && window_prev<KT>(cprev, N, t0)) {
+      V r[TG + KT - 1], g[TG];
 #pragma unroll
-    for (int e = 0; e < VW; ++e) acc[0][e] = fmaf(Vec<VW>::get(g, e), Vec<VW>::get(x0, e), acc[0][e]);
+      for (int i = 0; i < TG + KT - 1; ++i) r[i] = *(const V*)(x + (size_t)(t0 - (KT - 1) + i) * C + k);
 #pragma unroll
-    for (int j = 1; j < 8; ++j) {
-      if (j >= K) break;
-      const int q = cprev[(size_t)t * (K - 1) + (j - 1)];
-      const V xq = *(const V*)(x + (size_t)(q >= 0 ? q : t) * C + k);
+      for (int tt = 0; tt < TG; ++tt) g[tt] = *(const V*)(dy + (size_t)(t0 + tt) * C + k);
 #pragma unroll
-      for (int e = 0; e < VW; ++e) acc[j][e] = fmaf(Vec<VW>::get(g, e), q >= 0 ? Vec<VW>::get(xq, e) : 0.f, acc[j][e]);
+      for (int tt = 0; tt < TG; ++tt)
+#pragma unroll
+        for (int j = 0; j < KT; ++j)
+#pragma unroll
+          for (int e = 0; e < VW; ++e)
+            acc[j][e] = fmaf(Vec<VW>::get(g[tt], e), Vec<VW>::get(r[tt + KT - 1 - j], e), acc[j][e]);
+      continue;
+    }
+    const int t1 = min(tend, t0 + TG);
+    for (int t = t0; t < t1; ++t) {
+      const V g = *(const V*)(dy + (size_t)t * C + k);
+      const V x0 = *(const V*)(x + (size_t)t * C + k);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) acc[0][e] = fmaf(Vec<VW>::get(g, e), Vec<VW>::get(x0, e), acc[0][e]);
+#pragma unroll
+      for (int j = 1; j < 8; ++j) {
+        if (j >= K) break;
+        const int q = cprev[(size_t)t * (K - 1) + (j - 1)];
+        const V xq = *(const V*)(x + (size_t)(q >= 0 ? q : t) * C + k);
+#pragma unroll
+        for (int e = 0; e < VW; ++e)
+          acc[j][e] = fmaf(Vec<VW>::get(g, e), q >= 0 ? Vec<VW>::get(xq, e) : 0.f, acc[j][e]);
+      }
     }
   }
+  if (!live) return;
 #pragma unroll
   for (int e = 0; e < VW; ++e)
 #pragma unroll
@@ -400,20 +498,62 @@ extern "C" ta_status tree_scan_bwd(const ta_route* R, const void* droute, const 
   return TA_OK;
 }
 
+namespace {
+
+// The conv launches for channel width VW and register-window width KT
+// (conv_k when it is 2..4, else 0: gather only).
+template <int VW, int KT>
+void launch_conv_fwd(const ta_route* R, const RouteDev& d, const float* x, const float* w, int C, float* y,
+                     hipStream_t st) {
+  const int cb = (C / VW + ssm::TH - 1) / ssm::TH;
+  hipLaunchKernelGGL((ssm::conv_fwd<VW, KT>), dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, st,
+                     d.cprev, R->n_tokens, R->conv_k, x, w, C, y);
+}
+
+template <int VW, int KT>
+void launch_conv_bwd(const ta_route* R, const RouteDev& d, const float* x, const float* w, const float* dy, int C,
+                     float* dx, float* part, hipStream_t st) {
+  const int cb = (C / VW + ssm::TH - 1) / ssm::TH;
+  const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
+  hipLaunchKernelGGL((ssm::conv_dx<VW, KT>), dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, st,
+                     d.cprev, d.succ_ptr, d.succ, R->n_tokens, R->conv_k, dy, w, C, dx);
+  hipLaunchKernelGGL((ssm::conv_dw_part<VW, KT>), dim3(nb, cb), dim3(ssm::TH), 0, st, d.cprev, R->n_tokens, R->conv_k,
+                     x, dy, C, part);
+}
+
+template <int VW>
+void conv_fwd_k(const ta_route* R, const RouteDev& d, const float* x, const float* w, int C, float* y,
+                hipStream_t st) {
+  switch (R->conv_k) {
+    case 2: launch_conv_fwd<VW, 2>(R, d, x, w, C, y, st); break;
+    case 3: launch_conv_fwd<VW, 3>(R, d, x, w, C, y, st); break;
+    case 4: launch_conv_fwd<VW, 4>(R, d, x, w, C, y, st); break;
+    default: launch_conv_fwd<VW, 0>(R, d, x, w, C, y, st); break;
+  }
+}
+
+template <int VW>
+void conv_bwd_k(const ta_route* R, const RouteDev& d, const float* x, const float* w, const float* dy, int C,
+                float* dx, float* part, hipStream_t st) {
+  switch (R->conv_k) {
+    case 2: launch_conv_bwd<VW, 2>(R, d, x, w, dy, C, dx, part, st); break;
+    case 3: launch_conv_bwd<VW, 3>(R, d, x, w, dy, C, dx, part, st); break;
+    case 4: launch_conv_bwd<VW, 4>(R, d, x, w, dy, C, dx, part, st); break;
+    default: launch_conv_bwd<VW, 0>(R, d, x, w, dy, C, dx, part, st); break;
+  }
+}
+
+}  // namespace
+
 extern "C" ta_status tree_conv_fwd(const ta_route* R, const void* droute, const float* x, const float* w, int32_t C,
                                    float* y, hipStream_t stream) {
   if (!R || !droute || !x || !w || !y || C <= 0) return TA_EINVAL;
   if (R->n_tokens == 0) return TA_OK;
   const RouteDev d = dev_tables(R, droute);
-  if (C % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0) {
-    const int cb = (C / 4 + ssm::TH - 1) / ssm::TH;
-    hipLaunchKernelGGL(ssm::conv_fwd<4>, dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens,
-                       R->conv_k, x, w, C, y);
-  } else {
-    const int cb = (C + ssm::TH - 1) / ssm::TH;
-    hipLaunchKernelGGL(ssm::conv_fwd<1>, dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens,
-                       R->conv_k, x, w, C, y);
-  }
+  if (C % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0)
+    conv_fwd_k<4>(R, d, x, w, C, y, stream);
+  else
+    conv_fwd_k<1>(R, d, x, w, C, y, stream);
   TA_LAUNCH_CHECK();
   return TA_OK;
 }
@@ -427,23 +567,11 @@ extern "C" ta_status tree_conv_bwd(const ta_route* R, const void* droute, const 
   if (!ws || ws_bytes < need) return TA_ENOMEM;
   const RouteDev d = dev_tables(R, droute);
   const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
-  if (C % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)dy % 16 == 0 && (uintptr_t)dx % 16 == 0) {
-    const int cb = (C / 4 + ssm::TH - 1) / ssm::TH;
-    hipLaunchKernelGGL(ssm::conv_dx<4>, dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, stream, d.succ_ptr, d.succ,
-                       R->n_tokens, R->conv_k, dy, w, C, dx);
-    TA_LAUNCH_CHECK();
-    hipLaunchKernelGGL(ssm::conv_dw_part<4>, dim3(nb, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens, R->conv_k,
-                       x, dy, C, (float*)ws);
-    TA_LAUNCH_CHECK();
-  } else {
-    const int cb = (C + ssm::TH - 1) / ssm::TH;
-    hipLaunchKernelGGL(ssm::conv_dx<1>, dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, stream, d.succ_ptr, d.succ,
-                       R->n_tokens, R->conv_k, dy, w, C, dx);
-    TA_LAUNCH_CHECK();
-    hipLaunchKernelGGL(ssm::conv_dw_part<1>, dim3(nb, cb), dim3(ssm::TH), 0, stream, d.cprev, R->n_tokens, R->conv_k,
-                       x, dy, C, (float*)ws);
-    TA_LAUNCH_CHECK();
-  }
+  if (C % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)dy % 16 == 0 && (uintptr_t)dx % 16 == 0)
+    conv_bwd_k<4>(R, d, x, w, dy, C, dx, (float*)ws, stream);
+  else
+    conv_bwd_k<1>(R, d, x, w, dy, C, dx, (float*)ws, stream);
+  TA_LAUNCH_CHECK();
   hipLaunchKernelGGL(ssm::conv_dw_sum, dim3((C * R->conv_k + ssm::TH - 1) / ssm::TH), dim3(ssm::TH), 0, stream,
                      (const float*)ws, nb, C, R->conv_k, dw);
   TA_LAUNCH_CHECK();

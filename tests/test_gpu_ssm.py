@@ -57,7 +57,7 @@ def test_six_node_and_short_parent():
     run(W.Tree(np.array([-1, 0, 1, 0]), np.array([4, 1, 3, 2]), "short_parent"), 64, 4, 1)
 
 
-@pytest.mark.parametrize("K", [1, 3, 8])
+@pytest.mark.parametrize("K", [1, 2, 3, 8])
 def test_random_trees(K):
     rng = np.random.default_rng(10 + K)
     for c in range(3):
