@@ -190,6 +190,47 @@ def time_lmhead(pkg, tree, steps, warmup, dev, V=151936, Dm=1024, seed=9):
     return res
 
 
+def time_nll(pkg, tree, steps, warmup, dev, V=151936, seed=10):
+    """g/K weighted NLL over materialised fp32 logits [N, V] (the spine tree's
+    tokens, the Qwen3-0.6B vocabulary; logits ~ N(0, 1), uniform labels with
+    10% ignored): loss alone and loss + dlogits.  GB/s on the bytes each must
+    move: V * 4 per row for the loss (read once), 3 V * 4 with the gradient
+    (read twice: the row's max/sum, then softmax; dlogits written once)."""
+    import torch
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    N = plan.n_tokens
+    g = torch.Generator(device=dev).manual_seed(seed)
+    x = torch.randn(N, V, generator=g, device=dev)
+    labels = torch.randint(0, V, (N,), generator=g, device=dev, dtype=torch.int32)
+    labels[torch.rand(N, generator=g, device=dev) < 0.1] = -100
+    w = torch.from_numpy((plan.view()["g"] / plan.n_leaves).astype("float32")).to(dev)
+    loss = torch.zeros(1, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dx = torch.empty_like(x)
+
+    def timed(grad):
+        for _ in range(warmup):
+            pkg.tree_weighted_nll(x, labels, w, need_grad=grad, loss=loss, dlogits=dx if grad else None,
+                                  err_flag=err)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            pkg.tree_weighted_nll(x, labels, w, need_grad=grad, loss=loss, dlogits=dx if grad else None,
+                                  err_flag=err)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    fwd = timed(False)
+    both = timed(True)
+    row = V * 4
+    res = dict(n_tokens=N, vocab=V, logits_gb=N * row / 1e9, loss_ms=fwd, loss_GBps=N * row / (fwd * 1e-3) / 1e9,
+               loss_grad_ms=both, loss_grad_GBps=3 * N * row / (both * 1e-3) / 1e9)
+    del x, dx
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_ssm(pkg, tree, steps, warmup, dev, C=4096, K=4, seed=11):
     """Tree-routed scan and causal conv (fp32, [N, C]) over the tree's tokens:
     forward and backward of each, GB/s on the bytes each must move."""
@@ -323,7 +364,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--secondary", default="random_agentic_tree,varlen_forest,spine_partitioned_4096,lmhead,ssm,decode",
+    ap.add_argument("--secondary", default="random_agentic_tree,varlen_forest,spine_partitioned_4096,lmhead,nll,ssm,decode",
                     help="comma-separated secondary workloads to run after the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -364,6 +405,10 @@ def main():
             print("[bench] output layer + weighted NLL over the spine tree's tokens", flush=True)
             r = time_lmhead(pkg, spine, max(3, args.steps // 2), args.warmup, dev)
             extra["lmhead"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        if "nll" in chosen:
+            print("[bench] weighted NLL over materialised logits of the spine tree's tokens", flush=True)
+            r = time_nll(pkg, spine, args.steps, args.warmup, dev)
+            extra["nll"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         if "ssm" in chosen:
             print("[bench] tree-routed scan and causal conv over the spine tree's tokens", flush=True)
             r = time_ssm(pkg, spine, args.steps, args.warmup, dev)

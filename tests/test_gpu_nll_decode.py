@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("N,V", [(96, 256), (4, 151936), (33, 1000), (1, 1)])
+@pytest.mark.parametrize("N,V", [(96, 256), (4, 151936), (33, 1000), (7, 1001), (1, 1)])
 def test_nll_matches_oracle(N, V):
     print(f"[nll] N={N} V={V}", flush=True)
     logits, labels = W.nll_inputs(N + V, N, V)
