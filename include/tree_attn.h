@@ -292,7 +292,7 @@ ta_status tree_weighted_nll(ta_dtype dt, const void* logits, const int32_t* labe
  * order sum: bitwise reproducible).  lse: optional [N] fp32 output (natural
  * log).  dh [N, Dm] and dW [V, Dm] (bf16, overwritten): both NULL for the
  * forward only, else both set.  vocab_chunk: vocabulary rows per backward
- * chunk (0 picks about 256 MB of dS; rounded down to whole 256-row tiles).
+ * chunk (0 picks about 512 MB of dS; rounded down to whole 256-row tiles).
  * Dm must be a multiple of 32.  ws: tree_lmhead_nll_ws_bytes bytes.
  * Precision: products of bf16 values accumulate in fp32; dS is rounded to
  * bf16 for the two backward products.
