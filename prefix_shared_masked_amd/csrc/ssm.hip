@@ -147,6 +147,106 @@ __global__ __launch_bounds__(TH) void scan_walk_bwd(const int4* __restrict__ ch,
   }
 }
 
+// The two walks with the per-chunk state of a workgroup's channels kept in
+// LDS: one wavefront per WC channels, column `lane` of an [n_chunks][WC]
+// array, so a chunk whose parent is not the previous one reads the parent's
+// end state (forward) or adds into the parent's incoming gradient (backward)
+// without a round trip to memory.  Each lane touches only its own column (no
+// barrier); the arithmetic and its order are those of scan_walk /
+// scan_walk_bwd.  Used while n_chunks * WC floats fit in LDS_WALK_MAX bytes.
+constexpr int WC = 64;
+constexpr size_t LDS_WALK_MAX = 64 * 1024;
+
+__global__ __launch_bounds__(WC) void scan_walk_lds(const int4* __restrict__ ch, int n_chunks, const float* __restrict__ A,
+                                                    const float* __restrict__ H, int C, float* __restrict__ hin,
+                                                    float* __restrict__ hend) {
+  extern __shared__ float se[];  // [n_chunks][WC] end states
+  const int lane = threadIdx.x, k0 = blockIdx.x * WC + lane;
+  const bool live = k0 < C;
+  const int k = live ? k0 : C - 1;
+  // inputs of the next group of 8 chunks are fetched while this group's chain runs
+  float prev_end = 0.f, av[8], hv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = min(u, n_chunks - 1);
+    av[u] = A[(size_t)c * C + k];
+    hv[u] = H[(size_t)c * C + k];
+  }
+  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+    float an[8], hn[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = min(c0 + 8 + u, n_chunks - 1);
+      an[u] = A[(size_t)c * C + k];
+      hn[u] = H[(size_t)c * C + k];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u;
+      if (c >= n_chunks) break;
+      const int p = ch[c].z;
+      const float s = p < 0 ? 0.f : (p == c - 1 ? prev_end : se[p * WC + lane]);
+      prev_end = fmaf(av[u], s, hv[u]);
+      se[c * WC + lane] = prev_end;
+      if (live) {
+        hin[(size_t)c * C + k] = s;
+        hend[(size_t)c * C + k] = prev_end;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      av[u] = an[u];
+      hv[u] = hn[u];
+    }
+  }
+}
+
+__global__ __launch_bounds__(WC) void scan_walk_bwd_lds(const int4* __restrict__ ch, int n_chunks,
+                                                        const float* __restrict__ a, const float* __restrict__ U,
+                                                        const float* __restrict__ B, int C, float* __restrict__ gin) {
+  extern __shared__ float sg[];  // [n_chunks][WC] incoming gradients
+  const int lane = threadIdx.x, k0 = blockIdx.x * WC + lane;
+  const bool live = k0 < C;
+  const int k = live ? k0 : C - 1;
+  for (int c = 0; c < n_chunks; ++c) sg[c * WC + lane] = 0.f;
+  // inputs of the next group of 8 chunks are fetched while this group's chain runs
+  float uv[8], bv[8], af[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = max(n_chunks - 1 - u, 0);
+    uv[u] = U[(size_t)c * C + k];
+    bv[u] = B[(size_t)c * C + k];
+    af[u] = a[(size_t)ch[c].x * C + k];
+  }
+  for (int c1 = n_chunks - 1; c1 >= 0; c1 -= 8) {
+    float un[8], bn[8], fn[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = max(c1 - 8 - u, 0);
+      un[u] = U[(size_t)c * C + k];
+      bn[u] = B[(size_t)c * C + k];
+      fn[u] = a[(size_t)ch[c].x * C + k];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c1 - u;
+      if (c < 0) break;
+      const int p = ch[c].z;
+      if (p < 0) continue;
+      const float dh0 = fmaf(bv[u], sg[c * WC + lane], uv[u]);
+      sg[p * WC + lane] += af[u] * dh0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      uv[u] = un[u];
+      bv[u] = bn[u];
+      af[u] = fn[u];
+    }
+  }
+  if (live)
+    for (int c = 0; c < n_chunks; ++c) gin[(size_t)c * C + k] = sg[c * WC + lane];
+}
+
 __global__ __launch_bounds__(TH) void scan_apply_bwd(const int4* __restrict__ ch, const float* __restrict__ a,
                                                      const float* __restrict__ h, const float* __restrict__ g, int C,
                                                      const float* __restrict__ gin, float* __restrict__ da,
@@ -464,8 +564,13 @@ extern "C" ta_status tree_scan_fwd(const ta_route* R, const void* droute, const 
   const int cb = (C + ssm::TH - 1) / ssm::TH;
   hipLaunchKernelGGL(ssm::scan_reduce, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, b, C, A, H);
   TA_LAUNCH_CHECK();
-  hipLaunchKernelGGL(ssm::scan_walk, dim3(cb), dim3(ssm::TH), 0, stream, d.ch, R->n_chunks, (const float*)A,
-                     (const float*)H, C, hin, hend);
+  const size_t lds = (size_t)R->n_chunks * ssm::WC * sizeof(float);
+  if (lds <= ssm::LDS_WALK_MAX)
+    hipLaunchKernelGGL(ssm::scan_walk_lds, dim3((C + ssm::WC - 1) / ssm::WC), dim3(ssm::WC), lds, stream, d.ch,
+                       R->n_chunks, (const float*)A, (const float*)H, C, hin, hend);
+  else
+    hipLaunchKernelGGL(ssm::scan_walk, dim3(cb), dim3(ssm::TH), 0, stream, d.ch, R->n_chunks, (const float*)A,
+                       (const float*)H, C, hin, hend);
   TA_LAUNCH_CHECK();
   hipLaunchKernelGGL(ssm::scan_apply, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, b, C,
                      (const float*)hin, h);
@@ -489,8 +594,13 @@ extern "C" ta_status tree_scan_bwd(const ta_route* R, const void* droute, const 
   const int cb = (C + ssm::TH - 1) / ssm::TH;
   hipLaunchKernelGGL(ssm::scan_reduce_bwd, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, dh, C, U, B);
   TA_LAUNCH_CHECK();
-  hipLaunchKernelGGL(ssm::scan_walk_bwd, dim3(cb), dim3(ssm::TH), 0, stream, d.ch, R->n_chunks, a, (const float*)U,
-                     (const float*)B, C, gin);
+  const size_t lds = (size_t)R->n_chunks * ssm::WC * sizeof(float);
+  if (lds <= ssm::LDS_WALK_MAX)
+    hipLaunchKernelGGL(ssm::scan_walk_bwd_lds, dim3((C + ssm::WC - 1) / ssm::WC), dim3(ssm::WC), lds, stream, d.ch,
+                       R->n_chunks, a, (const float*)U, (const float*)B, C, gin);
+  else
+    hipLaunchKernelGGL(ssm::scan_walk_bwd, dim3(cb), dim3(ssm::TH), 0, stream, d.ch, R->n_chunks, a,
+                       (const float*)U, (const float*)B, C, gin);
   TA_LAUNCH_CHECK();
   hipLaunchKernelGGL(ssm::scan_apply_bwd, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, h, dh, C,
                      (const float*)gin, da, db);

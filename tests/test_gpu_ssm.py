@@ -65,6 +65,16 @@ def test_random_trees(K):
         run(t, 300, K, c)
 
 
+def test_many_chunks_walk_in_memory():
+    """More than 256 chunks: the chunk-tree walks keep their per-chunk state in
+    memory instead of LDS (a 300-node random tree, nodes of 1-12 tokens)."""
+    rng = np.random.default_rng(21)
+    t = W.random_tree(rng, 300, max_len=12, p_zero=0.0, n_roots=3)
+    plan = pkg.tree_plan(t.parent, t.seg_len)
+    assert pkg.tree_route(plan, 4).n_chunks > 256
+    run(t, 70, 4, 5)
+
+
 def test_long_nodes_several_chunks():
     run(W.Tree(np.array([-1, 0, 0, 1]), np.array([700, 300, 256, 513]), "long"), 129, 4, 3)
 
