@@ -8,24 +8,31 @@
 // (Tree Training post, sections 6.2 and 7: one forward of the shared prefix,
 // the branches' gradients add up at the ancestors).
 //
-// Three launches on one stream, no atomics, bitwise deterministic:
-//  1. fp16 copy of K (rotated with RoPE) and, with RoPE, a rotated bf16 K;
-//  2. dQ, query-stationary: one workgroup per (32-row query tile, KV head),
-//     one wavefront per query head, walking the forward's gathered key
-//     chunks.  P is recomputed from LSE; S^T, dP^T and dQ^T are MFMA tiles
-//     with the query on the lane, K^T read with the LDS transpose read.  It
-//     also writes D and an fp16 copy of the rotated Q for step 3;
-//  3. dK/dV, key-stationary: one workgroup per (node-aligned tile of at most
-//     128 keys, KV head), one wavefront per 32 keys.  Every query in
-//     [k0, kend) of the node's DFS interval reads every key of the tile
-//     (only a wavefront's diagonal block needs the causal compare), so Q and
-//     dO stream as contiguous 32-row blocks with no gather; each block is
-//     staged in LDS once and shared by the four wavefronts, and the loop runs
-//     over every query head of the GQA group, so the group's sum stays in
-//     registers.  Scores use the fp16 copies of rotated Q and K (finer
-//     rounding than bf16 for rotated values; same MFMA rate), so P matches
-//     the forward's.  K and V stay in registers; dV += P^T dO and
-//     dK += dS^T Q use the LDS transpose read of the staged blocks.
+// On one stream, no atomics, bitwise deterministic.  bf16 with the full
+// workspace (the dS path):
+//  1. preparation: fp16 copy of K times scale * log2(e) (rotated with RoPE);
+//     prep_kernel: fp16 copy of the rotated Q, -D and -LSE * log2(e);
+//  2. dK/dV, key-stationary, over the planner's work pieces: four wavefronts,
+//     each owning the dK/dV of up to 32 keys of one node (a sub-tile), over a
+//     common run of 32-row query blocks on the query-tile grid.  Every query
+//     of a node's DFS interval reads every key of the node, so Q and dO
+//     stream as contiguous blocks with no gather; each block is staged in LDS
+//     once for the four wavefronts, and the loop runs over every query head
+//     of the GQA group, so the group's sum stays in registers.  Scores use
+//     the fp16 copies of rotated Q and K (finer rounding than bf16 for
+//     rotated values; same MFMA rate), so P matches the forward's.  K and V
+//     stay in registers; dV += P^T dO and dK += dS^T Q use the LDS transpose
+//     read of the staged blocks.  The fp16 dS of every (query tile, sub-tile)
+//     block is stored for step 3, and sub-tiles cut over several query
+//     windows leave fp32 partials that dkv_sum_kernel adds in a fixed order;
+//  3. dQ = scale dS K from the stored dS (dq_ds_kernel), query-stationary
+//     over each query tile's list of sub-tiles.
+// With the smallest workspace the dQ kernel (dq_bf16_kernel) runs before
+// dK/dV instead, walks the forward's gathered key chunks and recomputes P
+// from LSE and dP (S^T, dP^T and dQ^T as MFMA tiles with the query on the
+// lane, K^T from the LDS transpose read); it also writes the fp16 rotated Q,
+// -D and -LSE * log2(e) that dK/dV reads.  The fp32 path keeps plain
+// reference kernels (a thread per query row / key).
 #include "common.h"
 #include "plan_internal.h"
 
@@ -609,9 +616,10 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   lds_copies_wait();
 
   agpr_fence8(dk, dv);
-  // Each wavefront owns its keys: a whole tile stores them (scaled, rotated
-  // back, bf16); a piece of a cut tile writes its raw accumulators to its
-  // partial slot for dkv_sum_kernel.
+  // Each wavefront owns its keys: a sub-tile read in one run stores them
+  // (scaled, rotated back, bf16); a run of a sub-tile cut over several
+  // windows writes its raw accumulators to its partial slot for
+  // dkv_sum_kernel.
   if (slot < 0) {
     store_dkv(P, kvh, kw, wkeys, half, col, dk, dv);
   } else if (wkeys > 0) {
