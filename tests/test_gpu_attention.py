@@ -121,6 +121,23 @@ def test_bf16_cut_key_tiles():
     close("dv", dv, ref["dv"], torch.bfloat16)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_bf16_random_sweep(seed):
+    """Random trees of every shape the workloads produce (chains, stars,
+    forests, one-token and zero-token nodes, nodes past one 128-key tile),
+    bf16 with and without RoPE, 8/2 and 32/8 heads, both backward paths,
+    against the float64 per-path oracle."""
+    rng = np.random.default_rng(300 + seed)
+    shape = ["random", "chain", "star"][seed % 3]
+    t = W.random_tree(rng, int(rng.integers(2, 40)), max_len=int(rng.integers(1, 300)), p_zero=0.1,
+                      n_roots=1 + seed % 3, shape=shape)
+    if t.n_tokens == 0:
+        return
+    Hq, Hkv = (32, 8) if seed % 2 and t.n_tokens <= 2500 else (8, 2)   # oracle time stays in seconds
+    run_case(t, Hq, Hkv, 128, torch.bfloat16, 10000.0 if seed % 4 < 2 else 0.0, seed=seed,
+             recompute_dq=seed % 5 == 4)
+
+
 def test_bf16_recompute_dq_path():
     """The smallest backward workspace: dQ recomputes S and dP (no stored dS)
     before dK/dV; same oracle bar, on trees with short and cut key tiles."""
