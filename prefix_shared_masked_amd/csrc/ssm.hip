@@ -381,17 +381,13 @@ __device__ __forceinline__ bool window_succ(const int32_t* __restrict__ cprev, c
   return __all(ok);
 }
 
+// dx of one group of TG tokens s0.. for this lane's channels.
 template <int VW, int KT>
-__global__ __launch_bounds__(TH) void conv_dx(const int32_t* __restrict__ cprev, const int32_t* __restrict__ sp,
-                                              const int32_t* __restrict__ sc, int N, int K, const float* __restrict__ dy,
-                                              const float* __restrict__ w, int C, float* __restrict__ dx) {
+__device__ __forceinline__ void conv_dx_group(const int32_t* __restrict__ cprev, const int32_t* __restrict__ sp,
+                                              const int32_t* __restrict__ sc, int N, int K,
+                                              const float* __restrict__ dy, const float (&wr)[8][VW], int C, int k,
+                                              bool live, int s0, float* __restrict__ dx) {
   typedef typename Vec<VW>::T V;
-  const int k0 = (blockIdx.y * TH + threadIdx.x) * VW;
-  const bool live = k0 < C;
-  const int k = live ? k0 : C - VW;
-  float wr[8][VW];
-  load_taps<VW>(w, k, K, wr);
-  const int s0 = blockIdx.x * TG;
   if (KT > 1 && window_succ<KT>(cprev, sp, N, s0)) {
     V r[TG + KT - 1];  // rows s0 .. s0 + TG + KT - 2
 #pragma unroll
@@ -430,18 +426,66 @@ __global__ __launch_bounds__(TH) void conv_dx(const int32_t* __restrict__ cprev,
   }
 }
 
-// dw partials: per block of TOKB tokens and channel, sum_t dy[t] x[prev^j(t)]
-// in token order (fixed); each group of TG tokens takes the register window
-// when its taps allow.
+// dw terms of one group of tokens t0 .. min(t0 + TG, tend) - 1: acc[j] +=
+// dy[t] x[prev^j(t)] in token order.
+template <int VW, int KT>
+__device__ __forceinline__ void conv_dw_group(const int32_t* __restrict__ cprev, int N, int K,
+                                              const float* __restrict__ x, const float* __restrict__ dy, int C, int k,
+                                              int t0, int tend, float (&acc)[8][VW]) {
+  typedef typename Vec<VW>::T V;
+  if (KT > 1 && t0 + TG <= tend && window_prev<KT>(cprev, N, t0)) {
+    V r[TG + KT - 1], g[TG];
+#pragma unroll
+    for (int i = 0; i < TG + KT - 1; ++i) r[i] = *(const V*)(x + (size_t)(t0 - (KT - 1) + i) * C + k);
+#pragma unroll
+    for (int tt = 0; tt < TG; ++tt) g[tt] = *(const V*)(dy + (size_t)(t0 + tt) * C + k);
+#pragma unroll
+    for (int tt = 0; tt < TG; ++tt)
+#pragma unroll
+      for (int j = 0; j < KT; ++j)
+#pragma unroll
+        for (int e = 0; e < VW; ++e)
+          acc[j][e] = fmaf(Vec<VW>::get(g[tt], e), Vec<VW>::get(r[tt + KT - 1 - j], e), acc[j][e]);
+    return;
+  }
+  const int t1 = min(tend, t0 + TG);
+  for (int t = t0; t < t1; ++t) {
+    const V g = *(const V*)(dy + (size_t)t * C + k);
+    const V x0 = *(const V*)(x + (size_t)t * C + k);
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[0][e] = fmaf(Vec<VW>::get(g, e), Vec<VW>::get(x0, e), acc[0][e]);
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      if (j >= K) break;
+      const int q = cprev[(size_t)t * (K - 1) + (j - 1)];
+      const V xq = *(const V*)(x + (size_t)(q >= 0 ? q : t) * C + k);
+#pragma unroll
+      for (int e = 0; e < VW; ++e)
+        acc[j][e] = fmaf(Vec<VW>::get(g, e), q >= 0 ? Vec<VW>::get(xq, e) : 0.f, acc[j][e]);
+    }
+  }
+}
+
+// The conv backward in one pass over x and dy.  dx[s] = sum_j w[j] dy[t] over
+// the (t, j) with prev^j(t) = s (the inverse table: sp / sc, codes t*K + j
+// ordered by t); window: every token s of a group has exactly the K - 1
+// successors s + 1 .. s + K - 1 (prev^j(s + j) = s and no other), so dx[s] =
+// sum_j w[j] dy[s + j] from TG + K - 1 rows.  dw partials: per block of TOKB
+// tokens and channel, sum_t dy[t] x[prev^j(t)] in token order (fixed).  A
+// block walks its TOKB tokens group by group, each group's dx and then its
+// dw terms, so the dy rows the two read are fetched from HBM once.
 constexpr int TOKB = 256;
 template <int VW, int KT>
-__global__ __launch_bounds__(TH) void conv_dw_part(const int32_t* __restrict__ cprev, int N, int K,
-                                                   const float* __restrict__ x, const float* __restrict__ dy, int C,
-                                                   float* __restrict__ part) {
-  typedef typename Vec<VW>::T V;
+__global__ __launch_bounds__(TH) void conv_bwd(const int32_t* __restrict__ cprev, const int32_t* __restrict__ sp,
+                                               const int32_t* __restrict__ sc, int N, int K,
+                                               const float* __restrict__ x, const float* __restrict__ dy,
+                                               const float* __restrict__ w, int C, float* __restrict__ dx,
+                                               float* __restrict__ part) {
   const int k0 = (blockIdx.y * TH + threadIdx.x) * VW, tb = blockIdx.x;
   const bool live = k0 < C;
   const int k = live ? k0 : C - VW;
+  float wr[8][VW];
+  load_taps<VW>(w, k, K, wr);
   float acc[8][VW];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -449,37 +493,8 @@ __global__ __launch_bounds__(TH) void conv_dw_part(const int32_t* __restrict__ c
     for (int e = 0; e < VW; ++e) acc[j][e] = 0.f;
   const int tend = min(N, (tb + 1) * TOKB);
   for (int t0 = tb * TOKB; t0 < tend; t0 += TG) {
-    if (KT > 1 && t0 + TG <= tend && window_prev<KT>(cprev, N, t0)) {
-      V r[TG + KT - 1], g[TG];
-#pragma unroll
-      for (int i = 0; i < TG + KT - 1; ++i) r[i] = *(const V*)(x + (size_t)(t0 - (KT - 1) + i) * C + k);
-#pragma unroll
-      for (int tt = 0; tt < TG; ++tt) g[tt] = *(const V*)(dy + (size_t)(t0 + tt) * C + k);
-#pragma unroll
-      for (int tt = 0; tt < TG; ++tt)
-#pragma unroll
-        for (int j = 0; j < KT; ++j)
-#pragma unroll
-          for (int e = 0; e < VW; ++e)
-            acc[j][e] = fmaf(Vec<VW>::get(g[tt], e), Vec<VW>::get(r[tt + KT - 1 - j], e), acc[j][e]);
-      continue;
-    }
-    const int t1 = min(tend, t0 + TG);
-    for (int t = t0; t < t1; ++t) {
-      const V g = *(const V*)(dy + (size_t)t * C + k);
-      const V x0 = *(const V*)(x + (size_t)t * C + k);
-#pragma unroll
-      for (int e = 0; e < VW; ++e) acc[0][e] = fmaf(Vec<VW>::get(g, e), Vec<VW>::get(x0, e), acc[0][e]);
-#pragma unroll
-      for (int j = 1; j < 8; ++j) {
-        if (j >= K) break;
-        const int q = cprev[(size_t)t * (K - 1) + (j - 1)];
-        const V xq = *(const V*)(x + (size_t)(q >= 0 ? q : t) * C + k);
-#pragma unroll
-        for (int e = 0; e < VW; ++e)
-          acc[j][e] = fmaf(Vec<VW>::get(g, e), q >= 0 ? Vec<VW>::get(xq, e) : 0.f, acc[j][e]);
-      }
-    }
+    conv_dx_group<VW, KT>(cprev, sp, sc, N, K, dy, wr, C, k, live, t0, dx);
+    conv_dw_group<VW, KT>(cprev, N, K, x, dy, C, k, t0, tend, acc);
   }
   if (!live) return;
 #pragma unroll
@@ -625,10 +640,8 @@ void launch_conv_bwd(const ta_route* R, const RouteDev& d, const float* x, const
                      float* dx, float* part, hipStream_t st) {
   const int cb = (C / VW + ssm::TH - 1) / ssm::TH;
   const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
-  hipLaunchKernelGGL((ssm::conv_dx<VW, KT>), dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, st,
-                     d.cprev, d.succ_ptr, d.succ, R->n_tokens, R->conv_k, dy, w, C, dx);
-  hipLaunchKernelGGL((ssm::conv_dw_part<VW, KT>), dim3(nb, cb), dim3(ssm::TH), 0, st, d.cprev, R->n_tokens, R->conv_k,
-                     x, dy, C, part);
+  hipLaunchKernelGGL((ssm::conv_bwd<VW, KT>), dim3(nb, cb), dim3(ssm::TH), 0, st, d.cprev, d.succ_ptr, d.succ,
+                     R->n_tokens, R->conv_k, x, dy, w, C, dx, part);
 }
 
 template <int VW>
