@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int32_t kChunk = 256;  // tokens per scan chunk
+constexpr int32_t kChunk = 128;  // tokens per scan chunk (256: 10% slower scans on the spine tree, 64: the walk dominates)
 
 ta_status build_route(const ta_plan* p, int32_t K, ta_route* R) {
   const int32_t n = p->n_nodes, N = p->n_tokens;

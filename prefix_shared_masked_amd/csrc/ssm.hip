@@ -3,7 +3,7 @@
 //
 // Scan h_t = a_t h_prev(t) + b_t, prev(t) following the root-to-token path
 // (section 9.1: a chunk starts from its parent's end state).  Chunks of up to
-// 256 tokens form a tree (parent = the previous chunk of the node, or the
+// 128 tokens form a tree (parent = the previous chunk of the node, or the
 // last chunk of the nearest ancestor holding tokens).  Three passes, all with
 // consecutive lanes on consecutive channels, so every row access is
 // coalesced:

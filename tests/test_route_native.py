@@ -62,9 +62,11 @@ def test_long_nodes_are_chunked():
     t = W.Tree(np.array([-1, 0, 0]), np.array([700, 300, 256]), "long")
     check(t, 4)
     plan = pkg.tree_plan(t.parent, t.seg_len)
-    ch = pkg.tree_route(plan, 4).view()["chunks"]
-    assert ch[:, 1].tolist() == [256, 256, 188, 256, 44, 256]
-    assert ch[:, 2].tolist() == [-1, 0, 1, 2, 3, 2]
+    r = pkg.tree_route(plan, 4)
+    ch = r.view()["chunks"]
+    assert r.chunk == 128
+    assert ch[:, 1].tolist() == [128, 128, 128, 128, 128, 60, 128, 128, 44, 128, 128]
+    assert ch[:, 2].tolist() == [-1, 0, 1, 2, 3, 4, 5, 6, 7, 5, 9]
 
 
 def test_spine_tree():
