@@ -89,3 +89,40 @@ def test_decode_32k_full_batch():
     """One of the decode workloads at full size: B = 8 items of 32K keys,
     32 query / 8 KV heads; checks every (item, head) against the oracle."""
     _decode_case([32768] * 8, 32, 8, 0, 4, gap=0)
+
+
+@pytest.mark.timeout(600)
+def test_decode_256k_sampled():
+    """The largest decode workload in the launch configuration the benchmark
+    times: B = 8 items of 256K keys each (8.6 GB of bf16 K/V), 32 query / 8 KV
+    heads, the default split count and workspace.  Inputs come from a seeded
+    device generator; two items x two KV heads (their four query heads each)
+    are checked against the oracle on those rows alone."""
+    B, Hq, Hkv, d, L = 8, 32, 8, 128, 1 << 18
+    print(f"[decode] B={B} L={L} sampled", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    q = torch.randn(B, Hq, d, generator=g, device=DEV).bfloat16()
+    k = torch.randn(B * L, Hkv, d, generator=g, device=DEV).bfloat16()
+    v = torch.randn(B * L, Hkv, d, generator=g, device=DEV).bfloat16()
+    span_ptr = torch.arange(B + 1, dtype=torch.int32, device=DEV)
+    spans = torch.stack([torch.arange(B, dtype=torch.int32) * L, torch.full((B,), L, dtype=torch.int32)], 1)
+    spans = spans.contiguous().to(DEV)
+    nbytes, n_splits = pkg.decode_ws_bytes(B, Hq, d, L)
+    assert n_splits > 1
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    o, lse = pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L, ws=ws)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for b in (0, B - 1):
+        for kvh in (0, 5):
+            hs = slice(kvh * G, (kvh + 1) * G)
+            qs = q[b:b + 1, hs].float().cpu().double().numpy()
+            ks = k[b * L:(b + 1) * L, kvh:kvh + 1].float().cpu().double().numpy()
+            vs = v[b * L:(b + 1) * L, kvh:kvh + 1].float().cpu().double().numpy()
+            ro, rl = oracle.decode_attention(qs, ks, vs, np.array([0, 1], np.int32), np.array([[0, L]], np.int32))
+            got = o[b, hs].float().cpu().numpy()
+            err = np.abs(got - ro[0])
+            assert (err <= 2e-2 + 1e-2 * np.abs(ro[0])).all(), (b, kvh, float(err.max()))
+            assert np.abs(lse[b, hs].cpu().numpy() - rl[0]).max() <= 1e-3, (b, kvh)
+    del k, v, ws
+    torch.cuda.empty_cache()
