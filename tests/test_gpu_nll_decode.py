@@ -23,6 +23,39 @@ def test_nll_matches_oracle(N, V):
     assert int(err.item()) == 0
 
 
+@pytest.mark.timeout(600)
+def test_nll_full_size():
+    """The NLL workload the benchmark times: the spine tree's 16,352 tokens
+    over the 151,936-word vocabulary (9.9 GB of fp32 logits from a seeded
+    device generator, 10% of labels ignored, w = g/K), loss and dlogits
+    compared with the oracle on every row, streamed to the host in blocks."""
+    tree = W.spine_tree()
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    N, V = plan.n_tokens, 151936
+    print(f"[nll] N={N} V={V} full", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(10)
+    x = torch.randn(N, V, generator=g, device=DEV)
+    labels = torch.randint(0, V, (N,), generator=g, device=DEV, dtype=torch.int32)
+    labels[torch.rand(N, generator=g, device=DEV) < 0.1] = -100
+    w = (plan.view()["g"] / plan.n_leaves).astype(np.float32)
+    loss, dl, err = pkg.tree_weighted_nll(x, labels, torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    y = labels.cpu().numpy()
+    total, worst = 0.0, 0.0
+    for r0 in range(0, N, 1024):
+        r1 = min(N, r0 + 1024)
+        rl, rdl, _ = oracle.weighted_nll(x[r0:r1].cpu().numpy(), y[r0:r1], w[r0:r1])
+        total += rl
+        worst = max(worst, float(np.abs(dl[r0:r1].cpu().numpy() - rdl).max()))
+        if r0 % 4096 == 0:
+            print(f"[nll] rows {r0}..{r1} checked", flush=True)
+    assert abs(loss.item() - total) <= 1e-5 * max(1.0, abs(total)), (loss.item(), total)
+    assert worst <= 1e-6, worst
+    del x, dl
+    torch.cuda.empty_cache()
+
+
 def test_nll_six_node_weights_and_bad_label():
     t = W.six_node_tree(16)
     plan = pkg.tree_plan(t.parent, t.seg_len)
