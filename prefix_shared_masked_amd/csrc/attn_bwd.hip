@@ -116,12 +116,15 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
   __shared__ __attribute__((aligned(1024))) bf16 sV[2][BN * D];
   __shared__ __attribute__((aligned(16))) int sJ[2][BN];
   __shared__ __attribute__((aligned(16))) int sE[2][BN];
+  __shared__ double sInv[D / 2];
 
   const int kvh = blockIdx.x % P.Hkv;
   const int tile = as_const(P.fq_order)[blockIdx.x / P.Hkv];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int hsub = blockIdx.y * 4 + wave;
+  rope_inv_table(sInv, D / 2, D, P.rope_base);
+  __syncthreads();
   const bool active = hsub < P.G;
   const int h = kvh * P.G + (active ? hsub : 0);
   const int qi = P.q0 + tile * BM + col;
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
         float x1 = qvalid ? (float)t1[e] : 0.f, x2 = qvalid ? (float)t2[e] : 0.f;
         if (rot) {
           float sn, cs;
-          rope_sincos(p, s * 16 + half * 8 + e, D, P.rope_base, &sn, &cs);
+          rope_sincos_at(p, sInv[s * 16 + half * 8 + e], &sn, &cs);
           const float y1 = x1 * cs - x2 * sn;
           x2 = x2 * cs + x1 * sn;
           x1 = y1;
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float sn, cs;
-          rope_sincos(p, dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3), D, P.rope_base, &sn, &cs);
+          rope_sincos_at(p, sInv[dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3)], &sn, &cs);
           const float y1 = g[dt][r], y2 = g[dt + 2][r];
           g[dt][r] = y1 * cs + y2 * sn;
           g[dt + 2][r] = y2 * cs - y1 * sn;
@@ -330,8 +333,9 @@ constexpr int PART_WAVE = 2 * 4 * 16 * 64;
 
 // dK (scaled, rotated back by -pos) and dV of one key in bf16, dimensions
 // dt*32 + col for dt = 0..3 (the rotate-half partner of d is tile dt + 2).
-__device__ __forceinline__ void store_key(const KVParams& P, int kvh, int key, int col, float (&g)[4],
-                                          const float (&v)[4]) {
+// inv: the inverse frequencies of dimensions col and 32 + col.
+__device__ __forceinline__ void store_key(const KVParams& P, int kvh, int key, int col, const double (&inv)[2],
+                                          float (&g)[4], const float (&v)[4]) {
   const size_t o = ((size_t)key * P.Hkv + kvh) * D;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) g[dt] *= P.scale;
@@ -339,7 +343,7 @@ __device__ __forceinline__ void store_key(const KVParams& P, int kvh, int key, i
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       float sn, cs;
-      rope_sincos(P.pos[key], dt * 32 + col, D, P.rope_base, &sn, &cs);
+      rope_sincos_at(P.pos[key], inv[dt], &sn, &cs);
       const float y1 = g[dt], y2 = g[dt + 2];
       g[dt] = y1 * cs + y2 * sn;
       g[dt + 2] = y2 * cs - y1 * sn;
@@ -356,13 +360,15 @@ __device__ __forceinline__ void store_key(const KVParams& P, int kvh, int key, i
 // r of tile dt <-> key kw + 8*(r/4) + 4*half + r%4, d = dt*32 + col.
 __device__ __forceinline__ void store_dkv(const KVParams& P, int kvh, int kw, int wkeys, int half, int col,
                                           const f32x16 (&dk)[4], const f32x16 (&dv)[4]) {
+  const double inv[2] = {P.rope_base > 0.f ? rope_inv(col, D, P.rope_base) : 0.0,
+                         P.rope_base > 0.f ? rope_inv(32 + col, D, P.rope_base) : 0.0};
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
     if (kr >= wkeys) continue;
     float g[4] = {dk[0][r], dk[1][r], dk[2][r], dk[3][r]};
     const float v[4] = {dv[0][r], dv[1][r], dv[2][r], dv[3][r]};
-    store_key(P, kvh, kw + kr, col, g, v);
+    store_key(P, kvh, kw + kr, col, inv, g, v);
   }
 }
 
@@ -675,13 +681,15 @@ __global__ __launch_bounds__(256) void dkv_sum_kernel(KVParams P) {
     }
   }
   // register 4g + j of tile dt <-> key kw + 8g + 4*half + j
+  const double inv[2] = {P.rope_base > 0.f ? rope_inv(lane & 31, D, P.rope_base) : 0.0,
+                         P.rope_base > 0.f ? rope_inv(32 + (lane & 31), D, P.rope_base) : 0.0};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int kr = 8 * g + 4 * (lane >> 5) + j;
     if (kr >= wkeys) continue;
     float gk[4] = {sk[0][j], sk[1][j], sk[2][j], sk[3][j]};
     const float gv[4] = {sv[0][j], sv[1][j], sv[2][j], sv[3][j]};
-    store_key(P, kvh, kw + kr, lane & 31, gk, gv);
+    store_key(P, kvh, kw + kr, lane & 31, inv, gk, gv);
   }
 }
 
@@ -710,6 +718,9 @@ struct PrepParams {
 };
 
 __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
+  __shared__ double sInv[D / 2];
+  rope_inv_table(sInv, D / 2, D, P.rope_base);
+  __syncthreads();
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t pr = gid >> 3;
   const int j = (int)(gid & 7);
@@ -729,7 +740,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
     float x1 = (float)q1[e], x2 = (float)q2[e];
     if (rot) {
       float sn, cs;
-      rope_sincos(p, 8 * j + e, D, P.rope_base, &sn, &cs);
+      rope_sincos_at(p, sInv[8 * j + e], &sn, &cs);
       const float y1 = x1 * cs - x2 * sn;
       x2 = x2 * cs + x1 * sn;
       x1 = y1;
@@ -774,9 +785,11 @@ constexpr int DS_COPIES = 4;  // copies per wavefront per entry: two of K rows, 
 __global__ __launch_bounds__(256, 3) void dq_ds_kernel(DSParams P) {
   __shared__ __attribute__((aligned(1024))) f16 sK[3][SUB * D];
   __shared__ __attribute__((aligned(1024))) f16 sS[3][4][SUB * SUB];
+  __shared__ double sInv[D / 2];  // read after the loop's barriers
 
   const int kvh = blockIdx.x % P.Hkv;
   const int tile = as_const(P.dq_order)[blockIdx.x / P.Hkv];
+  rope_inv_table(sInv, D / 2, D, P.rope_base);
   const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hsub = blockIdx.y * 4 + w;
@@ -859,7 +872,7 @@ __global__ __launch_bounds__(256, 3) void dq_ds_kernel(DSParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float sn, cs;
-          rope_sincos(p, dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3), D, P.rope_base, &sn, &cs);
+          rope_sincos_at(p, sInv[dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3)], &sn, &cs);
           const float y1 = gq[dt][r], y2 = gq[dt + 2][r];
           gq[dt][r] = y1 * cs + y2 * sn;
           gq[dt + 2][r] = y2 * cs - y1 * sn;

@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
   __shared__ __attribute__((aligned(1024))) bf16 sV[2][BN * D];
   __shared__ __attribute__((aligned(16))) int sJ[2][BN];
   __shared__ __attribute__((aligned(16))) int sE[2][BN];
+  __shared__ double sInv[D / 2];
 
   const int kvh = blockIdx.x % P.Hkv;
   const int tile = as_const(P.fq_order)[blockIdx.x / P.Hkv];
@@ -164,6 +165,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
   const int col = lane & 31, half = lane >> 5;
   const int hsub = blockIdx.y * 4 + wave;
   const bool active = hsub < P.G;
+  rope_inv_table(sInv, D / 2, D, P.rope_base);
+  __syncthreads();
   const int h = kvh * P.G + (active ? hsub : 0);
   const int qi = P.q0 + tile * BM + col;
   const bool qvalid = qi < P.N;
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
         float x1 = qvalid ? (float)t1[e] : 0.f, x2 = qvalid ? (float)t2[e] : 0.f;
         if (rot) {
           float sn, cs;
-          rope_sincos(p, s * 16 + half * 8 + e, D, P.rope_base, &sn, &cs);
+          rope_sincos_at(p, sInv[s * 16 + half * 8 + e], &sn, &cs);
           const float y1 = x1 * cs - x2 * sn;
           x2 = x2 * cs + x1 * sn;
           x1 = y1;

@@ -98,12 +98,17 @@ __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_e
 // Rotary angle pos * base^(-2i/d): the product and the reduction by
 // quadrants (multiples of pi/2) are done in double precision, so long depths
 // lose no accuracy; sin and cos of the remainder r in [-pi/4, pi/4] come from
-// their Taylor series (truncation error below 2e-9 at |r| = pi/4).
-__device__ __forceinline__ void rope_sincos(int pos, int i, int d, float base, float* s, float* c) {
-  const double inv = exp2(-(2.0 * i / d) * log2((double)base));
+// their Taylor series (truncation error below 2e-9 at |r| = pi/4).  The
+// inverse frequency base^(-2i/d) depends on i alone: kernels that rotate many
+// elements compute it once per dimension (rope_inv, into LDS or a register)
+// and then call rope_sincos_at; the two paths give bitwise the same values.
+__device__ __forceinline__ double rope_inv(int i, int d, float base) {
+  return exp2(-(2.0 * i / d) * log2((double)base));
+}
+__device__ __forceinline__ void rope_sincos_at(int pos, double inv, float* s, float* c) {
   const double ang = (double)pos * inv;
   const double half_pi = 1.5707963267948966;
-  const double kq = rint(ang / half_pi);
+  const double kq = rint(ang * 0.63661977236758134);  // 2/pi: a multiply, not a division
   const float r = (float)(ang - kq * half_pi);
   const float r2 = r * r;
   const float sr = r * (1.f + r2 * (-1.f / 6 + r2 * (1.f / 120 + r2 * (-1.f / 5040 + r2 * (1.f / 362880)))));
@@ -111,6 +116,14 @@ __device__ __forceinline__ void rope_sincos(int pos, int i, int d, float base, f
   const int q = (int)((long long)kq & 3);
   *s = q == 0 ? sr : q == 1 ? cr : q == 2 ? -sr : -cr;
   *c = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
+}
+__device__ __forceinline__ void rope_sincos(int pos, int i, int d, float base, float* s, float* c) {
+  rope_sincos_at(pos, rope_inv(i, d, base), s, c);
+}
+// The inverse frequencies of dimensions 0 .. n-1 into LDS by the first n
+// threads of the workgroup (the caller puts a barrier before reading them).
+__device__ __forceinline__ void rope_inv_table(double* tab, int n, int d, float base) {
+  if ((int)threadIdx.x < n) tab[threadIdx.x] = base > 0.f ? rope_inv(threadIdx.x, d, base) : 0.0;
 }
 
 // Gathered key chunk of the plan: slot v -> packed key index and the end of
