@@ -54,14 +54,13 @@ struct DQParams {
   const bf16* dO;
   const float* lse;
   bf16* dq;
-  float* nd;    // [Hq, N] out: -D
-  float* nl2;   // [Hq, N] out: -LSE * log2(e)
+  float* nld;   // [Hq][nqb][64] out: per 32-row query block, -LSE * log2(e) of its rows, then -D
   f16* qs;      // [N, Hq, d] out: fp16 copy of Q (rotated when RoPE is on)
   const int32_t* pos;
   const int32_t* fq_ptr;
   const int32_t* fq_chunk;
   const int32_t* fq_order;
-  int N, Hq, Hkv, G;
+  int N, Hq, Hkv, G, nqb;
   int q0;  // first query row (rows below are a key-only prefix)
   float scale, scale_log2, rope_base;
 };
@@ -176,11 +175,12 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
     Di = dsum + __shfl_xor(dsum, 32);
     if (!qvalid) Di = 0.f;
     lse_i = qvalid ? P.lse[(size_t)h * P.N + qi] * TA_LOG2E : 0.f;
-    if (active && qvalid) {
-      if (half == 0) {
-        P.nd[(size_t)h * P.N + qi] = -Di;
-        P.nl2[(size_t)h * P.N + qi] = -lse_i;
-      }
+    // rows past the last token get zeros: the dK/dV kernel stages whole
+    // 32-row blocks and masks those rows, and 0 * (finite) stays 0
+    if (active && half == 0) {
+      float* rec = P.nld + ((size_t)h * P.nqb + tile) * (2 * BM);
+      rec[col] = qvalid ? -lse_i : 0.f;
+      rec[BM + col] = qvalid ? -Di : 0.f;
     }
   }
 
@@ -305,8 +305,7 @@ struct KVParams {
   const f16* k;   // fp16 copy of K (rotated when RoPE is on) times scale * log2(e)
   const bf16* v;
   const bf16* dO;
-  const float* nl2;  // -LSE * log2(e), [Hq, N]
-  const float* nd;   // -D, [Hq, N]
+  const float* nld;  // [Hq][nqb][64]: per 32-row query block, -LSE * log2(e) of its rows, then -D
   bf16* dk;
   bf16* dv;
   const int32_t* pos;
@@ -317,6 +316,7 @@ struct KVParams {
   f16* ds_spare;      // a 32 x 32 block that absorbs the stores of blocks a wavefront does not own
   int n_sum;          // cut sub-tiles
   int n_dsblk;
+  int nqb;            // 32-row query blocks from q0 (the plan's query tiles)
   int N, Hq, Hkv, G;
   int q0;  // first query row (rows below are a key-only prefix)
   float scale, scale_log2, rope_base;
@@ -446,58 +446,66 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     }
 
   // Items are (32-row block, query head) of the piece's rows [qlo, qhi),
-  // blocks qlo + 32i from the end down and the heads of the group innermost:
-  // the workgroups resident on an XCD share a KV head and mostly the same
-  // rows (pieces are listed by length and last row), so they stream the same
-  // rows at about the same time and one fetch serves them from L2.  All four
-  // wavefronts share each staged block.  Each wavefront issues exactly five
-  // copies per block: two 1 KiB copies of Q rows, two of dO rows (rows
-  // 4i..4i+3 for i = w, w + 4), and sixteen LSE or D values (wavefront w: LSE
-  // rows 16w.. for w < 2, D rows 16(w-2).. otherwise).  Rows past qhi copy
-  // the last row and, like every row outside a wavefront's [key, rhi), are
-  // masked to P = 0 below, so they contribute nothing.
+  // blocks qlo + 32 bi from the end down and the heads of the group
+  // innermost: the workgroups resident on an XCD share a KV head and mostly
+  // the same rows (pieces are listed by length and last row), so they stream
+  // the same rows at about the same time and one fetch serves them from L2.
+  // All four wavefronts share each staged block.  Rows past qhi (and past the
+  // last token, clamped to it) are masked to P = 0 below, like every row
+  // outside a wavefront's [key, rhi), so they contribute nothing.
+  const int G = P.G;
   const int nblk = (qhi - qlo + SUB - 1) / SUB;   // >= 1: the plan gives every piece a query row
-  const int nitem = P.G * nblk;
-  auto stage = [&](int it, char* base) {
-    const int h = kvh * P.G + it % P.G;
-    const int qb = qlo + SUB * (nblk - 1 - it / P.G);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = w + 4 * k;
-      const int row = 4 * i + (lane >> 4);
-      const size_t off = ((size_t)min(qb + row, qhi - 1) * P.Hq + h) * D + (((lane & 15) ^ swz(row & 15)) << 3);
-      copy16_to_lds(P.q + off, base + L::Q16 + 4 * i * D * 2);
-      copy16_to_lds(P.dO + off, base + L::DO + 4 * i * D * 2);
-    }
-    if (lane < 16) {
-      const int r = min(qb + 16 * (w & 1) + lane, qhi - 1);
-      copy4_to_lds((w < 2 ? P.nl2 : P.nd) + (size_t)h * P.N + r, base + L::LS + 64 * w);
-    }
+  const int nitem = G * nblk;
+  // Staging: wavefront w copies rows 4i + lane/16 (i = w and w + 4) of the
+  // block's fp16 Q and bf16 dO (a swizzled 16-byte piece per lane), and
+  // wavefront 0 also the block's 32 -LSE * log2(e) and 32 -D values (one
+  // 256-byte record).  The per-lane offsets inside a block are fixed, so only
+  // the scalar base (block, head) changes from item to item.
+  const int rowA = 4 * w + (lane >> 4);  // row of copy i = w; copy i = w + 4 is rowA + 16 (same swizzle)
+  const uint32_t piece = (uint32_t)(((lane & 15) ^ swz(rowA & 15)) << 4);
+  const uint32_t rstride = (uint32_t)P.Hq * (D * 2);
+  const uint32_t lds0 = lds_addr(smem);
+  auto stage = [&](int bi, int g, int b) {
+    const int qb = qlo + SUB * bi;
+    const int h = kvh * G + g;
+    const int lim = P.N - 1 - qb;
+    const uint32_t vA = (uint32_t)min(rowA, lim) * rstride + piece;
+    const uint32_t vB = (uint32_t)min(rowA + 16, lim) * rstride + piece;
+    const size_t off = ((size_t)qb * P.Hq + h) * (D * 2);
+    const char* sq = (const char*)P.q + off;
+    const char* so = (const char*)P.dO + off;
+    const uint32_t lb = lds0 + b * L::BYTES;
+    copy16_to_lds_s(sq, vA, lb + L::Q16 + w * 1024);
+    copy16_to_lds_s(sq, vB, lb + L::Q16 + (w + 4) * 1024);
+    copy16_to_lds_s(so, vA, lb + L::DO + w * 1024);
+    copy16_to_lds_s(so, vB, lb + L::DO + (w + 4) * 1024);
+    if (w == 0) copy4_to_lds_s(P.nld + ((size_t)h * P.nqb + ((qb - P.q0) >> 5)) * (2 * SUB), lane * 4, lb + L::LS);
   };
-  // scores(): S = Q K^T - LSE (fp16 MFMA, in log2 units: the K copy carries
-  // scale * log2(e)) and dP = dO V^T - D of one staged block; the
-  // accumulators start from the staged -LSE and -D, so P = exp2(S) and
-  // dS = P dP need no further per-element terms.
-  // grads(): P and dS in registers, then dV += P^T dO (bf16) and
-  // dK += dS^T Q (fp16).  Every wavefront runs every block: blocks that end
+  // One step per item `it`, two register sets for the score accumulators:
+  // the step masks and exponentiates the scores of item it (computed in the
+  // previous step), runs the score MFMAs of item it + 1 (S = Q K^T - LSE on
+  // fp16 operands, in log2 units since the K copy carries scale * log2(e),
+  // and dP = dO V^T - D; both start from the staged -LSE and -D, so
+  // P = exp2(S) and dS = P dP need no further per-element terms), then the
+  // accumulating MFMAs of item it (dV += P^T dO in bf16, dK += dS^T Q in
+  // fp16).  The source order below is the issue order: scheduling fences
+  // keep the exponentials and products of item it between the score MFMAs
+  // of item it + 1, and the copies of item it + 3 and the dS stores between
+  // the accumulating MFMAs, so the matrix unit always has independent work
+  // queued while the other units run.  LDS operands are read one k-group
+  // ahead of their MFMAs.  Every wavefront runs every block: blocks that end
   // before its first key are fully masked by the causal compare, and keys
   // past the tile are never stored.  (Keeping the accumulating MFMAs
   // unconditional lets the accumulators stay in AGPRs.)
-  // dS path: the block computed in one step is stored at the start of the
-  // next, always (no branch in the loop), into the spare block when the
-  // wavefront does not own it; ds_blk is wave-uniform
-  f16* ds_blk = P.ds_spare;
-  f16x8 ds_val[2] = {f16x8{}, f16x8{}};
-  const int ds_lane = col * SUB + half * 16;  // this lane's 16 elements in a block
+  const int ds_lane = col * SUB + half * 16;  // this lane's 16 elements in a dS block
   // element mask limit: key <= row < rhi is (row - key) < lim; keys past a
   // short sub-tile read no rows, so their dS (and P) is exactly zero
   const unsigned lim = kvalid ? (unsigned)max(rhi - key, 0) : 0u;
-  auto scores = [&](const char* base, f32x16& S, f32x16& dP) {
-    const f16* q16 = (const f16*)(base + L::Q16);
-    const bf16* dob = (const bf16*)(base + L::DO);
+  // seeds of a score accumulator pair from a staged block: register r <->
+  // query row 8*(r/4) + 4*half + r%4 of the block
+  auto seed = [&](const char* base, f32x16& S, f32x16& dP) {
     const float* ls = (const float*)(base + L::LS);
     const float* dd = (const float*)(base + L::DD);
-    // register r <-> query row 8*(r/4) + 4*half + r%4 of the block
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const float4 l4 = *(const float4*)(ls + 8 * r4 + 4 * half);
@@ -511,114 +519,161 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
       dP[4 * r4 + 2] = d4.z;
       dP[4 * r4 + 3] = d4.w;
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      S = mfma32h(*(const f16x8*)(q16 + koff[s]), kf[s], S);
-      dP = mfma32(*(const bf16x8*)(dob + koff[s]), vf[s], dP);
+  };
+  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
+
+  // Four LDS buffers: an item's block sits in buffer (item % 4) and its
+  // copies are issued three items ahead.  Staging and score MFMAs run
+  // unconditionally (past the last item they repeat the last item, into a
+  // buffer / registers nobody uses).  The staging cursor (sbi, sg) walks the
+  // items without divisions; each buffer remembers the item it holds.
+  char* const bb[4] = {smem, smem + L::BYTES, smem + 2 * L::BYTES, smem + 3 * L::BYTES};
+  int sbi = nblk - 1, sg = 0;
+  int bbi[4], bg[4];
+  auto stage_next = [&](int b) {
+    stage(sbi, sg, b);
+    bbi[b] = sbi;
+    bg[b] = sg;
+    if (sg + 1 < G) {
+      ++sg;
+    } else if (sbi > 0) {
+      sg = 0;
+      --sbi;
     }
   };
-  auto grads = [&](int it, const char* base, const f32x16& S, const f32x16& dP) {
-    const int qb = qlo + SUB * (nblk - 1 - it / P.G);
-    const f16* q16 = (const f16*)(base + L::Q16);
-    const bf16* dob = (const bf16*)(base + L::DO);
-    // transpose reads first: their latency hides behind the exponentials
-    bf16x8 od[4][2];
-    f16x8 oq[4][2];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        od[dt][qs] = cat(lds_read_tr(dob + qs * 16 * D + toff[dt][0]), lds_read_tr(dob + qs * 16 * D + toff[dt][1]));
-        oq[dt][qs] = cat(lds_read_tr(q16 + qs * 16 * D + toff[dt][0]), lds_read_tr(q16 + qs * 16 * D + toff[dt][1]));
-      }
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = exp2f_fast(S[r]);
-    // register r <-> query row qb + 8*(r/4) + 4*half + r%4, key kw + col.
-    // Only blocks that start before the wavefront's last key or end past its
-    // rows need the element mask key <= row < rhi, one unsigned compare:
-    // (row - key) < (rhi - key), with no rows at all for a key >= rhi (a
-    // window may end inside the wavefront's keys).
+  auto step = [&](int u, f32x16& Sg, f32x16& dPg, f32x16& Sn, f32x16& dPn) {
+    const char* gb = bb[u];              // item it: transpose-read operands of the accumulating MFMAs
+    const char* nb = bb[(u + 1) & 3];    // item it + 1: score operands and seeds
+    const int qb = qlo + SUB * bbi[u];
+    const int hg = bg[u];
+    // element mask of item it (register r <-> row qb + 8*(r/4) + 4*half +
+    // r%4, key kw + col), applied to S before the exponentials; only blocks
+    // that start before the wavefront's last key or end past its rows need
+    // it: one unsigned compare (row - key) < (rhi - key), with no rows at
+    // all for a key >= rhi (a window may end inside the wavefront's keys)
     if (qb < kw + SUB || qb + SUB > rhi || wkeys < SUB) {
       const int d0 = qb + 4 * half - key;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if ((unsigned)(d0 + 8 * (r >> 2) + (r & 3)) >= lim) p[r] = 0.f;
+        if ((unsigned)(d0 + 8 * (r >> 2) + (r & 3)) >= lim) Sg[r] = -INFINITY;
     }
+    fence();
+    const f16* q16n = (const f16*)(nb + L::Q16);
+    const bf16* don = (const bf16*)(nb + L::DO);
+    const f16* q16g = (const f16*)(gb + L::Q16);
+    const bf16* dog = (const bf16*)(gb + L::DO);
+    seed(nb, Sn, dPn);
+    f16x8 qa[8];
+    bf16x8 oa[8];
+    qa[0] = *(const f16x8*)(q16n + koff[0]);
+    oa[0] = *(const bf16x8*)(don + koff[0]);
+    qa[1] = *(const f16x8*)(q16n + koff[1]);
+    oa[1] = *(const bf16x8*)(don + koff[1]);
+    fence();
+    float p[16];
     bf16x8 pa[2];
-    float ds[16];
+    f16x8 sa[2];
+    bf16x8 od[4][2];
+    f16x8 oq[4][2];
+    f16* blk = P.ds_spare;  // dS block of item it (see the stores below)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pa[r >> 3][r & 7] = (bf16)p[r];
-      ds[r] = p[r] * dP[r];
+    for (int s = 0; s < 8; ++s) {
+      if (DS && s == 1) {  // scalar work, placed among the score MFMAs
+        const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
+        if (own) blk = P.ds + (((size_t)kvh * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * G + hg) * (SUB * SUB);
+      }
+      // operands of k-group s + 2, then the MFMAs of k-group s
+      if (s < 6) {
+        qa[s + 2] = *(const f16x8*)(q16n + koff[s + 2]);
+        oa[s + 2] = *(const bf16x8*)(don + koff[s + 2]);
+      }
+      Sn = mfma32h(qa[s], kf[s], Sn);
+      dPn = mfma32(oa[s], vf[s], dPn);
+      // transpose-read operands of the accumulating MFMAs (d-tile s / 2)
+      {
+        const int dt = s >> 1, qs = s & 1;
+        od[dt][qs] = cat(lds_read_tr(dog + qs * 16 * D + toff[dt][0]), lds_read_tr(dog + qs * 16 * D + toff[dt][1]));
+        oq[dt][qs] = cat(lds_read_tr(q16g + qs * 16 * D + toff[dt][0]), lds_read_tr(q16g + qs * 16 * D + toff[dt][1]));
+      }
+      // P of item it, two elements per k-group; products and packing once a
+      // half of the block's registers is exponentiated
+      // (the empty asm statements pin each result to this k-group: without
+      // them the compiler sinks the arithmetic to its first use, after the
+      // last score MFMA)
+      p[2 * s] = exp2f_fast(Sg[2 * s]);
+      p[2 * s + 1] = exp2f_fast(Sg[2 * s + 1]);
+      asm volatile("" : "+v"(p[2 * s]), "+v"(p[2 * s + 1]));
+      if (s == 3 || s == 7) {
+        const int hh = s >> 2;
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pa[hh][e] = (bf16)p[8 * hh + e];
+          ds[e] = p[8 * hh + e] * dPg[8 * hh + e];
+        }
+        sa[hh] = pack_f16_rtz(ds);
+        asm volatile("" : "+v"(pa[hh]), "+v"(sa[hh]));
+      }
+      fence();
     }
-    const f16x8 sa[2] = {pack_f16_rtz(ds), pack_f16_rtz(ds + 8)};
-    // dS of this block goes out at the start of the next step (see the
-    // loop): block qb is query tile (qb - q0) / 32; stored as [key][position]
-    // with position half*16 + r, so each lane writes 32 contiguous bytes
+    // dS of item it (block qb is query tile (qb - q0) / 32), stored as
+    // [key][position] with position half*16 + r, so each lane writes 32
+    // contiguous bytes; into the spare block when the wavefront does not own
+    // it (the store stays unconditional).  Non-temporal: dS is read once, by
+    // the dQ pass, and should not linger dirty in the caches.  The stores go
+    // out before the step's copies (see the wait below).
     if (DS) {
-      const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
-      const int hg = it - (it / P.G) * P.G;
-      f16* const blk = P.ds + (((size_t)kvh * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * P.G + hg) * (SUB * SUB);
-      ds_blk = own ? blk : P.ds_spare;
-      ds_val[0] = sa[0];
-      ds_val[1] = sa[1];
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[0]), (u32x4*)(blk + ds_lane));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[1]), (u32x4*)(blk + ds_lane + 8));
     }
+    // accumulating MFMAs of item it, with the copies of item it + 3 issued
+    // between them
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
         mfma32_acc(dv[dt], pa[qs], od[dt][qs]);
         mfma32h_acc(dk[dt], sa[qs], oq[dt][qs]);
       }
-  };
-
-  // Four LDS buffers: block b sits in buffer b % 4 and its copies are issued
-  // three blocks ahead.  Step `it` issues the copies of block it + 3, the
-  // score MFMAs of block it + 1 and the softmax / gradient work of block it,
-  // so the matrix unit has independent work while the VALU computes P and
-  // dS.  Staging and scores run unconditionally (past the last item they
-  // repeat the last item, into a buffer / registers nobody uses), so every
-  // wavefront always has exactly five copies per block in flight and "at
-  // most five outstanding" after a step means block it + 2 has landed.
-  // nitem >= 1: every tile's query range holds at least one row.
-  const int last = nitem - 1;
-  char* const bb[4] = {smem, smem + L::BYTES, smem + 2 * L::BYTES, smem + 3 * L::BYTES};
-  // The dS stores of a step are issued at the start of the next one, before
-  // its copies: the ring's "at most five outstanding" wait then still means
-  // the copies two blocks ahead have landed (loads complete in order, and the
-  // stores, older than the newest five copies, are complete as well).
-  auto flush_ds = [&]() {
-    if (DS) {  // non-temporal: dS is read once, by the dQ pass, and should not linger dirty in the caches
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ds_val[0]), (u32x4*)(ds_blk + ds_lane));
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ds_val[1]), (u32x4*)(ds_blk + ds_lane + 8));
+      if (dt == 0) stage_next((u + 3) & 3);
+      fence();
     }
   };
-  stage(0, bb[0]);
-  stage(min(1, last), bb[1]);
-  stage(min(2, last), bb[2]);
-  asm volatile("s_waitcnt vmcnt(5)" ::: "memory");  // blocks 0 and 1 landed
+
+  // Wavefronts 1-3 issue four copies per item and wavefront 0 five, after
+  // the step's two dS stores, so "at most four outstanding" after a step
+  // means every earlier copy and store is complete (they complete in order):
+  // for wavefronts 1-3 exactly the items up to it + 2, for wavefront 0 also
+  // the first copy of item it + 3.
+  stage_next(0);
+  stage_next(1);
+  stage_next(2);
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // items 0 and 1 landed
   __syncthreads();
   f32x16 Sa, dPa, Sb, dPb;
-  scores(bb[0], Sa, dPa);
+  // scores of item 0
+  {
+    const f16* q16 = (const f16*)(bb[0] + L::Q16);
+    const bf16* dob = (const bf16*)(bb[0] + L::DO);
+    seed(bb[0], Sa, dPa);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      Sa = mfma32h(*(const f16x8*)(q16 + koff[s]), kf[s], Sa);
+      dPa = mfma32(*(const bf16x8*)(dob + koff[s]), vf[s], dPa);
+    }
+  }
   for (int it = 0; it < nitem; it += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (u > 0 && it + u >= nitem) break;
-      flush_ds();
-      stage(min(it + u + 3, last), bb[(u + 3) & 3]);
-      if (u & 1) {
-        scores(bb[(u + 1) & 3], Sa, dPa);
-        grads(it + u, bb[u], Sb, dPb);
-      } else {
-        scores(bb[(u + 1) & 3], Sb, dPb);
-        grads(it + u, bb[u], Sa, dPa);
-      }
-      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      if (u & 1)
+        step(u, Sb, dPb, Sa, dPa);
+      else
+        step(u, Sa, dPa, Sb, dPb);
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       __syncthreads();
     }
   }
-  flush_ds();
   lds_copies_wait();
 
   agpr_fence8(dk, dv);
@@ -710,10 +765,9 @@ struct PrepParams {
   const bf16* dO;
   const float* lse;
   f16* qs;
-  float* nd;
-  float* nl2;
+  float* nld;  // [Hq][nqb][64]: per 32-row query block, -LSE * log2(e), then -D
   const int32_t* pos;
-  int N, Hq, q0;
+  int N, Hq, q0, nqb;
   float rope_base;
 };
 
@@ -724,8 +778,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t pr = gid >> 3;
   const int j = (int)(gid & 7);
-  if (pr >= (size_t)(P.N - P.q0) * P.Hq) return;  // whole groups of eight lanes
+  if (pr >= (size_t)P.nqb * 32 * P.Hq) return;  // whole groups of eight lanes
   const int row = P.q0 + (int)(pr / P.Hq), h = (int)(pr % P.Hq);
+  const int rb = row - P.q0;
+  float* rec = P.nld + ((size_t)h * P.nqb + (rb >> 5)) * 64 + (rb & 31);
+  if (row >= P.N) {  // padding rows of the last block: zeros (the dK/dV kernel masks them)
+    if (j == 0) rec[0] = rec[32] = 0.f;
+    return;
+  }
   const size_t off = ((size_t)row * P.Hq + h) * D + 8 * j;
   const bf16x8 q1 = *(const bf16x8*)(P.q + off), q2 = *(const bf16x8*)(P.q + off + D / 2);
   const bf16x8 o1 = *(const bf16x8*)(P.o + off), o2 = *(const bf16x8*)(P.o + off + D / 2);
@@ -754,8 +814,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
   dsum += __shfl_xor(dsum, 2);
   dsum += __shfl_xor(dsum, 4);
   if (j == 0) {
-    P.nd[(size_t)h * P.N + row] = -dsum;
-    P.nl2[(size_t)h * P.N + row] = -P.lse[(size_t)h * P.N + row] * TA_LOG2E;
+    rec[0] = -P.lse[(size_t)h * P.N + row] * TA_LOG2E;
+    rec[32] = -dsum;
   }
 }
 
@@ -978,16 +1038,17 @@ constexpr size_t SUB_SQ = TA_KV_SUB * TA_KV_SUB;
 // (32 x 32 fp16 per (query tile, sub-tile) block and query head).
 size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base, bool with_ds) {
   const size_t N = p->n_tokens;
-  size_t b = align256(N * Hq * sizeof(float));  // D
+  size_t b = 0;
   if (dt == TA_BF16) {
-    b += align256(N * Hq * sizeof(float));                                             // LSE * log2(e)
+    b += align256((size_t)Hq * p->n_qtiles * 64 * sizeof(float));                    // -LSE log2(e), -D blocks
     b += align256(N * Hq * d * sizeof(f16)) + align256(N * Hkv * d * sizeof(f16));  // fp16 Q, K
     if (rope_base > 0.f) b += align256(N * Hkv * d * sizeof(bf16));                 // rotated bf16 K
     b += align256((size_t)p->n_kslots * Hkv * bwd::PART_WAVE * sizeof(float));       // dK/dV partials
     if (with_ds) b += align256((size_t)p->n_dsblk * Hq * SUB_SQ * sizeof(f16)) +     // dS blocks
                       align256(SUB_SQ * sizeof(f16));                                // + a spare one
-  } else if (rope_base > 0.f) {
-    b += align256(N * Hq * d * sizeof(float)) + align256(N * Hkv * d * sizeof(float));
+  } else {
+    b += align256(N * Hq * sizeof(float));  // D
+    if (rope_base > 0.f) b += align256(N * Hq * d * sizeof(float)) + align256(N * Hkv * d * sizeof(float));
   }
   return b;
 }
@@ -1027,12 +1088,10 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   const int32_t* kr = (const int32_t*)(base + p->off_kr);
   const bool rope = rope_base > 0.f;
   char* w = (char*)ws;
-  float* Dd = (float*)w;
-  w += align256((size_t)N * Hq * sizeof(float));
 
   if (dt == TA_BF16) {
-    float* l2 = (float*)w;
-    w += align256((size_t)N * Hq * sizeof(float));
+    float* nld = (float*)w;
+    w += align256((size_t)Hq * p->n_qtiles * 64 * sizeof(float));
     f16* qs = (f16*)w;
     w += align256((size_t)N * Hq * d * sizeof(f16));
     f16* ks = (f16*)w;
@@ -1060,14 +1119,14 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
       R.dO = (const bf16*)dO;
       R.lse = lse;
       R.qs = qs;
-      R.nd = Dd;
-      R.nl2 = l2;
+      R.nld = nld;
       R.pos = pos;
       R.N = N;
       R.Hq = Hq;
       R.q0 = p->q_start;
+      R.nqb = p->n_qtiles;
       R.rope_base = rope_base;
-      const size_t lanes = (size_t)(N - p->q_start) * Hq * 8;
+      const size_t lanes = (size_t)p->n_qtiles * 32 * Hq * 8;
       if (lanes > 0) {
         hipLaunchKernelGGL(bwd::prep_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, R);
         TA_LAUNCH_CHECK();
@@ -1082,8 +1141,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     A.dO = (const bf16*)dO;
     A.lse = lse;
     A.dq = (bf16*)dq;
-    A.nd = Dd;
-    A.nl2 = l2;
+    A.nld = nld;
     A.qs = qs;
     A.pos = pos;
     A.fq_ptr = fq_ptr;
@@ -1093,6 +1151,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     A.Hq = Hq;
     A.Hkv = Hkv;
     A.G = Hq / Hkv;
+    A.nqb = p->n_qtiles;
     A.q0 = p->q_start;
     A.scale = scale;
     A.scale_log2 = scale * TA_LOG2E;
@@ -1108,8 +1167,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.k = ks;
     B.v = (const bf16*)v;
     B.dO = (const bf16*)dO;
-    B.nl2 = l2;
-    B.nd = Dd;
+    B.nld = nld;
     B.dk = (bf16*)dk;
     B.dv = (bf16*)dv;
     B.pos = pos;
@@ -1120,6 +1178,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.ds_spare = ds_spare;
     B.n_dsblk = (int)p->n_dsblk;
     B.n_sum = p->n_ksplit;
+    B.nqb = p->n_qtiles;
     B.N = N;
     B.Hq = Hq;
     B.Hkv = Hkv;
@@ -1163,6 +1222,8 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     return TA_OK;
   }
 
+  float* Dd = (float*)w;
+  w += align256((size_t)N * Hq * sizeof(float));
   void* qrot = rope ? (void*)w : nullptr;
   if (rope) w += align256((size_t)N * Hq * d * sizeof(float));
   void* krot = rope ? (void*)w : nullptr;

@@ -107,50 +107,32 @@ struct Params {
   float rope_base;
 };
 
-// Copies chunk c's 64 K and V rows into one LDS buffer (swizzled 256-byte
-// rows) and its key indices / DFS-interval ends into sJ / sE.  Copy
-// instruction i of a tile fills rows 4i..4i+3; wavefront w issues i = w + 4k.
-__device__ __forceinline__ void stage_chunk(const Params& P, int c, int kvh, f16* sKb, bf16* sVb, int* sJb,
-                                            int* sEb) {
-  const ChunkRec ch = load_chunk(as_const(P.fq_chunk) + (size_t)c * TA_CHUNK_INTS);
-  const int t = threadIdx.x, l = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  // this lane's row within each 4-row copy and its swizzled 16-byte piece
-  // (rows 4i + l/16 with i = w + 4k share their low four bits)
-  const int sub = l >> 4;
-  const int poff = ((l & 15) ^ swz((4 * w + sub) & 15)) << 3;
-  if (ch.h[0] == 1 && ch.h[1] == BN) {
-    // one segment filling all 64 slots: slot v holds key v + delta
-    const int delta = ch.ks[0] - ch.ko[0];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = w + 4 * k;
-      const size_t off = ((size_t)(4 * i + sub + delta) * P.Hkv + kvh) * D + poff;
-      copy16_to_lds(P.k + off, sKb + 4 * i * D);
-      copy16_to_lds(P.v + off, sVb + 4 * i * D);
-    }
-    if (t < BN) {
-      sJb[t] = t + delta;
-      sEb[t] = ch.ke[0];
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = w + 4 * k;
-      int j, e;
-      chunk_slot(ch, 4 * i + sub, j, e);
-      const size_t off = ((size_t)j * P.Hkv + kvh) * D + poff;
-      copy16_to_lds(P.k + off, sKb + 4 * i * D);
-      copy16_to_lds(P.v + off, sVb + 4 * i * D);
-    }
-    int j, e;
-    chunk_slot(ch, l, j, e);
-    if (t < BN) {
-      sJb[t] = j;
-      sEb[t] = e;
-    }
-  }
+// The two halves of a wavefront (lanes l and l + 32) hold the same query
+// column; v_permlane32_swap with x in both operands leaves x[l % 32] in the
+// first and x[32 + l % 32] in the second, in every lane, so one instruction
+// combines both halves.  It is issued from inline asm: when both results of
+// the compiler builtin feed one arithmetic instruction, this compiler reads
+// the first result register twice (checked in the generated code: r0 + r1
+// became v_add v2, v3, v3).  s_nop 1: a VALU write of an operand needs two
+// wait states before the swap reads it.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
 }
+__device__ __forceinline__ float halves_max(float x) {
+  float a, b;
+  halves(x, a, b);
+  return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float a, b;
+  halves(x, a, b);
+  return a + b;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
   __shared__ __attribute__((aligned(1024))) f16 sK[2][BN * D];
@@ -198,23 +180,70 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
     }
   }
 
-  float m = -INFINITY, l = 0.f;
-  f32x16 acc[4];
+  // Staging.  Copy k (k = 0..3) of wavefront w fills rows 4(w + 4k) + l/16
+  // of a chunk's K and V tiles (a swizzled 16-byte piece per lane).  A chunk
+  // of one 64-key segment (most chunks) holds keys delta .. delta + 63, so
+  // its copies take a scalar base and fixed per-lane offsets; other chunks
+  // gather their rows per lane.  The key indices and interval ends of the
+  // slots go to sJ / sE only for chunks that need the element mask.
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int sub = lane >> 4;
+  const uint32_t kvrow = (uint32_t)P.Hkv * (D * 2);  // bytes between consecutive tokens
+  const uint32_t piece = (uint32_t)(((lane & 15) ^ swz((4 * w + sub) & 15)) << 4);
+  uint32_t voff[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-
-  const int c0 = as_const(P.fq_ptr)[tile], c1 = as_const(P.fq_ptr)[tile + 1];
-  stage_chunk(P, c0, kvh, sK[0], sV[0], sJ[0], sE[0]);
-  lds_copies_wait();
-  __syncthreads();
+  for (int k = 0; k < 4; ++k) voff[k] = (uint32_t)(4 * (w + 4 * k) + sub) * kvrow + piece;
+  const uint32_t ldsK = lds_addr(&sK[0][0]), ldsV = lds_addr(&sV[0][0]);
+  // copies chunk c into buffer b; returns the chunk's "fully visible" flag
+  auto stage = [&](int c, int b) -> int {
+    const ChunkRec ch = load_chunk(as_const(P.fq_chunk) + (size_t)c * TA_CHUNK_INTS);
+    const int full = ch.h[2];
+    if (ch.h[0] == 1 && ch.h[1] == BN) {
+      const int delta = ch.ks[0] - ch.ko[0];
+      const size_t off = ((size_t)delta * P.Hkv + kvh) * (D * 2);
+      const char* kb = (const char*)P.k + off;
+      const char* vb = (const char*)P.v + off;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t r = (uint32_t)(4 * (w + 4 * k)) * (D * 2);
+        copy16_to_lds_s(kb, voff[k], ldsK + b * (BN * D * 2) + r);
+        copy16_to_lds_s(vb, voff[k], ldsV + b * (BN * D * 2) + r);
+      }
+      if (!full && t < BN) {
+        sJ[b][t] = t + delta;
+        sE[b][t] = ch.ke[0];
+      }
+    } else {
+      const int poff = (int)(piece >> 1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = w + 4 * k;
+        int j, e;
+        chunk_slot(ch, 4 * i + sub, j, e);
+        const size_t off = ((size_t)j * P.Hkv + kvh) * D + poff;
+        copy16_to_lds(P.k + off, sK[b] + 4 * i * D);
+        copy16_to_lds(P.v + off, sV[b] + 4 * i * D);
+      }
+      if (!full) {
+        int j, e;
+        chunk_slot(ch, lane, j, e);
+        if (t < BN) {
+          sJ[b][t] = j;
+          sE[b][t] = e;
+        }
+      }
+    }
+    return full;
+  };
 
   // Swizzled LDS offsets (in elements), fixed per lane: koff[s] for the
   // 16-byte K row read of k-group s (rows col and col + 32 share them);
-  // voff[dt][x] for the V transpose read of d-tile dt, rows trow + 8x of
+  // voff_t[dt][x] for the V transpose read of d-tile dt, rows trow + 8x of
   // each 16-row group.
   const int trow = half * 4 + ((lane & 15) >> 2);
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  int koff[8], voff[4][2];
+  int koff[8], vto[4][2];
 #pragma unroll
   for (int s = 0; s < 8; ++s) koff[s] = col * D + (((2 * s + half) ^ swz(col & 15)) << 3);
 #pragma unroll
@@ -222,97 +251,135 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int r = trow + 8 * x;
-      voff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
+      vto[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
     }
 
-  for (int c = c0; c < c1; ++c) {
-    const int buf = (c - c0) & 1;
-    // copy the next chunk into the other buffer (the last iteration copies
-    // its own chunk again, into the buffer nobody reads)
-    stage_chunk(P, c + 1 < c1 ? c + 1 : c, kvh, sK[buf ^ 1], sV[buf ^ 1], sJ[buf ^ 1], sE[buf ^ 1]);
-    if (active) {
-      const f16* kb = sK[buf];
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // Online softmax with a lazily moved reference.  The score accumulators
+  // start from -mref (the MFMA's C operand), so S - mref comes out of the
+  // matrix unit and the exponentials need no subtraction.  mref moves (and
+  // O, l are rescaled) only when some lane's chunk max exceeds it by more
+  // than 8 (log2 units), or at the lane's first chunk with a visible key;
+  // otherwise the stale reference keeps P <= 2^8, and O / l and
+  // LSE = mref + log2(l) do not depend on it.
+  float mref = 0.f, l = 0.f;
+  bool has = false;  // a visible key has been seen (mref is then a max reference)
+  f32x16 seed;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 a0 = *(const f16x8*)(kb + koff[s]);
-        const f16x8 a1 = *(const f16x8*)(kb + 32 * D + koff[s]);
-        s0 = mfma32h(a0, qf[s], s0);
-        s1 = mfma32h(a1, qf[s], s1);
-      }
-      // S^T register r of tile kt <-> key slot kt*32 + 8*(r/4) + 4*half + r%4;
-      // the fp16 K copy carries the factor scale * log2(e), so S^T is
-      // already in log2 units
-      const int full = as_const(P.fq_chunk)[(size_t)c * TA_CHUNK_INTS + 2];
-      if (!full) {
+  for (int r = 0; r < 16; ++r) seed[r] = 0.f;
+  f32x16 acc[4];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int v0 = r4 * 8 + half * 4;
-          const int4 J0 = *(const int4*)&sJ[buf][v0], E0 = *(const int4*)&sE[buf][v0];
-          const int4 J1 = *(const int4*)&sJ[buf][32 + v0], E1 = *(const int4*)&sE[buf][32 + v0];
-          const int j0[4] = {J0.x, J0.y, J0.z, J0.w}, e0[4] = {E0.x, E0.y, E0.z, E0.w};
-          const int j1[4] = {J1.x, J1.y, J1.z, J1.w}, e1[4] = {E1.x, E1.y, E1.z, E1.w};
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+
+  // one chunk: scores from buffer b (static after unrolling), softmax, PV
+  auto compute = [&](int b, int full) {
+    const f16* kb = sK[b];
+    f32x16 s0, s1;
+    {
+      const f16x8 a0 = *(const f16x8*)(kb + koff[0]);
+      const f16x8 a1 = *(const f16x8*)(kb + 32 * D + koff[0]);
+      s0 = mfma32h(a0, qf[0], seed);
+      s1 = mfma32h(a1, qf[0], seed);
+    }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (!(j0[u] <= qi && qi < e0[u])) s0[r4 * 4 + u] = -INFINITY;
-            if (!(j1[u] <= qi && qi < e1[u])) s1[r4 * 4 + u] = -INFINITY;
-          }
+    for (int s = 1; s < 8; ++s) {
+      const f16x8 a0 = *(const f16x8*)(kb + koff[s]);
+      const f16x8 a1 = *(const f16x8*)(kb + 32 * D + koff[s]);
+      s0 = mfma32h(a0, qf[s], s0);
+      s1 = mfma32h(a1, qf[s], s1);
+    }
+    // S^T register r of tile kt <-> key slot kt*32 + 8*(r/4) + 4*half + r%4,
+    // in log2 units (the fp16 K copy carries scale * log2(e)), minus mref
+    if (!full) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int v0 = r4 * 8 + half * 4;
+        const int4 J0 = *(const int4*)&sJ[b][v0], E0 = *(const int4*)&sE[b][v0];
+        const int4 J1 = *(const int4*)&sJ[b][32 + v0], E1 = *(const int4*)&sE[b][32 + v0];
+        const int j0[4] = {J0.x, J0.y, J0.z, J0.w}, e0[4] = {E0.x, E0.y, E0.z, E0.w};
+        const int j1[4] = {J1.x, J1.y, J1.z, J1.w}, e1[4] = {E1.x, E1.y, E1.z, E1.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (!(j0[u] <= qi && qi < e0[u])) s0[r4 * 4 + u] = -INFINITY;
+          if (!(j1[u] <= qi && qi < e1[u])) s1[r4 * 4 + u] = -INFINITY;
         }
       }
-      // Row max of the chunk with the NaN-propagating maximum (v_maximum3):
-      // unlike fmaxf it needs no canonicalising instruction per MFMA result.
-      float mx = -INFINITY;
+    }
+    // chunk max relative to mref, NaN-propagating (v_maximum3)
+    float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
-      mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
-      // Lazy rescaling: the reference m moves (and O, l are rescaled) only when
-      // some lane's chunk max exceeds it by more than 8 (log2 units).  Otherwise
-      // the exponentials use the stale m, so P <= 2^8, and O / l and
-      // LSE = m + log2(l) are unchanged: the softmax does not depend on the
-      // reference as long as O, l and m agree.
-      if (__builtin_amdgcn_ballot_w64(mx > m + 8.f)) {
-        const float mnew = __builtin_elementwise_maximum(m, mx);
-        const float alpha = exp2f_fast(m - ((mnew == -INFINITY) ? 0.f : mnew));
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-        m = mnew;
-      }
-      const float muse = (m == -INFINITY) ? 0.f : m;
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = exp2f_fast(s0[r] - muse);
-        s1[r] = exp2f_fast(s1[r] - muse);
-        rs += s0[r] + s1[r];
-      }
-      l += rs;  // per-lane partial over this lane's key rows
-      bf16x8 pb[4];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[0][e] = (bf16)s0[e];
-        pb[1][e] = (bf16)s0[8 + e];
-        pb[2][e] = (bf16)s1[e];
-        pb[3][e] = (bf16)s1[8 + e];
-      }
-      const bf16* vb = sV[buf];
+    for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
+    mx = halves_max(mx);
+    const bool need = (!has || mx > 8.f) && mx != -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float delta = need ? mx : 0.f;
+      const float alpha = exp2f_fast(-delta);
+      l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x4 t0 = lds_read_tr(vb + kk * 16 * D + voff[dt][0]);
-          const bf16x4 t1 = lds_read_tr(vb + kk * 16 * D + voff[dt][1]);
-          acc[dt] = mfma32(cat(t0, t1), pb[kk], acc[dt]);
-        }
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      mref += delta;
+      has = has || need;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        seed[r] = -mref;
+        s0[r] -= delta;
+        s1[r] -= delta;
+      }
     }
-    lds_copies_wait();
-    __syncthreads();
+    bf16x8 pb[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pb[0][e] = (bf16)exp2f_fast(s0[e]);
+      pb[1][e] = (bf16)exp2f_fast(s0[8 + e]);
+      pb[2][e] = (bf16)exp2f_fast(s1[e]);
+      pb[3][e] = (bf16)exp2f_fast(s1[8 + e]);
+    }
+    // row sum of the rounded P that enters P V (per lane: its key rows)
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[x][e], pb[x][e + 1]}, ones, l, false);
+    const bf16* vb = sV[b];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x4 t0 = lds_read_tr(vb + kk * 16 * D + vto[dt][0]);
+        const bf16x4 t1 = lds_read_tr(vb + kk * 16 * D + vto[dt][1]);
+        acc[dt] = mfma32(cat(t0, t1), pb[kk], acc[dt]);
+      }
+  };
+
+  const int c0 = as_const(P.fq_ptr)[tile], c1 = as_const(P.fq_ptr)[tile + 1];
+  int full = stage(c0, 0);
+  lds_copies_wait();
+  __syncthreads();
+  // Double buffer, unrolled by two so each buffer's LDS offsets are
+  // immediates: the next chunk's copies go into the other buffer while this
+  // one is computed (the last chunk copies itself again, into the buffer
+  // nobody reads).  Wavefronts without a head (fewer than four heads per KV
+  // head) stage and wait but compute nothing.
+  for (int c = c0; c < c1; c += 2) {
+    {
+      const int fn = stage(c + 1 < c1 ? c + 1 : c, 1);
+      if (active) compute(0, full);
+      full = fn;
+      lds_copies_wait();
+      __syncthreads();
+    }
+    if (c + 1 < c1) {
+      const int fn = stage(c + 2 < c1 ? c + 2 : c + 1, 0);
+      if (active) compute(1, full);
+      full = fn;
+      lds_copies_wait();
+      __syncthreads();
+    }
   }
 
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = halves_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (active && qvalid) {
     bf16* orow = P.o + ((size_t)qi * P.Hq + h) * D;
@@ -320,12 +387,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 w;
+        bf16x4 wv;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = (bf16)(acc[dt][r4 * 4 + u] * inv);
-        *(bf16x4*)(orow + dt * 32 + r4 * 8 + half * 4) = w;
+        for (int u = 0; u < 4; ++u) wv[u] = (bf16)(acc[dt][r4 * 4 + u] * inv);
+        *(bf16x4*)(orow + dt * 32 + r4 * 8 + half * 4) = wv;
       }
-    if (half == 0) P.lse[(size_t)h * P.N + qi] = (m + log2f(lt)) * TA_LN2;
+    if (half == 0) P.lse[(size_t)h * P.N + qi] = (has ? mref + log2f(lt) : -INFINITY) * TA_LN2;
   }
 }
 

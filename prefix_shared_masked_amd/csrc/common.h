@@ -173,6 +173,20 @@ __device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds_base
 }
 __device__ __forceinline__ void lds_copies_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Scalar-base forms: lane i copies the bytes at sbase + voff_i, where sbase
+// is wave-uniform (an SGPR pair) and voff_i a 32-bit per-lane byte offset,
+// into lds + 16 i (16-byte form) or lds + 4 i (4-byte form).  A loop whose
+// per-lane offsets do not change only recomputes the scalar base, so a copy
+// costs no vector instructions.  lds is an LDS byte address (lds_addr).
+__device__ __forceinline__ void copy16_to_lds_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
 // Plan tables are read-only for a kernel's lifetime.  Reading them through
 // the constant address space lets uniform reads become scalar loads, which
 // issue early and never make the vector-memory counter wait on them.

@@ -214,3 +214,52 @@ def test_rows_attention_grads_matches_dense():
     np.testing.assert_allclose(dq, ref["dq"][rows], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(dk, ref["dk"][keys], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(dv, ref["dv"][keys], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("rope_base", [0.0, 10000.0])
+@pytest.mark.parametrize("heads", [(4, 2), (8, 2), (3, 3)])
+def test_rows_attention_matches_dense(rope_base, heads):
+    """The per-row forward oracle used for full-size spot checks, on every row
+    and head of small trees (forests, chains, stars, zero-length nodes)
+    against the literal dense mask of the Tree Training post (section 4.2)
+    with depth positions (section 5): a wrong path slice, query position or
+    GQA head would show in O or LSE."""
+    Hq, Hkv = heads
+    rng = np.random.default_rng(31)
+    trees = [W.six_node_tree(3)] + [
+        W.random_tree(rng, int(rng.integers(2, 10)), max_len=7, p_zero=0.25, n_roots=int(rng.integers(1, 4)),
+                      shape=["random", "chain", "star"][c % 3]) for c in range(6)]
+    for t in trees:
+        op = oracle.oracle_plan(t.parent, t.seg_len)
+        if op.n_tokens == 0:
+            continue
+        q, k, v, _ = W.attention_inputs(5, op.n_tokens, Hq, Hkv, 16)
+        ref = oracle.dense_mask_attention(op, q, k, v, rope_base=rope_base)
+        rows = list(range(op.n_tokens))
+        o, lse = oracle.rows_attention(op, q, k, v, rows, list(range(Hq)), rope_base=rope_base)
+        np.testing.assert_allclose(o, ref["o"], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse, ref["lse"], rtol=1e-10, atol=1e-12)
+        # a subset of heads in a different order keeps each head's own values
+        hs = [Hq - 1, 0]
+        o2, lse2 = oracle.rows_attention(op, q, k, v, rows[::2], hs, rope_base=rope_base)
+        np.testing.assert_allclose(o2, ref["o"][rows[::2]][:, hs], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse2, ref["lse"][hs][:, rows[::2]], rtol=1e-10, atol=1e-12)
+
+
+def test_rows_attention_grads_matches_dense_everywhere():
+    """rows_attention_grads on every row and key of forests with zero-length
+    nodes, GQA 8/2 and RoPE on, against the dense-mask backward."""
+    rng = np.random.default_rng(41)
+    for c in range(3):
+        tree = W.random_tree(rng, int(rng.integers(3, 9)), max_len=6, p_zero=0.25, n_roots=1 + c % 2,
+                             shape=["random", "star", "chain"][c])
+        op = oracle.oracle_plan(tree.parent, tree.seg_len)
+        if op.n_tokens == 0:
+            continue
+        q, k, v, do = W.attention_inputs(9 + c, op.n_tokens, 8, 2, 8)
+        ref = oracle.dense_mask_attention(op, q, k, v, rope_base=10000.0, dO=do)
+        allr = list(range(op.n_tokens))
+        dq, dk, dv = oracle.rows_attention_grads(op, q, k, v, do, allr, allr, rope_base=10000.0)
+        np.testing.assert_allclose(dq, ref["dq"], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk, ref["dk"], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, ref["dv"], rtol=1e-10, atol=1e-12)
