@@ -257,9 +257,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
   // Online softmax with a lazily moved reference.  The score accumulators
   // start from -mref (the MFMA's C operand), so S - mref comes out of the
   // matrix unit and the exponentials need no subtraction.  mref moves (and
-  // O, l are rescaled) only when some lane's chunk max exceeds it by more
-  // than 8 (log2 units), or at the lane's first chunk with a visible key;
-  // otherwise the stale reference keeps P <= 2^8, and O / l and
+  // O, l are rescaled) only when some lane's max over a 32-key half exceeds
+  // it by more than 8 (log2 units), or at the lane's first half with a
+  // visible key; otherwise the stale reference keeps P <= 2^8, and O / l and
   // LSE = mref + log2(l) do not depend on it.
   float mref = 0.f, l = 0.f;
   bool has = false;  // a visible key has been seen (mref is then a max reference)
@@ -270,48 +270,32 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
 
-  // one chunk: scores from buffer b (static after unrolling), softmax, PV
-  auto compute = [&](int b, int full) {
-    const f16* kb = sK[b];
-    f32x16 s0, s1;
-    {
-      const f16x8 a0 = *(const f16x8*)(kb + koff[0]);
-      const f16x8 a1 = *(const f16x8*)(kb + 32 * D + koff[0]);
-      s0 = mfma32h(a0, qf[0], seed);
-      s1 = mfma32h(a1, qf[0], seed);
-    }
-#pragma unroll
-    for (int s = 1; s < 8; ++s) {
-      const f16x8 a0 = *(const f16x8*)(kb + koff[s]);
-      const f16x8 a1 = *(const f16x8*)(kb + 32 * D + koff[s]);
-      s0 = mfma32h(a0, qf[s], s0);
-      s1 = mfma32h(a1, qf[s], s1);
-    }
-    // S^T register r of tile kt <-> key slot kt*32 + 8*(r/4) + 4*half + r%4,
-    // in log2 units (the fp16 K copy carries scale * log2(e)), minus mref
+  // Softmax of one 32-key half (S^T register r <-> key slot
+  // kt*32 + 8*(r/4) + 4*half + r%4, in log2 units, minus the reference the
+  // accumulators were seeded with; `shift` is how far mref has moved since):
+  // element mask on partial chunks, max, lazy rescale, P = exp2 in bf16, and
+  // the row sum of the rounded P that enters P V.
+  auto softmax_half = [&](f32x16& s, int b, int kt, int full, float& shift, bf16x8& p0, bf16x8& p1) {
     if (!full) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int v0 = r4 * 8 + half * 4;
-        const int4 J0 = *(const int4*)&sJ[b][v0], E0 = *(const int4*)&sE[b][v0];
-        const int4 J1 = *(const int4*)&sJ[b][32 + v0], E1 = *(const int4*)&sE[b][32 + v0];
-        const int j0[4] = {J0.x, J0.y, J0.z, J0.w}, e0[4] = {E0.x, E0.y, E0.z, E0.w};
-        const int j1[4] = {J1.x, J1.y, J1.z, J1.w}, e1[4] = {E1.x, E1.y, E1.z, E1.w};
+        const int v0 = kt * 32 + r4 * 8 + half * 4;
+        const int4 J = *(const int4*)&sJ[b][v0], E = *(const int4*)&sE[b][v0];
+        const int j[4] = {J.x, J.y, J.z, J.w}, e[4] = {E.x, E.y, E.z, E.w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (!(j0[u] <= qi && qi < e0[u])) s0[r4 * 4 + u] = -INFINITY;
-          if (!(j1[u] <= qi && qi < e1[u])) s1[r4 * 4 + u] = -INFINITY;
-        }
+        for (int u = 0; u < 4; ++u)
+          if (!(j[u] <= qi && qi < e[u])) s[r4 * 4 + u] = -INFINITY;
       }
     }
-    // chunk max relative to mref, NaN-propagating (v_maximum3)
+    // max relative to the current mref, NaN-propagating (v_maximum3)
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
-    mx = halves_max(mx);
+    for (int r = 0; r < 16; r += 2) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[r], s[r + 1]));
+    mx = halves_max(mx) - shift;
     const bool need = (!has || mx > 8.f) && mx != -INFINITY;
-    if (__builtin_amdgcn_ballot_w64(need)) {
+    if (__builtin_amdgcn_ballot_w64(need || shift != 0.f)) {
       const float delta = need ? mx : 0.f;
       const float alpha = exp2f_fast(-delta);
       l *= alpha;
@@ -321,36 +305,77 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
       mref += delta;
       has = has || need;
+      const float sub = shift + delta;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        seed[r] = -mref;
-        s0[r] -= delta;
-        s1[r] -= delta;
-      }
+      for (int r = 0; r < 16; ++r) s[r] -= sub;
+      shift += delta;
     }
-    bf16x8 pb[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pb[0][e] = (bf16)exp2f_fast(s0[e]);
-      pb[1][e] = (bf16)exp2f_fast(s0[8 + e]);
-      pb[2][e] = (bf16)exp2f_fast(s1[e]);
-      pb[3][e] = (bf16)exp2f_fast(s1[8 + e]);
+      p0[e] = (bf16)exp2f_fast(s[e]);
+      p1[e] = (bf16)exp2f_fast(s[8 + e]);
     }
-    // row sum of the rounded P that enters P V (per lane: its key rows)
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[x][e], pb[x][e + 1]}, ones, l, false);
+    for (int e = 0; e < 8; e += 2) {
+      l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[e], p0[e + 1]}, ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[e], p1[e + 1]}, ones, l, false);
+    }
+    asm volatile("" : "+v"(p0), "+v"(p1), "+v"(l));
+  };
+
+  // One chunk from buffer b (static after unrolling), as two 32-key halves
+  // so the matrix unit has queued work while the VALU runs: score MFMAs of
+  // both halves (K rows read two k-groups ahead), softmax of half 0 while
+  // half 1's score MFMAs run, P V of half 0, softmax of half 1 while those
+  // run, P V of half 1.  The source order is the issue order (scheduling
+  // fences; empty asm statements pin the softmax results in place).
+  auto compute = [&](int b, int full) {
+    const f16* kb = sK[b];
     const bf16* vb = sV[b];
+    f32x16 st[2];
+    f16x8 ka[16];
+    ka[0] = *(const f16x8*)(kb + koff[0]);
+    ka[1] = *(const f16x8*)(kb + koff[1]);
+    fence();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // i = kt * 8 + s
+      if (i + 2 < 16) ka[i + 2] = *(const f16x8*)(kb + ((i + 2) >> 3) * 32 * D + koff[(i + 2) & 7]);
+      const int kt = i >> 3, s = i & 7;
+      st[kt] = mfma32h(ka[i], qf[s], s == 0 ? seed : st[kt]);
+      fence();
+    }
+    float shift = 0.f;
+    bf16x8 pb[4];
+    // transpose-read operands of half 0's P V, then its softmax
+    bf16x8 vt[4][2];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x4 t0 = lds_read_tr(vb + kk * 16 * D + vto[dt][0]);
-        const bf16x4 t1 = lds_read_tr(vb + kk * 16 * D + vto[dt][1]);
-        acc[dt] = mfma32(cat(t0, t1), pb[kk], acc[dt]);
-      }
+      for (int kk = 0; kk < 2; ++kk)
+        vt[dt][kk] = cat(lds_read_tr(vb + kk * 16 * D + vto[dt][0]), lds_read_tr(vb + kk * 16 * D + vto[dt][1]));
+    softmax_half(st[0], b, 0, full, shift, pb[0], pb[1]);
+    fence();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc[dt] = mfma32(vt[dt][kk], pb[kk], acc[dt]);
+    fence();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        vt[dt][kk] =
+            cat(lds_read_tr(vb + (kk + 2) * 16 * D + vto[dt][0]), lds_read_tr(vb + (kk + 2) * 16 * D + vto[dt][1]));
+    softmax_half(st[1], b, 1, full, shift, pb[2], pb[3]);
+    fence();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc[dt] = mfma32(vt[dt][kk], pb[kk + 2], acc[dt]);
+    if (__builtin_amdgcn_ballot_w64(shift != 0.f)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) seed[r] = -mref;
+    }
   };
 
   const int c0 = as_const(P.fq_ptr)[tile], c1 = as_const(P.fq_ptr)[tile + 1];
