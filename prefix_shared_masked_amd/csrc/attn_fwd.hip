@@ -143,10 +143,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
 
   const int kvh = blockIdx.x % P.Hkv;
   const int tile = as_const(P.fq_order)[blockIdx.x / P.Hkv];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int hsub = blockIdx.y * 4 + wave;
-  const bool active = hsub < P.G;
+  const bool active = hsub < P.G;  // wave-uniform
   rope_inv_table(sInv, D / 2, D, P.rope_base);
   __syncthreads();
   const int h = kvh * P.G + (active ? hsub : 0);

@@ -178,12 +178,24 @@ __device__ __forceinline__ void lds_copies_wait() { asm volatile("s_waitcnt vmcn
 // into lds + 16 i (16-byte form) or lds + 4 i (4-byte form).  A loop whose
 // per-lane offsets do not change only recomputes the scalar base, so a copy
 // costs no vector instructions.  lds is an LDS byte address (lds_addr).
+// The base goes through readfirstlane so it is an SGPR pair even where the
+// compiler cannot prove it uniform.  The builtin returns int: each half is
+// taken back to uint32_t before widening, or the low half would be
+// sign-extended into the high one.
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
 __device__ __forceinline__ void copy16_to_lds_s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
+               "s"(lds)
                : "memory", "m0");
 }
 __device__ __forceinline__ void copy4_to_lds_s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
+               "s"(lds)
                : "memory", "m0");
 }
 
