@@ -40,7 +40,10 @@
  *    errors are returned before anything is launched; a failed launch
  *    returns TA_EHIP.
  *  - Plans are immutable after tree_plan returns and may be shared between
- *    threads.  The library keeps no global mutable state.
+ *    threads.  The library's only global mutable state is one hipBLASLt
+ *    handle per device (with the mutex that guards its creation), created by
+ *    the first tree_lmhead_nll call with gradients on that device and kept
+ *    until the process ends; every other call keeps nothing between calls.
  */
 #ifndef TREE_ATTN_H
 #define TREE_ATTN_H
@@ -316,7 +319,11 @@ ta_status tree_decode_ws_bytes(int32_t B, int32_t Hq, int32_t d, int32_t max_len
  * q, o: [B, Hq, d]; k, v: [L_total, Hkv, d]; lse: [B, Hq] fp32.
  * span_ptr [B + 1] and spans [.., 2] (device int32): item b reads the rows
  * spans[s] = (start, len) for s in [span_ptr[b], span_ptr[b+1]) in order
- * (plain decode: one span; tree decode: the ancestor chain of a leaf).
+ * (plain decode: one span; tree decode: the ancestor chain of a leaf).  The
+ * call does not know the K/V row count and does not read the span tables on
+ * the host: the caller guarantees every span lies inside k / v and every
+ * item's total length is at most max_len (the Python binding checks both on
+ * the host unless asked not to).
  * max_len bounds every item's total length.  dt: TA_BF16, d = 128.
  * Precision: q.k products of bf16 values accumulate exactly in fp32; the
  * probabilities are rounded to bf16 for the P V product (fp32 accumulation);

@@ -403,14 +403,20 @@ def _stream(t):
 
 
 def _need(t, name, shape, dtype, device):
-    if not t.is_cuda or t.device != device:
-        raise ValueError(f"{name} must live on {device}")
+    """Every tensor handed to the library (inputs, and outputs the caller
+    supplies) must have exactly this shape and dtype, be contiguous and live
+    on the call's device: the kernels take raw pointers."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must live on {device}")
 
 
 def _events(events):
@@ -458,7 +464,14 @@ class HipEvents:
 
 
 def _workspace(nbytes, device, ws):
+    """A caller-supplied workspace must be a contiguous uint8 tensor on the
+    call's device; one smaller than nbytes is replaced by a fresh buffer."""
     import torch
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous uint8 tensor")
+        if not ws.is_cuda or ws.device != device:
+            raise ValueError(f"ws must live on {device}")
     if nbytes == 0:
         return None, 0
     if ws is not None and ws.numel() >= nbytes:
@@ -518,6 +531,9 @@ def tree_attn_bwd(plan: Plan, q, k, v, o, lse, dO, scale: float = 0.0, rope_base
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", (N, Hq, d), q.dtype, dev)
+    _need(dk, "dk", (N, Hkv, d), q.dtype, dev)
+    _need(dv, "dv", (N, Hkv, d), q.dtype, dev)
     dt = _dt(q)
     wsb = attn_ws_bytes(plan, 2 if recompute_dq else 1, dt, Hq, Hkv, d, rope_base)
     ws, wsn = _workspace(wsb, dev, ws)
@@ -578,6 +594,9 @@ def tree_partition_bwd(part: Partition, q, k, v, o, lse, dO, scale: float = 0.0,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", (N, Hq, d), q.dtype, dev)
+    _need(dk, "dk", (N, Hkv, d), q.dtype, dev)
+    _need(dv, "dv", (N, Hkv, d), q.dtype, dev)
     dt = _dt(q)
     ws, wsn = _workspace(partition_ws_bytes(part, 1, dt, Hq, Hkv, d, rope_base), dev, ws)
     _check("tree_partition_bwd", load_library().tree_partition_bwd(
@@ -609,6 +628,9 @@ def tree_lmhead_nll(h, W, labels, w, ignore_index: int = -100, need_grad: bool =
     loss = torch.zeros(1, dtype=torch.float32, device=dev) if loss is None else loss
     lse = torch.empty(N, dtype=torch.float32, device=dev) if lse is None else lse
     err_flag = torch.zeros(1, dtype=torch.int32, device=dev) if err_flag is None else err_flag
+    _need(loss, "loss", (1,), torch.float32, dev)
+    _need(lse, "lse", (N,), torch.float32, dev)
+    _need(err_flag, "err_flag", (1,), torch.int32, dev)
     if need_grad:
         dh = torch.empty_like(h) if dh is None else dh
         dW = torch.empty_like(W) if dW is None else dW
@@ -643,6 +665,7 @@ def tree_scan_fwd(route: Route, a, b, h=None, ws=None):
     for name, t in (("a", a), ("b", b)):
         _need_rows(route, name, t, C)
     h = torch.empty_like(a) if h is None else h
+    _need_rows(route, "h", h, C)
     ws, wsn = _workspace(_route_ws("tree_scan_ws_bytes", route, C), a.device, ws)
     _check("tree_scan_fwd", load_library().tree_scan_fwd(route.handle, _ptr(route.device(a.device)), _ptr(a), _ptr(b),
                                                          C, _ptr(h), _ptr(ws), wsn, _stream(a)))
@@ -656,6 +679,8 @@ def tree_scan_bwd(route: Route, a, h, dh, da=None, db=None, ws=None):
         _need_rows(route, name, t, C)
     da = torch.empty_like(a) if da is None else da
     db = torch.empty_like(a) if db is None else db
+    _need_rows(route, "da", da, C)
+    _need_rows(route, "db", db, C)
     ws, wsn = _workspace(_route_ws("tree_scan_ws_bytes", route, C), a.device, ws)
     _check("tree_scan_bwd", load_library().tree_scan_bwd(route.handle, _ptr(route.device(a.device)), _ptr(a), _ptr(h),
                                                          _ptr(dh), C, _ptr(da), _ptr(db), _ptr(ws), wsn, _stream(a)))
@@ -669,6 +694,7 @@ def tree_conv_fwd(route: Route, x, w, y=None):
     _need_rows(route, "x", x, C)
     _need(w, "w", (C, route.conv_k), torch.float32, x.device)
     y = torch.empty_like(x) if y is None else y
+    _need_rows(route, "y", y, C)
     _check("tree_conv_fwd", load_library().tree_conv_fwd(route.handle, _ptr(route.device(x.device)), _ptr(x), _ptr(w),
                                                          C, _ptr(y), _stream(x)))
     return y
@@ -682,6 +708,8 @@ def tree_conv_bwd(route: Route, x, w, dy, dx=None, dw=None, ws=None):
     _need(w, "w", (C, route.conv_k), torch.float32, x.device)
     dx = torch.empty_like(x) if dx is None else dx
     dw = torch.empty_like(w) if dw is None else dw
+    _need_rows(route, "dx", dx, C)
+    _need(dw, "dw", (C, route.conv_k), torch.float32, x.device)
     ws, wsn = _workspace(_route_ws("tree_conv_ws_bytes", route, C), x.device, ws)
     _check("tree_conv_bwd", load_library().tree_conv_bwd(route.handle, _ptr(route.device(x.device)), _ptr(x), _ptr(w),
                                                          _ptr(dy), C, _ptr(dx), _ptr(dw), _ptr(ws), wsn, _stream(x)))
@@ -702,6 +730,10 @@ def tree_weighted_nll(logits, labels, w, ignore_index: int = -100, need_grad: bo
         dlogits = torch.empty_like(logits)
     if err_flag is None:
         err_flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(loss, "loss", (1,), torch.float32, dev)
+    _need(err_flag, "err_flag", (1,), torch.int32, dev)
+    if need_grad:
+        _need(dlogits, "dlogits", (N, V), torch.float32, dev)
     n = ctypes.c_size_t()
     L = load_library()
     _check("tree_nll_ws_bytes", L.tree_nll_ws_bytes(N, V, ctypes.byref(n)))
@@ -720,10 +752,30 @@ def decode_ws_bytes(B, Hq, d, max_len, n_splits=0):
     return int(n.value), int(s.value)
 
 
+def _check_spans(span_ptr, spans, n_rows: int, max_len: int):
+    """Host check of the decode span tables (one small device-to-host copy):
+    span_ptr non-decreasing from 0 to the span count, every (start, len) span
+    inside [0, n_rows), and every item's total length at most max_len."""
+    sp = span_ptr.cpu().numpy().astype(np.int64)
+    s = spans.cpu().numpy().astype(np.int64).reshape(-1, 2)
+    if sp[0] != 0 or np.any(np.diff(sp) < 0) or sp[-1] > len(s):
+        raise ValueError("span_ptr must rise from 0 to at most the number of spans")
+    used = s[:sp[-1]]
+    if np.any(used[:, 1] < 0) or np.any(used[:, 0] < 0) or np.any(used[:, 0] + used[:, 1] > n_rows):
+        raise ValueError(f"a span lies outside the {n_rows} K/V rows")
+    tot = np.add.reduceat(np.concatenate([used[:, 1], [0]]), sp[:-1]) if len(sp) > 1 else np.zeros(0)
+    tot = np.where(np.diff(sp) > 0, tot, 0)
+    if np.any(tot > max_len):
+        raise ValueError(f"an item's spans add up to more than max_len = {max_len}")
+
+
 def tree_decode_splitkv(q, k, v, span_ptr, spans, max_len: int, scale: float = 0.0, n_splits: int = 0,
-                        o=None, lse=None, ws=None, events=None):
+                        o=None, lse=None, ws=None, events=None, check_spans: bool = True):
     """Split-KV single-query decode.  q [B,Hq,d] bf16; k/v [L,Hkv,d] bf16;
-    span_ptr [B+1], spans [S,2] int32 on the device -> o [B,Hq,d], lse [B,Hq]."""
+    span_ptr [B+1], spans [S,2] int32 on the device -> o [B,Hq,d], lse [B,Hq].
+    check_spans: verify on the host (one synchronising copy of the two small
+    tables) that every span lies inside k's rows and every item within
+    max_len; with False the caller guarantees it, as the C call requires."""
     import torch
     B, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -733,8 +785,14 @@ def tree_decode_splitkv(q, k, v, span_ptr, spans, max_len: int, scale: float = 0
     _need(v, "v", tuple(k.shape), torch.bfloat16, dev)
     _need(span_ptr, "span_ptr", (B + 1,), torch.int32, dev)
     _need(spans, "spans", tuple(spans.shape), torch.int32, dev)
+    if spans.dim() != 2 or spans.shape[1] != 2:
+        raise ValueError("spans must have shape (S, 2)")
+    if check_spans:
+        _check_spans(span_ptr, spans, k.shape[0], max_len)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty(B, Hq, dtype=torch.float32, device=dev) if lse is None else lse
+    _need(o, "o", (B, Hq, d), torch.bfloat16, dev)
+    _need(lse, "lse", (B, Hq), torch.float32, dev)
     wsb, _ = decode_ws_bytes(B, Hq, d, max_len, n_splits)
     ws, wsn = _workspace(wsb, dev, ws)
     ev, nev = _events(events)

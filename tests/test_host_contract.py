@@ -31,3 +31,57 @@ def test_missing_library_fails_loudly():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("raised"), r.stdout
+
+
+def test_binding_checks_buffers_on_the_host():
+    """The binding rejects, before any launch, tensors whose shape, dtype,
+    layout or device differ from what the kernels assume (they take raw
+    pointers), malformed workspaces, and decode span tables that leave the
+    K/V rows or exceed max_len."""
+    import numpy as np
+    import pytest
+    import torch
+    import prefix_shared_masked_amd as pkg
+    cpu = torch.device("cpu")
+    x = torch.zeros(4, 2, 8)
+    with pytest.raises(ValueError, match="shape"):
+        pkg._need(x, "dq", (4, 2, 16), torch.float32, cpu)
+    with pytest.raises(ValueError, match="dtype"):
+        pkg._need(x, "dq", (4, 2, 8), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        pkg._need(x.transpose(0, 1), "dq", (2, 4, 8), torch.float32, cpu)
+    with pytest.raises(ValueError, match="live on"):
+        pkg._need(x, "dq", (4, 2, 8), torch.float32, cpu)  # a CPU tensor is never accepted
+    with pytest.raises(ValueError, match="uint8"):
+        pkg._workspace(64, cpu, torch.zeros(64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="contiguous uint8"):
+        pkg._workspace(64, cpu, torch.zeros(128, dtype=torch.uint8)[::2])
+    with pytest.raises(ValueError, match="live on"):
+        pkg._workspace(64, cpu, torch.zeros(64, dtype=torch.uint8))
+    i32 = lambda a: torch.tensor(np.asarray(a, np.int32))
+    pkg._check_spans(i32([0, 1, 3]), i32([[0, 10], [10, 5], [20, 4]]), 24, 10)
+    with pytest.raises(ValueError, match="outside"):
+        pkg._check_spans(i32([0, 1, 3]), i32([[0, 10], [10, 5], [20, 5]]), 24, 10)
+    with pytest.raises(ValueError, match="outside"):
+        pkg._check_spans(i32([0, 1]), i32([[-1, 3]]), 24, 10)
+    with pytest.raises(ValueError, match="max_len"):
+        pkg._check_spans(i32([0, 1, 3]), i32([[0, 10], [10, 5], [20, 4]]), 24, 8)
+    with pytest.raises(ValueError, match="span_ptr"):
+        pkg._check_spans(i32([0, 2, 1]), i32([[0, 1], [1, 1]]), 24, 10)
+    pkg._check_spans(i32([0, 0, 1]), i32([[3, 2]]), 24, 10)  # an empty item is fine
+
+
+def test_library_global_state_is_the_documented_handle():
+    """The header states that the library's only global mutable state is the
+    hipBLASLt handle table of the output layer (and the mutex guarding it):
+    list the writable data objects the built library defines in its own
+    namespace (kernel launch stubs, which are functions, excluded)."""
+    import re
+    lib = os.path.join(ROOT, "prefix_shared_masked_amd", "libtree_attn.so")
+    out = subprocess.run(["nm", "-C", "--defined-only", lib], capture_output=True, text=True, check=True).stdout
+    objs = set()
+    for line in out.splitlines():
+        parts = line.split(maxsplit=2)
+        if len(parts) == 3 and parts[1] in "bBdD" and parts[2].startswith("ta::") and "(" not in parts[2]:
+            objs.add(parts[2])
+    assert objs == {"ta::lmh::g_mu", "ta::lmh::g_handles"}, objs
