@@ -211,8 +211,14 @@ ta_status tree_attn_ws_bytes(const ta_plan* plan, int32_t op, ta_dtype dt, int32
  * 0 disables it.  ws: tree_attn_ws_bytes(op = 0) bytes of device memory.
  * Precision of the bf16 path: scores use fp16 copies of (rotated) Q and K,
  * which hold every bf16 value of magnitude <= 65504 exactly and rotated
- * values with 8x finer rounding than bf16 (larger magnitudes saturate);
- * P is rounded to bf16 for P V; accumulation is fp32 throughout.
+ * values with 8x finer rounding than bf16; P is rounded to bf16 for P V;
+ * accumulation is fp32 throughout.
+ * Saturation flag (TA_BF16): the first int32 of ws.  A (rotated, scaled) Q
+ * or K value beyond the fp16 range is clamped to +-65504 and the call stores
+ * 1 there; NaN inputs pass through unclamped (and reach the outputs as NaN).
+ * The library never clears the flag: the caller zeroes it and reads it back
+ * when it wants to know (tree_attn_bwd uses the same word of its workspace,
+ * the partition calls the first word of theirs).
  * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_ENOMEM (ws too small), TA_EHIP. */
 ta_status tree_attn_fwd(const ta_plan* plan, const void* dplan, ta_dtype dt, const void* q,
                         const void* k, const void* v, int32_t Hq, int32_t Hkv, int32_t d,

@@ -22,6 +22,7 @@ import os
 import numpy as np
 
 __all__ = ["TreeAttnError", "Plan", "Partition", "HipEvents", "tree_plan", "tree_partition", "tree_attn_fwd",
+           "saturation_flag", "clear_saturation_flag",
            "tree_attn_bwd", "tree_partition_fwd", "tree_partition_bwd", "tree_weighted_nll", "tree_lmhead_nll",
            "Route", "tree_route", "tree_scan_fwd", "tree_scan_bwd", "tree_conv_fwd", "tree_conv_bwd",
            "tree_decode_splitkv", "library_path", "load_library", "TA_BLOCK_M", "TA_BLOCK_N", "TA_BLOCK_KV"]
@@ -463,6 +464,18 @@ class HipEvents:
                 self._hip.hipEventDestroy(self.arr[i])
 
 
+def saturation_flag(ws) -> int:
+    """The bf16 attention calls' saturation flag (the first int32 of their
+    workspace): 1 when a Q or K value beyond the fp16 range was clamped since
+    the flag was last cleared (a synchronising read)."""
+    return int(ws[:4].view(__import__("torch").int32).item())
+
+
+def clear_saturation_flag(ws) -> None:
+    """Zero the saturation flag of a workspace (asynchronously, on the current stream)."""
+    ws[:4].zero_()
+
+
 def _workspace(nbytes, device, ws):
     """A caller-supplied workspace must be a contiguous uint8 tensor on the
     call's device; one smaller than nbytes is replaced by a fresh buffer."""
@@ -477,6 +490,7 @@ def _workspace(nbytes, device, ws):
     if ws is not None and ws.numel() >= nbytes:
         return ws, ws.numel()
     buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    buf[:min(nbytes, 4)].zero_()  # a fresh workspace starts with a clear saturation flag
     return buf, nbytes
 
 

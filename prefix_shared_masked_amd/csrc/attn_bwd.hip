@@ -56,6 +56,7 @@ struct DQParams {
   bf16* dq;
   float* nld;   // [Hq][nqb][64] out: per 32-row query block, -LSE * log2(e) of its rows, then -D
   f16* qs;      // [N, Hq, d] out: fp16 copy of Q (rotated when RoPE is on)
+  int32_t* sat;  // saturation flag (fp16 conversion of Q clamped)
   const int32_t* pos;
   const int32_t* fq_ptr;
   const int32_t* fq_chunk;
@@ -134,6 +135,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
   bf16x8 qf[8], df[8];
   float Di, lse_i;
   {
+    bool sat = false;
     const bool rot = P.rope_base > 0.f && qvalid;
     const int p = qvalid ? P.pos[qi] : 0;
     float dsum = 0.f;
@@ -154,8 +156,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
         }
         qf[s][e] = (bf16)x1;
         qf[s + 4][e] = (bf16)x2;
-        qh1[e] = to_f16_sat(x1);
-        qh2[e] = to_f16_sat(x2);
+        qh1[e] = to_f16_sat(x1, sat);
+        qh2[e] = to_f16_sat(x2, sat);
       }
       if (active && qvalid) {
         *(f16x8*)(P.qs + rowoff + s * 16 + half * 8) = qh1;
@@ -172,6 +174,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
         dsum += (float)td[e] * (float)to[e];
       }
     }
+    report_sat(P.sat, sat && active);
     Di = dsum + __shfl_xor(dsum, 32);
     if (!qvalid) Di = 0.f;
     lse_i = qvalid ? P.lse[(size_t)h * P.N + qi] * TA_LOG2E : 0.f;
@@ -766,6 +769,7 @@ struct PrepParams {
   const float* lse;
   f16* qs;
   float* nld;  // [Hq][nqb][64]: per 32-row query block, -LSE * log2(e), then -D
+  int32_t* sat;  // saturation flag (fp16 conversion of Q clamped)
   const int32_t* pos;
   int N, Hq, q0, nqb;
   float rope_base;
@@ -793,6 +797,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
   const bool rot = P.rope_base > 0.f;
   const int p = P.pos[row];
   float dsum = 0.f;
+  bool sat = false;
   f16x8 h1, h2;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -805,9 +810,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
       x2 = x2 * cs + x1 * sn;
       x1 = y1;
     }
-    h1[e] = to_f16_sat(x1);
-    h2[e] = to_f16_sat(x2);
+    h1[e] = to_f16_sat(x1, sat);
+    h2[e] = to_f16_sat(x2, sat);
   }
+  report_sat(P.sat, sat);
   *(f16x8*)(P.qs + off) = h1;
   *(f16x8*)(P.qs + off + D / 2) = h2;
   dsum += __shfl_xor(dsum, 1);
@@ -1040,6 +1046,7 @@ size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t
   const size_t N = p->n_tokens;
   size_t b = 0;
   if (dt == TA_BF16) {
+    b += TA_WS_FLAG_BYTES;                                                           // saturation flag
     b += align256((size_t)Hq * p->n_qtiles * 64 * sizeof(float));                    // -LSE log2(e), -D blocks
     b += align256(N * Hq * d * sizeof(f16)) + align256(N * Hkv * d * sizeof(f16));  // fp16 Q, K
     if (rope_base > 0.f) b += align256(N * Hkv * d * sizeof(bf16));                 // rotated bf16 K
@@ -1090,6 +1097,8 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   char* w = (char*)ws;
 
   if (dt == TA_BF16) {
+    int32_t* sat = (int32_t*)w;
+    w += TA_WS_FLAG_BYTES;
     float* nld = (float*)w;
     w += align256((size_t)Hq * p->n_qtiles * 64 * sizeof(float));
     f16* qs = (f16*)w;
@@ -1110,7 +1119,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     // the rotated bf16 K for dQ
     const bf16* kb = rope ? krot : (const bf16*)k;
     if (launch_rope<bf16, f16>((const bf16*)k, ks, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E,
-                               ds_path ? nullptr : krot) != hipSuccess)
+                               ds_path ? nullptr : krot, sat) != hipSuccess)
       return TA_EHIP;
     if (ds_path) {
       bwd::PrepParams R;
@@ -1120,6 +1129,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
       R.lse = lse;
       R.qs = qs;
       R.nld = nld;
+      R.sat = sat;
       R.pos = pos;
       R.N = N;
       R.Hq = Hq;
@@ -1143,6 +1153,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     A.dq = (bf16*)dq;
     A.nld = nld;
     A.qs = qs;
+    A.sat = sat;
     A.pos = pos;
     A.fq_ptr = fq_ptr;
     A.fq_chunk = fq_chunk;

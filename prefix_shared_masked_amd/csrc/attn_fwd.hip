@@ -40,13 +40,14 @@ namespace ta {
 // pair are computed once and applied to all H heads (consecutive lanes take
 // consecutive i, so every access is coalesced).
 template <typename T>
-__device__ __forceinline__ T cvt_out(float x) { return (T)x; }
+__device__ __forceinline__ T cvt_out(float x, bool&) { return (T)x; }
 template <>
-__device__ __forceinline__ f16 cvt_out<f16>(float x) { return to_f16_sat(x); }
+__device__ __forceinline__ f16 cvt_out<f16>(float x, bool& sat) { return to_f16_sat(x, sat); }
 
 template <typename Ti, typename To>
 __global__ void rope_kernel(const Ti* x, To* y, bf16* y2, const int32_t* __restrict__ pos,  // x may alias y
-                            int N, int H, int d, float base, int transpose, float mul) {
+                            int N, int H, int d, float base, int transpose, float mul, int32_t* sat_flag) {
+  bool sat = false;
   const int half = d / 2;
   const size_t total = (size_t)N * half;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -60,31 +61,32 @@ __global__ void rope_kernel(const Ti* x, To* y, bf16* y2, const int32_t* __restr
       const size_t row = ((size_t)t * H + h) * d;
       const float x1 = (float)x[row + i], x2 = (float)x[row + i + half];
       const float r1 = x1 * c - x2 * s, r2 = x2 * c + x1 * s;
-      y[row + i] = cvt_out<To>(mul * r1);
-      y[row + i + half] = cvt_out<To>(mul * r2);
+      y[row + i] = cvt_out<To>(mul * r1, sat);
+      y[row + i + half] = cvt_out<To>(mul * r2, sat);
       if (y2) {
         y2[row + i] = (bf16)r1;
         y2[row + i + half] = (bf16)r2;
       }
     }
   }
+  report_sat(sat_flag, sat);
 }
 
 template <typename Ti, typename To>
 hipError_t launch_rope(const Ti* x, To* y, const int32_t* pos, int N, int H, int d, float base, int transpose,
-                       hipStream_t st, float mul, bf16* y2) {
+                       hipStream_t st, float mul, bf16* y2, int32_t* sat_flag) {
   const size_t total = (size_t)N * (d / 2);
   if (total == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
   hipLaunchKernelGGL((rope_kernel<Ti, To>), dim3(blocks), dim3(256), 0, st, x, y, y2, pos, N, H, d, base, transpose,
-                     mul);
+                     mul, sat_flag);
   return hipGetLastError();
 }
 
 template hipError_t launch_rope<float, float>(const float*, float*, const int32_t*, int, int, int, float, int,
-                                              hipStream_t, float, bf16*);
+                                              hipStream_t, float, bf16*, int32_t*);
 template hipError_t launch_rope<bf16, f16>(const bf16*, f16*, const int32_t*, int, int, int, float, int,
-                                           hipStream_t, float, bf16*);
+                                           hipStream_t, float, bf16*, int32_t*);
 
 namespace fwd {
 
@@ -102,6 +104,7 @@ struct Params {
   const int32_t* fq_ptr;
   const int32_t* fq_chunk;
   const int32_t* fq_order;
+  int32_t* sat;  // saturation flag (fp16 conversion of Q clamped), may be null
   int N, Hq, Hkv, G;
   int q0;  // first query row (rows below are a key-only prefix)
   float rope_base;
@@ -157,6 +160,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
   // column, k-slots s*16 + half*8 + e.
   f16x8 qf[8];
   {
+    bool sat = false;
     const bf16* qrow = P.q + ((size_t)(qvalid ? qi : 0) * P.Hq + h) * D + half * 8;
     const bool rot = P.rope_base > 0.f && qvalid;
     const int p = qvalid ? P.pos[qi] : 0;
@@ -174,10 +178,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(Params P) {
           x2 = x2 * cs + x1 * sn;
           x1 = y1;
         }
-        qf[s][e] = to_f16_sat(x1);
-        qf[s + 4][e] = to_f16_sat(x2);
+        qf[s][e] = to_f16_sat(x1, sat);
+        qf[s + 4][e] = to_f16_sat(x2, sat);
       }
     }
+    report_sat(P.sat, sat && active);
   }
 
   // Staging.  Copy k (k = 0..3) of wavefront w fills rows 4(w + 4k) + l/16
@@ -511,7 +516,7 @@ ta_status check_common(const ta_plan* p, const void* dplan, ta_dtype dt, int32_t
 
 size_t fwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base) {
   const size_t N = p->n_tokens;
-  if (dt == TA_BF16) return align256(N * Hkv * d * sizeof(f16));  // fp16 (rotated) K
+  if (dt == TA_BF16) return TA_WS_FLAG_BYTES + align256(N * Hkv * d * sizeof(f16));  // flag, fp16 (rotated) K
   if (rope_base <= 0.f) return 0;
   return align256(N * Hq * d * sizeof(float)) + align256(N * Hkv * d * sizeof(float));
 }
@@ -556,9 +561,10 @@ extern "C" ta_status tree_attn_fwd_ex(const ta_plan* p, const void* dplan, ta_dt
 
   mark(ev, nev, 0, stream);
   if (dt == TA_BF16) {
-    f16* kk = (f16*)ws;
-    if (launch_rope<bf16, f16>((const bf16*)k, kk, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E) !=
-        hipSuccess)
+    int32_t* sat = (int32_t*)ws;
+    f16* kk = (f16*)((char*)ws + TA_WS_FLAG_BYTES);
+    if (launch_rope<bf16, f16>((const bf16*)k, kk, pos, N, Hkv, d, rope_base, 0, stream, scale * TA_LOG2E, nullptr,
+                               sat) != hipSuccess)
       return TA_EHIP;
     mark(ev, nev, 1, stream);
     fwd::Params P;
@@ -571,6 +577,7 @@ extern "C" ta_status tree_attn_fwd_ex(const ta_plan* p, const void* dplan, ta_dt
     P.fq_ptr = fq_ptr;
     P.fq_chunk = fq_chunk;
     P.fq_order = fq_order;
+    P.sat = sat;
     P.N = N;
     P.Hq = Hq;
     P.Hkv = Hkv;

@@ -59,9 +59,19 @@ __device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const 
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// fp32 -> fp16 with saturation at the largest finite fp16 (65504), so an
-// out-of-range activation can never turn into inf inside a score.
-__device__ __forceinline__ f16 to_f16_sat(float x) { return (f16)fminf(fmaxf(x, -65504.f), 65504.f); }
+// fp32 -> fp16 for the score operands: a value beyond the largest finite
+// fp16 (65504) clamps to +-65504, so it never becomes inf inside a score, and
+// sets `sat`; NaN passes through unchanged (the NaN-propagating maximum and
+// minimum), so a NaN input still shows up as NaN in the outputs it reaches.
+__device__ __forceinline__ f16 to_f16_sat(float x, bool& sat) {
+  sat |= fabsf(x) > 65504.f;  // false for NaN
+  return (f16)__builtin_elementwise_minimum(__builtin_elementwise_maximum(x, -65504.f), 65504.f);
+}
+// Raise a caller-visible saturation flag (a device int32; may be null) from
+// every lane that clamped.  Every writer stores the same 1.
+__device__ __forceinline__ void report_sat(int32_t* flag, bool sat) {
+  if (flag && sat) *(volatile int32_t*)flag = 1;
+}
 
 // LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lane x points at row x/4, columns 4*(x%4)..+3 of a 4x16 bf16 block and
@@ -252,7 +262,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // receives the rotated values (without mul) in bf16.
 template <typename Ti, typename To>
 hipError_t launch_rope(const Ti* x, To* y, const int32_t* pos, int N, int H, int d, float base, int transpose,
-                       hipStream_t st, float mul = 1.f, bf16* y2 = nullptr);
+                       hipStream_t st, float mul = 1.f, bf16* y2 = nullptr, int32_t* sat_flag = nullptr);
+
+// Saturation flag of the bf16 attention calls: a device int32 at the start of
+// their workspaces (the scratch they use starts TA_WS_FLAG_BYTES later).
+constexpr size_t TA_WS_FLAG_BYTES = 256;
 
 }  // namespace ta
 

@@ -171,8 +171,10 @@ hipError_t cast(const float* x, bf16* y, int64_t n, hipStream_t st) {
 }
 
 // Workspace layout of the drivers (offsets in bytes, each 256-aligned).
+// The local attention workspace comes first, so its saturation flag is the
+// first word of the partition workspace, as in tree_attn_fwd / _bwd.
 struct WsLayout {
-  size_t q, k, v, o, lse, dO, dq, dk, dv, acc_k, acc_v, attn, total;
+  size_t attn, attn_bytes, q, k, v, o, lse, dO, dq, dk, dv, acc_k, acc_v, total;
 };
 
 WsLayout layout(const ta_partition* P, int op, ta_dtype dt, int Hq, int Hkv, int d, float rope_base) {
@@ -186,6 +188,16 @@ WsLayout layout(const ta_partition* P, int op, ta_dtype dt, int Hq, int Hkv, int
     off += b;
     return x;
   };
+  size_t attn = 0;
+  for (int p = 0; p < P->n_parts; ++p) {
+    const ta_plan* pl = P->plans[p];
+    if (!pl) continue;
+    size_t b = 0;
+    tree_attn_ws_bytes(pl, op, dt, Hq, Hkv, d, rope_base, &b);
+    attn = std::max(attn, b);
+  }
+  L.attn_bytes = align256(attn);
+  L.attn = take(L.attn_bytes);
   L.q = take(qb);
   L.k = take(kb);
   L.v = take(kb);
@@ -201,15 +213,6 @@ WsLayout layout(const ta_partition* P, int op, ta_dtype dt, int Hq, int Hkv, int
       L.acc_v = take(align256(N * Hkv * d * sizeof(float)));
     }
   }
-  size_t attn = 0;
-  for (int p = 0; p < P->n_parts; ++p) {
-    const ta_plan* pl = P->plans[p];
-    if (!pl) continue;
-    size_t b = 0;
-    tree_attn_ws_bytes(pl, op, dt, Hq, Hkv, d, rope_base, &b);
-    attn = std::max(attn, b);
-  }
-  L.attn = take(align256(attn));
   L.total = off;
   return L;
 }
@@ -289,7 +292,7 @@ extern "C" ta_status tree_partition_fwd(const ta_partition* P, const void* dpart
     GW_HIP(gw::gather(k, idx, w + L.k, R, 0, krow, 1, 0, 0, stream));
     GW_HIP(gw::gather(v, idx, w + L.v, R, 0, krow, 1, 0, 0, stream));
     GW_TA(tree_attn_fwd(pl, dp + P->off_plan[p], dt, w + L.q, w + L.k, w + L.v, Hq, Hkv, d, scale, rope_base,
-                        w + L.o, (float*)(w + L.lse), w + L.attn, ws_bytes - L.attn, stream));
+                        w + L.o, (float*)(w + L.lse), w + L.attn, L.attn_bytes, stream));
     // own rows back to the whole tree: O rows, LSE columns ([Hq, N] layout)
     GW_HIP(gw::scatter(w + L.o + q0 * qrow, idx + q0, o, R - q0, qrow, 1, 0, 0, stream));
     GW_HIP(gw::scatter(w + L.lse + q0 * sizeof(float), idx + q0, lse, R - q0, sizeof(float), Hq,
@@ -330,7 +333,7 @@ extern "C" ta_status tree_partition_bwd(const ta_partition* P, const void* dpart
                       stream));
     GW_TA(tree_attn_bwd(pl, dp + P->off_plan[p], dt, w + L.q, w + L.k, w + L.v, w + L.o, (const float*)(w + L.lse),
                         w + L.dO, Hq, Hkv, d, scale, rope_base, w + L.dq, w + L.dk, w + L.dv, w + L.attn,
-                        ws_bytes - L.attn, stream));
+                        L.attn_bytes, stream));
     GW_HIP(gw::scatter(w + L.dq + q0 * qrow, idx + q0, dq, R - q0, qrow, 1, 0, 0, stream));
     // relay: every local key row, the gateway chain included, into fp32
     GW_HIP(gw::scatter_add(dt, w + L.dk, idx, acc_k, R, kel, stream));

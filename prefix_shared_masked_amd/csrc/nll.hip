@@ -29,12 +29,14 @@ __global__ __launch_bounds__(THREADS) void row_kernel(const float* __restrict__ 
   const int row = blockIdx.x;
   const float* x = logits + (size_t)row * V;
   float m = -INFINITY, s = 0.f;
+  // A masked logit (-inf) adds nothing: its term is skipped rather than
+  // evaluated as exp(-inf - -inf).
   for (int j = threadIdx.x; j < V; j += THREADS) {
     const float v = x[j];
     if (v > m) {
       s = s * expf(m - v) + 1.f;
       m = v;
-    } else {
+    } else if (v != -INFINITY) {
       s += expf(v - m);
     }
   }
@@ -77,11 +79,14 @@ __global__ __launch_bounds__(THREADS) void row_kernel(const float* __restrict__ 
 // 16-byte pieces.  exp2 is the hardware's; the reductions keep a fixed order.
 constexpr int UNROLL = 4;
 
+// Masked logits (-inf) contribute exp2(-inf) = 0; while every value seen so
+// far is -inf, the reference is taken as 0 so no -inf - -inf is evaluated.
 __device__ __forceinline__ void fold4(float& m, float& s, const float4& v) {
   const float pm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
   const float M = fmaxf(m, pm);
-  const float e = exp2f_fast((v.x - M) * TA_LOG2E) + exp2f_fast((v.y - M) * TA_LOG2E) +
-                  exp2f_fast((v.z - M) * TA_LOG2E) + exp2f_fast((v.w - M) * TA_LOG2E);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  const float e = exp2f_fast((v.x - Mu) * TA_LOG2E) + exp2f_fast((v.y - Mu) * TA_LOG2E) +
+                  exp2f_fast((v.z - Mu) * TA_LOG2E) + exp2f_fast((v.w - Mu) * TA_LOG2E);
   s = (m == -INFINITY ? 0.f : s * exp2f_fast((m - M) * TA_LOG2E)) + e;
   m = M;
 }

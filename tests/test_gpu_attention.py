@@ -244,3 +244,53 @@ def test_varlen_forest_full_size_sampled():
     close("dq(sampled)", dq[rows[:4]], gq, torch.bfloat16)
     close("dk(sampled)", dk[keys], gk, torch.bfloat16)
     close("dv(sampled)", dv[keys], gv, torch.bfloat16)
+
+
+def test_bf16_saturation_flag_and_nan_passthrough():
+    """fp16 score operands: a Q or K value beyond the fp16 range is clamped
+    and raises the workspace's saturation flag (forward and backward, both
+    backward paths); ordinary inputs leave it clear; a NaN in one query
+    element passes through to exactly that (row, head) of O and LSE and
+    raises no flag, the other rows keep matching the oracle."""
+    tree = W.six_node_tree(16)
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    Hq, Hkv, d = 4, 2, 128
+    q, k, v, do = W.attention_inputs(3, plan.n_tokens, Hq, Hkv, d)
+    (Q, q64), (K, k64), (V, v64), (DO, _) = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+
+    def flags(Qx, Kx, rope):
+        wf = torch.empty(pkg.attn_ws_bytes(plan, 0, 1, Hq, Hkv, d, rope), dtype=torch.uint8, device=DEV)
+        pkg.clear_saturation_flag(wf)
+        o, lse = pkg.tree_attn_fwd(plan, Qx, Kx, V, rope_base=rope, ws=wf)
+        out = [pkg.saturation_flag(wf)]
+        for op_ in (1, 2):
+            wb = torch.empty(pkg.attn_ws_bytes(plan, op_, 1, Hq, Hkv, d, rope), dtype=torch.uint8, device=DEV)
+            pkg.clear_saturation_flag(wb)
+            pkg.tree_attn_bwd(plan, Qx, Kx, V, o, lse, DO, rope_base=rope, ws=wb, recompute_dq=op_ == 2)
+            out.append(pkg.saturation_flag(wb))
+        return out, o, lse
+
+    for rope in (0.0, 10000.0):
+        assert flags(Q, K, rope)[0] == [0, 0, 0]
+        Qb = Q.clone()
+        Qb[37, 1, 5] = 1e5
+        assert flags(Qb, K, rope)[0] == [1, 1, 1]
+        Kb = K.clone()
+        Kb[20, 0, 100] = -1e5
+        assert flags(Q, Kb, rope)[0] == [1, 1, 1]
+    Qn = Q.clone()
+    Qn[50, 2, 7] = float("nan")
+    fl, o, lse = flags(Qn, K, 0.0)
+    assert fl == [0, 0, 0]
+    torch.cuda.synchronize()
+    on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.isnan(on[50, 2]).all() and np.isnan(ln[2, 50])
+    mask = np.ones(on.shape[:2], bool)
+    mask[50, 2] = False
+    ref = oracle.per_path_attention(op, q64, k64, v64)
+    assert np.isfinite(on[mask]).all()
+    close("o", on[mask], ref["o"][mask], torch.bfloat16)
+    lmask = np.ones(ln.shape, bool)
+    lmask[2, 50] = False
+    close("lse", ln[lmask], ref["lse"][lmask], torch.bfloat16)

@@ -159,3 +159,37 @@ def test_decode_256k_sampled():
             assert np.abs(lse[b, hs].cpu().numpy() - rl[0]).max() <= 1e-3, (b, kvh)
     del k, v, ws
     torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("V,case", [(1001, "first256"), (256, "group4"), (151936, "mostly")])
+def test_nll_masked_logits(V, case):
+    """Masked logits (-inf) contribute nothing and get a zero gradient: -inf
+    in a lane's first columns (rows whose length is not a multiple of four),
+    a whole 16-byte group of -inf (V = 256), and rows almost entirely masked
+    at the vocabulary size of the benchmark; labels sit on unmasked columns."""
+    rng = np.random.default_rng(V)
+    n = 6 if V > 100000 else 40
+    x = rng.standard_normal((n, V)).astype(np.float32)
+    if case == "first256":
+        x[:, :256] = -np.inf
+        x[:, 300] = 0.5
+    elif case == "group4":
+        x[:, 8:12] = -np.inf
+        x[::2, :128] = -np.inf
+    else:
+        mask = rng.random((n, V)) < 0.999
+        mask[:, -5:] = False
+        x[mask] = -np.inf
+    labels = np.array([int(rng.choice(np.flatnonzero(np.isfinite(x[i])))) for i in range(n)], np.int32)
+    labels[1] = -100
+    w = rng.random(n).astype(np.float32)
+    loss, dl, err = pkg.tree_weighted_nll(torch.from_numpy(x).to(DEV), torch.from_numpy(labels).to(DEV),
+                                          torch.from_numpy(w).to(DEV))
+    rl, rdl, _ = oracle.weighted_nll(x, labels, w)
+    got = dl.cpu().numpy()
+    assert np.isfinite(loss.item()) and np.all(np.isfinite(got))
+    assert abs(loss.item() - rl) <= 1e-5 * max(1.0, abs(rl)), (loss.item(), rl)
+    assert float(np.abs(got - rdl).max()) <= 1e-6
+    assert np.all(got[~np.isfinite(x)] == 0.0)
+    assert int(err.item()) == 0

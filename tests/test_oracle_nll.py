@@ -60,3 +60,26 @@ def test_gradient_finite_difference():
             m[i, j] -= eps
             num = (oracle.weighted_nll(p, labels, w)[0] - oracle.weighted_nll(m, labels, w)[0]) / (2 * eps)
             assert dl[i, j] == pytest.approx(num, rel=1e-6, abs=1e-9)
+
+
+def test_masked_logits_equal_removed_columns():
+    """A logit of -inf (a masked vocabulary entry or action) is the same as
+    the column being absent: loss and the remaining gradient equal those of
+    the row without it, and the masked gradient is exactly zero."""
+    rng = np.random.default_rng(7)
+    n, V = 12, 40
+    x = rng.standard_normal((n, V))
+    keep = rng.random((n, V)) > 0.6
+    keep[:, 0] = True
+    labels = np.array([int(rng.choice(np.flatnonzero(keep[i]))) for i in range(n)])
+    labels[3] = -100
+    w = rng.random(n)
+    xm = np.where(keep, x, -np.inf)
+    loss, dl, tok = oracle.weighted_nll(xm, labels, w)
+    for i in range(n):
+        cols = np.flatnonzero(keep[i])
+        yi = -100 if labels[i] == -100 else int(np.flatnonzero(cols == labels[i])[0])
+        li, dli, toki = oracle.weighted_nll(x[i:i + 1, cols], np.array([yi]), w[i:i + 1])
+        assert tok[i] == pytest.approx(toki[0], rel=1e-13, abs=1e-15)
+        np.testing.assert_allclose(dl[i, cols], dli[0], rtol=1e-12, atol=1e-15)
+        assert np.all(dl[i, ~keep[i]] == 0.0)
