@@ -234,13 +234,30 @@ ta_status tree_attn_fwd(const ta_plan* plan, const void* dplan, ta_dtype dt, con
  * ws: tree_attn_ws_bytes(op = 1) bytes, or at least op = 2 bytes.  TA_BF16
  * with the op-1 size: the dK/dV kernel stores the fp16 dS of every (query
  * tile, 32-key sub-tile) block and dQ = scale * dS K reads it back (one
- * product); with less: dQ recomputes S and dP (three products) before dK/dV.
+ * product).  With less, the call uses what fits: when the dS blocks of at
+ * least one KV head fit, the KV heads run in rounds of as many as fit (a
+ * query head's dQ depends on its own KV head's keys only, so the results are
+ * bitwise the same); below that, dQ recomputes S and dP (three products)
+ * before dK/dV.  tree_attn_bwd_ws_budget picks the size for a byte budget.
  * Errors as tree_attn_fwd (TA_ENOMEM below the op-2 size). */
 ta_status tree_attn_bwd(const ta_plan* plan, const void* dplan, ta_dtype dt, const void* q,
                         const void* k, const void* v, const void* o, const float* lse,
                         const void* dO, int32_t Hq, int32_t Hkv, int32_t d, float scale,
                         float rope_base, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                         hipStream_t stream);
+
+/* The dS workspace grows with the visible pairs (2 bytes per pair and query
+ * head: 2.8 GB for the 16K-token spine tree at 32 query heads, 22 GB for a
+ * 133K-token varlen batch), so callers bound it.  tree_attn_bwd_ws_budget
+ * returns in *bytes the largest tree_attn_bwd workspace within `budget`
+ * bytes (0 selects TA_BWD_WS_BUDGET_DEFAULT) and in *kv_heads_per_round how
+ * many KV heads' dS blocks it holds: Hkv = one round (the op-1 size), fewer =
+ * rounds over the KV heads, 0 = the recompute path (the op-2 size).  Returns
+ * TA_ENOMEM, with *bytes = the op-2 size, when even that exceeds the budget. */
+#define TA_BWD_WS_BUDGET_DEFAULT ((size_t)8 << 30) /* 8 GiB */
+ta_status tree_attn_bwd_ws_budget(const ta_plan* plan, ta_dtype dt, int32_t Hq, int32_t Hkv,
+                                  int32_t d, float rope_base, size_t budget, size_t* bytes,
+                                  int32_t* kv_heads_per_round);
 
 /* Stage timing.  The *_ex variants behave exactly like the plain calls and,
  * when events is not NULL, also record events[i] (created by the caller with
@@ -251,9 +268,10 @@ ta_status tree_attn_bwd(const ta_plan* plan, const void* dplan, ta_dtype dt, con
  *                           [2] after the attention kernel.
  *   tree_attn_bwd_ex:       [0] start, [1] after the preparation passes;
  *                           bf16 with the dS workspace: [2] after the dK/dV
- *                           kernel and its partial sum, [3] after the dQ
- *                           kernel; otherwise [2] after the dQ kernel, [3]
- *                           after dK/dV.
+ *                           kernel and its partial sum (of the first round of
+ *                           KV heads), [3] after the (last) dQ kernel;
+ *                           otherwise [2] after the dQ kernel, [3] after
+ *                           dK/dV.
  *   tree_decode_splitkv_ex: [0] start, [1] after the partial kernel,
  *                           [2] after the merge kernel. */
 typedef struct ihipEvent_t* hipEvent_t;

@@ -99,6 +99,7 @@ def load_library():
         "tree_plan_upload": (I32, [P, P, SZ, P]),
         "tree_plan_free": (None, [P]),
         "tree_attn_ws_bytes": (I32, [P, I32, I32, I32, I32, I32, F32, ctypes.POINTER(SZ)]),
+        "tree_attn_bwd_ws_budget": (I32, [P, I32, I32, I32, I32, F32, SZ, ctypes.POINTER(SZ), pI32]),
         "tree_attn_fwd": (I32, [P, P, I32, P, P, P, I32, I32, I32, F32, F32, P, P, P, SZ, P]),
         "tree_attn_bwd": (I32, [P, P, I32, P, P, P, P, P, P, I32, I32, I32, F32, F32, P, P, P, P, SZ, P]),
         "tree_nll_ws_bytes": (I32, [I32, I32, ctypes.POINTER(SZ)]),
@@ -134,8 +135,13 @@ def load_library():
         "tree_conv_bwd": (I32, [P, P, P, P, P, I32, P, P, P, SZ, P]),
         "ta_status_string": (ctypes.c_char_p, [I32]),
     }
+    host_only = os.environ.get("TA_HOST_ONLY_LIBRARY") == "1"  # a planner-only build (sanitizer tests)
     for name, (res, args) in sigs.items():
-        fn = getattr(L, name)
+        fn = getattr(L, name, None)
+        if fn is None:
+            if host_only:
+                continue
+            raise TreeAttnError("load_library", 6) from AttributeError(f"{_LIB_PATH} lacks {name}")
         fn.restype = res
         fn.argtypes = args
     _lib = L
@@ -527,11 +533,26 @@ def tree_attn_fwd(plan: Plan, q, k, v, scale: float = 0.0, rope_base: float = 0.
     return o, lse
 
 
+def bwd_ws_budget(plan: Plan, dtype_code: int, Hq: int, Hkv: int, d: int, rope_base: float, budget: int = 0):
+    """(bytes, kv_heads_per_round) of the largest backward workspace within
+    `budget` bytes (0: the library default, 8 GiB); raises when even the
+    smallest workspace exceeds it."""
+    n, h = ctypes.c_size_t(), ctypes.c_int32()
+    _check("tree_attn_bwd_ws_budget", load_library().tree_attn_bwd_ws_budget(
+        plan.handle, dtype_code, Hq, Hkv, d, float(rope_base), int(budget), ctypes.byref(n), ctypes.byref(h)))
+    return int(n.value), int(h.value)
+
+
 def tree_attn_bwd(plan: Plan, q, k, v, o, lse, dO, scale: float = 0.0, rope_base: float = 0.0,
-                  dq=None, dk=None, dv=None, ws=None, events=None, recompute_dq: bool = False):
+                  dq=None, dk=None, dv=None, ws=None, events=None, recompute_dq: bool = False,
+                  ws_budget: int = 0):
     """Backward of tree_attn_fwd -> (dq, dk, dv), overwritten, deterministic.
-    recompute_dq: use the smallest workspace, in which dQ recomputes S and dP
-    instead of reading the dS blocks the dK/dV kernel stores (bf16)."""
+    Without a caller workspace the binding allocates the largest one within
+    ws_budget bytes (0: the library default, 8 GiB): the full dS workspace
+    when it fits, else the dS blocks of as many KV heads as fit (run in
+    rounds), else the smallest one.  recompute_dq: use the smallest workspace,
+    in which dQ recomputes S and dP instead of reading the dS blocks the dK/dV
+    kernel stores (bf16)."""
     import torch
     N, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -549,7 +570,12 @@ def tree_attn_bwd(plan: Plan, q, k, v, o, lse, dO, scale: float = 0.0, rope_base
     _need(dk, "dk", (N, Hkv, d), q.dtype, dev)
     _need(dv, "dv", (N, Hkv, d), q.dtype, dev)
     dt = _dt(q)
-    wsb = attn_ws_bytes(plan, 2 if recompute_dq else 1, dt, Hq, Hkv, d, rope_base)
+    if recompute_dq:
+        wsb = attn_ws_bytes(plan, 2, dt, Hq, Hkv, d, rope_base)
+    elif ws is not None:
+        wsb = attn_ws_bytes(plan, 2, dt, Hq, Hkv, d, rope_base)  # a caller workspace: the call uses what fits
+    else:
+        wsb = bwd_ws_budget(plan, dt, Hq, Hkv, d, rope_base, ws_budget)[0]
     ws, wsn = _workspace(wsb, dev, ws)
     if recompute_dq:
         wsn = min(wsn, wsb)

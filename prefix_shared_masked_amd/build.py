@@ -42,5 +42,23 @@ def build_library(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+# Host planner sources (plain C++, no device code): the tables the kernels read.
+HOST_SOURCES = ["plan.cpp", "partition.cpp", "route.cpp"]
+
+
+def build_host_sanitized(out_path: str) -> str:
+    """The host planner alone (plan, partition, route) built with g++ under
+    AddressSanitizer and UndefinedBehaviorSanitizer, as a shared library the
+    binding can load in host-only mode (for the sanitized planner test)."""
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in HOST_SOURCES], "-o", out_path]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ failed ({res.returncode}):\n{res.stderr}")
+    return out_path
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))

@@ -33,6 +33,8 @@
 // lane, K^T from the LDS transpose read); it also writes the fp16 rotated Q,
 // -D and -LSE * log2(e) that dK/dV reads.  The fp32 path keeps plain
 // reference kernels (a thread per query row / key).
+#include <algorithm>
+
 #include "common.h"
 #include "plan_internal.h"
 
@@ -315,10 +317,11 @@ struct KVParams {
   const int32_t* kp;  // work pieces, TA_KPIECE_INTS each
   const int32_t* kr;  // cut sub-tiles: (kw, wk, first slot, n_windows)
   float* part;        // partial dK/dV slots (PART_WAVE floats per slot and KV head)
-  f16* ds;            // dS blocks [Hkv][n_dsblk][G][32 keys][32 positions] (dS path only)
+  f16* ds;            // dS blocks [nkv][n_dsblk][G][32 keys][32 positions] of this round's KV heads (dS path only)
   f16* ds_spare;      // a 32 x 32 block that absorbs the stores of blocks a wavefront does not own
   int n_sum;          // cut sub-tiles
   int n_dsblk;
+  int kv0, nkv;       // this launch's KV heads: kv0 .. kv0 + nkv - 1 (the backward may run them in rounds)
   int nqb;            // 32-row query blocks from q0 (the plan's query tiles)
   int N, Hq, Hkv, G;
   int q0;  // first query row (rows below are a key-only prefix)
@@ -394,8 +397,8 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
   using L = KVStageLayout;
   __shared__ __attribute__((aligned(1024))) char smem[4 * L::BYTES];
 
-  const int kvh = blockIdx.x % P.Hkv;
-  const cint_ptr tl = as_const(P.kp) + (size_t)(blockIdx.x / P.Hkv) * TA_KPIECE_INTS;
+  const int kvr = blockIdx.x % P.nkv, kvh = P.kv0 + kvr;
+  const cint_ptr tl = as_const(P.kp) + (size_t)(blockIdx.x / P.nkv) * TA_KPIECE_INTS;
   const int qlo = tl[0], qhi = tl[1];             // the piece's query rows, staged for all four
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int col = lane & 31, half = lane >> 5;
@@ -583,7 +586,7 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
     for (int s = 0; s < 8; ++s) {
       if (DS && s == 1) {  // scalar work, placed among the score MFMAs
         const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
-        if (own) blk = P.ds + (((size_t)kvh * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * G + hg) * (SUB * SUB);
+        if (own) blk = P.ds + (((size_t)kvr * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * G + hg) * (SUB * SUB);
       }
       // operands of k-group s + 2, then the MFMAs of k-group s
       if (s < 6) {
@@ -707,8 +710,8 @@ __global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
 // every tile (keys 8g + 4*half + 0..3).
 __global__ __launch_bounds__(256) void dkv_sum_kernel(KVParams P) {
   const int g = blockIdx.x & 3, rest = blockIdx.x >> 2;
-  const int kvh = rest % P.Hkv;
-  const int i = (rest / P.Hkv) * 4 + (threadIdx.x >> 6);
+  const int kvh = P.kv0 + rest % P.nkv;
+  const int i = (rest / P.nkv) * 4 + (threadIdx.x >> 6);
   if (i >= P.n_sum) return;
   const int32_t* tl = P.kr + (size_t)i * 4;
   const int kw = tl[0], wkeys = tl[1], slot0 = tl[2], np = tl[3];
@@ -827,13 +830,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
 
 struct DSParams {
   const f16* k;   // fp16 K * scale * log2(e) (rotated when RoPE is on)
-  const f16* ds;  // [Hkv][n_dsblk][G][32 keys][32 positions]
+  const f16* ds;  // [nkv][n_dsblk][G][32 keys][32 positions]: this round's KV heads
   bf16* dq;
   const int32_t* pos;
   const int32_t* dq_ptr;
   const int32_t* dq_ent;
   const int32_t* dq_order;
   int N, Hq, Hkv, G, q0, n_dsblk;
+  int kv0, nkv;  // this launch's KV heads
   float rope_base;
 };
 
@@ -853,8 +857,8 @@ __global__ __launch_bounds__(256, 3) void dq_ds_kernel(DSParams P) {
   __shared__ __attribute__((aligned(1024))) f16 sS[3][4][SUB * SUB];
   __shared__ double sInv[D / 2];  // read after the loop's barriers
 
-  const int kvh = blockIdx.x % P.Hkv;
-  const int tile = as_const(P.dq_order)[blockIdx.x / P.Hkv];
+  const int kvr = blockIdx.x % P.nkv, kvh = P.kv0 + kvr;
+  const int tile = as_const(P.dq_order)[blockIdx.x / P.nkv];
   rope_inv_table(sInv, D / 2, D, P.rope_base);
   const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -876,7 +880,7 @@ __global__ __launch_bounds__(256, 3) void dq_ds_kernel(DSParams P) {
       const size_t off = ((size_t)(kw + min(row, wk - 1)) * P.Hkv + kvh) * D + (((lane & 15) ^ swz(row & 15)) << 3);
       copy16_to_lds(P.k + off, sK[b] + 4 * i * D);
     }
-    const f16* src = P.ds + (((size_t)kvh * P.n_dsblk + blk) * P.G + g) * (SUB * SUB) + lane * 8;
+    const f16* src = P.ds + (((size_t)kvr * P.n_dsblk + blk) * P.G + g) * (SUB * SUB) + lane * 8;
     copy16_to_lds_nt(src, sS[b][w]);
     copy16_to_lds_nt(src + 512, sS[b][w] + 512);
   };
@@ -1040,9 +1044,17 @@ using namespace ta;
 
 constexpr size_t SUB_SQ = TA_KV_SUB * TA_KV_SUB;
 
-// Backward workspace.  with_ds: the dS path (bf16), which adds the dS blocks
-// (32 x 32 fp16 per (query tile, sub-tile) block and query head).
-size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base, bool with_ds) {
+// dS blocks of one KV head (its Hq / Hkv query heads): 32 x 32 fp16 per
+// (query tile, sub-tile) block and query head.
+static size_t ds_head_bytes(const ta_plan* p, int32_t Hq, int32_t Hkv) {
+  return (size_t)p->n_dsblk * (Hq / Hkv) * SUB_SQ * sizeof(f16);
+}
+
+// Backward workspace.  ds_heads > 0 (bf16): the dS path with room for the dS
+// blocks of ds_heads KV heads at a time (the KV heads then run in rounds of
+// that many), plus a spare block.
+size_t ta_bwd_ws_heads(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base,
+                       int ds_heads) {
   const size_t N = p->n_tokens;
   size_t b = 0;
   if (dt == TA_BF16) {
@@ -1051,13 +1063,36 @@ size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t
     b += align256(N * Hq * d * sizeof(f16)) + align256(N * Hkv * d * sizeof(f16));  // fp16 Q, K
     if (rope_base > 0.f) b += align256(N * Hkv * d * sizeof(bf16));                 // rotated bf16 K
     b += align256((size_t)p->n_kslots * Hkv * bwd::PART_WAVE * sizeof(float));       // dK/dV partials
-    if (with_ds) b += align256((size_t)p->n_dsblk * Hq * SUB_SQ * sizeof(f16)) +     // dS blocks
-                      align256(SUB_SQ * sizeof(f16));                                // + a spare one
+    if (ds_heads > 0) b += align256((size_t)ds_heads * ds_head_bytes(p, Hq, Hkv)) +  // dS blocks
+                           align256(SUB_SQ * sizeof(f16));                           // + a spare one
   } else {
     b += align256(N * Hq * sizeof(float));  // D
     if (rope_base > 0.f) b += align256(N * Hq * d * sizeof(float)) + align256(N * Hkv * d * sizeof(float));
   }
   return b;
+}
+
+size_t ta_bwd_ws(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d, float rope_base, bool with_ds) {
+  return ta_bwd_ws_heads(p, dt, Hq, Hkv, d, rope_base, with_ds && dt == TA_BF16 ? Hkv : 0);
+}
+
+// KV heads whose dS blocks fit a workspace of ws_bytes (0: the recompute path).
+static int ds_heads_for(const ta_plan* p, int32_t Hq, int32_t Hkv, int32_t d, float rope_base, size_t ws_bytes) {
+  for (int h = Hkv; h >= 1; --h)
+    if (ta_bwd_ws_heads(p, TA_BF16, Hq, Hkv, d, rope_base, h) <= ws_bytes) return h;
+  return 0;
+}
+
+extern "C" ta_status tree_attn_bwd_ws_budget(const ta_plan* p, ta_dtype dt, int32_t Hq, int32_t Hkv, int32_t d,
+                                             float rope_base, size_t budget, size_t* bytes,
+                                             int32_t* kv_heads_per_round) {
+  if (!p || !bytes || !kv_heads_per_round || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return TA_EINVAL;
+  if (budget == 0) budget = TA_BWD_WS_BUDGET_DEFAULT;
+  const size_t smallest = ta_bwd_ws_heads(p, dt, Hq, Hkv, d, rope_base, 0);
+  const int h = dt == TA_BF16 ? ds_heads_for(p, Hq, Hkv, d, rope_base, budget) : 0;
+  *kv_heads_per_round = h;
+  *bytes = h > 0 ? ta_bwd_ws_heads(p, dt, Hq, Hkv, d, rope_base, h) : smallest;
+  return *bytes <= budget ? TA_OK : TA_ENOMEM;
 }
 
 extern "C" ta_status tree_attn_bwd(const ta_plan* p, const void* dplan, ta_dtype dt, const void* q, const void* k,
@@ -1077,11 +1112,13 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return TA_EINVAL;
   if (dt == TA_BF16 ? d != 128 : (dt != TA_F32 || (d != 64 && d != 128))) return TA_EUNSUPPORTED;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return TA_EINVAL;
-  // bf16: the dS path when the workspace holds the dS blocks, else dQ
+  // bf16: the dS path when the workspace holds the dS blocks of at least one
+  // KV head (the KV heads then run in rounds of as many as fit), else dQ
   // recomputes S and dP
   const size_t need = ta_bwd_ws(p, dt, Hq, Hkv, d, rope_base, false);
   if (!ws || ws_bytes < need) return TA_ENOMEM;
-  const bool ds_path = dt == TA_BF16 && ws_bytes >= ta_bwd_ws(p, dt, Hq, Hkv, d, rope_base, true);
+  const int ds_heads = dt == TA_BF16 ? ds_heads_for(p, Hq, Hkv, d, rope_base, ws_bytes) : 0;
+  const bool ds_path = ds_heads > 0;
   const int N = p->n_tokens;
   if (N == 0) return TA_OK;
   if (scale <= 0.f) scale = 1.f / sqrtf((float)d);
@@ -1110,7 +1147,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     float* part = (float*)w;
     w += align256((size_t)p->n_kslots * Hkv * bwd::PART_WAVE * sizeof(float));
     f16* dsb = ds_path ? (f16*)w : nullptr;
-    f16* ds_spare = ds_path ? (f16*)(w + align256((size_t)p->n_dsblk * Hq * SUB_SQ * sizeof(f16))) : nullptr;
+    f16* ds_spare = ds_path ? (f16*)(w + align256((size_t)ds_heads * ds_head_bytes(p, Hq, Hkv))) : nullptr;
     const int32_t* dq_ptr = (const int32_t*)(base + p->off_dq_ptr);
     const int32_t* dq_ent = (const int32_t*)(base + p->off_dq_ent);
     const int32_t* dq_order = (const int32_t*)(base + p->off_dq_order);
@@ -1198,18 +1235,8 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
     B.scale = scale;
     B.scale_log2 = scale * TA_LOG2E;
     B.rope_base = rope_base;
-    if (ds_path)
-      hipLaunchKernelGGL(bwd::dkv_bf16_kernel<true>, dim3(p->n_kpieces * Hkv), dim3(256), 0, stream, B);
-    else
-      hipLaunchKernelGGL(bwd::dkv_bf16_kernel<false>, dim3(p->n_kpieces * Hkv), dim3(256), 0, stream, B);
-    TA_LAUNCH_CHECK();
-    if (p->n_ksplit > 0) {
-      hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3((p->n_ksplit + 3) / 4 * Hkv * 4), dim3(256), 0, stream, B);
-      TA_LAUNCH_CHECK();
-    }
+    bwd::DSParams Q;
     if (ds_path) {
-      mark(ev, nev, 2, stream);
-      bwd::DSParams Q;
       Q.k = ks;
       Q.ds = dsb;
       Q.dq = (bf16*)dq;
@@ -1224,9 +1251,33 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
       Q.q0 = p->q_start;
       Q.n_dsblk = (int)p->n_dsblk;
       Q.rope_base = rope_base;
-      if (p->n_qtiles > 0) {
-        hipLaunchKernelGGL(bwd::dq_ds_kernel, dim3(p->n_qtiles * Hkv, (Q.G + 3) / 4), dim3(256), 0, stream, Q);
+    }
+    // dK/dV (storing dS) and then dQ from the stored dS, for the KV heads
+    // whose dS blocks fit the workspace at once: a query head's dQ depends on
+    // its own KV head's keys only, so rounds over KV heads give the same
+    // results bit for bit.  Without the dS workspace, one round of dK/dV.
+    const int per_round = ds_path ? ds_heads : Hkv;
+    for (int kv0 = 0; kv0 < Hkv; kv0 += per_round) {
+      const int nkv = std::min(per_round, Hkv - kv0);
+      B.kv0 = kv0;
+      B.nkv = nkv;
+      if (ds_path)
+        hipLaunchKernelGGL(bwd::dkv_bf16_kernel<true>, dim3(p->n_kpieces * nkv), dim3(256), 0, stream, B);
+      else
+        hipLaunchKernelGGL(bwd::dkv_bf16_kernel<false>, dim3(p->n_kpieces * nkv), dim3(256), 0, stream, B);
+      TA_LAUNCH_CHECK();
+      if (p->n_ksplit > 0) {
+        hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3((p->n_ksplit + 3) / 4 * nkv * 4), dim3(256), 0, stream, B);
         TA_LAUNCH_CHECK();
+      }
+      if (ds_path) {
+        if (kv0 == 0) mark(ev, nev, 2, stream);
+        Q.kv0 = kv0;
+        Q.nkv = nkv;
+        if (p->n_qtiles > 0) {
+          hipLaunchKernelGGL(bwd::dq_ds_kernel, dim3(p->n_qtiles * nkv, (Q.G + 3) / 4), dim3(256), 0, stream, Q);
+          TA_LAUNCH_CHECK();
+        }
       }
     }
     mark(ev, nev, 3, stream);

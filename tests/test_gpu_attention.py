@@ -277,7 +277,7 @@ def test_bf16_saturation_flag_and_nan_passthrough():
         Qb[37, 1, 5] = 1e5
         assert flags(Qb, K, rope)[0] == [1, 1, 1]
         Kb = K.clone()
-        Kb[20, 0, 100] = -1e5
+        Kb[20, 0, 100] = -1e6  # K enters fp16 times scale * log2(e) = 0.1275: beyond 65504 / 0.1275
         assert flags(Q, Kb, rope)[0] == [1, 1, 1]
     Qn = Q.clone()
     Qn[50, 2, 7] = float("nan")
@@ -294,3 +294,40 @@ def test_bf16_saturation_flag_and_nan_passthrough():
     lmask = np.ones(ln.shape, bool)
     lmask[2, 50] = False
     close("lse", ln[lmask], ref["lse"][lmask], torch.bfloat16)
+
+
+def test_bf16_backward_in_kv_head_rounds():
+    """A backward workspace below the full dS size runs the KV heads in
+    rounds of as many as fit: bitwise the same dQ/dK/dV as one round (a query
+    head's dQ depends only on its own KV head's keys), and within the bar
+    against the oracle; below one KV head's dS it takes the recompute path."""
+    tree = W.Tree(np.array([-1, 0, 1, 1, 0], np.int32), np.array([100, 300, 500, 200, 260], np.int32), "rounds")
+    Hq, Hkv, d, rope = 8, 4, 128, 10000.0
+    plan = pkg.tree_plan(tree.parent, tree.seg_len)
+    op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    q, k, v, do = W.attention_inputs(21, plan.n_tokens, Hq, Hkv, d)
+    (Q, q64), (K, k64), (V, v64), (DO, do64) = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    o, lse = pkg.tree_attn_fwd(plan, Q, K, V, rope_base=rope)
+    full = pkg.attn_ws_bytes(plan, 1, 1, Hq, Hkv, d, rope)
+    one = pkg.tree_attn_bwd(plan, Q, K, V, o, lse, DO, rope_base=rope,
+                            ws=torch.empty(full, dtype=torch.uint8, device=DEV))
+    ref = oracle.per_path_attention(op, q64, k64, v64, rope_base=rope, dO=do64)
+    for heads in (3, 2, 1):
+        nbytes = None
+        for budget in range(full, 0, -4096):
+            nb, hh = pkg.bwd_ws_budget(plan, 1, Hq, Hkv, d, rope, budget=budget)
+            if hh == heads:
+                nbytes = nb
+                break
+        assert nbytes is not None
+        print(f"[case] rounds of {heads} KV heads, ws {nbytes} of {full}", flush=True)
+        got = pkg.tree_attn_bwd(plan, Q, K, V, o, lse, DO, rope_base=rope,
+                                ws=torch.empty(nbytes, dtype=torch.uint8, device=DEV))
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(one, got)), heads
+    for name, t in zip(("dq", "dk", "dv"), one):
+        close(name, t, ref[name], torch.bfloat16)
+    got = pkg.tree_attn_bwd(plan, Q, K, V, o, lse, DO, rope_base=rope, ws_budget=pkg.bwd_ws_budget(
+        plan, 1, Hq, Hkv, d, rope, budget=pkg.attn_ws_bytes(plan, 2, 1, Hq, Hkv, d, rope) + 1)[0])
+    for name, t in zip(("dq", "dk", "dv"), got):
+        close(name, t, ref[name], torch.bfloat16)
