@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -80,7 +81,9 @@ def time_tree(pkg, tree, steps, warmup, dev, seed=0, Hq=32, Hkv=8, d=128, rope=1
         step(i)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) * 1e3 / steps
-    avg = lambda a, b: sum(ev.elapsed_ms(7 * i + a, 7 * i + b) for i in range(steps)) / steps
+    span = lambda a, b: [ev.elapsed_ms(7 * i + a, 7 * i + b) for i in range(steps)]
+    avg = lambda a, b: sum(span(a, b)) / steps
+    med = lambda a, b: float(statistics.median(span(a, b)))
     P, flop_pair = plan.visible_pairs, d * Hq
     res = dict(
         n_tokens=plan.n_tokens, n_leaves=plan.n_leaves, n_flat=plan.n_flat, visible_pairs=P,
@@ -88,11 +91,13 @@ def time_tree(pkg, tree, steps, warmup, dev, seed=0, Hq=32, Hkv=8, d=128, rope=1
         fwd_tile_efficiency=round(P / plan.computed_pairs_fwd, 4),
         bwd_tile_efficiency=round(P / plan.computed_pairs_bwd, 4),
         plan_ms=round(plan_ms, 3), upload_ms=round(upload_ms, 3),
-        ms_per_step=avg(0, 6), wall_ms_per_step=wall,
+        # the timed region: K steps between two device synchronisations (host wall clock)
+        ms_per_step=wall, event_ms_per_step=avg(0, 6), event_median_ms_per_step=med(0, 6),
         fwd_ms=avg(0, 2), bwd_ms=avg(3, 6),
         # backward events: [0] start, [1] after the preparation passes, [2] after dK/dV (and its
         # partial sum), [3] after dQ, which reads the dS blocks dK/dV stored (one product)
         k_fwd_prep_ms=avg(0, 1), k_fwd_ms=avg(1, 2), k_bwd_prep_ms=avg(3, 4), k_dkv_ms=avg(4, 5), k_dq_ms=avg(5, 6),
+        k_median_ms=dict(fwd=med(1, 2), dkv=med(4, 5), dq=med(5, 6)),
         flops_fwd=4 * flop_pair * P, flops_bwd=10 * flop_pair * P,
         flops_alg=dict(fwd=4 * flop_pair * P, dq=2 * flop_pair * P, dkv=8 * flop_pair * P))
     res["tflops"] = (res["flops_fwd"] + res["flops_bwd"]) / (res["ms_per_step"] * 1e-3) / 1e12
@@ -284,27 +289,37 @@ def time_decode(pkg, L, steps, warmup, dev, B=8, Hq=32, Hkv=8, d=128, seed=5):
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    call = lambda evs=None: pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L, o=o, lse=lse, ws=ws, events=evs,
+                                                    check_spans=False)
+    pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L, o=o, lse=lse, ws=ws)  # spans checked once
     for _ in range(warmup):
-        pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L, o=o, lse=lse, ws=ws)
-    # whole calls back to back between two events (events inside a call add gaps between its kernels)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L, o=o, lse=lse, ws=ws)
-    e1.record()
+        call()
+    # each rep: overwrite a 512 MiB buffer (flushes the 4 MiB L2s and the 256 MiB MALL), then one
+    # whole call between two events; the median over the reps
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    reps = max(steps, 20)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        flush.fill_(1)
+        e0.record()
+        call()
+        e1.record()
     torch.cuda.synchronize()
-    call = e0.elapsed_time(e1) / steps
-    # the partial kernel alone, from the library's stage events in a separate pass
-    ev = pkg.HipEvents(3 * steps)
-    for i in range(steps):
-        pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L, o=o, lse=lse, ws=ws, events=ev.slice(3 * i, 3))
+    times = [e0.elapsed_time(e1) for e0, e1 in evs]
+    call_ms = float(statistics.median(times))
+    # the partial kernel alone, from the library's stage events (also after a flush)
+    ev = pkg.HipEvents(3 * reps)
+    for i in range(reps):
+        flush.fill_(1)
+        call(ev.slice(3 * i, 3))
     torch.cuda.synchronize()
-    part = sum(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(steps)) / steps
+    part = float(statistics.median(ev.elapsed_ms(3 * i, 3 * i + 1) for i in range(reps)))
     kv_bytes = 2 * B * L * Hkv * d * 2
-    del k, v
+    del k, v, flush
     torch.cuda.empty_cache()
-    return dict(L=L, n_splits=n_splits, kv_bytes=kv_bytes, call_us=call * 1e3, partial_us=part * 1e3,
-                GBps=kv_bytes / (call * 1e-3) / 1e9, partial_GBps=kv_bytes / (part * 1e-3) / 1e9)
+    return dict(L=L, n_splits=n_splits, kv_bytes=kv_bytes, reps=reps, call_us=call_ms * 1e3,
+                call_us_mean=sum(times) / reps * 1e3, partial_us=part * 1e3,
+                GBps=kv_bytes / (call_ms * 1e-3) / 1e9, partial_GBps=kv_bytes / (part * 1e-3) / 1e9)
 
 
 def cpu_baseline(tree, budget_s=20.0, seed=0):
@@ -316,17 +331,21 @@ def cpu_baseline(tree, budget_s=20.0, seed=0):
     import oracle
     import workloads as W
     from oracle.plan import OraclePlan
+    t0 = time.perf_counter()
     op = oracle.oracle_plan(tree.parent, tree.seg_len)
+    plan_s = time.perf_counter() - t0
     q, k, v, do = W.attention_inputs(seed, op.n_tokens, 32, 8, 128)
     heads = [0, 1, 2, 3]
-    done_pairs, t_total, n_paths = 0, 0.0, 0
+    path_pairs, t_total, n_paths = 0, 0.0, 0
+    covered = np.zeros(op.n_tokens, bool)
     for idx in op.paths:
         sub = OraclePlan(**{**op.__dict__, "paths": [idx]})
         t0 = time.perf_counter()
         oracle.per_path_attention(sub, q, k, v, rope_base=10000.0, dO=do, heads=heads, check_consistency=False)
         t_total += time.perf_counter() - t0
         L = len(idx)
-        done_pairs += L * (L + 1) // 2 * len(heads)
+        path_pairs += L * (L + 1) // 2 * len(heads)
+        covered[np.asarray(idx)] = True
         n_paths += 1
         if t_total >= budget_s:
             break
@@ -335,11 +354,16 @@ def cpu_baseline(tree, budget_s=20.0, seed=0):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
     except Exception:
         cores = os.cpu_count()
-    flops = 14 * 128 * done_pairs
-    return dict(value=flops / t_total / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+    # the metric counts the tree's visible pairs: the sampled paths cover a subtree, whose tokens
+    # see pos(t) + 1 keys each (every key of a token's path is in the subtree); the per-path run
+    # computes each shared prefix once per path, the causal pairs counted separately below
+    visible = int((op.pos[covered].astype(np.int64) + 1).sum()) * len(heads)
+    return dict(value=14 * 128 * visible / t_total / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
                 sample=f"per-path float64 oracle, fwd+bwd, query heads 0-3 (one KV group), first {n_paths} of "
-                       f"{len(op.paths)} root-to-leaf paths of the spine tree ({done_pairs} causal pairs), "
-                       f"{t_total:.1f} s", seconds=round(t_total, 2))
+                       f"{len(op.paths)} root-to-leaf paths of the spine tree: {visible} visible pairs of the "
+                       f"subtree they cover ({path_pairs} per-path causal pairs), {t_total:.1f} s",
+                seconds=round(t_total, 2), visible_pairs=visible, per_path_causal_pairs=path_pairs,
+                per_path_tflops=14 * 128 * path_pairs / t_total / 1e12, oracle_plan_s=round(plan_s, 3))
 
 
 # kernels launched between the same two events as the named one (their HBM
@@ -362,6 +386,21 @@ def load_traffic(kernel):
             return None
         total += e.get("bytes_per_launch")
     return total
+
+
+def load_mfma(kernel):
+    """MFMA counters of a kernel (profiles/mfma.json, rocprofv3 --pmc on the spine-tree
+    headline), when recorded for the current kernel sources: the MFMA-busy share of SIMD
+    cycles and the FLOPs the matrix units executed per launch (SQ_INSTS_VALU_MFMA_MOPS_*
+    x 512)."""
+    path = os.path.join(ROOT, "profiles", "mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        e = json.load(f).get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e
 
 
 def main():
@@ -434,8 +473,19 @@ def main():
     roofline = dict(bound="mfma", kernel=names[dom], achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=load_traffic(names[dom]),
                     avg_launch_ms=round(kernels[dom], 4))
-    per_kernel = {names[k2]: dict(ms=round(v, 4), tflops=round(head["flops_alg"][k2] / (v * 1e-3) / 1e12, 2))
-                  for k2, v in kernels.items()}
+    mdom = load_mfma(names[dom])
+    roofline["mfma_busy"] = mdom["mfma_busy"] if mdom else None
+    per_kernel = {}
+    for k2, v in kernels.items():
+        e = dict(ms=round(v, 4), median_ms=round(head["k_median_ms"][k2], 4),
+                 tflops=round(head["flops_alg"][k2] / (v * 1e-3) / 1e12, 2))
+        m = load_mfma(names[k2])
+        if m:
+            e["mfma_busy"] = m["mfma_busy"]
+            e["mfma_flops_over_algorithmic"] = round(m["mfma_flops_per_launch"] / head["flops_alg"][k2], 4)
+            e["valu_mfma_coexec"] = m.get("coexec_over_busy")
+            e["clock_ghz_under_counters"] = m.get("clock_ghz")
+        per_kernel[names[k2]] = e
     per_kernel["k_prep_fwd"] = dict(ms=round(head["k_fwd_prep_ms"], 4))
     per_kernel["k_prep_bwd"] = dict(ms=round(head["k_bwd_prep_ms"], 4))
 
@@ -460,7 +510,8 @@ def main():
         "roofline": roofline,
         "per_kernel": per_kernel,
         "fwd_ms": round(head["fwd_ms"], 4), "bwd_ms": round(head["bwd_ms"], 4),
-        "wall_ms_per_step": round(head["wall_ms_per_step"], 4),
+        "event_ms_per_step": round(head["event_ms_per_step"], 4),
+        "event_median_ms_per_step": round(head["event_median_ms_per_step"], 4),
         "plan_ms": head["plan_ms"], "plan_upload_ms": head["upload_ms"],
         "por": head["por"], "fwd_tile_efficiency": head["fwd_tile_efficiency"],
         "bwd_tile_efficiency": head["bwd_tile_efficiency"],
