@@ -40,9 +40,11 @@
  *    errors are returned before anything is launched; a failed launch
  *    returns TA_EHIP.
  *  - Plans are immutable after tree_plan returns and may be shared between
- *    threads.  The library's only global mutable state is one hipBLASLt
- *    handle per device (with the mutex that guards its creation), created by
- *    the first tree_lmhead_nll call with gradients on that device and kept
+ *    threads.  The library's global mutable state is: one hipBLASLt handle
+ *    per device (with the mutex that guards its creation), created by the
+ *    first tree_lmhead_nll call with gradients on that device; and the
+ *    scratch array of tree_decode_splitkv_noalloc (one per device) with the
+ *    table of its per-device addresses and that table's mutex.  Both are kept
  *    until the process ends; every other call keeps nothing between calls.
  */
 #ifndef TREE_ATTN_H
@@ -358,6 +360,24 @@ ta_status tree_decode_splitkv(ta_dtype dt, const void* q, const void* k, const v
                               int32_t Hq, int32_t Hkv, int32_t d, int32_t max_len, float scale,
                               int32_t n_splits, void* o, float* lse, void* ws, size_t ws_bytes,
                               hipStream_t stream);
+
+/* Allocation-free tree_decode_splitkv, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and arguments without a workspace; the
+ * per-slice partials go to a fixed device array of TA_DECODE_SCRATCH_BYTES
+ * inside the library (one per GPU, resolved on the first call on that GPU
+ * and held until the process ends).  The call allocates nothing.  Calls whose
+ * partials (tree_decode_ws_bytes) exceed the array return TA_ENOMEM before
+ * launching anything.  Every call on a GPU uses that GPU's one array, so calls
+ * that overlap on one GPU (other streams, other threads) race: serialise them.
+ * Nothing in the array needs clearing between calls (every partial a call
+ * reads it writes first).  Errors as tree_decode_splitkv. */
+#define TA_DECODE_SCRATCH_BYTES ((size_t)16 << 20) /* 16 MiB: e.g. B = 8, 32 heads, 64 slices */
+ta_status tree_decode_splitkv_noalloc(ta_dtype dt, const void* q, const void* k, const void* v,
+                                      const int32_t* span_ptr, const int32_t* spans, int32_t B,
+                                      int32_t Hq, int32_t Hkv, int32_t d, int32_t max_len,
+                                      float scale, int32_t n_splits, void* o, float* lse,
+                                      hipStream_t stream);
 
 ta_status tree_decode_splitkv_ex(ta_dtype dt, const void* q, const void* k, const void* v,
                                  const int32_t* span_ptr, const int32_t* spans, int32_t B,

@@ -111,6 +111,7 @@ def load_library():
                                    P]),
         "tree_decode_splitkv_ex": (I32, [I32, P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P, P, P, SZ, P, I32,
                                          P]),
+        "tree_decode_splitkv_noalloc": (I32, [I32, P, P, P, P, P, I32, I32, I32, I32, I32, F32, I32, P, P, P]),
         "tree_partition": (I32, [pI32, pI32, I32, I64, I32, I32, ctypes.POINTER(P)]),
         "tree_partition_view": (I32, [P, ctypes.POINTER(_PartView)]),
         "tree_partition_plan": (I32, [P, I32, ctypes.POINTER(P)]),
@@ -839,4 +840,36 @@ def tree_decode_splitkv(q, k, v, span_ptr, spans, max_len: int, scale: float = 0
     _check("tree_decode_splitkv", load_library().tree_decode_splitkv_ex(
         TA_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(span_ptr), _ptr(spans), B, Hq, Hkv, d, int(max_len),
         float(scale), int(n_splits), _ptr(o), _ptr(lse), _ptr(ws), wsn, ev, nev, _stream(q)))
+    return o, lse
+
+
+DECODE_SCRATCH_BYTES = 16 << 20  # TA_DECODE_SCRATCH_BYTES
+
+
+def tree_decode_splitkv_noalloc(q, k, v, span_ptr, spans, max_len: int, o, lse, scale: float = 0.0,
+                                n_splits: int = 0):
+    """tree_decode_splitkv without any allocation, for graph capture and
+    serving loops: the caller passes the outputs o [B,Hq,d] bf16 and lse
+    [B,Hq] fp32, and the per-slice partials use the library's fixed scratch
+    (DECODE_SCRATCH_BYTES per GPU; larger requests raise before any launch).
+    Calls that overlap on one GPU share that scratch and race.  The span
+    tables are not checked here (no host copy): the caller guarantees them."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _need(q, "q", (B, Hq, d), torch.bfloat16, dev)
+    _need(k, "k", tuple(k.shape), torch.bfloat16, dev)
+    _need(v, "v", tuple(k.shape), torch.bfloat16, dev)
+    _need(span_ptr, "span_ptr", (B + 1,), torch.int32, dev)
+    _need(spans, "spans", tuple(spans.shape), torch.int32, dev)
+    _need(o, "o", (B, Hq, d), torch.bfloat16, dev)
+    _need(lse, "lse", (B, Hq), torch.float32, dev)
+    need, _ = decode_ws_bytes(B, Hq, d, max_len, n_splits)
+    if need > DECODE_SCRATCH_BYTES:
+        raise ValueError(f"the decode partials need {need} bytes, more than the {DECODE_SCRATCH_BYTES}-byte "
+                         "scratch of the allocation-free call")
+    _check("tree_decode_splitkv_noalloc", load_library().tree_decode_splitkv_noalloc(
+        TA_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(span_ptr), _ptr(spans), B, Hq, Hkv, d, int(max_len),
+        float(scale), int(n_splits), _ptr(o), _ptr(lse), _stream(q)))
     return o, lse

@@ -11,6 +11,8 @@
 // arithmetic to the matrix cores, so the vector ALU does only the softmax.
 // Merge kernel: one workgroup per (batch item, query head); round r merges
 // slice pairs (i, i + 2^r) in parallel over the head dimension.
+#include <mutex>
+
 #include "common.h"
 
 namespace ta {
@@ -302,9 +304,34 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float* __restrict__ p
 }  // namespace dec
 }  // namespace ta
 
+// Scratch of the allocation-free decode entry point: the per-slice partials
+// live in this file-scope device array (one copy per GPU the library runs
+// on, held until the process ends) instead of a caller workspace.  Host code
+// never uses the array's name as an address: each device's copy is resolved
+// once with hipGetSymbolAddress and that pointer is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[TA_DECODE_SCRATCH_BYTES];
+
 using namespace ta;
 
 namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device id -> its copy of scratch, resolved on first use
+
+ta_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TA_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return TA_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TA_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TA_OK;
+}
+
 int32_t pick_splits(int32_t max_len, int32_t n_splits) {
   if (n_splits > 0) return n_splits;
   int32_t s = (max_len + 2047) / 2048;  // about 2K keys (512 per wavefront) per workgroup
@@ -367,4 +394,22 @@ extern "C" ta_status tree_decode_splitkv_ex(ta_dtype dt, const void* q, const vo
   TA_LAUNCH_CHECK();
   mark(ev, nev, 2, stream);
   return TA_OK;
+}
+
+extern "C" ta_status tree_decode_splitkv_noalloc(ta_dtype dt, const void* q, const void* k, const void* v,
+                                                 const int32_t* span_ptr, const int32_t* spans, int32_t B,
+                                                 int32_t Hq, int32_t Hkv, int32_t d, int32_t max_len, float scale,
+                                                 int32_t n_splits, void* o, float* lse, hipStream_t stream) {
+  if (dt != TA_BF16 || d != dec::D) return TA_EUNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_len < 0 || n_splits < 0) return TA_EINVAL;
+  size_t need;
+  int32_t S;
+  ta_status st = tree_decode_ws_bytes(B, Hq, d, max_len, n_splits, &need, &S);
+  if (st != TA_OK) return st;
+  if (need > TA_DECODE_SCRATCH_BYTES) return TA_ENOMEM;  // the partials do not fit the fixed scratch
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != TA_OK) return st;
+  return tree_decode_splitkv_ex(dt, q, k, v, span_ptr, spans, B, Hq, Hkv, d, max_len, scale, n_splits, o, lse, ws,
+                                TA_DECODE_SCRATCH_BYTES, nullptr, 0, stream);
 }
