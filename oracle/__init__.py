@@ -28,9 +28,10 @@ Parity status of each function is stated in its docstring; the pins live in
 from .plan import (oracle_plan, fwd_tile_keys, bwd_tiles, OraclePlan, dense_mask,  # noqa: F401
                    por, speedup_upper)
 from .attention import (per_path_attention, dense_mask_attention, rope,  # noqa: F401
-                        rope_transpose, rows_attention, rows_attention_grads)
+                        rope_transpose, rows_attention, rows_attention_grads,
+                        causal_sequence_grads)
 from .nll import weighted_nll, per_path_loss  # noqa: F401
 from .ssm import tree_scan, tree_conv  # noqa: F401
-from .lmhead import lmhead_weighted_nll, chunked_lmhead_weighted_nll  # noqa: F401
+from .lmhead import lmhead_weighted_nll, chunked_lmhead_weighted_nll, lmhead_vocab_rows  # noqa: F401
 from .decode import (decode_attention, partial_triple, merge_triples,  # noqa: F401
                      finalize_triple, triple_from_lse, IDENTITY)

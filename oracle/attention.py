@@ -31,6 +31,11 @@ RoPE reading (the pages only say positions are tree depth; the rotary base
 pos * base^(-2i/d).  GQA reading: query head h uses KV head h // (Hq / Hkv).
 LSE is the natural log of sum_j exp(scale * q.k_j).
 
+``rows_attention``, ``rows_attention_grads``, ``causal_sequence_grads``
+    Spot-check forms for full sizes: outputs of selected rows from each row's
+    own path, and gradients of selected rows and keys (per row, or per block
+    of rows of one causal sequence) from the dense backward's definitions.
+
 Parity: pinned by the dense/per-path agreement, by single-path and forest
 special cases against torch's CPU scaled_dot_product_attention, by finite
 differences of the backward and by the leak invariants of section 14.2
@@ -325,3 +330,59 @@ def rows_attention_grads(plan, q, k, v, dO, rows, keys, scale=None, rope_base=0.
                 dv[kj, g] += P[at] * do
         dk[kj] = rope_transpose(dk[kj][None], np.array([plan.pos[j]]), rope_base)[0]
     return dq, dk, dv
+
+
+def causal_sequence_grads(q, k, v, dO, rows, keys, scale=None, rope_base=0.0, block=1024):
+    """Gradients of selected query rows and keys of ONE causal sequence (a
+    single root-to-leaf path, or one item of a varlen forest) with positions
+    0..L-1, from the dense backward's definitions (dP = dO V^T,
+    D = rowsum(dO * O), dS = P (dP - D), dQ = dS K s, dK = dS^T Q s,
+    dV = P^T dO).  A key early in a long sequence is read by thousands of
+    rows, each needing its own whole-row softmax; the rows are therefore taken
+    a block at a time (each row's softmax, O and D still formed over its full
+    row of keys), and only the selected columns of dS and P are kept.
+    Products and exponentials run as torch float64 CPU ops.
+    q, dO [L, Hq, d]; k, v [L, Hkv, d]; rows, keys: indices into 0..L-1.
+    Returns dq [len(rows), Hq, d], dk [len(keys), Hkv, d], dv [len(keys), Hkv, d]."""
+    import torch
+    q = np.asarray(q, np.float64)
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(d) if not scale else float(scale)
+    pos = np.arange(L)
+    rows = np.asarray(rows, np.int64)
+    keys = np.asarray(keys, np.int64)
+    qr = torch.from_numpy(rope(q, pos, rope_base))
+    kr = torch.from_numpy(rope(np.asarray(k, np.float64), pos, rope_base))
+    vv = torch.from_numpy(np.asarray(v, np.float64))
+    do = torch.from_numpy(np.asarray(dO, np.float64))
+    kidx = torch.from_numpy(keys)
+    dq_rot = torch.zeros(len(rows), Hq, d, dtype=torch.float64)
+    dk_rot = torch.zeros(len(keys), Hkv, d, dtype=torch.float64)
+    dv = torch.zeros(len(keys), Hkv, d, dtype=torch.float64)
+    for r0 in range(0, L, block):
+        r1 = min(L, r0 + block)
+        causal = torch.arange(r1)[None, :] <= torch.arange(r0, r1)[:, None]          # [rows, keys]
+        sel_rows = [(ri, int(i) - r0) for ri, i in enumerate(rows) if r0 <= i < r1]
+        for h in range(Hq):
+            g = h // G
+            S = (qr[r0:r1, h] @ kr[:r1, g].T) * scale
+            S = S.masked_fill(~causal, float("-inf"))
+            P = torch.exp(S - S.max(dim=1, keepdim=True).values)
+            P /= P.sum(dim=1, keepdim=True)
+            O = P @ vv[:r1, g]
+            Drow = (do[r0:r1, h] * O).sum(dim=1)                                     # [rows]
+            seen = torch.nonzero(kidx < r1).flatten()                                 # keys these rows can read
+            if len(seen):
+                kj = kidx[seen]
+                Pk = P[:, kj]                                                        # [rows, keys]
+                dSk = Pk * (do[r0:r1, h] @ vv[kj, g].T - Drow[:, None])
+                dk_rot[seen, g] += (dSk.T @ qr[r0:r1, h]) * scale
+                dv[seen, g] += Pk.T @ do[r0:r1, h]
+            for ri, li in sel_rows:
+                dS = P[li] * (vv[:r1, g] @ do[r0 + li, h] - Drow[li])
+                dq_rot[ri, h] = (dS @ kr[:r1, g]) * scale
+    dq = rope_transpose(dq_rot.numpy(), pos[rows], rope_base)
+    dk = rope_transpose(dk_rot.numpy(), pos[keys], rope_base)
+    return dq, dk, dv.numpy()

@@ -13,6 +13,12 @@ exactly what the full form returns), and the Tree Training post, section 6.2
 ``lmhead_weighted_nll``
     The full form, by definition: logits = h W^T (a library matmul in
     float64), then ``weighted_nll`` on them; dh = dlogits W, dW = dlogits^T h.
+``lmhead_vocab_rows``
+    For full-size spot checks: every token's log-sum-exp over the whole
+    vocabulary (chunks of tokens, torch float64 CPU products), and the rows
+    dW_v = sum_t dlogits_tv h_t of selected vocabulary entries only, with
+    sum_t |dlogits_tv| |h_t| beside them (the magnitude that bounds the
+    rounding error of such a sum).
 ``chunked_lmhead_weighted_nll``
     The section 14.3 form: tokens in chunks of ``chunk``; each chunk's logits
     are formed, reduced to its weighted token losses and dropped; the
@@ -40,7 +46,7 @@ def lmhead_weighted_nll(h, W, labels, w, ignore_index: int = -100):
     loss, dlogits, tok = weighted_nll(logits, labels, w, ignore_index)
     m = logits.max(axis=1)
     lse = m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
-    return dict(loss=loss, lse=lse, token_loss=tok, dh=dlogits @ W, dW=dlogits.T @ h)
+    return dict(loss=loss, lse=lse, token_loss=tok, dh=dlogits @ W, dW=dlogits.T @ h, dlogits=dlogits)
 
 
 def chunked_lmhead_weighted_nll(h, W, labels, w, chunk: int = 1024, ignore_index: int = -100):
@@ -71,3 +77,34 @@ def chunked_lmhead_weighted_nll(h, W, labels, w, chunk: int = 1024, ignore_index
         dh[s:e] = dx @ W
         dW += dx.T @ h[s:e]
     return dict(loss=loss, lse=lse, token_loss=tok, dh=dh, dW=dW)
+
+
+def lmhead_vocab_rows(h, W, labels, w, vocab_rows, chunk: int = 2048, ignore_index: int = -100):
+    """Full-form dW on selected vocabulary rows.  Each token's softmax is
+    formed over the whole vocabulary (its logits h_t W^T computed whole, one
+    chunk of tokens at a time); dlogits_tv = w_t [y_t != ignore]
+    (softmax(x_t)_v - [y_t = v]) is kept for the selected v only.
+    h [N, D], W [V, D] -> dict(lse [N], dW [R, D], dW_abs [R, D]) in float64,
+    where dW_abs = sum_t |dlogits_tv| |h_t|."""
+    import torch
+    h = torch.from_numpy(np.asarray(h, np.float64))
+    Wt = torch.from_numpy(np.asarray(W, np.float64))
+    y = torch.from_numpy(np.asarray(labels, np.int64))
+    wt = torch.from_numpy(np.asarray(w, np.float64))
+    rows = torch.from_numpy(np.asarray(vocab_rows, np.int64))
+    N, D = h.shape
+    lse = torch.zeros(N, dtype=torch.float64)
+    dW = torch.zeros(len(rows), D, dtype=torch.float64)
+    dW_abs = torch.zeros(len(rows), D, dtype=torch.float64)
+    for s in range(0, N, chunk):
+        e = min(N, s + chunk)
+        x = h[s:e] @ Wt.T                                                   # [c, V]
+        m = x.max(dim=1).values
+        l = m + torch.log(torch.exp(x - m[:, None]).sum(dim=1))
+        lse[s:e] = l
+        valid = (y[s:e] != ignore_index).to(torch.float64)
+        dl = torch.exp(x[:, rows] - l[:, None]) - (y[s:e, None] == rows[None, :]).to(torch.float64)
+        dl *= (wt[s:e] * valid)[:, None]                                    # [c, R]
+        dW += dl.T @ h[s:e]
+        dW_abs += dl.abs().T @ h[s:e].abs()
+    return dict(lse=lse.numpy(), dW=dW.numpy(), dW_abs=dW_abs.numpy())

@@ -218,7 +218,11 @@ def test_varlen_forest_full_size_sampled():
     """The varlen workload at full size (64 sequences, 133K tokens, up to 16K
     each, bf16, RoPE): O and LSE of sampled (row, head) pairs, dQ of sampled
     rows (all heads) and dK/dV of keys near sequence ends (all KV heads),
-    each from the per-row / per-key oracle."""
+    each from the per-row / per-key oracle; then, for the three longest
+    sequences, dK/dV of their first four keys (each read by every row of the
+    sequence) on all KV heads and dQ of their last rows (each reading the
+    whole sequence) on all heads, from the row-blocked oracle of one causal
+    sequence."""
     tree = W.varlen_forest(0)
     plan = pkg.tree_plan(tree.parent, tree.seg_len)
     op = oracle.oracle_plan(tree.parent, tree.seg_len)
@@ -244,6 +248,16 @@ def test_varlen_forest_full_size_sampled():
     close("dq(sampled)", dq[rows[:4]], gq, torch.bfloat16)
     close("dk(sampled)", dk[keys], gk, torch.bfloat16)
     close("dv(sampled)", dv[keys], gv, torch.bfloat16)
+    assert (np.asarray(tree.parent) == -1).all()          # every item is one causal sequence
+    for b in longest:
+        a, L = int(starts[b]), int(lens[b])
+        print(f"[full] varlen heavy keys of item {b} (L={L})", flush=True)
+        sl = slice(a, a + L)
+        hq, hk, hv = oracle.causal_sequence_grads(q64[sl], k64[sl], v64[sl], do64[sl], [L - 2, L - 1],
+                                                  [0, 1, 2, 3], rope_base=10000.0)
+        close("dq(last rows)", dq[a + L - 2:a + L], hq, torch.bfloat16, f" item {b}")
+        close("dk(first keys)", dk[a:a + 4], hk, torch.bfloat16, f" item {b}")
+        close("dv(first keys)", dv[a:a + 4], hv, torch.bfloat16, f" item {b}")
 
 
 def test_bf16_saturation_flag_and_nan_passthrough():

@@ -3,14 +3,18 @@ against the float64 oracle (oracle/lmhead.py).
 
 Inputs are bf16, rounded once on the host; the oracle sees the rounded values.
 Bars: loss to 1e-4 relative, LSE to 1e-3 absolute (fp32 accumulation of exact
-bf16 products); dh and dW (bf16 outputs built from a bf16-rounded dS) to
-|gpu - ref| <= 1e-2 |ref| + 5e-3 max|ref| elementwise."""
+bf16 products).  dh and dW are sums over the vocabulary / the tokens of
+dlogits rounded to bf16 (relative error 2^-9 per term) times bf16 operands,
+accumulated in fp32 and stored in bf16 (2^-9 of the result): elementwise
+|gpu - ref| <= 1e-2 |ref| + 4e-3 M, where M is the sum of the magnitudes of
+the element's terms (|dlogits| |W| for dh, |dlogits|^T |h| for dW), the
+quantity that bounds the rounding error of a sum."""
 import numpy as np
 import pytest
 import torch
 
 import prefix_shared_masked_amd as pkg
-from oracle.lmhead import lmhead_weighted_nll
+from oracle.lmhead import lmhead_vocab_rows, lmhead_weighted_nll
 import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -27,10 +31,10 @@ def inputs(N, V, Dm, seed, p_ignore=0.2):
     return h, Wt, labels, w
 
 
-def grad_close(name, got, ref):
+def grad_close(name, got, ref, mag):
     got = got.float().cpu().double().numpy()
     err = np.abs(got - ref)
-    bar = 1e-2 * np.abs(ref) + 5e-3 * np.abs(ref).max()
+    bar = 1e-2 * np.abs(ref) + 4e-3 * mag
     bad = err > bar
     assert not bad.any(), f"{name}: {int(bad.sum())} of {bad.size} outside, max err {err.max():.3e}"
 
@@ -47,8 +51,9 @@ def run(N, V, Dm, seed, vocab_chunk=0, grads=True):
     assert loss.item() == pytest.approx(ref["loss"], rel=1e-4)
     np.testing.assert_allclose(lse.cpu().numpy(), ref["lse"], rtol=0, atol=1e-3)
     if grads:
-        grad_close("dh", dh, ref["dh"])
-        grad_close("dW", dW, ref["dW"])
+        absdl = np.abs(ref["dlogits"])
+        grad_close("dh", dh, ref["dh"], absdl @ np.abs(Wt.double().numpy()))
+        grad_close("dW", dW, ref["dW"], absdl.T @ np.abs(h.double().numpy()))
     return loss, dh, dW
 
 
@@ -82,16 +87,19 @@ def test_bad_label_flag_and_ignore():
     ok[3] = -100
     ref = lmhead_weighted_nll(h.double().numpy(), Wt.double().numpy(), ok, w)
     assert loss.item() == pytest.approx(ref["loss"], rel=1e-4)
-    grad_close("dh", dh, ref["dh"])
-    grad_close("dW", dW, ref["dW"])
+    absdl = np.abs(ref["dlogits"])
+    grad_close("dh", dh, ref["dh"], absdl @ np.abs(Wt.double().numpy()))
+    grad_close("dW", dW, ref["dW"], absdl.T @ np.abs(h.double().numpy()))
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_full_output_layer_sampled():
     """The Qwen3-0.6B output-layer shape (V = 151,936, Dm = 1,024) over the
     spine tree's 16,352 tokens with g/K weights: LSE, token loss and dh of
-    sampled tokens against the oracle row by row; <dW, W> == <dh, h> (both
-    equal sum_t,v dlogits_tv logits_tv); bitwise repeatable."""
+    sampled tokens against the oracle row by row; dW on 64 sampled
+    vocabulary rows (labels among them) element by element against the
+    full-vocabulary oracle; <dW, W> == <dh, h> (both equal
+    sum_t,v dlogits_tv logits_tv); bitwise repeatable."""
     tree = W.spine_tree()
     plan = pkg.tree_plan(tree.parent, tree.seg_len)
     N, V, Dm = plan.n_tokens, 151936, 1024
@@ -120,8 +128,15 @@ def test_full_output_layer_sampled():
             p = np.exp(x - lse_t)
             p[lab[t]] -= 1.0
             ref_dh = w[t].item() * (p @ W64)
+            mag = w[t].item() * (np.abs(p) @ np.abs(W64))
             got = dh[t].float().cpu().double().numpy()
-            assert (np.abs(got - ref_dh) <= 1e-2 * np.abs(ref_dh) + 5e-3 * np.abs(ref_dh).max()).all(), t
+            assert (np.abs(got - ref_dh) <= 1e-2 * np.abs(ref_dh) + 4e-3 * mag).all(), t
+    rng = np.random.default_rng(1)
+    vrows = np.unique(np.concatenate([rng.choice(V, 56, replace=False), lab[lab >= 0][:6], [0, V - 1]]))
+    print(f"[lmhead] full-size dW on {len(vrows)} vocabulary rows", flush=True)
+    rv = lmhead_vocab_rows(h64, W64, lab, w.numpy(), vrows)
+    assert np.abs(lse.cpu().numpy() - rv["lse"]).max() <= 1e-3
+    grad_close("dW(sampled rows)", dW[torch.from_numpy(vrows).to(DEV)], rv["dW"], rv["dW_abs"])
     a = float((dW.double() * Wt.to(DEV).double()).sum())
     b = float((dh.double() * h.to(DEV).double()).sum())
     assert a == pytest.approx(b, rel=2e-2)

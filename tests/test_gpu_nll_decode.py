@@ -161,6 +161,42 @@ def test_decode_256k_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
+def test_decode_mixed_lengths_sampled():
+    """The mixed-length decode batch at full size: 8 items of 32K, 64K, 128K
+    and 256K keys (two of each, 960K keys, 3.9 GB of bf16 K/V), 32 query /
+    8 KV heads, laid out back to back in a shuffled order, with the default
+    split count that the longest item sets (each item spreads its own keys
+    over all splits, so a short item's slices are shorter).  One (item, KV head) slice of every length class, plus a second
+    head of the shortest and longest items, is checked against the oracle."""
+    B, Hq, Hkv, d = 8, 32, 8, 128
+    lens = np.array([128, 32, 256, 64, 32, 128, 64, 256]) * 1024
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    L = int(lens.max())
+    print(f"[decode] mixed lens={list(lens)}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    q = torch.randn(B, Hq, d, generator=g, device=DEV).bfloat16()
+    k = torch.randn(int(lens.sum()), Hkv, d, generator=g, device=DEV).bfloat16()
+    v = torch.randn(int(lens.sum()), Hkv, d, generator=g, device=DEV).bfloat16()
+    span_ptr = torch.arange(B + 1, dtype=torch.int32).to(DEV)
+    spans = torch.from_numpy(np.stack([starts, lens], 1).astype(np.int32)).to(DEV)
+    o, lse = pkg.tree_decode_splitkv(q, k, v, span_ptr, spans, L)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for b, kvh in ((1, 0), (1, 7), (3, 2), (0, 5), (2, 3), (7, 6)):
+        a, n = int(starts[b]), int(lens[b])
+        hs = slice(kvh * G, (kvh + 1) * G)
+        qs = q[b:b + 1, hs].float().cpu().double().numpy()
+        ks = k[a:a + n, kvh:kvh + 1].float().cpu().double().numpy()
+        vs = v[a:a + n, kvh:kvh + 1].float().cpu().double().numpy()
+        ro, rl = oracle.decode_attention(qs, ks, vs, np.array([0, 1], np.int32), np.array([[0, n]], np.int32))
+        err = np.abs(o[b, hs].float().cpu().numpy() - ro[0])
+        assert (err <= 2e-2 + 1e-2 * np.abs(ro[0])).all(), (b, kvh, float(err.max()))
+        assert np.abs(lse[b, hs].cpu().numpy() - rl[0]).max() <= 1e-3, (b, kvh)
+    del k, v
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("V,case", [(1001, "first256"), (256, "group4"), (151936, "mostly")])
 def test_nll_masked_logits(V, case):

@@ -1,6 +1,11 @@
 """GPU parity of the tree-routed scan and causal conv (Tree Training post,
 section 9) against the float64 per-path oracle (oracle/ssm.py).  fp32 on the
-GPU: |gpu - ref| <= 1e-4 |ref| + 1e-5 max|ref| elementwise."""
+GPU: |gpu - ref| <= 1e-4 |ref| + 2e-5 M elementwise, where M is the sum of the
+magnitudes of the terms that make the element (about 170 fp32 units of M,
+which bounds the rounding error of a sum of products): every output here is
+a sum of products, so M is the oracle's own result on |b|, |x|, |w|, |g|
+(the decay a is positive, and da = dh h_prev is bounded by the product of
+the two magnitudes, which is what the oracle returns for it)."""
 import numpy as np
 import pytest
 import torch
@@ -14,10 +19,10 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def close(name, got, ref):
+def close(name, got, ref, mag):
     got = got.cpu().double().numpy() if torch.is_tensor(got) else got
     err = np.abs(got - ref)
-    bad = err > 1e-4 * np.abs(ref) + 1e-5 * np.abs(ref).max()
+    bad = err > 1e-4 * np.abs(ref) + 2e-5 * mag
     assert not bad.any(), f"{name}: {int(bad.sum())} of {bad.size} outside, max err {err.max():.3e}"
 
 
@@ -42,13 +47,15 @@ def run(tree, C, K, seed, chans=None):
     cs = np.arange(C) if chans is None else np.asarray(chans)
     rs = ssm.tree_scan(op, a[:, cs], b[:, cs], g[:, cs])
     rc = ssm.tree_conv(op, x[:, cs], w[cs], g[:, cs])
-    close("h", h[:, cs], rs["h"])
-    close("da", da[:, cs], rs["da"])
-    close("db", db[:, cs], rs["db"])
-    close("y", y[:, cs], rc["y"])
-    close("dx", dx[:, cs], rc["dx"])
+    ms = ssm.tree_scan(op, a[:, cs], np.abs(b[:, cs]), np.abs(g[:, cs]))
+    mc = ssm.tree_conv(op, np.abs(x[:, cs]), np.abs(w[cs]), np.abs(g[:, cs]))
+    close("h", h[:, cs], rs["h"], ms["h"])
+    close("da", da[:, cs], rs["da"], ms["da"])
+    close("db", db[:, cs], rs["db"], ms["db"])
+    close("y", y[:, cs], rc["y"], mc["y"])
+    close("dx", dx[:, cs], rc["dx"], mc["dx"])
     if chans is None:
-        close("dw", dw, rc["dw"])
+        close("dw", dw, rc["dw"], mc["dw"])
     return route
 
 

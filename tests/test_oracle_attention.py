@@ -263,3 +263,30 @@ def test_rows_attention_grads_matches_dense_everywhere():
         np.testing.assert_allclose(dq, ref["dq"], rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(dk, ref["dk"], rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(dv, ref["dv"], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("rope_base,heads,block", [(0.0, (4, 2), 64), (10000.0, (8, 2), 50), (10000.0, (3, 3), 1024)])
+def test_causal_sequence_grads_matches_sdpa_and_dense(rope_base, heads, block):
+    """The row-blocked gradient oracle of one causal sequence (for the heavy
+    first keys of long varlen items) on 300 tokens: several row blocks and a
+    ragged last block.  Without RoPE it equals torch's CPU
+    scaled_dot_product_attention backward (causal, enable_gqa); with RoPE it
+    equals the dense-mask backward of a one-node tree (the same sequence with
+    depth positions 0..L-1)."""
+    Hq, Hkv = heads
+    L, d = 300, 16
+    q, k, v, do = _inputs(L, Hq, Hkv, d, seed=13)
+    rows = [0, 1, 63, 64, 150, L - 2, L - 1]
+    keys = [0, 1, 2, 49, 50, 64, 200, L - 1]
+    dq, dk, dv = oracle.causal_sequence_grads(q, k, v, do, rows, keys, rope_base=rope_base, block=block)
+    if rope_base == 0.0:
+        tq, tk, tv = (torch.tensor(np.transpose(x, (1, 0, 2)), requires_grad=True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True)
+        out.backward(torch.tensor(np.transpose(do, (1, 0, 2))))
+        ref = {n: np.transpose(t.grad.numpy(), (1, 0, 2)) for n, t in (("dq", tq), ("dk", tk), ("dv", tv))}
+    else:
+        op = oracle.oracle_plan(np.array([-1], np.int32), np.array([L], np.int32))
+        ref = oracle.dense_mask_attention(op, q, k, v, rope_base=rope_base, dO=do)
+    np.testing.assert_allclose(dq, ref["dq"][rows], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dk, ref["dk"][keys], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dv, ref["dv"][keys], rtol=1e-9, atol=1e-12)

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.lmhead import chunked_lmhead_weighted_nll, lmhead_weighted_nll
+from oracle.lmhead import chunked_lmhead_weighted_nll, lmhead_vocab_rows, lmhead_weighted_nll
 import workloads as W
 
 
@@ -84,3 +84,26 @@ def test_tree_weights_equal_per_path_average():
     h, Wt, labels, _ = _case(N=op.n_tokens, V=17, D=8, seed=6, p_ignore=0.0)
     r = lmhead_weighted_nll(h, Wt, labels, op.g / op.n_leaves)
     assert r["loss"] == pytest.approx(oracle.per_path_loss(op, r["token_loss"]), rel=1e-13)
+
+
+@pytest.mark.parametrize("chunk", [1, 13, 2048])
+def test_vocab_rows_match_torch_autograd(chunk):
+    """The full-size spot-check form (lse of every token, dW on selected
+    vocabulary rows, the label rows among them) against torch's CPU
+    cross_entropy with autograd in float64; its magnitude sum
+    sum_t |dlogits_tv| |h_t| against the same product formed from the
+    absolute values of torch's per-token gradient (autograd w.r.t. the
+    logits)."""
+    h, Wt, labels, w = _case(N=50, V=37, D=12, seed=8)
+    rows = np.unique(np.concatenate([[0, 36, 5], labels[labels >= 0][:3]]))
+    r = lmhead_vocab_rows(h, Wt, labels, w, rows, chunk=chunk)
+    th = torch.tensor(h)
+    tW = torch.tensor(Wt, requires_grad=True)
+    logits = (th @ tW.T).detach().requires_grad_(True)
+    tok = torch.nn.functional.cross_entropy(logits, torch.tensor(labels, dtype=torch.int64), reduction="none",
+                                            ignore_index=-100)
+    (tok * torch.tensor(w)).sum().backward()
+    G = logits.grad.numpy()
+    np.testing.assert_allclose(r["lse"], torch.logsumexp(logits.detach(), 1).numpy(), rtol=1e-14)
+    np.testing.assert_allclose(r["dW"], (G.T @ h)[rows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["dW_abs"], (np.abs(G).T @ np.abs(h))[rows], rtol=1e-12, atol=1e-15)
