@@ -12,19 +12,21 @@
 // workspace (the dS path):
 //  1. preparation: fp16 copy of K times scale * log2(e) (rotated with RoPE);
 //     prep_kernel: fp16 copy of the rotated Q, -D and -LSE * log2(e);
-//  2. dK/dV, key-stationary, over the planner's work pieces: four wavefronts,
-//     each owning the dK/dV of up to 32 keys of one node (a sub-tile), over a
-//     common run of 32-row query blocks on the query-tile grid.  Every query
-//     of a node's DFS interval reads every key of the node, so Q and dO
+//  2. dK/dV, key-stationary, over the planner's work pieces: up to four
+//     32-key sub-tiles of one node per workgroup, each worked by two
+//     wavefronts on one SIMD (one holds K and forms S, P and dV; the other
+//     holds V and forms dP, dS and dK, taking P from the first through LDS),
+//     over a common run of 32-row query blocks on the query-tile grid.  Every
+//     query of a node's DFS interval reads every key of the node, so Q and dO
 //     stream as contiguous blocks with no gather; each block is staged in LDS
-//     once for the four wavefronts, and the loop runs over every query head
+//     once for the eight wavefronts, and the loop runs over every query head
 //     of the GQA group, so the group's sum stays in registers.  Scores use
 //     the fp16 copies of rotated Q and K (finer rounding than bf16 for
-//     rotated values; same MFMA rate), so P matches the forward's.  K and V
-//     stay in registers; dV += P^T dO and dK += dS^T Q use the LDS transpose
-//     read of the staged blocks.  The fp16 dS of every (query tile, sub-tile)
-//     block is stored for step 3, and sub-tiles cut over several query
-//     windows leave fp32 partials that dkv_sum_kernel adds in a fixed order;
+//     rotated values; same MFMA rate), so P matches the forward's.  dV += P^T
+//     dO and dK += dS^T Q use the LDS transpose read of the staged blocks.
+//     The fp16 dS of every (query tile, sub-tile) block is stored for step 3,
+//     and sub-tiles cut over several query windows leave fp32 partials that
+//     dkv_sum_kernel adds in a fixed order;
 //  3. dQ = scale dS K from the stored dS (dq_ds_kernel), query-stationary
 //     over each query tile's list of sub-tiles.
 // With the smallest workspace the dQ kernel (dq_bf16_kernel) runs before
@@ -337,11 +339,11 @@ constexpr int SUB = TA_KV_SUB;  // keys per wavefront = rows per query block
 // 32, dimension dt*32 + l%32).
 constexpr int PART_WAVE = 2 * 4 * 16 * 64;
 
-// dK (scaled, rotated back by -pos) and dV of one key in bf16, dimensions
-// dt*32 + col for dt = 0..3 (the rotate-half partner of d is tile dt + 2).
-// inv: the inverse frequencies of dimensions col and 32 + col.
-__device__ __forceinline__ void store_key(const KVParams& P, int kvh, int key, int col, const double (&inv)[2],
-                                          float (&g)[4], const float (&v)[4]) {
+// dK of one key (scaled, rotated back by -pos) and dV of one key, in bf16,
+// dimensions dt*32 + col for dt = 0..3 (the rotate-half partner of d is tile
+// dt + 2).  inv: the inverse frequencies of dimensions col and 32 + col.
+__device__ __forceinline__ void store_k(const KVParams& P, int kvh, int key, int col, const double (&inv)[2],
+                                        float (&g)[4]) {
   const size_t o = ((size_t)key * P.Hkv + kvh) * D;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) g[dt] *= P.scale;
@@ -356,26 +358,12 @@ __device__ __forceinline__ void store_key(const KVParams& P, int kvh, int key, i
     }
   }
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    P.dk[o + dt * 32 + col] = (bf16)g[dt];
-    P.dv[o + dt * 32 + col] = (bf16)v[dt];
-  }
+  for (int dt = 0; dt < 4; ++dt) P.dk[o + dt * 32 + col] = (bf16)g[dt];
 }
-
-// dK and dV of one wavefront's keys [kw, kw + wkeys).  Accumulator register
-// r of tile dt <-> key kw + 8*(r/4) + 4*half + r%4, d = dt*32 + col.
-__device__ __forceinline__ void store_dkv(const KVParams& P, int kvh, int kw, int wkeys, int half, int col,
-                                          const f32x16 (&dk)[4], const f32x16 (&dv)[4]) {
-  const double inv[2] = {P.rope_base > 0.f ? rope_inv(col, D, P.rope_base) : 0.0,
-                         P.rope_base > 0.f ? rope_inv(32 + col, D, P.rope_base) : 0.0};
+__device__ __forceinline__ void store_v(const KVParams& P, int kvh, int key, int col, const float (&v)[4]) {
+  const size_t o = ((size_t)key * P.Hkv + kvh) * D;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
-    if (kr >= wkeys) continue;
-    float g[4] = {dk[0][r], dk[1][r], dk[2][r], dk[3][r]};
-    const float v[4] = {dv[0][r], dv[1][r], dv[2][r], dv[3][r]};
-    store_key(P, kvh, kw + kr, col, inv, g, v);
-  }
+  for (int dt = 0; dt < 4; ++dt) P.dv[o + dt * 32 + col] = (bf16)v[dt];
 }
 
 // One staged query block in LDS: fp16 Q rows (scores, and the transpose-read
@@ -390,316 +378,379 @@ struct KVStageLayout {
   static constexpr int BYTES = DD + SUB * 4;
 };
 static_assert(KVStageLayout::BYTES % 16 == 0, "stage buffers stay 16-byte aligned");
+constexpr int KV_NBUF = 7;           // staged blocks: copies run five items ahead, a block lives three steps
+constexpr int KV_XCH = 2 * 64 * 16;  // one sub-tile's P block in fp16: [register half 2][lane 64][16 bytes]
 
+// Two wavefronts per 32-key sub-tile, one of each role, eight per workgroup
+// (wavefronts w and w + 4 share sub-tile w and, as the hardware places a
+// workgroup's wavefronts round-robin over the four SIMDs, one SIMD):
+//  role A (w < 4) holds the sub-tile's K, computes S = Q K^T - LSE, P and
+//    dV += P^T dO, and hands P (fp16) to its partner through LDS;
+//  role B (w >= 4) holds V, computes dP = dO V^T - D, dS = P dP (with the P
+//    of the previous step) and dK += dS^T Q, and stores the fp16 dS blocks.
+// Each role keeps 64 accumulators instead of 128, so two wavefronts fit on
+// every SIMD and one's MFMAs run while the other waits on its exponentials,
+// LDS reads or conversions.  All eight share the staged blocks; a block is
+// read by A one step before its item (scores), by both during it, and by B
+// one step after (dK); seven buffers rotate and copies run five items
+// ahead, so a copy has three steps to land.  Items are (32-row block, query head) of the piece's rows
+// [qlo, qhi), blocks from the end down and the heads of the group innermost:
+// the workgroups resident on an XCD share a KV head and mostly the same
+// rows, so one fetch serves them from L2.  Rows past qhi (and past the last
+// token, clamped to it) are masked to P = 0, like every row outside a
+// sub-tile's [key, rhi), so they contribute nothing.
 // DS: also store the fp16 dS blocks for the dQ pass (the dS path).
 template <bool DS>
-__global__ __launch_bounds__(256, 1) void dkv_bf16_kernel(KVParams P) {
+__global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
   using L = KVStageLayout;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * L::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[KV_NBUF * L::BYTES + 2 * 4 * KV_XCH];
 
   const int kvr = blockIdx.x % P.nkv, kvh = P.kv0 + kvr;
   const cint_ptr tl = as_const(P.kp) + (size_t)(blockIdx.x / P.nkv) * TA_KPIECE_INTS;
-  const int qlo = tl[0], qhi = tl[1];             // the piece's query rows, staged for all four
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int qlo = tl[0], qhi = tl[1];
+  const int lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(wave);
-  // this wavefront's keys [kw, kw + wkeys) (0: idle), its rows [rlo, rhi)
-  // within [qlo, qhi) (each key reads rows [max(key, rlo), rhi)), its
-  // partial slot or -1, and the dS block of query tile t: dsoff + t
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = wv & 3;
+  const bool roleB = wv >= 4;
+  // sub-tile w: keys [kw, kw + wkeys) (0: idle), rows [rlo, rhi) within
+  // [qlo, qhi) (each key reads rows [max(key, rlo), rhi)), partial slot or
+  // -1, and the dS block of query tile t: dsoff + t
   const cint_ptr tw = tl + 4 + TA_KWAVE_INTS * w;
   const int kw = tw[0], wkeys = tw[1], rlo = tw[2], rhi = tw[3], slot = tw[4], dsoff = tw[5];
   const bool kvalid = col < wkeys;
   const int key = kw + col;
 
-  // K (fp16) and V as B operands held in registers: lane = key column,
-  // k-slots s*16 + half*8 + e; keys past the tile are zero.
-  f16x8 kf[8];
-  bf16x8 vf[8];
+  // K (fp16, role A) or V (bf16, role B) as the B operand of the score
+  // MFMAs, held in registers: lane = key column, k-slots s*16 + half*8 + e;
+  // keys past the tile are zero.
+  u32x4 fr[8];
   {
-    const size_t off = ((size_t)(kvalid ? key : kw) * P.Hkv + kvh) * D + half * 8;
+    const char* src = roleB ? (const char*)P.v : (const char*)P.k;
+    const size_t off = (((size_t)(kvalid ? key : kw) * P.Hkv + kvh) * D + half * 8) * 2;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x4 a0 = *(const u32x4*)(P.k + off + s * 16), c0 = *(const u32x4*)(P.v + off + s * 16);
-      const u32x4 a = kvalid ? a0 : z, c = kvalid ? c0 : z;
-      kf[s] = __builtin_bit_cast(f16x8, a);
-      vf[s] = __builtin_bit_cast(bf16x8, c);
+      const u32x4 a = *(const u32x4*)(src + off + s * 32);
+      fr[s] = kvalid ? a : z;
     }
   }
-  // dK and dV accumulate in AGPRs for the whole loop
-  f32x16 dk[4], dv[4];
+  // dV (role A) or dK (role B) accumulates in registers for the whole loop
+  f32x16 acc[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
-  }
-  agpr_fence8(dk, dv);
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+  acc_fence4(acc);
 
-  // Swizzled LDS offsets (in elements), fixed per lane: koff[s] for the
-  // 16-byte row reads of k-group s (Q for S, dO for dP), toff[dt][x] for the
+  // Swizzled LDS offsets (in bytes), fixed per lane: koff[s] for the 16-byte
+  // row reads of k-group s (Q for S, dO for dP), toff[dt][x] for the
   // transpose reads of d-tile dt, rows trow + 8x of each 16-row group.
   const int trow = half * 4 + ((lane & 15) >> 2);
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
   int koff[8], toff[4][2];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) koff[s] = col * D + (((2 * s + half) ^ swz(col & 15)) << 3);
+  for (int s = 0; s < 8; ++s) koff[s] = 2 * (col * D + (((2 * s + half) ^ swz(col & 15)) << 3));
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int r = trow + 8 * x;
-      toff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
+      toff[dt][x] = 2 * (r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7));
     }
 
-  // Items are (32-row block, query head) of the piece's rows [qlo, qhi),
-  // blocks qlo + 32 bi from the end down and the heads of the group
-  // innermost: the workgroups resident on an XCD share a KV head and mostly
-  // the same rows (pieces are listed by length and last row), so they stream
-  // the same rows at about the same time and one fetch serves them from L2.
-  // All four wavefronts share each staged block.  Rows past qhi (and past the
-  // last token, clamped to it) are masked to P = 0 below, like every row
-  // outside a wavefront's [key, rhi), so they contribute nothing.
   const int G = P.G;
   const int nblk = (qhi - qlo + SUB - 1) / SUB;   // >= 1: the plan gives every piece a query row
   const int nitem = G * nblk;
-  // Staging: wavefront w copies rows 4i + lane/16 (i = w and w + 4) of the
-  // block's fp16 Q and bf16 dO (a swizzled 16-byte piece per lane), and
-  // wavefront 0 also the block's 32 -LSE * log2(e) and 32 -D values (one
-  // 256-byte record).  The per-lane offsets inside a block are fixed, so only
-  // the scalar base (block, head) changes from item to item.
-  const int rowA = 4 * w + (lane >> 4);  // row of copy i = w; copy i = w + 4 is rowA + 16 (same swizzle)
+  // Staging: wavefront wv copies rows 4 wv + lane/16 of the block's fp16 Q
+  // and bf16 dO (a swizzled 16-byte piece per lane), and wavefront 0 also
+  // the block's 32 -LSE * log2(e) and 32 -D values (one 256-byte record).
+  // The per-lane offsets inside a block are fixed, so only the scalar base
+  // (block, head) changes from item to item.  The staging cursor (sbi, sg)
+  // walks the items without divisions (past the last item it repeats the
+  // last one, into the buffer nobody reads); sbuf is the buffer it fills.
+  const int rowA = 4 * wv + (lane >> 4);
   const uint32_t piece = (uint32_t)(((lane & 15) ^ swz(rowA & 15)) << 4);
   const uint32_t rstride = (uint32_t)P.Hq * (D * 2);
   const uint32_t lds0 = lds_addr(smem);
-  auto stage = [&](int bi, int g, int b) {
-    const int qb = qlo + SUB * bi;
-    const int h = kvh * G + g;
-    const int lim = P.N - 1 - qb;
-    const uint32_t vA = (uint32_t)min(rowA, lim) * rstride + piece;
-    const uint32_t vB = (uint32_t)min(rowA + 16, lim) * rstride + piece;
+  int sbi = nblk - 1, sg = 0, sbuf = 0;
+  auto stage_next = [&]() {
+    const int qb = qlo + SUB * sbi;
+    const int h = kvh * G + sg;
+    const uint32_t v = (uint32_t)min(rowA, P.N - 1 - qb) * rstride + piece;
     const size_t off = ((size_t)qb * P.Hq + h) * (D * 2);
-    const char* sq = (const char*)P.q + off;
-    const char* so = (const char*)P.dO + off;
-    const uint32_t lb = lds0 + b * L::BYTES;
-    copy16_to_lds_s(sq, vA, lb + L::Q16 + w * 1024);
-    copy16_to_lds_s(sq, vB, lb + L::Q16 + (w + 4) * 1024);
-    copy16_to_lds_s(so, vA, lb + L::DO + w * 1024);
-    copy16_to_lds_s(so, vB, lb + L::DO + (w + 4) * 1024);
-    if (w == 0) copy4_to_lds_s(P.nld + ((size_t)h * P.nqb + ((qb - P.q0) >> 5)) * (2 * SUB), lane * 4, lb + L::LS);
-  };
-  // One step per item `it`, two register sets for the score accumulators:
-  // the step masks and exponentiates the scores of item it (computed in the
-  // previous step), runs the score MFMAs of item it + 1 (S = Q K^T - LSE on
-  // fp16 operands, in log2 units since the K copy carries scale * log2(e),
-  // and dP = dO V^T - D; both start from the staged -LSE and -D, so
-  // P = exp2(S) and dS = P dP need no further per-element terms), then the
-  // accumulating MFMAs of item it (dV += P^T dO in bf16, dK += dS^T Q in
-  // fp16).  The source order below is the issue order: scheduling fences
-  // keep the exponentials and products of item it between the score MFMAs
-  // of item it + 1, and the copies of item it + 3 and the dS stores between
-  // the accumulating MFMAs, so the matrix unit always has independent work
-  // queued while the other units run.  LDS operands are read one k-group
-  // ahead of their MFMAs.  Every wavefront runs every block: blocks that end
-  // before its first key are fully masked by the causal compare, and keys
-  // past the tile are never stored.  (Keeping the accumulating MFMAs
-  // unconditional lets the accumulators stay in AGPRs.)
-  const int ds_lane = col * SUB + half * 16;  // this lane's 16 elements in a dS block
-  // element mask limit: key <= row < rhi is (row - key) < lim; keys past a
-  // short sub-tile read no rows, so their dS (and P) is exactly zero
-  const unsigned lim = kvalid ? (unsigned)max(rhi - key, 0) : 0u;
-  // seeds of a score accumulator pair from a staged block: register r <->
-  // query row 8*(r/4) + 4*half + r%4 of the block
-  auto seed = [&](const char* base, f32x16& S, f32x16& dP) {
-    const float* ls = (const float*)(base + L::LS);
-    const float* dd = (const float*)(base + L::DD);
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 l4 = *(const float4*)(ls + 8 * r4 + 4 * half);
-      const float4 d4 = *(const float4*)(dd + 8 * r4 + 4 * half);
-      S[4 * r4 + 0] = l4.x;
-      S[4 * r4 + 1] = l4.y;
-      S[4 * r4 + 2] = l4.z;
-      S[4 * r4 + 3] = l4.w;
-      dP[4 * r4 + 0] = d4.x;
-      dP[4 * r4 + 1] = d4.y;
-      dP[4 * r4 + 2] = d4.z;
-      dP[4 * r4 + 3] = d4.w;
-    }
-  };
-  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
-
-  // Four LDS buffers: an item's block sits in buffer (item % 4) and its
-  // copies are issued three items ahead.  Staging and score MFMAs run
-  // unconditionally (past the last item they repeat the last item, into a
-  // buffer / registers nobody uses).  The staging cursor (sbi, sg) walks the
-  // items without divisions; each buffer remembers the item it holds.
-  char* const bb[4] = {smem, smem + L::BYTES, smem + 2 * L::BYTES, smem + 3 * L::BYTES};
-  int sbi = nblk - 1, sg = 0;
-  int bbi[4], bg[4];
-  auto stage_next = [&](int b) {
-    stage(sbi, sg, b);
-    bbi[b] = sbi;
-    bg[b] = sg;
+    const uint32_t lb = lds0 + sbuf * L::BYTES;
+    copy16_to_lds_s((const char*)P.q + off, v, lb + L::Q16 + wv * 1024);
+    copy16_to_lds_s((const char*)P.dO + off, v, lb + L::DO + wv * 1024);
+    if (wv == 0) copy4_to_lds_s(P.nld + ((size_t)h * P.nqb + ((qb - P.q0) >> 5)) * (2 * SUB), lane * 4, lb + L::LS);
     if (sg + 1 < G) {
       ++sg;
     } else if (sbi > 0) {
       sg = 0;
       --sbi;
     }
+    sbuf = sbuf + 1 == KV_NBUF ? 0 : sbuf + 1;
   };
-  auto step = [&](int u, f32x16& Sg, f32x16& dPg, f32x16& Sn, f32x16& dPn) {
-    const char* gb = bb[u];              // item it: transpose-read operands of the accumulating MFMAs
-    const char* nb = bb[(u + 1) & 3];    // item it + 1: score operands and seeds
-    const int qb = qlo + SUB * bbi[u];
-    const int hg = bg[u];
-    // element mask of item it (register r <-> row qb + 8*(r/4) + 4*half +
-    // r%4, key kw + col), applied to S before the exponentials; only blocks
-    // that start before the wavefront's last key or end past its rows need
-    // it: one unsigned compare (row - key) < (rhi - key), with no rows at
-    // all for a key >= rhi (a window may end inside the wavefront's keys)
-    if (qb < kw + SUB || qb + SUB > rhi || wkeys < SUB) {
-      const int d0 = qb + 4 * half - key;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if ((unsigned)(d0 + 8 * (r >> 2) + (r & 3)) >= lim) Sg[r] = -INFINITY;
-    }
-    fence();
-    const f16* q16n = (const f16*)(nb + L::Q16);
-    const bf16* don = (const bf16*)(nb + L::DO);
-    const f16* q16g = (const f16*)(gb + L::Q16);
-    const bf16* dog = (const bf16*)(gb + L::DO);
-    seed(nb, Sn, dPn);
-    f16x8 qa[8];
-    bf16x8 oa[8];
-    qa[0] = *(const f16x8*)(q16n + koff[0]);
-    oa[0] = *(const bf16x8*)(don + koff[0]);
-    qa[1] = *(const f16x8*)(q16n + koff[1]);
-    oa[1] = *(const bf16x8*)(don + koff[1]);
-    fence();
-    float p[16];
-    bf16x8 pa[2];
-    f16x8 sa[2];
-    bf16x8 od[4][2];
-    f16x8 oq[4][2];
-    f16* blk = P.ds_spare;  // dS block of item it (see the stores below)
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (DS && s == 1) {  // scalar work, placed among the score MFMAs
-        const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
-        if (own) blk = P.ds + (((size_t)kvr * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * G + hg) * (SUB * SUB);
-      }
-      // operands of k-group s + 2, then the MFMAs of k-group s
-      if (s < 6) {
-        qa[s + 2] = *(const f16x8*)(q16n + koff[s + 2]);
-        oa[s + 2] = *(const bf16x8*)(don + koff[s + 2]);
-      }
-      Sn = mfma32h(qa[s], kf[s], Sn);
-      dPn = mfma32(oa[s], vf[s], dPn);
-      // transpose-read operands of the accumulating MFMAs (d-tile s / 2)
-      {
-        const int dt = s >> 1, qs = s & 1;
-        od[dt][qs] = cat(lds_read_tr(dog + qs * 16 * D + toff[dt][0]), lds_read_tr(dog + qs * 16 * D + toff[dt][1]));
-        oq[dt][qs] = cat(lds_read_tr(q16g + qs * 16 * D + toff[dt][0]), lds_read_tr(q16g + qs * 16 * D + toff[dt][1]));
-      }
-      // P of item it, two elements per k-group; products and packing once a
-      // half of the block's registers is exponentiated
-      // (the empty asm statements pin each result to this k-group: without
-      // them the compiler sinks the arithmetic to its first use, after the
-      // last score MFMA)
-      p[2 * s] = exp2f_fast(Sg[2 * s]);
-      p[2 * s + 1] = exp2f_fast(Sg[2 * s + 1]);
-      asm volatile("" : "+v"(p[2 * s]), "+v"(p[2 * s + 1]));
-      if (s == 3 || s == 7) {
-        const int hh = s >> 2;
-        float ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pa[hh][e] = (bf16)p[8 * hh + e];
-          ds[e] = p[8 * hh + e] * dPg[8 * hh + e];
-        }
-        sa[hh] = pack_f16_rtz(ds);
-        asm volatile("" : "+v"(pa[hh]), "+v"(sa[hh]));
-      }
-      fence();
-    }
-    // dS of item it (block qb is query tile (qb - q0) / 32), stored as
-    // [key][position] with position half*16 + r, so each lane writes 32
-    // contiguous bytes; into the spare block when the wavefront does not own
-    // it (the store stays unconditional).  Non-temporal: dS is read once, by
-    // the dQ pass, and should not linger dirty in the caches.  The stores go
-    // out before the step's copies (see the wait below).
-    if (DS) {
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[0]), (u32x4*)(blk + ds_lane));
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[1]), (u32x4*)(blk + ds_lane + 8));
-    }
-    // accumulating MFMAs of item it, with the copies of item it + 3 issued
-    // between them
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        mfma32_acc(dv[dt], pa[qs], od[dt][qs]);
-        mfma32h_acc(dk[dt], sa[qs], oq[dt][qs]);
-      }
-      if (dt == 0) stage_next((u + 3) & 3);
-      fence();
+  // Each wavefront issues two copies per step (wavefront 0 three), role B
+  // after its two dS stores.  Vector memory operations complete in issue
+  // order, so "at most six outstanding" at the end of step j means the
+  // copies of the items up to j + 2 (all the next step reads) have landed:
+  // for role A the six are the copies of items j + 3 .. j + 5, for role B
+  // at most the copies of j + 4 and j + 5 and this step's stores (the dS
+  // stores of earlier steps must then be acknowledged, two steps after
+  // their issue).
+  auto end_step = []() {
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    __syncthreads();
+  };
+  auto buf = [&](int b) { return smem + b * L::BYTES; };
+  auto next_buf = [](int b) { return b + 1 == KV_NBUF ? 0 : b + 1; };
+  auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
+  // an item cursor (block bi, head g), advanced like the staging cursor
+  auto adv = [&](int& bi, int& g) {
+    if (g + 1 < G) {
+      ++g;
+    } else {
+      g = 0;
+      --bi;
     }
   };
+  char* const xch = smem + KV_NBUF * L::BYTES + w * KV_XCH + lane * 16;  // this lane's P slot, parity 0
 
-  // Wavefronts 1-3 issue four copies per item and wavefront 0 five, after
-  // the step's two dS stores, so "at most four outstanding" after a step
-  // means every earlier copy and store is complete (they complete in order):
-  // for wavefronts 1-3 exactly the items up to it + 2, for wavefront 0 also
-  // the first copy of item it + 3.
-  stage_next(0);
-  stage_next(1);
-  stage_next(2);
-  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // items 0 and 1 landed
+#pragma unroll
+  for (int i = 0; i < 5; ++i) stage_next();
+  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // items 0 and 1 landed
   __syncthreads();
-  f32x16 Sa, dPa, Sb, dPb;
-  // scores of item 0
-  {
-    const f16* q16 = (const f16*)(bb[0] + L::Q16);
-    const bf16* dob = (const bf16*)(bb[0] + L::DO);
-    seed(bb[0], Sa, dPa);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      Sa = mfma32h(*(const f16x8*)(q16 + koff[s]), kf[s], Sa);
-      dPa = mfma32(*(const bf16x8*)(dob + koff[s]), vf[s], dPa);
-    }
-  }
-  for (int it = 0; it < nitem; it += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u > 0 && it + u >= nitem) break;
-      if (u & 1)
-        step(u, Sb, dPb, Sa, dPa);
-      else
-        step(u, Sa, dPa, Sb, dPb);
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      __syncthreads();
-    }
-  }
-  lds_copies_wait();
 
-  agpr_fence8(dk, dv);
-  // Each wavefront owns its keys: a sub-tile read in one run stores them
-  // (scaled, rotated back, bf16); a run of a sub-tile cut over several
-  // windows writes its raw accumulators to its partial slot for
-  // dkv_sum_kernel.
-  if (slot < 0) {
-    store_dkv(P, kvh, kw, wkeys, half, col, dk, dv);
-  } else if (wkeys > 0) {
-    float* dst = P.part + ((size_t)slot * P.Hkv + kvh) * PART_WAVE + lane * 4;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  if (!roleB) {
+    // ---- role A: S, P, dV ------------------------------------------------
+    // element mask limit: key <= row < rhi is (row - key) < lim; keys past a
+    // short sub-tile read no rows, so their P is exactly zero
+    const unsigned lim = kvalid ? (unsigned)max(rhi - key, 0) : 0u;
+    auto seed = [&](const char* b, f32x16& S) {  // register r <-> row 8*(r/4) + 4*half + r%4
+      const float* ls = (const float*)(b + L::LS);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int o = (dt * 4 + r4) * 256;
-        *(float4*)(dst + o) = float4{dk[dt][4 * r4], dk[dt][4 * r4 + 1], dk[dt][4 * r4 + 2], dk[dt][4 * r4 + 3]};
-        *(float4*)(dst + PART_WAVE / 2 + o) =
-            float4{dv[dt][4 * r4], dv[dt][4 * r4 + 1], dv[dt][4 * r4 + 2], dv[dt][4 * r4 + 3]};
+        const float4 l4 = *(const float4*)(ls + 8 * r4 + 4 * half);
+        S[4 * r4 + 0] = l4.x;
+        S[4 * r4 + 1] = l4.y;
+        S[4 * r4 + 2] = l4.z;
+        S[4 * r4 + 3] = l4.w;
       }
+    };
+    int cb = 0, ibi = nblk - 1, ig = 0;  // item j: buffer, block, head
+    f32x16 Sa, Sb;
+    {
+      const char* b0 = buf(0);
+      seed(b0, Sa);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        Sa = mfma32h(*(const f16x8*)(b0 + L::Q16 + koff[s]), __builtin_bit_cast(f16x8, fr[s]), Sa);
+    }
+    // One step per item j: first the operands of the step's first MFMAs
+    // are requested, then S(j) (computed in the previous step) is masked and
+    // exponentiated and P(j) handed to role B; then the score MFMAs of item
+    // j + 1 (a dependent chain) alternate with the dV += P(j)^T dO(j) MFMAs
+    // (independent of it), so the matrix unit always has a ready MFMA.  The
+    // copies of item j + 5 go out among them.  LDS operands are read two
+    // MFMA pairs ahead.  The source order is the issue order.
+    auto step = [&](int j, f32x16& Sg, f32x16& Sn) {
+      const char* gb = buf(cb);
+      const char* nb = buf(next_buf(cb));
+      const int qb = qlo + SUB * ibi;
+      f16x8 qa[8];
+      bf16x8 od[8];  // transpose reads of dO(j): MFMA m = 2 dt + qs
+      auto read_od = [&](int m) {
+        const char* o = gb + L::DO + (m & 1) * 16 * D * 2;
+        od[m] = cat(lds_read_tr((const bf16*)(o + toff[m >> 1][0])), lds_read_tr((const bf16*)(o + toff[m >> 1][1])));
+      };
+      seed(nb, Sn);
+      qa[0] = *(const f16x8*)(nb + L::Q16 + koff[0]);
+      read_od(0);
+      qa[1] = *(const f16x8*)(nb + L::Q16 + koff[1]);
+      read_od(1);
+      if (qb < kw + SUB || qb + SUB > rhi || wkeys < SUB) {
+        const int d0 = qb + 4 * half - key;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((unsigned)(d0 + 8 * (r >> 2) + (r & 3)) >= lim) Sg[r] = -INFINITY;
+      }
+      bf16x8 pa[2];
+      {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = exp2f_fast(Sg[r]);
+        char* const xp = xch + (j & 1) * (4 * KV_XCH);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pa[hh][e] = (bf16)p[8 * hh + e];
+          *(f16x8*)(xp + hh * 1024) = pack_f16_rte(p + 8 * hh);
+        }
+      }
+      fence();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s < 6) {
+          qa[s + 2] = *(const f16x8*)(nb + L::Q16 + koff[s + 2]);
+          read_od(s + 2);
+        }
+        Sn = mfma32h(qa[s], __builtin_bit_cast(f16x8, fr[s]), Sn);
+        mfma32_accv(acc[s >> 1], pa[s & 1], od[s]);
+        if (s == 1) stage_next();
+        fence();
+      }
+      mfma_operand_hold(pa[0], pa[1], od[6], od[7]);
+      cb = next_buf(cb);
+      adv(ibi, ig);
+    };
+    for (int j = 0; j < nitem; j += 2) {
+      step(j, Sa, Sb);
+      end_step();
+      if (j + 1 >= nitem) break;
+      step(j + 1, Sb, Sa);
+      end_step();
+    }
+    lds_copies_wait();
+    acc_fence4(acc);
+    if (slot < 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
+        if (kr >= wkeys) continue;
+        const float v[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+        store_v(P, kvh, kw + kr, col, v);
+      }
+    } else if (wkeys > 0) {
+      float* dst = P.part + ((size_t)slot * P.Hkv + kvh) * PART_WAVE + PART_WAVE / 2 + lane * 4;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(float4*)(dst + (dt * 4 + r4) * 256) =
+              float4{acc[dt][4 * r4], acc[dt][4 * r4 + 1], acc[dt][4 * r4 + 2], acc[dt][4 * r4 + 3]};
+    }
+  } else {
+    // ---- role B: dP, dS, dK ------------------------------------------------
+    auto seed = [&](const char* b, f32x16& dP) {
+      const float* dd = (const float*)(b + L::DD);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 d4 = *(const float4*)(dd + 8 * r4 + 4 * half);
+        dP[4 * r4 + 0] = d4.x;
+        dP[4 * r4 + 1] = d4.y;
+        dP[4 * r4 + 2] = d4.z;
+        dP[4 * r4 + 3] = d4.w;
+      }
+    };
+    const int ds_lane = col * SUB + half * 16;  // this lane's 16 elements in a dS block
+    int cb = 0, ibi = nblk - 1, ig = 0;         // item j - 1 of step j: buffer, block, head
+    f32x16 dPa, dPb;
+    {  // step 0: dP of item 0 only
+      const char* b0 = buf(0);
+      seed(b0, dPa);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        dPa = mfma32(*(const bf16x8*)(b0 + L::DO + koff[s]), __builtin_bit_cast(bf16x8, fr[s]), dPa);
+      stage_next();
+      end_step();
+    }
+    // Step j: first the operands of the step's first MFMAs are requested,
+    // then dS(j - 1) = P dP is formed (the P role A handed over in step
+    // j - 1, dP from the previous step) and stored; then the dP MFMAs of item
+    // j (unless `last`; a dependent chain) alternate with the
+    // dK += dS(j - 1)^T Q(j - 1) MFMAs, with the copies of item j + 5 among
+    // them.  LDS operands are read two MFMA pairs ahead.
+    auto step = [&](int j, f32x16& dPg, f32x16& dPn, bool last) {
+      const char* gb = buf(cb);               // item j - 1: transpose-read Q
+      const char* nb = buf(next_buf(cb));     // item j: dO rows and -D
+      const int qb = qlo + SUB * ibi;
+      bf16x8 oa[8];
+      f16x8 oq[8];  // transpose reads of Q(j - 1): MFMA m = 2 dt + qs
+      auto read_oq = [&](int m) {
+        const char* q = gb + L::Q16 + (m & 1) * 16 * D * 2;
+        oq[m] = cat(lds_read_tr((const f16*)(q + toff[m >> 1][0])), lds_read_tr((const f16*)(q + toff[m >> 1][1])));
+      };
+      const char* xp = xch + ((j - 1) & 1) * (4 * KV_XCH);
+      const f16x8 ph0 = *(const f16x8*)xp;
+      const f16x8 ph1 = *(const f16x8*)(xp + 1024);
+      if (!last) {
+        seed(nb, dPn);
+        oa[0] = *(const bf16x8*)(nb + L::DO + koff[0]);
+      }
+      read_oq(0);
+      if (!last) oa[1] = *(const bf16x8*)(nb + L::DO + koff[1]);
+      read_oq(1);
+      f16x8 sa[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f16x8 ph = hh ? ph1 : ph0;
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ds[e] = (float)ph[e] * dPg[8 * hh + e];
+        sa[hh] = pack_f16_rtz(ds);
+      }
+      // dS of item j - 1 (block qb is query tile (qb - q0) / 32), stored as
+      // [key][position] with position half*16 + r, so each lane writes 32
+      // contiguous bytes; into the spare block when the sub-tile does not
+      // own it (the store stays unconditional).  Non-temporal: dS is read
+      // once, by the dQ pass.
+      if (DS) {
+        f16* blk = P.ds_spare;
+        const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
+        if (own) blk = P.ds + (((size_t)kvr * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * G + ig) * (SUB * SUB);
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[0]), (u32x4*)(blk + ds_lane));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[1]), (u32x4*)(blk + ds_lane + 8));
+      }
+      fence();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (s < 6) {
+          if (!last) oa[s + 2] = *(const bf16x8*)(nb + L::DO + koff[s + 2]);
+          read_oq(s + 2);
+        }
+        if (!last) dPn = mfma32(oa[s], __builtin_bit_cast(bf16x8, fr[s]), dPn);
+        mfma32h_accv(acc[s >> 1], sa[s & 1], oq[s]);
+        if (s == 1 && !last) stage_next();
+        fence();
+      }
+      mfma_operand_hold(sa[0], sa[1], oq[6], oq[7]);
+      cb = next_buf(cb);
+      adv(ibi, ig);
+    };
+    int j = 1;
+    for (; j + 1 < nitem; j += 2) {
+      step(j, dPa, dPb, false);
+      end_step();
+      step(j + 1, dPb, dPa, false);
+      end_step();
+    }
+    if (j < nitem) {  // one more full step (item j), then the last from dPb
+      step(j, dPa, dPb, false);
+      end_step();
+      step(nitem, dPb, dPa, true);
+    } else {
+      step(nitem, dPa, dPb, true);
+    }
+    lds_copies_wait();
+    acc_fence4(acc);
+    if (slot < 0) {
+      const double inv[2] = {P.rope_base > 0.f ? rope_inv(col, D, P.rope_base) : 0.0,
+                             P.rope_base > 0.f ? rope_inv(32 + col, D, P.rope_base) : 0.0};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
+        if (kr >= wkeys) continue;
+        float g[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+        store_k(P, kvh, kw + kr, col, inv, g);
+      }
+    } else if (wkeys > 0) {
+      float* dst = P.part + ((size_t)slot * P.Hkv + kvh) * PART_WAVE + lane * 4;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(float4*)(dst + (dt * 4 + r4) * 256) =
+              float4{acc[dt][4 * r4], acc[dt][4 * r4 + 1], acc[dt][4 * r4 + 2], acc[dt][4 * r4 + 3]};
+    }
   }
 }
 
@@ -750,7 +801,8 @@ __global__ __launch_bounds__(256) void dkv_sum_kernel(KVParams P) {
     if (kr >= wkeys) continue;
     float gk[4] = {sk[0][j], sk[1][j], sk[2][j], sk[3][j]};
     const float gv[4] = {sv[0][j], sv[1][j], sv[2][j], sv[3][j]};
-    store_key(P, kvh, kw + kr, lane & 31, inv, gk, gv);
+    store_k(P, kvh, kw + kr, lane & 31, inv, gk);
+    store_v(P, kvh, kw + kr, lane & 31, gv);
   }
 }
 
@@ -1262,9 +1314,9 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
       B.kv0 = kv0;
       B.nkv = nkv;
       if (ds_path)
-        hipLaunchKernelGGL(bwd::dkv_bf16_kernel<true>, dim3(p->n_kpieces * nkv), dim3(256), 0, stream, B);
+        hipLaunchKernelGGL(bwd::dkv_bf16_kernel<true>, dim3(p->n_kpieces * nkv), dim3(512), 0, stream, B);
       else
-        hipLaunchKernelGGL(bwd::dkv_bf16_kernel<false>, dim3(p->n_kpieces * nkv), dim3(256), 0, stream, B);
+        hipLaunchKernelGGL(bwd::dkv_bf16_kernel<false>, dim3(p->n_kpieces * nkv), dim3(512), 0, stream, B);
       TA_LAUNCH_CHECK();
       if (p->n_ksplit > 0) {
         hipLaunchKernelGGL(bwd::dkv_sum_kernel, dim3((p->n_ksplit + 3) / 4 * nkv * 4), dim3(256), 0, stream, B);

@@ -54,6 +54,27 @@ __device__ __forceinline__ void agpr_fence8(f32x16 (&x)[4], f32x16 (&y)[4]) {
                : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
 }
 
+// The same accumulating MFMAs with the accumulator in arch VGPRs (for
+// kernels that run two wavefronts per SIMD, where arch VGPRs and AGPRs share
+// one budget of 256 and a fixed AGPR block would leave too few arch VGPRs).
+__device__ __forceinline__ void mfma32_accv(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32h_accv(f32x16& acc, const f16x8& a, const f16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// Keeps the A/B operand registers of the last accumulating MFMAs of a step
+// from being rewritten for 32 wait states after their issue: the compiler
+// cannot see the MFMAs inside the asm statements, and a chained MFMA waiting
+// on its predecessor's accumulator still reads them after it issues.
+template <typename A, typename B>
+__device__ __forceinline__ void mfma_operand_hold(A& a0, A& a1, B& b0, B& b1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1));
+}
+__device__ __forceinline__ void acc_fence4(f32x16 (&x)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+}
+
 // Same shape with fp16 operands (same rate; 10 stored mantissa bits).
 __device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -94,6 +115,13 @@ __device__ __forceinline__ f16x8 pack_f16_rtz(const float* x) {
   w.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[4], x[5]));
   w.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[6], x[7]));
   return __builtin_bit_cast(f16x8, w);
+}
+
+// Eight floats to fp16, rounding to nearest even (for values in [0, 1]).
+__device__ __forceinline__ f16x8 pack_f16_rte(const float* x) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, f16x8);
 }
 
 __device__ __forceinline__ bf16x8 cat(const bf16x4& a, const bf16x4& b) {

@@ -280,8 +280,9 @@ ta_status build(const int32_t* parent, const int32_t* seg_len, int32_t n, int32_
   }
   p->computed_pairs_bwd = comp_bwd;
 
-  // dK/dV work pieces.  A dK/dV workgroup has four wavefronts, each owning
-  // the dK/dV of up to 32 keys of one node (a sub-tile) over a common run of
+  // dK/dV work pieces.  A dK/dV workgroup works four sub-tiles (a pair of
+  // wavefronts each), each owning the dK/dV of up to 32 keys of one node
+  // over a common run of
   // 32-row query blocks [q_lo, q_hi) staged once in LDS; blocks lie on the
   // query-tile grid q_start + 32t, so each (block, sub-tile) is one dS block
   // the dQ pass reads back.  Two things make whole tiles a poor unit: the
