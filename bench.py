@@ -64,7 +64,10 @@ def time_tree(pkg, tree, steps, warmup, dev, seed=0, Hq=32, Hkv=8, d=128, rope=1
     lse = torch.empty(Hq, plan.n_tokens, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     wf = torch.empty(max(1, pkg.attn_ws_bytes(plan, 0, 1, Hq, Hkv, d, rope)), dtype=torch.uint8, device=dev)
-    wb = torch.empty(max(1, pkg.attn_ws_bytes(plan, 1, 1, Hq, Hkv, d, rope)), dtype=torch.uint8, device=dev)
+    # the backward workspace the binding picks by default: the full dS workspace when it fits the
+    # default budget (8 GiB), else the dS blocks of as many KV heads as fit, run in rounds
+    wb_bytes, kv_per_round = pkg.bwd_ws_budget(plan, 1, Hq, Hkv, d, rope)
+    wb = torch.empty(max(1, wb_bytes), dtype=torch.uint8, device=dev)
     ev = pkg.HipEvents(7 * steps)
 
     def step(i=None):
@@ -91,6 +94,7 @@ def time_tree(pkg, tree, steps, warmup, dev, seed=0, Hq=32, Hkv=8, d=128, rope=1
         fwd_tile_efficiency=round(P / plan.computed_pairs_fwd, 4),
         bwd_tile_efficiency=round(P / plan.computed_pairs_bwd, 4),
         plan_ms=round(plan_ms, 3), upload_ms=round(upload_ms, 3),
+        bwd_ws_bytes=wb_bytes, bwd_kv_heads_per_round=kv_per_round,
         # the timed region: K steps between two device synchronisations (host wall clock)
         ms_per_step=wall, event_ms_per_step=avg(0, 6), event_median_ms_per_step=med(0, 6),
         fwd_ms=avg(0, 2), bwd_ms=avg(3, 6),
