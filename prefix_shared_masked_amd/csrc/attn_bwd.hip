@@ -307,6 +307,18 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(DQParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// A dS block holds the fp16 dS of 32 keys x 32 positions (position
+// half*16 + r is accumulator register r of the dK/dV lanes of half `half`,
+// i.e. query row 8*(r/4) + 4*half + r%4 of the block) in the dK/dV lanes'
+// register order: plane i = r/8 holds, for lane l = key + 32*half, the
+// eight values r%8 = 0..7 as one 16-byte unit, at unit l in plane 0 and
+// unit l^4 in plane 1.  Each plane is one contiguous 1 KiB store of the
+// producing wavefront; the XOR keeps the two planes' units of a transpose
+// read on different LDS banks.  Element offset (in f16 units):
+__device__ __forceinline__ constexpr int ds_elem(int key, int pos) {
+  return ((pos >> 3) & 1) * 512 + ((key + 32 * (pos >> 4)) ^ (4 * ((pos >> 3) & 1))) * 8 + (pos & 7);
+}
+
 struct KVParams {
   const f16* q;   // fp16 copy of Q (rotated when RoPE is on)
   const f16* k;   // fp16 copy of K (rotated when RoPE is on) times scale * log2(e)
@@ -319,7 +331,7 @@ struct KVParams {
   const int32_t* kp;  // work pieces, TA_KPIECE_INTS each
   const int32_t* kr;  // cut sub-tiles: (kw, wk, first slot, n_windows)
   float* part;        // partial dK/dV slots (PART_WAVE floats per slot and KV head)
-  f16* ds;            // dS blocks [nkv][n_dsblk][G][32 keys][32 positions] of this round's KV heads (dS path only)
+  f16* ds;            // dS blocks [nkv][n_dsblk][G] of 32 keys x 32 positions (ds_elem) of this round's KV heads (dS path only)
   f16* ds_spare;      // a 32 x 32 block that absorbs the stores of blocks a wavefront does not own
   int n_sum;          // cut sub-tiles
   int n_dsblk;
@@ -641,7 +653,7 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
         dP[4 * r4 + 3] = d4.w;
       }
     };
-    const int ds_lane = col * SUB + half * 16;  // this lane's 16 elements in a dS block
+    const int ds_lane0 = ds_elem(col, half * 16), ds_lane1 = ds_elem(col, half * 16 + 8);  // this lane's two units
     int cb = 0, ibi = nblk - 1, ig = 0;         // item j - 1 of step j: buffer, block, head
     f32x16 dPa, dPb;
     {  // step 0: dP of item 0 only
@@ -688,17 +700,17 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
         for (int e = 0; e < 8; ++e) ds[e] = (float)ph[e] * dPg[8 * hh + e];
         sa[hh] = pack_f16_rtz(ds);
       }
-      // dS of item j - 1 (block qb is query tile (qb - q0) / 32), stored as
-      // [key][position] with position half*16 + r, so each lane writes 32
-      // contiguous bytes; into the spare block when the sub-tile does not
-      // own it (the store stays unconditional).  Non-temporal: dS is read
-      // once, by the dQ pass.
+      // dS of item j - 1 (block qb is query tile (qb - q0) / 32) in the
+      // register-order layout of ds_elem: each of the two stores writes one
+      // contiguous 1 KiB plane; into the spare block when the sub-tile does
+      // not own it (the store stays unconditional).  Non-temporal: dS is
+      // read once, by the dQ pass.
       if (DS) {
         f16* blk = P.ds_spare;
         const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
         if (own) blk = P.ds + (((size_t)kvr * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * G + ig) * (SUB * SUB);
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[0]), (u32x4*)(blk + ds_lane));
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[1]), (u32x4*)(blk + ds_lane + 8));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[0]), (u32x4*)(blk + ds_lane0));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[1]), (u32x4*)(blk + ds_lane1));
       }
       fence();
 #pragma unroll
@@ -882,7 +894,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepParams P) {
 
 struct DSParams {
   const f16* k;   // fp16 K * scale * log2(e) (rotated when RoPE is on)
-  const f16* ds;  // [nkv][n_dsblk][G][32 keys][32 positions]: this round's KV heads
+  const f16* ds;  // [nkv][n_dsblk][G] blocks of 32 keys x 32 positions (ds_elem): this round's KV heads
   bf16* dq;
   const int32_t* pos;
   const int32_t* dq_ptr;
@@ -938,14 +950,16 @@ __global__ __launch_bounds__(256, 3) void dq_ds_kernel(DSParams P) {
   };
 
   // transpose-read offsets: K^T of d-tile dt (256-byte swizzled rows), dS^T
-  // (64-byte rows); rows trow + 8x of each 16-key group
+  // (the ds_elem layout: positions tcol..tcol+3 of one key are 8 contiguous
+  // bytes); rows (keys) trow + 8x of each 16-key group kk, soff[kk][x]
   const int trow = half * 4 + ((lane & 15) >> 2);
   const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  int toff[4][2], soff[2];
+  int toff[4][2], soff[2][2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int r = trow + 8 * x;
-    soff[x] = r * SUB + tcol;
+    soff[0][x] = ds_elem(r, tcol);
+    soff[1][x] = ds_elem(16 + r, tcol);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) toff[dt][x] = r * D + (((4 * dt + (tcol >> 3)) ^ swz(r)) << 3) + (tcol & 7);
   }
@@ -964,8 +978,8 @@ __global__ __launch_bounds__(256, 3) void dq_ds_kernel(DSParams P) {
     stage(min(e + 2, last), (e - e0 + 2) % 3);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const f16* sb = sS[b][w] + kk * 16 * SUB;
-      const f16x8 bs = cat(lds_read_tr(sb + soff[0]), lds_read_tr(sb + soff[1]));
+      const f16* sb = sS[b][w];
+      const f16x8 bs = cat(lds_read_tr(sb + soff[kk][0]), lds_read_tr(sb + soff[kk][1]));
       const f16* kb = sK[b] + kk * 16 * D;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
