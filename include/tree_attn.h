@@ -40,12 +40,11 @@
  *    errors are returned before anything is launched; a failed launch
  *    returns TA_EHIP.
  *  - Plans are immutable after tree_plan returns and may be shared between
- *    threads.  The library's global mutable state is: one hipBLASLt handle
- *    per device (with the mutex that guards its creation), created by the
- *    first tree_lmhead_nll call with gradients on that device; and the
- *    scratch array of tree_decode_splitkv_noalloc (one per device) with the
- *    table of its per-device addresses and that table's mutex.  Both are kept
- *    until the process ends; every other call keeps nothing between calls.
+ *    threads.  The library's only global mutable state is the scratch array
+ *    of tree_decode_splitkv_noalloc (one per device) with the table of its
+ *    per-device addresses and that table's mutex, kept until the process
+ *    ends; every other call keeps nothing between calls.  Every kernel is
+ *    the library's own (no vendor library is called).
  */
 #ifndef TREE_ATTN_H
 #define TREE_ATTN_H

@@ -27,8 +27,7 @@ FLAGS = [
 def build_library(verbose: bool = False, extra=()) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     cmd = [hipcc, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-L/opt/rocm/lib", "-lhipblaslt",
-           "-Wl,-rpath,/opt/rocm/lib", "-o", LIB + ".tmp"]
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -14,14 +14,12 @@
 //    workgroup sums the token losses in a fixed order (bitwise reproducible).
 //  - ds_kernel (backward, per vocabulary chunk): the same tiles recomputed,
 //    epilogue dS = w [valid] (exp(S - LSE) - onehot(y)) in bf16, laid out
-//    [N, chunk rows]; then two plain GEMMs on the library's matrix kernels:
+//    [tokens rounded up to 32, chunk rows] with zeros past the last token and
+//    the last vocabulary row; then gemm_kernel twice on the same tiling:
 //    dh += dS W_chunk (fp32 accumulator) and dW_chunk = dS^T h.
 #include <hip/hip_runtime.h>
-#include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
-#include <map>
-#include <mutex>
 
 #include "common.h"
 
@@ -76,6 +74,7 @@ struct Params {
   bf16* ds;             // [N][ld_ds] (ds_kernel): the chunk's dS, token-major
   int ld_ds;            // row stride of ds (the chunk's row capacity)
   int N, V, Dm;
+  int n_pad;            // rows of ds: N rounded up to KS (the rows past N are written as zeros)
   int vt_per_wg;        // vocabulary tiles per workgroup
   int vt_first;         // first vocabulary tile of the launch
   int vt_last;          // one past the last vocabulary tile of the launch
@@ -218,11 +217,12 @@ __global__ __launch_bounds__(256, 1) void ds_kernel(Params P) {
   // the lane's four tokens: log2-scaled LSE, weight (0 when not supervised), label
   float lse2[4], wt_[4];
   int y[4];
-  bool tv[4];
+  bool tv[4], tz[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = blockIdx.x * BT + 128 * wt + 32 * j + rr;
     tv[j] = t < P.N;
+    tz[j] = t < P.n_pad;  // rows past the last token are stored as zeros
     const int tc = tv[j] ? t : 0;
     y[j] = P.labels[tc];
     const bool valid = tv[j] && y[j] != P.ignore_index && y[j] >= 0 && y[j] < P.V;
@@ -232,11 +232,10 @@ __global__ __launch_bounds__(256, 1) void ds_kernel(Params P) {
   const int vrow0 = P.vt_first * BV;  // first vocabulary row of this chunk
   tile_loop(P, ring, [&](int vt, f32x16 (&acc)[4][4]) {
     const int vb = vt * BV + 128 * wv;
-    const bool ragged = vb + 128 > P.V;  // uniform
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = blockIdx.x * BT + 128 * wt + 32 * j + rr;
-      bf16* row = P.ds + (size_t)(tv[j] ? t : 0) * P.ld_ds + (vb - vrow0) + 4 * half;
+      bf16* row = P.ds + (size_t)(tz[j] ? t : 0) * P.ld_ds + (vb - vrow0) + 4 * half;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -248,9 +247,11 @@ __global__ __launch_bounds__(256, 1) void ds_kernel(Params P) {
           for (int u = 0; u < 4; ++u) {
             const float p = exp2f_fast(acc[i][j][4 * r4 + u] * L2E - lse2[j]);
             const float g = wt_[j] * (p - (v0 + u == y[j] ? 1.f : 0.f));
-            o[u] = (bf16)(v0 + u < P.V ? g : 0.f);
+            o[u] = (bf16)(tv[j] && v0 + u < P.V ? g : 0.f);
           }
-          if (tv[j] && (!ragged || v0 < P.V)) *(bf16x4*)(row + 32 * i + 8 * r4) = o;
+          // every row up to n_pad and every column of the tile: the products
+          // read them as zero padding of their contraction
+          if (tz[j]) *(bf16x4*)(row + 32 * i + 8 * r4) = o;
         }
     }
     // stores count on vmcnt too and may complete out of order with the ring
@@ -311,68 +312,163 @@ __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ x, 
 }
 
 // ---------------------------------------------------------------------------
-// Plain GEMMs of the backward on the library matrix kernels.  One handle per
-// device, created on first use and kept for the life of the process.
-std::mutex g_mu;
-std::map<int, hipblasLtHandle_t> g_handles;
+// The backward's two products, hand-written on the same 256 x 256 tiles,
+// written transposed so the MFMA rows run along the model dimension d and
+// each lane stores four consecutive d of one output row:
+//   dh^T       = W_chunk^T dS^T   (d x tokens;          k = the chunk's vocabulary rows)
+//   dW_chunk^T = h^T dS           (d x vocabulary rows; k = tokens)
+// A (W_chunk or h, stored [k][d]) is a "k-row" tile of 32 k rows x 256 d
+// (512-byte rows) read with the LDS transpose read; B is dS: for dh its rows
+// (vocabulary contiguous) form a k-contiguous tile read with 16-byte row
+// reads like the logits tiles, for dW it is a k-row tile of 32 tokens x 256
+// vocabulary rows.  In a k-row tile the 32-byte unit u of row r sits at
+// u ^ (r % 4), so the four rows one transpose read touches land on four
+// different bank groups.
+struct GemmParams {
+  const bf16* A;  // [k][d] rows of A (W_chunk or h)
+  int lda, a_rmax, a_cmax;  // row stride; last valid row; columns (d) available
+  const bf16* B;  // dS
+  int ldb, b_rmax, b_cmax;  // row stride; last valid row; columns available (k-row form)
+  int K;          // contraction length, a multiple of KS (operand rows past the data are zero)
+  int n_cols;     // output columns (tokens for dh, vocabulary rows for dW)
+  int Dm;
+  float* out32;   // dh accumulator [tokens][Dm] (fp32), or
+  bf16* out16;    // dW_chunk [rows][Dm] (bf16)
+  int accumulate; // out32 += (else =)
+};
 
-hipblasLtHandle_t lt_handle() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(g_mu);
-  auto it = g_handles.find(dev);
-  if (it != g_handles.end()) return it->second;
-  hipblasLtHandle_t hd = nullptr;
-  if (hipblasLtCreate(&hd) != HIPBLAS_STATUS_SUCCESS) return nullptr;
-  g_handles[dev] = hd;
-  return hd;
-}
-
-// D = op(A) op(B) + beta D in column-major terms; A, B bf16, D of type dtD,
-// fp32 compute.  m x n result, k the contraction.
-ta_status lt_gemm(bool ta_, bool tb, int m, int n, int k, const void* A, int lda, const void* B, int ldb, void* D,
-                  hipDataType dtD, int ldd, float beta, void* ws, size_t wsb, hipStream_t st) {
-  hipblasLtHandle_t hd = lt_handle();
-  if (!hd) return TA_EHIP;
-  hipblasLtMatmulDesc_t desc = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-  hipblasLtMatmulPreference_t pref = nullptr;
-  ta_status rc = TA_OK;
-  const hipblasOperation_t opa = ta_ ? HIPBLAS_OP_T : HIPBLAS_OP_N, opb = tb ? HIPBLAS_OP_T : HIPBLAS_OP_N;
-  const uint64_t wsz = wsb;
-  hipblasLtMatmulHeuristicResult_t res{};
-  int got = 0;
-  const float alpha = 1.f;
-  if (hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opa, sizeof(opa)) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof(opb)) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, ta_ ? k : m, ta_ ? m : k, lda) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, tb ? n : k, tb ? k : n, ldb) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatrixLayoutCreate(&ld, dtD, m, n, ldd) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz, sizeof(wsz)) !=
-          HIPBLAS_STATUS_SUCCESS) {
-    rc = TA_EHIP;
-  } else if (hipblasLtMatmulAlgoGetHeuristic(hd, desc, la, lb, ld, ld, pref, 1, &res, &got) != HIPBLAS_STATUS_SUCCESS ||
-             got < 1) {
-    rc = TA_EUNSUPPORTED;
-  } else if (hipblasLtMatmul(hd, desc, &alpha, A, la, B, lb, &beta, D, ld, D, ld, &res.algo, ws, wsb, st) !=
-             HIPBLAS_STATUS_SUCCESS) {
-    rc = TA_EHIP;
+// Rows k0 .. k0 + 31 (clamped to rmax) x columns c0 .. c0 + 255 (clamped to
+// cmax - 8) of X [rows][ld] into a k-row tile.  Copy q (0..15) fills rows
+// 2q, 2q + 1 (lane i: row 2q + i/32, 16-byte slot i % 32 holding global
+// piece ((slot/2) ^ (row % 4)) * 2 + slot % 2); wave w issues q = w + 4i.
+__device__ __forceinline__ void stage_krows(const bf16* X, int ld, int rmax, int cmax, int k0, int c0, char* tile) {
+  const int l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = w + 4 * i;
+    const int row = 2 * q + (l >> 5);
+    const int slot = l & 31;
+    const int piece = ((((slot >> 1) ^ (row & 3))) << 1) | (slot & 1);
+    const int gc = min(c0 + 8 * piece, cmax - 8);
+    const int gr = min(k0 + row, rmax);
+    copy16_to_lds(X + (size_t)gr * ld + gc, tile + q * 1024);
   }
-  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (ld) hipblasLtMatrixLayoutDestroy(ld);
-  if (lb) hipblasLtMatrixLayoutDestroy(lb);
-  if (la) hipblasLtMatrixLayoutDestroy(la);
-  if (desc) hipblasLtMatmulDescDestroy(desc);
-  return rc;
 }
 
-constexpr size_t LT_WS = size_t(64) << 20;  // library GEMM workspace
+// B_KC: B is dS rows (dh); else B is a k-row tile of dS (dW).
+template <bool B_KC>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams G) {
+  __shared__ __attribute__((aligned(1024))) char ring[NBUF * STAGE_BYTES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rr = lane & 31, half = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;   // this wave's 128 d x 128 columns
+  const int c0 = blockIdx.x * 256, d0 = blockIdx.y * 256;
+  const int total = G.K / KS;
+
+  auto issue = [&](int p) {
+    char* buf = ring + (p % NBUF) * STAGE_BYTES;
+    stage_krows(G.A, G.lda, G.a_rmax, G.a_cmax, p * KS, d0, buf);
+    if (B_KC)
+      stage_tile(G.B, c0, G.b_rmax + 1, G.ldb, p * KS, buf + TILE_BYTES);
+    else
+      stage_krows(G.B, G.ldb, G.b_rmax, G.b_cmax, p * KS, c0, buf + TILE_BYTES);
+  };
+
+  // Transpose-read offsets (bytes) in a k-row tile for MFMA tile t (32
+  // columns at 128 * w + 32 t): the lane reads row 8*half + 4x + x16/4 of
+  // k-group s (+ 16 s rows, + 4x rows: immediates) and columns
+  // 16 g + 4 (x16 % 4) of the tile, g = (lane / 16) % 2, and receives
+  // column lane % 32 with k-slots 16 s + 8 half + 0..7 (consecutive).
+  const int x16 = lane & 15, g = (lane >> 4) & 1, q4 = x16 >> 2;
+  auto kroff = [&](int w, int t) {
+    return (8 * half + q4) * 512 + (((8 * w + 2 * t + g) ^ q4) << 5) + 8 * (x16 & 3);
+  };
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    aoff[t] = kroff(wm, t);
+    boff[t] = TILE_BYTES + kroff(wn, t);
+  }
+  // k-contiguous B (as in the logits tiles): row 128 wn + 32 t + rr, piece 2s + half
+  const int sw = swz4(rr);
+  const int po[2] = {((0 + half) ^ sw) << 4, ((2 + half) ^ sw) << 4};
+  const int bbase = TILE_BYTES + (128 * wn + rr) * 64;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  agpr_fence16(acc);
+
+  for (int p = 0; p < min(NBUF - 1, total); ++p) issue(p);
+  for (int it = 0; it < total; ++it) {
+    const int after = min(NBUF - 2, total - 1 - it);
+    if (after >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (after == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's copies of stage it landed; every wave is done with stage it - 1
+    if (it + NBUF - 1 < total) issue(it + NBUF - 1);
+    const char* buf = ring + (it % NBUF) * STAGE_BYTES;
+    // both k-groups' operands are read before the first MFMA
+    bf16x8 a[2][4], b[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16* pa = (const bf16*)(buf + aoff[t] + 16 * s * 512);
+        a[s][t] = cat(lds_read_tr(pa), lds_read_tr(pa + 4 * 256));
+        if (B_KC) {
+          b[s][t] = *(const bf16x8*)(buf + bbase + 2048 * t + po[s]);
+        } else {
+          const bf16* pb = (const bf16*)(buf + boff[t] + 16 * s * 512);
+          b[s][t] = cat(lds_read_tr(pb), lds_read_tr(pb + 4 * 256));
+        }
+      }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma32_acc(acc[i][j], a[s][i], b[s][j]);
+  }
+  lds_copies_wait();
+  agpr_fence16(acc);
+
+  // acc[i][j] register r <-> d = d0 + 128 wm + 32 i + 8 (r/4) + 4 half + r%4,
+  // column c0 + 128 wn + 32 j + rr
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = c0 + 128 * wn + 32 * j + rr;
+    if (c >= G.n_cols) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = d0 + 128 * wm + 32 * i + 8 * r4 + 4 * half;
+        if (d >= G.Dm) continue;
+        const float4 v = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
+        if (G.out32) {
+          float4* o = (float4*)(G.out32 + (size_t)c * G.Dm + d);
+          float4 x = v;
+          if (G.accumulate) {
+            const float4 y = *o;
+            x = make_float4(v.x + y.x, v.y + y.y, v.z + y.z, v.w + y.w);
+          }
+          *o = x;
+        } else {
+          const bf16x4 o = {(bf16)v.x, (bf16)v.y, (bf16)v.z, (bf16)v.w};
+          *(bf16x4*)(G.out16 + (size_t)c * G.Dm + d) = o;
+        }
+      }
+  }
+}
 
 struct Sizes {
   int n_tt, n_vt, vsplit, vt_per_wg, n_parts, chunk_vt, n_chunks;
-  size_t off_part, off_tok, off_lse, off_ds, off_dh, off_lt, total;
+  int n_pad;
+  size_t off_part, off_tok, off_lse, off_ds, off_dh, total;
 };
 
 Sizes sizes(int N, int V, int Dm, bool grad, int vocab_chunk) {
@@ -394,6 +490,7 @@ Sizes sizes(int N, int V, int Dm, bool grad, int vocab_chunk) {
   }
   s.chunk_vt = std::min(s.chunk_vt, s.n_vt);
   s.n_chunks = (s.n_vt + s.chunk_vt - 1) / s.chunk_vt;
+  s.n_pad = (N + KS - 1) / KS * KS;
   size_t off = 0;
   auto take = [&](size_t b) {
     const size_t x = off;
@@ -404,9 +501,8 @@ Sizes sizes(int N, int V, int Dm, bool grad, int vocab_chunk) {
   s.off_tok = take((size_t)N * sizeof(float));
   s.off_lse = take((size_t)N * sizeof(float));
   if (grad) {
-    s.off_ds = take((size_t)s.chunk_vt * BV * N * sizeof(bf16));
+    s.off_ds = take((size_t)s.chunk_vt * BV * s.n_pad * sizeof(bf16));
     s.off_dh = take((size_t)N * Dm * sizeof(float));
-    s.off_lt = take(LT_WS);
   }
   s.total = off;
   return s;
@@ -468,8 +564,8 @@ extern "C" ta_status tree_lmhead_nll(ta_dtype dt, const void* h, const void* W, 
 
   bf16* ds = (bf16*)(wsb + S.off_ds);
   float* dh_acc = (float*)(wsb + S.off_dh);
-  void* ltws = wsb + S.off_lt;
   P.ds = ds;
+  P.n_pad = S.n_pad;
   P.ld_ds = S.chunk_vt * lmh::BV;
   for (int c = 0; c < S.n_chunks; ++c) {
     const int vt_a = c * S.chunk_vt, vt_b = std::min(S.n_vt, vt_a + S.chunk_vt);
@@ -482,14 +578,34 @@ extern "C" ta_status tree_lmhead_nll(ta_dtype dt, const void* h, const void* W, 
     hipLaunchKernelGGL(lmh::ds_kernel, dim3(S.n_tt, (ntile + P.vt_per_wg - 1) / P.vt_per_wg), dim3(256), 0, stream,
                        P);
     TA_LAUNCH_CHECK();
-    // column-major views: dS is (cv x N) with ld = ld_ds; W_chunk (Dm x cv), h (Dm x N), dh (Dm x N),
-    // dW_chunk (Dm x cv)
-    ta_status st = lmh::lt_gemm(false, false, Dm, N, cv, (const bf16*)W + (size_t)v0 * Dm, Dm, ds, P.ld_ds, dh_acc,
-                                HIP_R_32F, Dm, c == 0 ? 0.f : 1.f, ltws, lmh::LT_WS, stream);
-    if (st != TA_OK) return st;
-    st = lmh::lt_gemm(false, true, Dm, cv, N, h, Dm, ds, P.ld_ds, (bf16*)dW + (size_t)v0 * Dm, HIP_R_16BF, Dm, 0.f,
-                      ltws, lmh::LT_WS, stream);
-    if (st != TA_OK) return st;
+    // dh^T += W_chunk^T dS^T over the chunk's rows (rounded up to KS: dS is zero past V), then
+    // dW_chunk^T = h^T dS over the tokens (rounded up: dS is zero past N)
+    lmh::GemmParams G{};
+    G.Dm = Dm;
+    G.A = (const bf16*)W + (size_t)v0 * Dm;
+    G.lda = Dm;
+    G.a_rmax = V - 1 - v0;
+    G.a_cmax = Dm;
+    G.B = ds;
+    G.ldb = P.ld_ds;
+    G.b_rmax = N - 1;
+    G.b_cmax = P.ld_ds;
+    G.K = (cv + lmh::KS - 1) / lmh::KS * lmh::KS;
+    G.n_cols = N;
+    G.out32 = dh_acc;
+    G.accumulate = c > 0;
+    hipLaunchKernelGGL(lmh::gemm_kernel<true>, dim3(S.n_tt, (Dm + 255) / 256), dim3(256), 0, stream, G);
+    TA_LAUNCH_CHECK();
+    G.A = (const bf16*)h;
+    G.a_rmax = N - 1;
+    G.b_rmax = S.n_pad - 1;
+    G.K = S.n_pad;
+    G.n_cols = cv;
+    G.out32 = nullptr;
+    G.out16 = (bf16*)dW + (size_t)v0 * Dm;
+    G.accumulate = 0;
+    hipLaunchKernelGGL(lmh::gemm_kernel<false>, dim3((cv + 255) / 256, (Dm + 255) / 256), dim3(256), 0, stream, G);
+    TA_LAUNCH_CHECK();
   }
   const size_t nel = (size_t)N * Dm;
   hipLaunchKernelGGL(lmh::cast_kernel, dim3((unsigned)std::min<size_t>((nel + 255) / 256, 16384)), dim3(256), 0,

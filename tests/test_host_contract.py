@@ -72,10 +72,9 @@ def test_binding_checks_buffers_on_the_host():
 
 
 def test_library_global_state_is_the_documented_state():
-    """The header lists the library's global mutable state: the hipBLASLt
-    handle table of the output layer with its mutex, and the scratch array of
-    the allocation-free decode call with its per-device address table and
-    mutex.  List the writable data objects the built library defines itself
+    """The header lists the library's only global mutable state: the scratch
+    array of the allocation-free decode call with its per-device address
+    table and mutex.  List the writable data objects the built library defines itself
     (kernel launch stubs, which are functions, and the compiler's and HIP
     runtime's own registration objects excluded)."""
     lib = os.path.join(ROOT, "prefix_shared_masked_amd", "libtree_attn.so")
@@ -90,5 +89,13 @@ def test_library_global_state_is_the_documented_state():
         if name.endswith(")") or name.startswith(("__", "_Z", "_DYNAMIC", "_GLOBAL_OFFSET_TABLE_", "DW.ref.")):
             continue
         objs.add(name)
-    assert objs == {"ta::lmh::g_mu", "ta::lmh::g_handles", "scratch", "(anonymous namespace)::g_scratch_mu",
-                    "(anonymous namespace)::g_scratch_ptr"}, objs
+    assert objs == {"scratch", "(anonymous namespace)::g_scratch_mu", "(anonymous namespace)::g_scratch_ptr"}, objs
+
+
+def test_library_links_no_vendor_math_library():
+    """Every kernel is the library's own: the built library links no BLAS
+    (hipBLASLt, rocBLAS) or other vendor math library."""
+    lib = os.path.join(ROOT, "prefix_shared_masked_amd", "libtree_attn.so")
+    out = subprocess.run(["readelf", "-d", lib], capture_output=True, text=True, check=True).stdout
+    needed = [l for l in out.splitlines() if "(NEEDED)" in l]
+    assert needed and not any(x in l.lower() for l in needed for x in ("blas", "miopen", "rocsolver", "hipfft")), needed
