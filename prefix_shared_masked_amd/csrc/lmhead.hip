@@ -322,8 +322,9 @@ __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ x, 
 // (vocabulary contiguous) form a k-contiguous tile read with 16-byte row
 // reads like the logits tiles, for dW it is a k-row tile of 32 tokens x 256
 // vocabulary rows.  In a k-row tile the 32-byte unit u of row r sits at
-// u ^ (r % 4), so the four rows one transpose read touches land on four
-// different bank groups.
+// u ^ (2 (r % 4)): the two adjacent units of the four rows that 32 lanes of
+// a transpose read touch then fill a whole 256-byte window of banks (with
+// u ^ (r % 4) they shared 128 bytes, a two-way conflict).
 struct GemmParams {
   const bf16* A;  // [k][d] rows of A (W_chunk or h)
   int lda, a_rmax, a_cmax;  // row stride; last valid row; columns (d) available
@@ -340,7 +341,7 @@ struct GemmParams {
 // Rows k0 .. k0 + 31 (clamped to rmax) x columns c0 .. c0 + 255 (clamped to
 // cmax - 8) of X [rows][ld] into a k-row tile.  Copy q (0..15) fills rows
 // 2q, 2q + 1 (lane i: row 2q + i/32, 16-byte slot i % 32 holding global
-// piece ((slot/2) ^ (row % 4)) * 2 + slot % 2); wave w issues q = w + 4i.
+// piece ((slot/2) ^ (2 (row % 4))) * 2 + slot % 2); wave w issues q = w + 4i.
 __device__ __forceinline__ void stage_krows(const bf16* X, int ld, int rmax, int cmax, int k0, int c0, char* tile) {
   const int l = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -349,7 +350,7 @@ __device__ __forceinline__ void stage_krows(const bf16* X, int ld, int rmax, int
     const int q = w + 4 * i;
     const int row = 2 * q + (l >> 5);
     const int slot = l & 31;
-    const int piece = ((((slot >> 1) ^ (row & 3))) << 1) | (slot & 1);
+    const int piece = (((slot >> 1) ^ (2 * (row & 3))) << 1) | (slot & 1);
     const int gc = min(c0 + 8 * piece, cmax - 8);
     const int gr = min(k0 + row, rmax);
     copy16_to_lds(X + (size_t)gr * ld + gc, tile + q * 1024);
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams G) {
   // column lane % 32 with k-slots 16 s + 8 half + 0..7 (consecutive).
   const int x16 = lane & 15, g = (lane >> 4) & 1, q4 = x16 >> 2;
   auto kroff = [&](int w, int t) {
-    return (8 * half + q4) * 512 + (((8 * w + 2 * t + g) ^ q4) << 5) + 8 * (x16 & 3);
+    return (8 * half + q4) * 512 + (((8 * w + 2 * t + g) ^ (2 * q4)) << 5) + 8 * (x16 & 3);
   };
   int aoff[4], boff[4];
 #pragma unroll
