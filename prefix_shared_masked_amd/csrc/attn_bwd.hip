@@ -394,8 +394,9 @@ constexpr int KV_NBUF = 7;           // staged blocks: copies run five items ahe
 constexpr int KV_XCH = 2 * 64 * 16;  // one sub-tile's P block in fp16: [register half 2][lane 64][16 bytes]
 
 // Two wavefronts per 32-key sub-tile, one of each role, eight per workgroup
-// (wavefronts w and w + 4 share sub-tile w and, as the hardware places a
-// workgroup's wavefronts round-robin over the four SIMDs, one SIMD):
+// (wavefronts w and w + 4 share sub-tile w; with eight wavefronts on four
+// SIMDs every SIMD holds two, so one's MFMAs can run while the other
+// waits, whichever pairing the dispatcher makes):
 //  role A (w < 4) holds the sub-tile's K, computes S = Q K^T - LSE, P and
 //    dV += P^T dO, and hands P (fp16) to its partner through LDS;
 //  role B (w >= 4) holds V, computes dP = dO V^T - D, dS = P dP (with the P
