@@ -501,9 +501,16 @@ void tree_route_free(ta_route* route); /* NULL-safe */
  * h = the recurrence's states (the layer's output).  Backward: given the
  * forward's h and the upstream gradient dh [N, C], writes da = dh_total *
  * h_prev and db = dh_total, where dh_total of a node's last token sums the
- * contributions of every child branch.  Deterministic (fixed-order sums, no
- * atomics).  ws: tree_scan_ws_bytes.  Errors: TA_EINVAL, TA_ERANGE,
- * TA_ENOMEM, TA_EHIP. */
+ * contributions of every child branch.  One pass per direction: the
+ * workgroup of a chunk waits for the end state of its parent chunk
+ * (forward), or the outgoing gradients of its child chunks (backward),
+ * which other workgroups of the same launch publish through ws.
+ * Deterministic: every sum and composition has a fixed order whatever the
+ * timing.  ws: tree_scan_ws_bytes, cleared by the call itself; its 32-bit
+ * word 1 is set to nonzero if a wait for a published value ran out (bounded
+ * waits; the workgroups' ticket order rules this out), in which case the
+ * outputs are not valid.  Calls that share a ws must not overlap.  Errors:
+ * TA_EINVAL, TA_ERANGE, TA_ENOMEM, TA_EUNSUPPORTED, TA_EHIP. */
 ta_status tree_scan_ws_bytes(const ta_route* route, int32_t C, size_t* bytes);
 ta_status tree_scan_fwd(const ta_route* route, const void* droute, const float* a, const float* b,
                         int32_t C, float* h, void* ws, size_t ws_bytes, hipStream_t stream);

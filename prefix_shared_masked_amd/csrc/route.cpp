@@ -49,6 +49,25 @@ ta_status build_route(const ta_plan* p, int32_t K, ta_route* R) {
     last_tok[v] = pt;
   }
   R->n_chunks = static_cast<int32_t>(R->chunks.size() / 4);
+  // child chunks, CSR, descending
+  R->kid_ptr.assign(R->n_chunks + 1, 0);
+  for (int32_t c = 0; c < R->n_chunks; ++c)
+    if (R->chunks[4 * c + 2] >= 0) R->kid_ptr[R->chunks[4 * c + 2] + 1]++;
+  for (int32_t c = 0; c < R->n_chunks; ++c) R->kid_ptr[c + 1] += R->kid_ptr[c];
+  R->kid.assign(R->kid_ptr[R->n_chunks], 0);
+  {
+    std::vector<int32_t> fill(R->kid_ptr.begin(), R->kid_ptr.end() - 1);
+    for (int32_t c = R->n_chunks - 1; c >= 0; --c)
+      if (R->chunks[4 * c + 2] >= 0) R->kid[fill[R->chunks[4 * c + 2]]++] = c;
+  }
+  {  // chunk depths (a parent precedes its children), then a stable sort by depth
+    std::vector<int32_t> depth(R->n_chunks, 0);
+    for (int32_t c = 0; c < R->n_chunks; ++c)
+      if (R->chunks[4 * c + 2] >= 0) depth[c] = depth[R->chunks[4 * c + 2]] + 1;
+    R->order.resize(R->n_chunks);
+    for (int32_t c = 0; c < R->n_chunks; ++c) R->order[c] = c;
+    std::stable_sort(R->order.begin(), R->order.end(), [&](int32_t x, int32_t y) { return depth[x] < depth[y]; });
+  }
   // path predecessor of every token, then its powers
   std::vector<int32_t> prev(N, -1);
   for (int32_t c = 0; c < R->n_chunks; ++c) {
@@ -86,6 +105,12 @@ ta_status build_route(const ta_plan* p, int32_t K, ta_route* R) {
   off += a256(R->succ_ptr.size() * 4);
   R->off_succ = off;
   off += a256(R->succ.size() * 4);
+  R->off_kid_ptr = off;
+  off += a256(R->kid_ptr.size() * 4);
+  R->off_kid = off;
+  off += a256(R->kid.size() * 4);
+  R->off_order = off;
+  off += a256(R->order.size() * 4);
   R->device_bytes = std::max<size_t>(off, 256);
   return TA_OK;
 }

@@ -4,19 +4,12 @@
 // Scan h_t = a_t h_prev(t) + b_t, prev(t) following the root-to-token path
 // (section 9.1: a chunk starts from its parent's end state).  Chunks of up to
 // 128 tokens form a tree (parent = the previous chunk of the node, or the
-// last chunk of the nearest ancestor holding tokens).  Three passes, all with
-// consecutive lanes on consecutive channels, so every row access is
-// coalesced:
-//   reduce: per (chunk, channel) the chunk's decay A = prod a and its end
-//           state H from a zero start;
-//   walk:   per channel, chunks in DFS order: start = end of the parent chunk,
-//           end = A start + H (a few hundred dependent steps, their inputs
-//           fetched in batches ahead of the chain);
-//   apply:  per (chunk, channel) the scan again from its start, writing h.
-// The backward runs the mirror image: a reverse local scan per chunk, a walk
-// in reverse DFS order that adds every chunk's outgoing gradient a_first dh_first
-// into its parent (the sum over branches a shared prefix receives), and a
-// reverse scan per chunk writing da = dh h_prev and db = dh.
+// last chunk of the nearest ancestor holding tokens).  One pass per
+// direction: a workgroup per (chunk, channel block) scans its chunk from
+// registers once the parent chunk's end state (forward) or the child chunks'
+// outgoing gradients (backward: the sum over branches a shared prefix
+// receives) have been published, so each element is read and written once
+// (see the kernels below).
 //
 // Causal conv y_t = sum_j w[c][j] x_{prev^j(t)} (section 9.2: the window runs
 // back along the path into the parent's tail): a gather over the planner's
@@ -25,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include "common.h"
 #include "route_internal.h"
@@ -34,241 +28,7 @@ namespace ssm {
 
 constexpr int TH = 256;
 
-__global__ __launch_bounds__(TH) void scan_reduce(const int4* __restrict__ ch, const float* __restrict__ a,
-                                                  const float* __restrict__ b, int C, float* __restrict__ A,
-                                                  float* __restrict__ H) {
-  const int c = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
-  if (k >= C) return;
-  const int4 r = ch[c];
-  float da = 1.f, h = 0.f;
-  const float* ap = a + (size_t)r.x * C + k;
-  const float* bp = b + (size_t)r.x * C + k;
-#pragma unroll 8
-  for (int i = 0; i < r.y; ++i) {
-    const float x = ap[(size_t)i * C], y = bp[(size_t)i * C];
-    h = fmaf(x, h, y);
-    da *= x;
-  }
-  A[(size_t)c * C + k] = da;
-  H[(size_t)c * C + k] = h;
-}
-
-// Chunks in DFS order; a chunk's parent precedes it.  The end state of the
-// previous chunk is kept in a register (the parent of most chunks), others
-// come back from memory.  Inputs of 8 chunks are fetched before their chain.
-__global__ __launch_bounds__(TH) void scan_walk(const int4* __restrict__ ch, int n_chunks, const float* __restrict__ A,
-                                                const float* __restrict__ H, int C, float* __restrict__ hin,
-                                                float* __restrict__ hend) {
-  const int k = blockIdx.x * TH + threadIdx.x;
-  if (k >= C) return;
-  float prev_end = 0.f;
-  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
-    float av[8], hv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = min(c0 + u, n_chunks - 1);
-      av[u] = A[(size_t)c * C + k];
-      hv[u] = H[(size_t)c * C + k];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c0 + u;
-      if (c >= n_chunks) break;
-      const int p = ch[c].z;
-      const float s = p < 0 ? 0.f : (p == c - 1 ? prev_end : hend[(size_t)p * C + k]);
-      prev_end = fmaf(av[u], s, hv[u]);
-      hin[(size_t)c * C + k] = s;
-      hend[(size_t)c * C + k] = prev_end;
-    }
-  }
-}
-
-__global__ __launch_bounds__(TH) void scan_apply(const int4* __restrict__ ch, const float* __restrict__ a,
-                                                 const float* __restrict__ b, int C, const float* __restrict__ hin,
-                                                 float* __restrict__ h) {
-  const int c = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
-  if (k >= C) return;
-  const int4 r = ch[c];
-  float s = hin[(size_t)c * C + k];
-  const size_t o = (size_t)r.x * C + k;
-#pragma unroll 8
-  for (int i = 0; i < r.y; ++i) {
-    s = fmaf(a[o + (size_t)i * C], s, b[o + (size_t)i * C]);
-    h[o + (size_t)i * C] = s;
-  }
-}
-
-// Backward, local pass: u = g_t + a_{t+1} u from the chunk's end with nothing
-// coming in; U = u at the first token, B = prod_{t > first} a_t.
-__global__ __launch_bounds__(TH) void scan_reduce_bwd(const int4* __restrict__ ch, const float* __restrict__ a,
-                                                      const float* __restrict__ g, int C, float* __restrict__ U,
-                                                      float* __restrict__ B) {
-  const int c = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
-  if (k >= C) return;
-  const int4 r = ch[c];
-  const size_t o = (size_t)r.x * C + k;
-  float u = 0.f, dec = 1.f, an = 0.f;  // an: a of the token after the current one
-#pragma unroll 8
-  for (int i = r.y - 1; i >= 0; --i) {
-    u = fmaf(an, u, g[o + (size_t)i * C]);
-    if (i + 1 < r.y) dec *= an;
-    an = a[o + (size_t)i * C];
-  }
-  U[(size_t)c * C + k] = u;
-  B[(size_t)c * C + k] = dec;
-}
-
-// Reverse DFS order: every successor of a chunk has a larger index, so a
-// chunk's incoming gradient is complete when the walk reaches it.
-__global__ __launch_bounds__(TH) void scan_walk_bwd(const int4* __restrict__ ch, int n_chunks, const float* __restrict__ a,
-                                                    const float* __restrict__ U, const float* __restrict__ B, int C,
-                                                    float* __restrict__ gin) {
-  const int k = blockIdx.x * TH + threadIdx.x;
-  if (k >= C) return;
-  for (int c = 0; c < n_chunks; ++c) gin[(size_t)c * C + k] = 0.f;
-  for (int c1 = n_chunks - 1; c1 >= 0; c1 -= 8) {
-    float uv[8], bv[8], af[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = max(c1 - u, 0);
-      uv[u] = U[(size_t)c * C + k];
-      bv[u] = B[(size_t)c * C + k];
-      af[u] = a[(size_t)ch[c].x * C + k];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c1 - u;
-      if (c < 0) break;
-      const int p = ch[c].z;
-      if (p < 0) continue;
-      const float dh0 = fmaf(bv[u], gin[(size_t)c * C + k], uv[u]);
-      gin[(size_t)p * C + k] += af[u] * dh0;
-    }
-  }
-}
-
-// The two walks with the per-chunk state of a workgroup's channels kept in
-// LDS: one wavefront per WC channels, column `lane` of an [n_chunks][WC]
-// array, so a chunk whose parent is not the previous one reads the parent's
-// end state (forward) or adds into the parent's incoming gradient (backward)
-// without a round trip to memory.  Each lane touches only its own column (no
-// barrier); the arithmetic and its order are those of scan_walk /
-// scan_walk_bwd.  Used while n_chunks * WC floats fit in LDS_WALK_MAX bytes.
-constexpr int WC = 64;
-constexpr size_t LDS_WALK_MAX = 64 * 1024;
-
-__global__ __launch_bounds__(WC) void scan_walk_lds(const int4* __restrict__ ch, int n_chunks, const float* __restrict__ A,
-                                                    const float* __restrict__ H, int C, float* __restrict__ hin,
-                                                    float* __restrict__ hend) {
-  extern __shared__ float se[];  // [n_chunks][WC] end states
-  const int lane = threadIdx.x, k0 = blockIdx.x * WC + lane;
-  const bool live = k0 < C;
-  const int k = live ? k0 : C - 1;
-  // inputs of the next group of 8 chunks are fetched while this group's chain runs
-  float prev_end = 0.f, av[8], hv[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int c = min(u, n_chunks - 1);
-    av[u] = A[(size_t)c * C + k];
-    hv[u] = H[(size_t)c * C + k];
-  }
-  for (int c0 = 0; c0 < n_chunks; c0 += 8) {
-    float an[8], hn[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = min(c0 + 8 + u, n_chunks - 1);
-      an[u] = A[(size_t)c * C + k];
-      hn[u] = H[(size_t)c * C + k];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c0 + u;
-      if (c >= n_chunks) break;
-      const int p = ch[c].z;
-      const float s = p < 0 ? 0.f : (p == c - 1 ? prev_end : se[p * WC + lane]);
-      prev_end = fmaf(av[u], s, hv[u]);
-      se[c * WC + lane] = prev_end;
-      if (live) {
-        hin[(size_t)c * C + k] = s;
-        hend[(size_t)c * C + k] = prev_end;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      av[u] = an[u];
-      hv[u] = hn[u];
-    }
-  }
-}
-
-__global__ __launch_bounds__(WC) void scan_walk_bwd_lds(const int4* __restrict__ ch, int n_chunks,
-                                                        const float* __restrict__ a, const float* __restrict__ U,
-                                                        const float* __restrict__ B, int C, float* __restrict__ gin) {
-  extern __shared__ float sg[];  // [n_chunks][WC] incoming gradients
-  const int lane = threadIdx.x, k0 = blockIdx.x * WC + lane;
-  const bool live = k0 < C;
-  const int k = live ? k0 : C - 1;
-  for (int c = 0; c < n_chunks; ++c) sg[c * WC + lane] = 0.f;
-  // inputs of the next group of 8 chunks are fetched while this group's chain runs
-  float uv[8], bv[8], af[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int c = max(n_chunks - 1 - u, 0);
-    uv[u] = U[(size_t)c * C + k];
-    bv[u] = B[(size_t)c * C + k];
-    af[u] = a[(size_t)ch[c].x * C + k];
-  }
-  for (int c1 = n_chunks - 1; c1 >= 0; c1 -= 8) {
-    float un[8], bn[8], fn[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = max(c1 - 8 - u, 0);
-      un[u] = U[(size_t)c * C + k];
-      bn[u] = B[(size_t)c * C + k];
-      fn[u] = a[(size_t)ch[c].x * C + k];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c1 - u;
-      if (c < 0) break;
-      const int p = ch[c].z;
-      if (p < 0) continue;
-      const float dh0 = fmaf(bv[u], sg[c * WC + lane], uv[u]);
-      sg[p * WC + lane] += af[u] * dh0;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      uv[u] = un[u];
-      bv[u] = bn[u];
-      af[u] = fn[u];
-    }
-  }
-  if (live)
-    for (int c = 0; c < n_chunks; ++c) gin[(size_t)c * C + k] = sg[c * WC + lane];
-}
-
-__global__ __launch_bounds__(TH) void scan_apply_bwd(const int4* __restrict__ ch, const float* __restrict__ a,
-                                                     const float* __restrict__ h, const float* __restrict__ g, int C,
-                                                     const float* __restrict__ gin, float* __restrict__ da,
-                                                     float* __restrict__ db) {
-  const int c = blockIdx.x, k = blockIdx.y * TH + threadIdx.x;
-  if (k >= C) return;
-  const int4 r = ch[c];
-  const size_t o = (size_t)r.x * C + k;
-  float u = gin[(size_t)c * C + k], an = 1.f;  // u carries a_{t+1} dh_{t+1} (the incoming sum at the end)
-#pragma unroll 4
-  for (int i = r.y - 1; i >= 0; --i) {
-    const float dh = g[o + (size_t)i * C] + an * u;
-    const float hp = i > 0 ? h[o + (size_t)(i - 1) * C] : (r.w >= 0 ? h[(size_t)r.w * C + k] : 0.f);
-    db[o + (size_t)i * C] = dh;
-    da[o + (size_t)i * C] = dh * hp;
-    u = dh;
-    an = a[o + (size_t)i * C];
-  }
-}
-
-// Causal conv over the path: y[t][k] = sum_j w[k][j] x[prev^j(t)][k].  VW
-// consecutive channels per lane (VW = 4: 16-byte accesses when C % 4 == 0).
+// VW consecutive channels per lane (VW = 4: 16-byte accesses when C % 4 == 0).
 template <int VW>
 struct Vec;
 template <>
@@ -283,6 +43,281 @@ struct Vec<4> {
   static __device__ __forceinline__ float get(const T& v, int i) { return v[i]; }
   static __device__ __forceinline__ void set(T& v, int i, float x) { v[i] = x; }
 };
+
+// Single pass.  One workgroup per (chunk, 64 VW channels): 128 / SG
+// wavefronts of SG tokens each cover a chunk (at most 128 tokens), lane l
+// holds channels VW l .. VW l + VW - 1 of the block.  The workgroups take
+// their (chunk, channel block) from a ticket counter in the route's chunk
+// order (parents first; reversed for the backward), so a chunk waits only on
+// chunks whose workgroups took a smaller ticket and are already running or
+// done: every wait ends.  Each wavefront keeps its segment's inputs in
+// registers, so every element is read once and written once:
+//   forward:  per segment the decay A = prod a and the end state H from a
+//             zero start; the chunk's start state is its parent chunk's end
+//             state, published by the parent's workgroup; segment starts
+//             follow by composing the segments before (s <- A s + H, in
+//             segment order); the scan from there writes h, and the chunk's
+//             last state is published for its children.
+//   backward: per segment the local reverse scan from the segment's end with
+//             nothing coming in (U = dh at its first token, B = prod of a
+//             after it); the chunk's incoming gradient is the sum over its
+//             child chunks (in the route's fixed order) of a_first dh_first,
+//             published by the children's workgroups -- the sum over branches
+//             a shared prefix receives; segment incomings follow from the
+//             last segment down; the reverse scan writes da = dh h_prev and
+//             db = dh, and the chunk publishes a_first dh_first.
+// A published value is one 64-bit word per (chunk, channel): flag in the high
+// half, the fp32 value in the low half, written and polled with agent-scope
+// atomics, so value and flag arrive together on every XCD.  Every result is
+// a fixed sequence of operations whatever the timing: bitwise repeatable.
+// The waits are bounded (SPIN_MAX polls); a wait that runs out (which the
+// ticket order rules out) sets the workspace's timeout word and goes on with
+// zero, so the kernel always exits.
+constexpr int SCAN_CHUNK = 128;  // most tokens a route chunk holds
+constexpr int SPIN_MAX = 1 << 20;
+
+// The sum, in list order, of the VW-channel values published at
+// p + idx[e] * stride for e in [e0, e1) (idx null: the single index e0);
+// up to four of them are polled together.
+template <int VW>
+__device__ __forceinline__ void wait_sum(const uint64_t* p, const int32_t* idx, int e0, int e1, size_t stride,
+                                         uint32_t* timeout, float (&sum)[VW]) {
+#pragma unroll
+  for (int x = 0; x < VW; ++x) sum[x] = 0.f;
+  for (int e = e0; e < e1; e += 4) {
+    const int m = min(4, e1 - e);
+    const uint64_t* q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = p + (size_t)(idx ? idx[e + min(j, m - 1)] : e0) * stride;
+    uint64_t v[4][VW];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int x = 0; x < VW; ++x) v[j][x] = 0;
+    bool all = false;
+    for (int it = 0; it < SPIN_MAX && !all; ++it) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int x = 0; x < VW; ++x)
+          if (j < m && !(v[j][x] >> 32)) v[j][x] = __hip_atomic_load(q[j] + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      all = true;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int x = 0; x < VW; ++x) all = all && (j >= m || (v[j][x] >> 32));
+      if (!all) __builtin_amdgcn_s_sleep(2);
+    }
+    if (!all) __hip_atomic_store(timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int x = 0; x < VW; ++x)
+        if (j < m) sum[x] += __uint_as_float((uint32_t)v[j][x]);
+  }
+}
+__device__ __forceinline__ void publish(uint64_t* p, float x) {
+  __hip_atomic_store(p, (1ull << 32) | __float_as_uint(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Clears the workspace header (ticket counter, timeout word) and the
+// published words before a pass (a kernel, not a memset: callers may capture
+// the calls in a graph).
+__global__ __launch_bounds__(TH) void scan_clear(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * TH + threadIdx.x; i < n16; i += (size_t)gridDim.x * TH) p[i] = uint4{0, 0, 0, 0};
+}
+
+template <int VW, int SG>
+__global__ __launch_bounds__(64 * (SCAN_CHUNK / SG)) void scan_fwd(const int4* __restrict__ ch,
+                                                                   const int32_t* __restrict__ order, int nkb,
+                                                                   const float* __restrict__ a,
+                                                                   const float* __restrict__ b, int C,
+                                                                   float* __restrict__ h, uint32_t* hdr, uint64_t* pub) {
+  constexpr int NW = SCAN_CHUNK / SG;
+  typedef Vec<VW> VV;
+  typedef typename VV::T V;
+  __shared__ int s_ticket;
+  __shared__ V sA[NW][64], sH[NW][64], s0[64];
+  if (threadIdx.x == 0) s_ticket = (int)atomicAdd(hdr, 1u);
+  __syncthreads();
+  const int t = s_ticket, q = t / nkb, kb = t - q * nkb, c = order[q];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k0 = (kb * 64 + lane) * VW;
+  const bool live = k0 < C;
+  const int k = live ? k0 : C - VW;
+  const int4 r = ch[c];
+  const int i0 = w * SG, n = max(0, min(SG, r.y - i0));
+  const size_t o = (size_t)(r.x + i0) * C + k;
+  // (rows past the segment's end repeat its last row: loads without branches)
+  V av[SG], bv[SG];
+  if (n > 0) {
+#pragma unroll
+    for (int i = 0; i < SG; ++i) {
+      const size_t oi = o + (size_t)min(i, n - 1) * C;
+      av[i] = *(const V*)(a + oi);
+      bv[i] = *(const V*)(b + oi);
+    }
+  }
+  V A, H;
+#pragma unroll
+  for (int x = 0; x < VW; ++x) {
+    float pa = 1.f, ph = 0.f;
+#pragma unroll
+    for (int i = 0; i < SG; ++i)
+      if (i < n) {
+        ph = fmaf(VV::get(av[i], x), ph, VV::get(bv[i], x));
+        pa *= VV::get(av[i], x);
+      }
+    VV::set(A, x, pa);
+    VV::set(H, x, ph);
+  }
+  sA[w][lane] = A;
+  sH[w][lane] = H;
+  if (w == 0) {
+    float st[VW];
+    if (r.z >= 0) {
+      wait_sum<VW>(pub + k, nullptr, r.z, r.z + 1, (size_t)C, hdr + 1, st);
+    } else {
+#pragma unroll
+      for (int x = 0; x < VW; ++x) st[x] = 0.f;
+    }
+    V sv;
+#pragma unroll
+    for (int x = 0; x < VW; ++x) VV::set(sv, x, st[x]);
+    s0[lane] = sv;
+  }
+  __syncthreads();
+  if (n == 0) return;
+  float s[VW];
+#pragma unroll
+  for (int x = 0; x < VW; ++x) s[x] = VV::get(s0[lane], x);
+  for (int u = 0; u < w; ++u) {
+    const V pa = sA[u][lane], ph = sH[u][lane];
+#pragma unroll
+    for (int x = 0; x < VW; ++x) s[x] = fmaf(VV::get(pa, x), s[x], VV::get(ph, x));
+  }
+#pragma unroll
+  for (int i = 0; i < SG; ++i)
+    if (i < n) {
+      V y;
+#pragma unroll
+      for (int x = 0; x < VW; ++x) {
+        s[x] = fmaf(VV::get(av[i], x), s[x], VV::get(bv[i], x));
+        VV::set(y, x, s[x]);
+      }
+      if (live) *(V*)(h + o + (size_t)i * C) = y;
+    }
+  if (live && i0 + n == r.y)
+#pragma unroll
+    for (int x = 0; x < VW; ++x) publish(pub + (size_t)c * C + k + x, s[x]);
+}
+
+template <int VW, int SG>
+__global__ __launch_bounds__(64 * (SCAN_CHUNK / SG)) void scan_bwd(
+    const int4* __restrict__ ch, const int32_t* __restrict__ order, const int32_t* __restrict__ kid_ptr,
+    const int32_t* __restrict__ kid, int n_chunks, int nkb, const float* __restrict__ a, const float* __restrict__ h,
+    const float* __restrict__ g, int C, float* __restrict__ da, float* __restrict__ db, uint32_t* hdr,
+    uint64_t* pub) {
+  constexpr int NW = SCAN_CHUNK / SG;
+  typedef Vec<VW> VV;
+  typedef typename VV::T V;
+  __shared__ int s_ticket;
+  __shared__ V sU[NW][64], sB[NW][64], sF[NW][64], sG[64];
+  if (threadIdx.x == 0) s_ticket = (int)atomicAdd(hdr, 1u);
+  __syncthreads();
+  const int t = s_ticket, q = t / nkb, kb = t - q * nkb, c = order[n_chunks - 1 - q];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k0 = (kb * 64 + lane) * VW;
+  const bool live = k0 < C;
+  const int k = live ? k0 : C - VW;
+  const int4 r = ch[c];
+  const int i0 = w * SG, n = max(0, min(SG, r.y - i0));
+  const size_t o = (size_t)(r.x + i0) * C + k;
+  // a, dh and h_prev of the segment's tokens (h_prev of the chunk's first
+  // token: the token before it on the path, or zero at a root)
+  V av[SG], gv[SG], hv[SG];
+  if (n > 0) {
+#pragma unroll
+    for (int i = 0; i < SG; ++i) {
+      const int ii = min(i, n - 1);
+      const size_t oi = o + (size_t)ii * C;
+      av[i] = *(const V*)(a + oi);
+      gv[i] = *(const V*)(g + oi);
+      if (i0 + ii > 0) {
+        hv[i] = *(const V*)(h + (size_t)(r.x + i0 + ii - 1) * C + k);
+      } else if (r.w >= 0) {
+        hv[i] = *(const V*)(h + (size_t)r.w * C + k);
+      } else {
+#pragma unroll
+        for (int x = 0; x < VW; ++x) VV::set(hv[i], x, 0.f);
+      }
+    }
+  }
+  // local reverse scan: u = g_i + a_{i+1} u from the segment's end
+  V U, B, F;
+#pragma unroll
+  for (int x = 0; x < VW; ++x) {
+    float u = 0.f, dec = 1.f, an = 0.f;
+#pragma unroll
+    for (int i = SG - 1; i >= 0; --i)
+      if (i < n) {
+        u = fmaf(an, u, VV::get(gv[i], x));
+        if (i + 1 < n) dec *= an;
+        an = VV::get(av[i], x);
+      }
+    VV::set(U, x, u);
+    VV::set(B, x, dec);
+    VV::set(F, x, n > 0 ? VV::get(av[0], x) : 0.f);
+  }
+  sU[w][lane] = U;
+  sB[w][lane] = B;
+  sF[w][lane] = F;
+  if (w == 0) {
+    float gin[VW];
+    wait_sum<VW>(pub + k, kid, kid_ptr[c], kid_ptr[c + 1], (size_t)C, hdr + 1, gin);
+    V gv0;
+#pragma unroll
+    for (int x = 0; x < VW; ++x) VV::set(gv0, x, gin[x]);
+    sG[lane] = gv0;
+  }
+  __syncthreads();
+  if (n == 0) return;
+  // the gradient arriving at this segment's last token from after it
+  const int last = (r.y - 1) / SG;
+  float dh[VW];
+#pragma unroll
+  for (int x = 0; x < VW; ++x) dh[x] = VV::get(sG[lane], x);
+  for (int v = last; v > w; --v) {
+    const V f = sF[v][lane], bb = sB[v][lane], uu = sU[v][lane];
+#pragma unroll
+    for (int x = 0; x < VW; ++x) dh[x] = VV::get(f, x) * fmaf(VV::get(bb, x), dh[x], VV::get(uu, x));
+  }
+  float an[VW];
+#pragma unroll
+  for (int x = 0; x < VW; ++x) an[x] = 1.f;
+#pragma unroll
+  for (int i = SG - 1; i >= 0; --i)
+    if (i < n) {
+      V vb, va;
+#pragma unroll
+      for (int x = 0; x < VW; ++x) {
+        dh[x] = fmaf(an[x], dh[x], VV::get(gv[i], x));
+        VV::set(vb, x, dh[x]);
+        VV::set(va, x, dh[x] * VV::get(hv[i], x));
+        an[x] = VV::get(av[i], x);
+      }
+      if (live) {
+        *(V*)(db + o + (size_t)i * C) = vb;
+        *(V*)(da + o + (size_t)i * C) = va;
+      }
+    }
+  if (live && w == 0)
+#pragma unroll
+    for (int x = 0; x < VW; ++x) publish(pub + (size_t)c * C + k + x, VV::get(av[0], x) * dh[x]);
+}
+
+// Causal conv over the path: y[t][k] = sum_j w[k][j] x[prev^j(t)][k].  VW
+// consecutive channels per lane (VW = 4: 16-byte accesses when C % 4 == 0).
 
 // A block covers TG tokens x (TH * VW) channels; each lane holds its
 // channels' taps in registers for all TG tokens.
@@ -521,14 +556,18 @@ using namespace ta;
 namespace {
 struct RouteDev {
   const int4* ch;
-  const int32_t *cprev, *succ_ptr, *succ;
+  const int32_t *cprev, *succ_ptr, *succ, *kid_ptr, *kid, *order;
 };
 RouteDev dev_tables(const ta_route* R, const void* d) {
   const char* b = (const char*)d;
-  return {(const int4*)(b + R->off_chunks), (const int32_t*)(b + R->off_cprev), (const int32_t*)(b + R->off_succ_ptr),
-          (const int32_t*)(b + R->off_succ)};
+  return {(const int4*)(b + R->off_chunks),    (const int32_t*)(b + R->off_cprev), (const int32_t*)(b + R->off_succ_ptr),
+          (const int32_t*)(b + R->off_succ),   (const int32_t*)(b + R->off_kid_ptr),
+          (const int32_t*)(b + R->off_kid),    (const int32_t*)(b + R->off_order)};
 }
-size_t scan_ws(const ta_route* R, int C) { return align256((size_t)R->n_chunks * C * sizeof(float)) * 4; }
+// scan workspace: a 256-byte header (ticket counter, timeout word), then one
+// published 64-bit word per (chunk, channel)
+constexpr size_t SCAN_HDR = 256;
+size_t scan_ws(const ta_route* R, int C) { return SCAN_HDR + align256((size_t)R->n_chunks * C * sizeof(uint64_t)); }
 size_t conv_ws(const ta_route* R, int C) {
   return align256((size_t)((R->n_tokens + ssm::TOKB - 1) / ssm::TOKB) * C * R->conv_k * sizeof(float));
 }
@@ -541,8 +580,9 @@ extern "C" ta_status tree_route_upload(const ta_route* R, void* droute, size_t b
   struct Part {
     size_t off;
     const std::vector<int32_t>* v;
-  } parts[] = {{R->off_chunks, &R->chunks}, {R->off_cprev, &R->cprev}, {R->off_succ_ptr, &R->succ_ptr},
-               {R->off_succ, &R->succ}};
+  } parts[] = {{R->off_chunks, &R->chunks},   {R->off_cprev, &R->cprev}, {R->off_succ_ptr, &R->succ_ptr},
+               {R->off_succ, &R->succ},       {R->off_kid_ptr, &R->kid_ptr}, {R->off_kid, &R->kid},
+               {R->off_order, &R->order}};
   for (const Part& x : parts) {
     if (x.v->empty()) continue;
     if (hipMemcpyAsync(b + x.off, x.v->data(), x.v->size() * 4, hipMemcpyHostToDevice, stream) != hipSuccess)
@@ -563,32 +603,62 @@ extern "C" ta_status tree_conv_ws_bytes(const ta_route* R, int32_t C, size_t* by
   return TA_OK;
 }
 
+namespace {
+// Clears the scan workspace and returns its header and published words.
+ta_status scan_prepare(const ta_route* R, int C, void* ws, size_t ws_bytes, hipStream_t stream, uint32_t** hdr,
+                       uint64_t** pub) {
+  const size_t need = scan_ws(R, C);
+  if (!ws || ws_bytes < need) return TA_ENOMEM;
+  if (R->chunk > ssm::SCAN_CHUNK) return TA_EUNSUPPORTED;
+  const size_t n16 = need / 16;
+  hipLaunchKernelGGL(ssm::scan_clear, dim3((unsigned)std::min<size_t>((n16 + ssm::TH - 1) / ssm::TH, 2048)),
+                     dim3(ssm::TH), 0, stream, (uint4*)ws, n16);
+  TA_LAUNCH_CHECK();
+  *hdr = (uint32_t*)ws;
+  *pub = (uint64_t*)((char*)ws + SCAN_HDR);
+  return TA_OK;
+}
+
+// 16-byte channel vectors (VW = 4) when every row is 16-byte aligned, with
+// SG = 16 tokens per wavefront: a 512-thread workgroup covers a chunk x 256
+// channels and each row access is one contiguous KiB (8-token segments with
+// 1,024 threads ran the forward 2% slower; the backward, holding three inputs
+// per token, would spill there); else one channel per lane, SG = 32.
+constexpr int SCAN_SG4 = 16, SCAN_SG1 = 32;
+bool scan_vec4(int C, std::initializer_list<const void*> ptrs) {
+  if (C % 4) return false;
+  for (const void* p : ptrs)
+    if ((uintptr_t)p % 16) return false;
+  return true;
+}
+int scan_blocks(const ta_route* R, int C, int vw, unsigned* grid) {
+  const int nkb = (C + 64 * vw - 1) / (64 * vw);
+  if ((int64_t)R->n_chunks * nkb > INT32_MAX) return -1;
+  *grid = (unsigned)(R->n_chunks * nkb);
+  return nkb;
+}
+}  // namespace
+
 extern "C" ta_status tree_scan_fwd(const ta_route* R, const void* droute, const float* a, const float* b, int32_t C,
                                    float* h, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!R || !droute || !a || !b || !h || C <= 0) return TA_EINVAL;
   if ((int64_t)R->n_tokens * C > ((int64_t)1 << 40)) return TA_ERANGE;
   if (R->n_chunks == 0) return TA_OK;
-  const size_t need = scan_ws(R, C);
-  if (!ws || ws_bytes < need) return TA_ENOMEM;
+  const bool v4 = scan_vec4(C, {a, b, h});
+  unsigned grid;
+  const int nkb = scan_blocks(R, C, v4 ? 4 : 1, &grid);
+  if (nkb < 0) return TA_ERANGE;
+  uint32_t* hdr;
+  uint64_t* pub;
+  const ta_status st = scan_prepare(R, C, ws, ws_bytes, stream, &hdr, &pub);
+  if (st != TA_OK) return st;
   const RouteDev d = dev_tables(R, droute);
-  const size_t seg = need / 4;
-  float* A = (float*)ws;
-  float* H = (float*)((char*)ws + seg);
-  float* hin = (float*)((char*)ws + 2 * seg);
-  float* hend = (float*)((char*)ws + 3 * seg);
-  const int cb = (C + ssm::TH - 1) / ssm::TH;
-  hipLaunchKernelGGL(ssm::scan_reduce, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, b, C, A, H);
-  TA_LAUNCH_CHECK();
-  const size_t lds = (size_t)R->n_chunks * ssm::WC * sizeof(float);
-  if (lds <= ssm::LDS_WALK_MAX)
-    hipLaunchKernelGGL(ssm::scan_walk_lds, dim3((C + ssm::WC - 1) / ssm::WC), dim3(ssm::WC), lds, stream, d.ch,
-                       R->n_chunks, (const float*)A, (const float*)H, C, hin, hend);
+  if (v4)
+    hipLaunchKernelGGL((ssm::scan_fwd<4, SCAN_SG4>), dim3(grid), dim3(64 * (ssm::SCAN_CHUNK / SCAN_SG4)), 0, stream,
+                       d.ch, d.order, nkb, a, b, C, h, hdr, pub);
   else
-    hipLaunchKernelGGL(ssm::scan_walk, dim3(cb), dim3(ssm::TH), 0, stream, d.ch, R->n_chunks, (const float*)A,
-                       (const float*)H, C, hin, hend);
-  TA_LAUNCH_CHECK();
-  hipLaunchKernelGGL(ssm::scan_apply, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, b, C,
-                     (const float*)hin, h);
+    hipLaunchKernelGGL((ssm::scan_fwd<1, SCAN_SG1>), dim3(grid), dim3(64 * (ssm::SCAN_CHUNK / SCAN_SG1)), 0, stream,
+                       d.ch, d.order, nkb, a, b, C, h, hdr, pub);
   TA_LAUNCH_CHECK();
   return TA_OK;
 }
@@ -599,26 +669,21 @@ extern "C" ta_status tree_scan_bwd(const ta_route* R, const void* droute, const 
   if (!R || !droute || !a || !h || !dh || !da || !db || C <= 0) return TA_EINVAL;
   if ((int64_t)R->n_tokens * C > ((int64_t)1 << 40)) return TA_ERANGE;
   if (R->n_chunks == 0) return TA_OK;
-  const size_t need = scan_ws(R, C);
-  if (!ws || ws_bytes < need) return TA_ENOMEM;
+  const bool v4 = scan_vec4(C, {a, h, dh, da, db});
+  unsigned grid;
+  const int nkb = scan_blocks(R, C, v4 ? 4 : 1, &grid);
+  if (nkb < 0) return TA_ERANGE;
+  uint32_t* hdr;
+  uint64_t* pub;
+  const ta_status st = scan_prepare(R, C, ws, ws_bytes, stream, &hdr, &pub);
+  if (st != TA_OK) return st;
   const RouteDev d = dev_tables(R, droute);
-  const size_t seg = need / 4;
-  float* U = (float*)ws;
-  float* B = (float*)((char*)ws + seg);
-  float* gin = (float*)((char*)ws + 2 * seg);
-  const int cb = (C + ssm::TH - 1) / ssm::TH;
-  hipLaunchKernelGGL(ssm::scan_reduce_bwd, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, dh, C, U, B);
-  TA_LAUNCH_CHECK();
-  const size_t lds = (size_t)R->n_chunks * ssm::WC * sizeof(float);
-  if (lds <= ssm::LDS_WALK_MAX)
-    hipLaunchKernelGGL(ssm::scan_walk_bwd_lds, dim3((C + ssm::WC - 1) / ssm::WC), dim3(ssm::WC), lds, stream, d.ch,
-                       R->n_chunks, a, (const float*)U, (const float*)B, C, gin);
+  if (v4)
+    hipLaunchKernelGGL((ssm::scan_bwd<4, SCAN_SG4>), dim3(grid), dim3(64 * (ssm::SCAN_CHUNK / SCAN_SG4)), 0, stream,
+                       d.ch, d.order, d.kid_ptr, d.kid, R->n_chunks, nkb, a, h, dh, C, da, db, hdr, pub);
   else
-    hipLaunchKernelGGL(ssm::scan_walk_bwd, dim3(cb), dim3(ssm::TH), 0, stream, d.ch, R->n_chunks, a,
-                       (const float*)U, (const float*)B, C, gin);
-  TA_LAUNCH_CHECK();
-  hipLaunchKernelGGL(ssm::scan_apply_bwd, dim3(R->n_chunks, cb), dim3(ssm::TH), 0, stream, d.ch, a, h, dh, C,
-                     (const float*)gin, da, db);
+    hipLaunchKernelGGL((ssm::scan_bwd<1, SCAN_SG1>), dim3(grid), dim3(64 * (ssm::SCAN_CHUNK / SCAN_SG1)), 0, stream,
+                       d.ch, d.order, d.kid_ptr, d.kid, R->n_chunks, nkb, a, h, dh, C, da, db, hdr, pub);
   TA_LAUNCH_CHECK();
   return TA_OK;
 }

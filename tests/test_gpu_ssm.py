@@ -26,6 +26,18 @@ def close(name, got, ref, mag):
     assert not bad.any(), f"{name}: {int(bad.sum())} of {bad.size} outside, max err {err.max():.3e}"
 
 
+def check_scan_header(ws, route, C):
+    """The scan workspace header after a pass: every (chunk, channel block)
+    workgroup took exactly one ticket (blocks of 64 lanes x 4 channels when C
+    is a multiple of 4 -- the tensors here are 16-byte aligned -- else 64
+    channels), and no wait for a published value ran out."""
+    torch.cuda.synchronize()
+    ticket, timeout = (int(v) for v in ws[:8].view(torch.int32).cpu())
+    block = 256 if C % 4 == 0 else 64
+    assert ticket == route.n_chunks * ((C + block - 1) // block)
+    assert timeout == 0
+
+
 def run(tree, C, K, seed, chans=None):
     print(f"[ssm] {tree.name or 'tree'} N={tree.n_tokens} C={C} K={K}", flush=True)
     plan = pkg.tree_plan(tree.parent, tree.seg_len)
@@ -39,8 +51,11 @@ def run(tree, C, K, seed, chans=None):
     w = rng.standard_normal((C, K)).astype(np.float32)
     g = rng.standard_normal((N, C)).astype(np.float32)
     A, B, X, Wt, G = (torch.from_numpy(z).to(DEV) for z in (a, b, x, w, g))
-    h = pkg.tree_scan_fwd(route, A, B)
-    da, db = pkg.tree_scan_bwd(route, A, h, G)
+    ws = torch.empty(pkg._route_ws("tree_scan_ws_bytes", route, C), dtype=torch.uint8, device=DEV)
+    h = pkg.tree_scan_fwd(route, A, B, ws=ws)
+    check_scan_header(ws, route, C)
+    da, db = pkg.tree_scan_bwd(route, A, h, G, ws=ws)
+    check_scan_header(ws, route, C)
     y = pkg.tree_conv_fwd(route, X, Wt)
     dx, dw = pkg.tree_conv_bwd(route, X, Wt, G)
     torch.cuda.synchronize()
@@ -72,9 +87,10 @@ def test_random_trees(K):
         run(t, 300, K, c)
 
 
-def test_many_chunks_walk_in_memory():
-    """More than 256 chunks: the chunk-tree walks keep their per-chunk state in
-    memory instead of LDS (a 300-node random tree, nodes of 1-12 tokens)."""
+def test_many_chunks_and_branches():
+    """More than 256 chunks, most of them one short node, many with several
+    child chunks: deep chains of waits on published states (a 300-node random
+    tree, nodes of 1-12 tokens)."""
     rng = np.random.default_rng(21)
     t = W.random_tree(rng, 300, max_len=12, p_zero=0.0, n_roots=3)
     plan = pkg.tree_plan(t.parent, t.seg_len)
