@@ -321,7 +321,7 @@ __global__ __launch_bounds__(64 * (SCAN_CHUNK / SG)) void scan_bwd(
 
 // A block covers TG tokens x (TH * VW) channels; each lane holds its
 // channels' taps in registers for all TG tokens.
-constexpr int TG = 8;
+constexpr int TG = 8;  // (4 or 16 tokens per forward block: 39% and 1% slower)
 template <int VW>
 __device__ __forceinline__ void load_taps(const float* __restrict__ w, int k, int K, float (&wr)[8][VW]) {
 #pragma unroll
@@ -352,14 +352,16 @@ __device__ __forceinline__ bool window_prev(const int32_t* __restrict__ cprev, i
 
 template <int VW, int KT>
 __global__ __launch_bounds__(TH) void conv_fwd(const int32_t* __restrict__ cprev, int N, int K, const float* __restrict__ x,
-                                               const float* __restrict__ w, int C, float* __restrict__ y) {
+                                               const float* __restrict__ w, int C, int cb, float* __restrict__ y) {
   typedef typename Vec<VW>::T V;
-  const int k0 = (blockIdx.y * TH + threadIdx.x) * VW;
+  // channel blocks innermost: consecutive blocks cover one token group's whole rows
+  const int tg = blockIdx.x / cb, kb = blockIdx.x - tg * cb;
+  const int k0 = (kb * TH + threadIdx.x) * VW;
   const bool live = k0 < C;
   const int k = live ? k0 : C - VW;
   float wr[8][VW];
   load_taps<VW>(w, k, K, wr);
-  const int t0 = blockIdx.x * TG;
+  const int t0 = tg * TG;
   if (KT > 1 && window_prev<KT>(cprev, N, t0)) {
     V r[TG + KT - 1];  // rows t0 - KT + 1 .. t0 + TG - 1 (all >= 0: every tap has a predecessor)
 #pragma unroll
@@ -509,14 +511,15 @@ __device__ __forceinline__ void conv_dw_group(const int32_t* __restrict__ cprev,
 // tokens and channel, sum_t dy[t] x[prev^j(t)] in token order (fixed).  A
 // block walks its TOKB tokens group by group, each group's dx and then its
 // dw terms, so the dy rows the two read are fetched from HBM once.
-constexpr int TOKB = 256;
+constexpr int TOKB = 256;  // (64 or 128: 37% and 22% slower, most of it in summing the partials)
 template <int VW, int KT>
 __global__ __launch_bounds__(TH) void conv_bwd(const int32_t* __restrict__ cprev, const int32_t* __restrict__ sp,
                                                const int32_t* __restrict__ sc, int N, int K,
                                                const float* __restrict__ x, const float* __restrict__ dy,
                                                const float* __restrict__ w, int C, float* __restrict__ dx,
-                                               float* __restrict__ part) {
-  const int k0 = (blockIdx.y * TH + threadIdx.x) * VW, tb = blockIdx.x;
+                                               int cb, float* __restrict__ part) {
+  const int tb = blockIdx.x / cb, kb = blockIdx.x - tb * cb;  // channel blocks innermost
+  const int k0 = (kb * TH + threadIdx.x) * VW;
   const bool live = k0 < C;
   const int k = live ? k0 : C - VW;
   float wr[8][VW];
@@ -631,9 +634,11 @@ bool scan_vec4(int C, std::initializer_list<const void*> ptrs) {
     if ((uintptr_t)p % 16) return false;
   return true;
 }
+// A launch's work-items (blocks x threads) must stay below 2^32.
+bool grid_fits(uint64_t blocks, int threads) { return blocks * (uint64_t)threads < (1ull << 32); }
 int scan_blocks(const ta_route* R, int C, int vw, unsigned* grid) {
   const int nkb = (C + 64 * vw - 1) / (64 * vw);
-  if ((int64_t)R->n_chunks * nkb > INT32_MAX) return -1;
+  if (!grid_fits((uint64_t)R->n_chunks * nkb, 64 * (ssm::SCAN_CHUNK / SCAN_SG4))) return -1;
   *grid = (unsigned)(R->n_chunks * nkb);
   return nkb;
 }
@@ -696,8 +701,9 @@ template <int VW, int KT>
 void launch_conv_fwd(const ta_route* R, const RouteDev& d, const float* x, const float* w, int C, float* y,
                      hipStream_t st) {
   const int cb = (C / VW + ssm::TH - 1) / ssm::TH;
-  hipLaunchKernelGGL((ssm::conv_fwd<VW, KT>), dim3((R->n_tokens + ssm::TG - 1) / ssm::TG, cb), dim3(ssm::TH), 0, st,
-                     d.cprev, R->n_tokens, R->conv_k, x, w, C, y);
+  const unsigned ntg = (unsigned)((R->n_tokens + ssm::TG - 1) / ssm::TG);
+  hipLaunchKernelGGL((ssm::conv_fwd<VW, KT>), dim3(ntg * cb), dim3(ssm::TH), 0, st, d.cprev, R->n_tokens,
+                     R->conv_k, x, w, C, cb, y);
 }
 
 template <int VW, int KT>
@@ -705,8 +711,8 @@ void launch_conv_bwd(const ta_route* R, const RouteDev& d, const float* x, const
                      float* dx, float* part, hipStream_t st) {
   const int cb = (C / VW + ssm::TH - 1) / ssm::TH;
   const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
-  hipLaunchKernelGGL((ssm::conv_bwd<VW, KT>), dim3(nb, cb), dim3(ssm::TH), 0, st, d.cprev, d.succ_ptr, d.succ,
-                     R->n_tokens, R->conv_k, x, dy, w, C, dx, part);
+  hipLaunchKernelGGL((ssm::conv_bwd<VW, KT>), dim3((unsigned)nb * cb), dim3(ssm::TH), 0, st, d.cprev, d.succ_ptr,
+                     d.succ, R->n_tokens, R->conv_k, x, dy, w, C, dx, cb, part);
 }
 
 template <int VW>
@@ -737,6 +743,8 @@ extern "C" ta_status tree_conv_fwd(const ta_route* R, const void* droute, const 
                                    float* y, hipStream_t stream) {
   if (!R || !droute || !x || !w || !y || C <= 0) return TA_EINVAL;
   if (R->n_tokens == 0) return TA_OK;
+  if (!grid_fits((uint64_t)((R->n_tokens + ssm::TG - 1) / ssm::TG) * ((C + ssm::TH - 1) / ssm::TH), ssm::TH))
+    return TA_ERANGE;
   const RouteDev d = dev_tables(R, droute);
   if (C % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0)
     conv_fwd_k<4>(R, d, x, w, C, y, stream);
@@ -751,10 +759,11 @@ extern "C" ta_status tree_conv_bwd(const ta_route* R, const void* droute, const 
                                    hipStream_t stream) {
   if (!R || !droute || !x || !w || !dy || !dx || !dw || C <= 0) return TA_EINVAL;
   if (R->n_tokens == 0) return TA_OK;
+  const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
+  if (!grid_fits((uint64_t)nb * ((C + ssm::TH - 1) / ssm::TH), ssm::TH)) return TA_ERANGE;
   const size_t need = conv_ws(R, C);
   if (!ws || ws_bytes < need) return TA_ENOMEM;
   const RouteDev d = dev_tables(R, droute);
-  const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
   if (C % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)dy % 16 == 0 && (uintptr_t)dx % 16 == 0)
     conv_bwd_k<4>(R, d, x, w, dy, C, dx, (float*)ws, stream);
   else
