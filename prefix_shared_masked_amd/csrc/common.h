@@ -42,9 +42,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma32h_acc(f32x16& acc, const f16x8& a, const f16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
 // Wait states between the accumulators' MFMA writes and any other access (an
 // XDL 16-pass result needs at most 18; this gives 24), and between VALU
 // writes (zero init) and the first MFMA.  The accumulators are operands, so
@@ -203,11 +200,6 @@ __device__ __forceinline__ void copy16_to_lds_nt(const void* g, const void* lds_
   const uint32_t a = lds_addr(lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(a)
                : "memory", "m0");
-}
-// 4-byte variant (global_load_lds_dword): lane i writes lds_base + 4 i.
-__device__ __forceinline__ void copy4_to_lds(const void* g, const void* lds_base) {
-  const uint32_t a = lds_addr(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(a) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_copies_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
