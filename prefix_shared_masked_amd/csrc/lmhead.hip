@@ -211,18 +211,20 @@ __global__ __launch_bounds__(256, 1) void lse_kernel(Params P) {
 
 __global__ __launch_bounds__(256, 1) void ds_kernel(Params P) {
   __shared__ __attribute__((aligned(1024))) char ring[NBUF * STAGE_BYTES];
+  // per wavefront, one 32-token x 128-row slice of dS in bf16 on its way to
+  // memory: row = token, 16-byte piece c of a row at c ^ (token % 16)
+  __shared__ __attribute__((aligned(1024))) char tbuf[4][32 * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rr = lane & 31, half = lane >> 5;
   const int wv = wave & 1, wt = wave >> 1;
   // the lane's four tokens: log2-scaled LSE, weight (0 when not supervised), label
   float lse2[4], wt_[4];
   int y[4];
-  bool tv[4], tz[4];
+  bool tv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = blockIdx.x * BT + 128 * wt + 32 * j + rr;
     tv[j] = t < P.N;
-    tz[j] = t < P.n_pad;  // rows past the last token are stored as zeros
     const int tc = tv[j] ? t : 0;
     y[j] = P.labels[tc];
     const bool valid = tv[j] && y[j] != P.ignore_index && y[j] >= 0 && y[j] < P.V;
@@ -230,12 +232,12 @@ __global__ __launch_bounds__(256, 1) void ds_kernel(Params P) {
     lse2[j] = P.lse[tc] * L2E;
   }
   const int vrow0 = P.vt_first * BV;  // first vocabulary row of this chunk
+  char* const tb = tbuf[wave];
   tile_loop(P, ring, [&](int vt, f32x16 (&acc)[4][4]) {
     const int vb = vt * BV + 128 * wv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = blockIdx.x * BT + 128 * wt + 32 * j + rr;
-      bf16* row = P.ds + (size_t)(tz[j] ? t : 0) * P.ld_ds + (vb - vrow0) + 4 * half;
+      // the lane's token rr: its 128 rows into the slice, 8 bytes at a time
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -249,10 +251,18 @@ __global__ __launch_bounds__(256, 1) void ds_kernel(Params P) {
             const float g = wt_[j] * (p - (v0 + u == y[j] ? 1.f : 0.f));
             o[u] = (bf16)(tv[j] && v0 + u < P.V ? g : 0.f);
           }
-          // every row up to n_pad and every column of the tile: the products
-          // read them as zero padding of their contraction
-          if (tz[j]) *(bf16x4*)(row + 32 * i + 8 * r4) = o;
+          *(bf16x4*)(tb + rr * 256 + (((4 * i + r4) ^ (rr & 15)) << 4) + 8 * half) = o;
         }
+      // then each store writes four tokens' 256-byte runs: every row up to
+      // n_pad and every column of the tile, which the products read as zero
+      // padding of their contraction
+      const int tj = blockIdx.x * BT + 128 * wt + 32 * j;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = 4 * q + (lane >> 4), c = lane & 15;
+        const u32x4 v = *(const u32x4*)(tb + row * 256 + ((c ^ (row & 15)) << 4));
+        if (tj + row < P.n_pad) *(u32x4*)(P.ds + (size_t)(tj + row) * P.ld_ds + (vb - vrow0) + 8 * c) = v;
+      }
     }
     // stores count on vmcnt too and may complete out of order with the ring
     // copies: let them drain so the ring's counted waits stay exact
