@@ -102,6 +102,25 @@ def test_long_nodes_several_chunks():
     run(W.Tree(np.array([-1, 0, 0, 1]), np.array([700, 300, 256, 513]), "long"), 129, 4, 3)
 
 
+def test_wide_fan_out():
+    """A 300-token root (three chunks) with 200 five-token children: the
+    root's last chunk sums 200 published gradients (polled four at a time);
+    with 16-byte channel vectors (C = 64: one block, 16 live lanes) and one
+    channel per lane (C = 66: two blocks)."""
+    parent = np.array([-1] + [0] * 200)
+    seg = np.array([300] + [5] * 200)
+    t = W.Tree(parent, seg, "fan_out_200")
+    run(t, 64, 4, 31)
+    run(t, 66, 3, 32)
+
+
+@pytest.mark.timeout(600)
+def test_random_agentic_tree_sampled_channels():
+    """The random agentic tree (34,538 tokens, 65 leaves, many chunks per
+    depth) at 512 channels, every token of six sampled channels."""
+    run(W.random_agentic_tree(), 512, 4, 33, chans=[0, 3, 64, 255, 256, 511])
+
+
 def test_deterministic():
     t = W.spine_tree(64, 16, 24, 6)
     plan = pkg.tree_plan(t.parent, t.seg_len)
