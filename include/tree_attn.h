@@ -220,6 +220,10 @@ ta_status tree_attn_ws_bytes(const ta_plan* plan, int32_t op, ta_dtype dt, int32
  * The library never clears the flag: the caller zeroes it and reads it back
  * when it wants to know (tree_attn_bwd uses the same word of its workspace,
  * the partition calls the first word of theirs).
+ * A plan without tokens returns TA_OK after checking plan, heads, d and dt,
+ * without touching any tensor pointer (empty tensors may be null); the same
+ * holds for tree_attn_bwd, and for the scan and conv calls on a route
+ * without tokens (tree_conv_bwd then zeroes dw).
  * Errors: TA_EINVAL, TA_EUNSUPPORTED, TA_ENOMEM (ws too small), TA_EHIP. */
 ta_status tree_attn_fwd(const ta_plan* plan, const void* dplan, ta_dtype dt, const void* q,
                         const void* k, const void* v, int32_t Hq, int32_t Hkv, int32_t d,

@@ -1178,6 +1178,7 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   if (!p || !dplan) return TA_EINVAL;
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return TA_EINVAL;
   if (dt == TA_BF16 ? d != 128 : (dt != TA_F32 || (d != 64 && d != 128))) return TA_EUNSUPPORTED;
+  if (p->n_tokens == 0) return TA_OK;  // nothing to read or write (empty tensors may be null)
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return TA_EINVAL;
   // bf16: the dS path when the workspace holds the dS blocks of at least one
   // KV head (the KV heads then run in rounds of as many as fit), else dQ
@@ -1187,7 +1188,6 @@ extern "C" ta_status tree_attn_bwd_ex(const ta_plan* p, const void* dplan, ta_dt
   const int ds_heads = dt == TA_BF16 ? ds_heads_for(p, Hq, Hkv, d, rope_base, ws_bytes) : 0;
   const bool ds_path = ds_heads > 0;
   const int N = p->n_tokens;
-  if (N == 0) return TA_OK;
   if (scale <= 0.f) scale = 1.f / sqrtf((float)d);
   const char* base = (const char*)dplan;
   const int32_t* pos = (const int32_t*)(base + p->off_pos);

@@ -547,11 +547,11 @@ extern "C" ta_status tree_attn_fwd_ex(const ta_plan* p, const void* dplan, ta_dt
                                       hipStream_t stream) {
   ta_status st = check_common(p, dplan, dt, Hq, Hkv, d);
   if (st != TA_OK) return st;
+  const int N = p->n_tokens;
+  if (N == 0) return TA_OK;  // nothing to read or write (empty tensors may be null)
   if (!q || !k || !v || !o || !lse) return TA_EINVAL;
   const size_t need = fwd_ws(p, dt, Hq, Hkv, d, rope_base);
   if (need && (!ws || ws_bytes < need)) return TA_ENOMEM;
-  const int N = p->n_tokens;
-  if (N == 0) return TA_OK;
   if (scale <= 0.f) scale = 1.f / sqrtf((float)d);
   const char* base = (const char*)dplan;
   const int32_t* pos = (const int32_t*)(base + p->off_pos);

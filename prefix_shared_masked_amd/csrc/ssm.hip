@@ -646,9 +646,10 @@ int scan_blocks(const ta_route* R, int C, int vw, unsigned* grid) {
 
 extern "C" ta_status tree_scan_fwd(const ta_route* R, const void* droute, const float* a, const float* b, int32_t C,
                                    float* h, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!R || !droute || !a || !b || !h || C <= 0) return TA_EINVAL;
+  if (!R || !droute || C <= 0) return TA_EINVAL;
+  if (R->n_chunks == 0) return TA_OK;  // no tokens: nothing to read or write
+  if (!a || !b || !h) return TA_EINVAL;
   if ((int64_t)R->n_tokens * C > ((int64_t)1 << 40)) return TA_ERANGE;
-  if (R->n_chunks == 0) return TA_OK;
   const bool v4 = scan_vec4(C, {a, b, h});
   unsigned grid;
   const int nkb = scan_blocks(R, C, v4 ? 4 : 1, &grid);
@@ -671,9 +672,10 @@ extern "C" ta_status tree_scan_fwd(const ta_route* R, const void* droute, const 
 extern "C" ta_status tree_scan_bwd(const ta_route* R, const void* droute, const float* a, const float* h,
                                    const float* dh, int32_t C, float* da, float* db, void* ws, size_t ws_bytes,
                                    hipStream_t stream) {
-  if (!R || !droute || !a || !h || !dh || !da || !db || C <= 0) return TA_EINVAL;
+  if (!R || !droute || C <= 0) return TA_EINVAL;
+  if (R->n_chunks == 0) return TA_OK;  // no tokens: nothing to read or write
+  if (!a || !h || !dh || !da || !db) return TA_EINVAL;
   if ((int64_t)R->n_tokens * C > ((int64_t)1 << 40)) return TA_ERANGE;
-  if (R->n_chunks == 0) return TA_OK;
   const bool v4 = scan_vec4(C, {a, h, dh, da, db});
   unsigned grid;
   const int nkb = scan_blocks(R, C, v4 ? 4 : 1, &grid);
@@ -741,8 +743,9 @@ void conv_bwd_k(const ta_route* R, const RouteDev& d, const float* x, const floa
 
 extern "C" ta_status tree_conv_fwd(const ta_route* R, const void* droute, const float* x, const float* w, int32_t C,
                                    float* y, hipStream_t stream) {
-  if (!R || !droute || !x || !w || !y || C <= 0) return TA_EINVAL;
-  if (R->n_tokens == 0) return TA_OK;
+  if (!R || !droute || C <= 0) return TA_EINVAL;
+  if (R->n_tokens == 0) return TA_OK;  // nothing to read or write
+  if (!x || !w || !y) return TA_EINVAL;
   if (!grid_fits((uint64_t)((R->n_tokens + ssm::TG - 1) / ssm::TG) * ((C + ssm::TH - 1) / ssm::TH), ssm::TH))
     return TA_ERANGE;
   const RouteDev d = dev_tables(R, droute);
@@ -757,8 +760,15 @@ extern "C" ta_status tree_conv_fwd(const ta_route* R, const void* droute, const 
 extern "C" ta_status tree_conv_bwd(const ta_route* R, const void* droute, const float* x, const float* w,
                                    const float* dy, int32_t C, float* dx, float* dw, void* ws, size_t ws_bytes,
                                    hipStream_t stream) {
-  if (!R || !droute || !x || !w || !dy || !dx || !dw || C <= 0) return TA_EINVAL;
-  if (R->n_tokens == 0) return TA_OK;
+  if (!R || !droute || C <= 0) return TA_EINVAL;
+  if (R->n_tokens == 0) {  // no tokens: dw = 0, nothing else to read or write
+    if (!dw) return TA_EINVAL;
+    hipLaunchKernelGGL(ssm::conv_dw_sum, dim3((C * R->conv_k + ssm::TH - 1) / ssm::TH), dim3(ssm::TH), 0, stream,
+                       (const float*)nullptr, 0, C, R->conv_k, dw);
+    TA_LAUNCH_CHECK();
+    return TA_OK;
+  }
+  if (!x || !w || !dy || !dx || !dw) return TA_EINVAL;
   const int nb = (R->n_tokens + ssm::TOKB - 1) / ssm::TOKB;
   if (!grid_fits((uint64_t)nb * ((C + ssm::TH - 1) / ssm::TH), ssm::TH)) return TA_ERANGE;
   const size_t need = conv_ws(R, C);

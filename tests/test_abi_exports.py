@@ -122,3 +122,29 @@ def test_validation_before_launch_new_calls():
     assert L.tree_scan_bwd(route.handle, fake, fake, fake, fake, 0, fake, fake, fake, 1 << 20, None) == 1
     assert L.tree_conv_bwd(route.handle, fake, fake, fake, fake, 8, fake, fake, fake, 16, None) == 4
     assert L.tree_scan_ws_bytes(route.handle, 8, ctypes.byref(n)) == 0 and n.value >= route.n_chunks * 8 * 4
+
+
+def test_empty_plan_calls_touch_no_pointer():
+    """A plan (or route) without tokens: the attention, scan and conv-forward
+    calls return TA_OK after checking the plan, heads, d and dtype, before any
+    tensor pointer is read, so empty tensors (null data pointers) are fine;
+    invalid heads or d still fail first."""
+    L = pkg.load_library()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # a device plan / route stand-in, never dereferenced
+    plan = pkg.tree_plan([-1, 0], [0, 0])
+    assert plan.n_tokens == 0
+    assert L.tree_attn_fwd(plan.handle, fake, 1, None, None, None, 4, 2, 128, 0.0, 10000.0, None, None, None, 0,
+                           None) == 0
+    assert L.tree_attn_bwd(plan.handle, fake, 1, None, None, None, None, None, None, 4, 2, 128, 0.0, 10000.0,
+                           None, None, None, None, 0, None) == 0
+    assert L.tree_attn_fwd(plan.handle, fake, 1, None, None, None, 3, 2, 128, 0.0, 0.0, None, None, None, 0,
+                           None) == 1
+    assert L.tree_attn_bwd(plan.handle, fake, 1, None, None, None, None, None, None, 4, 2, 64, 0.0, 0.0,
+                           None, None, None, None, 0, None) == 5
+    route = pkg.tree_route(plan, 4)
+    assert route.n_chunks == 0
+    assert L.tree_scan_fwd(route.handle, fake, None, None, 8, None, None, 0, None) == 0
+    assert L.tree_scan_bwd(route.handle, fake, None, None, None, 8, None, None, None, 0, None) == 0
+    assert L.tree_conv_fwd(route.handle, fake, None, None, 8, None, None) == 0
+    assert L.tree_scan_fwd(route.handle, fake, None, None, 0, None, None, 0, None) == 1

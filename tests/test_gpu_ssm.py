@@ -140,3 +140,26 @@ def test_spine_full_size_sampled_channels():
     """The spine workload (16,352 tokens) at 4,096 channels: every token of
     eight sampled channels (the channels are independent) against the oracle."""
     run(W.spine_tree(), 4096, 4, 7, chans=[0, 1, 255, 256, 1023, 2048, 4000, 4095])
+
+
+def test_empty_tree_through_the_binding():
+    """A tree whose nodes hold no token: attention forward and backward, the
+    scan and the conv run through the binding on empty tensors and return
+    empty results; the conv backward's dw comes back zero."""
+    plan = pkg.tree_plan(np.array([-1, 0], np.int32), np.array([0, 0], np.int32))
+    assert plan.n_tokens == 0
+    q = torch.empty(0, 4, 128, device=DEV, dtype=torch.bfloat16)
+    k = torch.empty(0, 2, 128, device=DEV, dtype=torch.bfloat16)
+    o, lse = pkg.tree_attn_fwd(plan, q, k, k, rope_base=10000.0)
+    dq, dk, dv = pkg.tree_attn_bwd(plan, q, k, k, o, lse, q, rope_base=10000.0)
+    assert o.shape == (0, 4, 128) and lse.numel() == 0 and dq.shape == (0, 4, 128) and dk.shape == (0, 2, 128)
+    route = pkg.tree_route(plan, 4)
+    a = torch.empty(0, 64, device=DEV)
+    h = pkg.tree_scan_fwd(route, a, a)
+    da, db = pkg.tree_scan_bwd(route, a, h, a)
+    w = torch.randn(64, 4, device=DEV)
+    y = pkg.tree_conv_fwd(route, a, w)
+    dx, dw = pkg.tree_conv_bwd(route, a, w, a, dw=torch.full((64, 4), 7.0, device=DEV))
+    torch.cuda.synchronize()
+    assert h.numel() == da.numel() == y.numel() == dx.numel() == 0
+    assert torch.equal(dw, torch.zeros_like(dw))
