@@ -494,6 +494,10 @@ typedef struct ta_route_view {
   const int32_t* cprev;     /* [N][conv_k - 1]: the j-th path predecessor of t (j = 1..), -1 past the root */
   const int32_t* succ_ptr;  /* [N + 1] CSR: the (t, j) whose j-th predecessor is s, */
   const int32_t* succ;      /* encoded t * conv_k + j, ascending t */
+  const int32_t* kid_ptr;   /* [n_chunks + 1] CSR: the child chunks of each chunk (those whose */
+  const int32_t* kid;       /* parent it is), each list in descending chunk order */
+  const int32_t* order;     /* [n_chunks]: the chunks by depth in the chunk tree, ties in DFS order
+                               (the scan's work order; parents before children) */
 } ta_route_view;
 ta_status tree_route(const ta_plan* plan, int32_t conv_k, ta_route** out);
 ta_status tree_route_view(const ta_route* route, ta_route_view* view);

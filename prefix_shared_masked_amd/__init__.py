@@ -70,7 +70,8 @@ class _PartView(ctypes.Structure):
 
 class _RouteView(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("n_tokens", "n_chunks", "chunk", "conv_k")] + \
-        [(n, ctypes.POINTER(ctypes.c_int32)) for n in ("chunks", "cprev", "succ_ptr", "succ")]
+        [(n, ctypes.POINTER(ctypes.c_int32)) for n in ("chunks", "cprev", "succ_ptr", "succ", "kid_ptr", "kid",
+                                                         "order")]
 
 
 _lib = None
@@ -356,9 +357,11 @@ class Route:
         def arr(name, n):
             return np.zeros(0, np.int32) if n == 0 else np.ctypeslib.as_array(getattr(self._v, name), shape=(n,)).copy()
         sp = arr("succ_ptr", self.n_tokens + 1)
+        kp = arr("kid_ptr", self.n_chunks + 1)
         return dict(chunks=arr("chunks", 4 * self.n_chunks).reshape(-1, 4),
                     cprev=arr("cprev", self.n_tokens * (self.conv_k - 1)).reshape(self.n_tokens, self.conv_k - 1),
-                    succ_ptr=sp, succ=arr("succ", int(sp[-1])))
+                    succ_ptr=sp, succ=arr("succ", int(sp[-1])),
+                    kid_ptr=kp, kid=arr("kid", int(kp[-1])), order=arr("order", self.n_chunks))
 
     @property
     def handle(self):

@@ -149,6 +149,9 @@ extern "C" ta_status tree_route_view(const ta_route* R, ta_route_view* v) {
   v->cprev = R->cprev.data();
   v->succ_ptr = R->succ_ptr.data();
   v->succ = R->succ.data();
+  v->kid_ptr = R->kid_ptr.data();
+  v->kid = R->kid.data();
+  v->order = R->order.data();
   return TA_OK;
 }
 

@@ -47,6 +47,19 @@ def check(tree, K):
     sp, sc = v["succ_ptr"], v["succ"]
     for s_ in range(N):
         assert list(sc[sp[s_]:sp[s_ + 1]]) == inv.get(s_, [])
+    # child chunks: exactly the chunks naming c as parent, descending
+    n = len(ch)
+    kp, kid = v["kid_ptr"], v["kid"]
+    assert len(kp) == n + 1 and kp[0] == 0
+    for c in range(n):
+        assert list(kid[kp[c]:kp[c + 1]]) == [q for q in range(n - 1, -1, -1) if ch[q, 2] == c]
+    # the work order: every chunk once, by depth in the chunk tree, ties ascending
+    depth = np.zeros(n, np.int64)
+    for c in range(n):  # a parent chunk precedes its children
+        if ch[c, 2] >= 0:
+            assert ch[c, 2] < c
+            depth[c] = depth[ch[c, 2]] + 1
+    assert list(v["order"]) == sorted(range(n), key=lambda c: (depth[c], c))
 
 
 @pytest.mark.parametrize("K", [1, 2, 4, 8])
