@@ -22,7 +22,7 @@ import os
 import numpy as np
 
 __all__ = ["TreeAttnError", "Plan", "Partition", "HipEvents", "tree_plan", "tree_partition", "tree_attn_fwd",
-           "saturation_flag", "clear_saturation_flag",
+           "saturation_flag", "clear_saturation_flag", "scan_wait_timed_out",
            "tree_attn_bwd", "tree_partition_fwd", "tree_partition_bwd", "tree_weighted_nll", "tree_lmhead_nll",
            "Route", "tree_route", "tree_scan_fwd", "tree_scan_bwd", "tree_conv_fwd", "tree_conv_bwd",
            "tree_decode_splitkv", "library_path", "load_library", "TA_BLOCK_M", "TA_BLOCK_N", "TA_BLOCK_KV"]
@@ -484,6 +484,13 @@ def saturation_flag(ws) -> int:
 def clear_saturation_flag(ws) -> None:
     """Zero the saturation flag of a workspace (asynchronously, on the current stream)."""
     ws[:4].zero_()
+
+
+def scan_wait_timed_out(ws) -> bool:
+    """After tree_scan_fwd/bwd with workspace ws: whether a wait for a
+    published value ran out (word 1 of the workspace; the outputs are then not
+    valid).  A synchronising read."""
+    return int(ws[4:8].view(__import__("torch").int32).item()) != 0
 
 
 def _workspace(nbytes, device, ws):

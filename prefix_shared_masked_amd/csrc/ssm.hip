@@ -74,7 +74,7 @@ struct Vec<4> {
 // ticket order rules out) sets the workspace's timeout word and goes on with
 // zero, so the kernel always exits.
 constexpr int SCAN_CHUNK = 128;  // most tokens a route chunk holds
-constexpr int SPIN_MAX = 1 << 20;
+constexpr int SPIN_MAX = 1 << 22;  // polls of at least ~100 cycles each: seconds, far past any real wait
 
 // The sum, in list order, of the VW-channel values published at
 // p + idx[e] * stride for e in [e0, e1) (idx null: the single index e0);

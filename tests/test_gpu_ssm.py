@@ -35,7 +35,7 @@ def check_scan_header(ws, route, C):
     ticket, timeout = (int(v) for v in ws[:8].view(torch.int32).cpu())
     block = 256 if C % 4 == 0 else 64
     assert ticket == route.n_chunks * ((C + block - 1) // block)
-    assert timeout == 0
+    assert timeout == 0 and not pkg.scan_wait_timed_out(ws)
 
 
 def run(tree, C, K, seed, chans=None):
