@@ -99,11 +99,42 @@ __device__ __forceinline__ void tile_loop(const Params& P, char* ring, Epi&& epi
   const int nk = P.Dm / KS;
   const int total = (vt1 - vt0) * nk;
 
-  auto issue = [&](int p) {
-    const int vt = vt0 + p / nk, kk = p % nk;
-    char* buf = ring + (p % NBUF) * STAGE_BYTES;
-    stage_tile(P.W, vt * BV, P.V, P.Dm, kk * KS, buf);
-    stage_tile(P.h, t0, P.N, P.Dm, kk * KS, buf + TILE_BYTES);
+  // Copy i of a stage fills rows 16 q .. 16 q + 15 (q = wave + 4 i) of each
+  // tile (stage_tile's lane map): with a scalar base at the stage's first row
+  // and k column, each lane's byte offset is fixed, the token rows clamped to
+  // the last token once; a vocabulary tile that runs past the last row takes
+  // the clamped stage_tile.  The stages are issued in order, so a cursor (vt,
+  // kk) replaces the division of the stage index.
+  const int l = threadIdx.x & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t offw[4], offh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * (wu + 4 * i) + (l >> 2);
+    const int piece = (l & 3) ^ swz4(row);
+    offw[i] = (uint32_t)(row * P.Dm + piece * 8) * 2u;
+    offh[i] = (uint32_t)(min(row, P.N - 1 - t0) * P.Dm + piece * 8) * 2u;
+  }
+  const uint32_t lds0 = lds_addr(ring);
+  int iv = vt0, ik = 0, ip = 0;  // the next stage to issue: vocabulary tile, k stage, index
+  auto issue = [&]() {
+    const uint32_t lb = lds0 + (ip % NBUF) * STAGE_BYTES;
+    const int k0 = ik * KS;
+    if ((iv + 1) * BV <= P.V) {
+      const bf16* wb = P.W + ((size_t)iv * BV * P.Dm + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) copy16_to_lds_s(wb, offw[i], lb + (wu + 4 * i) * 1024);
+    } else {
+      stage_tile(P.W, iv * BV, P.V, P.Dm, k0, ring + (ip % NBUF) * STAGE_BYTES);
+    }
+    const bf16* hb = P.h + ((size_t)t0 * P.Dm + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy16_to_lds_s(hb, offh[i], lb + TILE_BYTES + (wu + 4 * i) * 1024);
+    ++ip;
+    if (++ik == nk) {
+      ik = 0;
+      ++iv;
+    }
   };
 
   // per-lane LDS offsets: vocab tile i at abase + 2048 i, token tile j at
@@ -120,7 +151,7 @@ __device__ __forceinline__ void tile_loop(const Params& P, char* ring, Epi&& epi
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   agpr_fence16(acc);
 
-  for (int p = 0; p < min(NBUF - 1, total); ++p) issue(p);
+  for (int p = 0; p < min(NBUF - 1, total); ++p) issue();
   for (int it = 0; it < total; ++it) {
     // this wave's copies of stage `it` have landed once at most the copies of
     // the stages issued after it (8 per stage) are outstanding
@@ -129,7 +160,7 @@ __device__ __forceinline__ void tile_loop(const Params& P, char* ring, Epi&& epi
     else if (after == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // every wave's copies landed; every wave is done with stage it - 1
-    if (it + NBUF - 1 < total) issue(it + NBUF - 1);  // refills the buffer of stage it - 1
+    if (it + NBUF - 1 < total) issue();  // stage it + NBUF - 1 refills the buffer of stage it - 1
     const char* buf = ring + (it % NBUF) * STAGE_BYTES;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -377,13 +408,54 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams G) {
   const int c0 = blockIdx.x * 256, d0 = blockIdx.y * 256;
   const int total = G.K / KS;
 
+  // The copies' per-lane byte offsets do not change from stage to stage (the
+  // lane-to-row and lane-to-piece maps of stage_krows / stage_tile, with the
+  // column clamps), so a stage whose k rows all exist issues each copy from a
+  // scalar base (the stage's first k row) plus that fixed offset; only the
+  // stage that runs past the last row takes the clamped path.
+  const int l = threadIdx.x & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t offa[4], offb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = wu + 4 * i;
+    const int row = 2 * q + (l >> 5), slot = l & 31;
+    const int piece = (((slot >> 1) ^ (2 * (row & 3))) << 1) | (slot & 1);
+    offa[i] = (uint32_t)(row * G.lda + min(d0 + 8 * piece, G.a_cmax - 8)) * 2u;
+    if (B_KC) {
+      const int brow = 16 * q + (l >> 2);
+      const int bpiece = (l & 3) ^ swz4(brow);
+      offb[i] = (uint32_t)((size_t)min(c0 + brow, G.b_rmax) * G.ldb + bpiece * 8) * 2u;
+    } else {
+      offb[i] = (uint32_t)(row * G.ldb + min(c0 + 8 * piece, G.b_cmax - 8)) * 2u;
+    }
+  }
+  const uint32_t lds0 = lds_addr(ring);
+  // (dS rows addressed by 32-bit offsets from the stage's column while the
+  // whole operand spans less than 4 GiB)
+  const bool b_off32 = (size_t)(G.b_rmax + 1) * G.ldb * 2 < ((size_t)1 << 32);
   auto issue = [&](int p) {
     char* buf = ring + (p % NBUF) * STAGE_BYTES;
-    stage_krows(G.A, G.lda, G.a_rmax, G.a_cmax, p * KS, d0, buf);
-    if (B_KC)
-      stage_tile(G.B, c0, G.b_rmax + 1, G.ldb, p * KS, buf + TILE_BYTES);
-    else
-      stage_krows(G.B, G.ldb, G.b_rmax, G.b_cmax, p * KS, c0, buf + TILE_BYTES);
+    const uint32_t lb = lds0 + (p % NBUF) * STAGE_BYTES;
+    const int k0 = p * KS;
+    if (k0 + KS - 1 <= G.a_rmax) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) copy16_to_lds_s(G.A + (size_t)k0 * G.lda, offa[i], lb + (wu + 4 * i) * 1024);
+    } else {
+      stage_krows(G.A, G.lda, G.a_rmax, G.a_cmax, k0, d0, buf);
+    }
+    if (B_KC && b_off32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) copy16_to_lds_s(G.B + k0, offb[i], lb + TILE_BYTES + (wu + 4 * i) * 1024);
+    } else if (B_KC) {
+      stage_tile(G.B, c0, G.b_rmax + 1, G.ldb, k0, buf + TILE_BYTES);
+    } else if (k0 + KS - 1 <= G.b_rmax) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        copy16_to_lds_s(G.B + (size_t)k0 * G.ldb, offb[i], lb + TILE_BYTES + (wu + 4 * i) * 1024);
+    } else {
+      stage_krows(G.B, G.ldb, G.b_rmax, G.b_cmax, k0, c0, buf + TILE_BYTES);
+    }
   };
 
   // Transpose-read offsets (bytes) in a k-row tile for MFMA tile t (32
