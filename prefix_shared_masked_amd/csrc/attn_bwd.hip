@@ -503,13 +503,13 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
     sbuf = sbuf + 1 == KV_NBUF ? 0 : sbuf + 1;
   };
   // Each wavefront issues two copies per step (wavefront 0 three), role B
-  // after its two dS stores.  Vector memory operations complete in issue
+  // two dS stores after them.  Vector memory operations complete in issue
   // order, so "at most six outstanding" at the end of step j means the
   // copies of the items up to j + 2 (all the next step reads) have landed:
-  // for role A the six are the copies of items j + 3 .. j + 5, for role B
-  // at most the copies of j + 4 and j + 5 and this step's stores (the dS
-  // stores of earlier steps must then be acknowledged, two steps after
-  // their issue).
+  // for role A the six are the copies of items j + 3 .. j + 5; for role B
+  // they are this step's copies and stores and the stores of step j - 1, so
+  // the copies of j + 4 and everything before them (the stores of step
+  // j - 2 included) have completed.
   auto end_step = []() {
     asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     __syncthreads();
@@ -558,13 +558,14 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
       for (int s = 0; s < 8; ++s)
         Sa = mfma32h(*(const f16x8*)(b0 + L::Q16 + koff[s]), __builtin_bit_cast(f16x8, fr[s]), Sa);
     }
-    // One step per item j: first the operands of the step's first MFMAs
-    // are requested, then S(j) (computed in the previous step) is masked and
-    // exponentiated and P(j) handed to role B; then the score MFMAs of item
-    // j + 1 (a dependent chain) alternate with the dV += P(j)^T dO(j) MFMAs
-    // (independent of it), so the matrix unit always has a ready MFMA.  The
-    // copies of item j + 5 go out among them.  LDS operands are read two
-    // MFMA pairs ahead.  The source order is the issue order.
+    // One step per item j, in two runs of eight MFMAs.  The score MFMAs of
+    // item j + 1 (a dependent chain) carry the element mask's result and the
+    // exponentials of S(j) (computed in the previous step) between them, so
+    // the VALU work of a step runs while this wavefront's own MFMAs do; then
+    // the dV += P(j)^T dO(j) MFMAs (d-tiles innermost, so consecutive ones are
+    // independent), with P(j) handed to role B through LDS among them.  The
+    // copies of item j + 5 go out in the first run.  LDS operands are read two
+    // MFMAs ahead.  The source order is the issue order.
     auto step = [&](int j, f32x16& Sg, f32x16& Sn) {
       const char* gb = buf(cb);
       const char* nb = buf(next_buf(cb));
@@ -577,41 +578,42 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
       };
       seed(nb, Sn);
       qa[0] = *(const f16x8*)(nb + L::Q16 + koff[0]);
-      read_od(0);
       qa[1] = *(const f16x8*)(nb + L::Q16 + koff[1]);
-      read_od(1);
       if (qb < kw + SUB || qb + SUB > rhi || wkeys < SUB) {
         const int d0 = qb + 4 * half - key;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if ((unsigned)(d0 + 8 * (r >> 2) + (r & 3)) >= lim) Sg[r] = -INFINITY;
       }
-      bf16x8 pa[2];
-      {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = exp2f_fast(Sg[r]);
-        char* const xp = xch + (j & 1) * (4 * KV_XCH);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pa[hh][e] = (bf16)p[8 * hh + e];
-          *(f16x8*)(xp + hh * 1024) = pack_f16_rte(p + 8 * hh);
-        }
-      }
       fence();
+      // score MFMAs of item j + 1 with the exponentials of item j between them
+      float p[16];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        if (s < 6) {
-          qa[s + 2] = *(const f16x8*)(nb + L::Q16 + koff[s + 2]);
-          read_od(s + 2);
-        }
+        if (s < 6) qa[s + 2] = *(const f16x8*)(nb + L::Q16 + koff[s + 2]);
+        if (s >= 6) read_od(2 * (s - 6));
         Sn = mfma32h(qa[s], __builtin_bit_cast(f16x8, fr[s]), Sn);
-        mfma32_accv(acc[s >> 1], pa[s & 1], od[s]);
+        p[2 * s] = exp2f_fast(Sg[2 * s]);
+        p[2 * s + 1] = exp2f_fast(Sg[2 * s + 1]);
         if (s == 1) stage_next();
         fence();
       }
-      mfma_operand_hold(pa[0], pa[1], od[6], od[7]);
+      bf16x8 pa[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pa[hh][e] = (bf16)p[8 * hh + e];
+      fence();
+      char* const xp = xch + (j & 1) * (4 * KV_XCH);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = 2 * (u & 3) + (u >> 2);  // d-tiles innermost: consecutive MFMAs are independent
+        if (u < 6) read_od(2 * ((u + 2) & 3) + ((u + 2) >> 2));
+        acc[s >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s & 1], od[s], acc[s >> 1], 0, 0, 0);
+        if (u == 2) *(f16x8*)xp = pack_f16_rte(p);
+        if (u == 3) *(f16x8*)(xp + 1024) = pack_f16_rte(p + 8);
+        fence();
+      }
       cb = next_buf(cb);
       adv(ibi, ig);
     };
@@ -666,12 +668,12 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
       stage_next();
       end_step();
     }
-    // Step j: first the operands of the step's first MFMAs are requested,
-    // then dS(j - 1) = P dP is formed (the P role A handed over in step
-    // j - 1, dP from the previous step) and stored; then the dP MFMAs of item
-    // j (unless `last`; a dependent chain) alternate with the
-    // dK += dS(j - 1)^T Q(j - 1) MFMAs, with the copies of item j + 5 among
-    // them.  LDS operands are read two MFMA pairs ahead.
+    // Step j, in two runs of eight MFMAs: the dP MFMAs of item j (unless
+    // `last`; a dependent chain) with dS(j - 1) = P dP formed between them
+    // (the P role A handed over in step j - 1, dP from the previous step),
+    // then dK += dS(j - 1)^T Q(j - 1) (d-tiles innermost) with the two dS
+    // stores among them.  The copies of item j + 5 go out in the first run.
+    // LDS operands are read two MFMAs ahead.
     auto step = [&](int j, f32x16& dPg, f32x16& dPn, bool last) {
       const char* gb = buf(cb);               // item j - 1: transpose-read Q
       const char* nb = buf(next_buf(cb));     // item j: dO rows and -D
@@ -688,44 +690,44 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
       if (!last) {
         seed(nb, dPn);
         oa[0] = *(const bf16x8*)(nb + L::DO + koff[0]);
-      }
-      read_oq(0);
-      if (!last) oa[1] = *(const bf16x8*)(nb + L::DO + koff[1]);
-      read_oq(1);
-      f16x8 sa[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const f16x8 ph = hh ? ph1 : ph0;
-        float ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ds[e] = (float)ph[e] * dPg[8 * hh + e];
-        sa[hh] = pack_f16_rtz(ds);
-      }
-      // dS of item j - 1 (block qb is query tile (qb - q0) / 32) in the
-      // register-order layout of ds_elem: each of the two stores writes one
-      // contiguous 1 KiB plane; into the spare block when the sub-tile does
-      // not own it (the store stays unconditional).  Non-temporal: dS is
-      // read once, by the dQ pass.
-      if (DS) {
-        f16* blk = P.ds_spare;
-        const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
-        if (own) blk = P.ds + (((size_t)kvr * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * G + ig) * (SUB * SUB);
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[0]), (u32x4*)(blk + ds_lane0));
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[1]), (u32x4*)(blk + ds_lane1));
+        oa[1] = *(const bf16x8*)(nb + L::DO + koff[1]);
       }
       fence();
+      // dP MFMAs of item j with dS(j - 1) = P dP formed between them
+      float ds[16];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        if (s < 6) {
-          if (!last) oa[s + 2] = *(const bf16x8*)(nb + L::DO + koff[s + 2]);
-          read_oq(s + 2);
+        if (!last) {
+          if (s < 6) oa[s + 2] = *(const bf16x8*)(nb + L::DO + koff[s + 2]);
         }
+        if (s >= 6) read_oq(2 * (s - 6));
         if (!last) dPn = mfma32(oa[s], __builtin_bit_cast(bf16x8, fr[s]), dPn);
-        mfma32h_accv(acc[s >> 1], sa[s & 1], oq[s]);
+        {
+          const f16x8 ph = s < 4 ? ph0 : ph1;
+          ds[2 * s] = (float)ph[(2 * s) & 7] * dPg[2 * s];
+          ds[2 * s + 1] = (float)ph[(2 * s + 1) & 7] * dPg[2 * s + 1];
+        }
         if (s == 1 && !last) stage_next();
         fence();
       }
-      mfma_operand_hold(sa[0], sa[1], oq[6], oq[7]);
+      f16x8 sa[2];
+      sa[0] = pack_f16_rtz(ds);
+      sa[1] = pack_f16_rtz(ds + 8);
+      f16* blk = P.ds_spare;
+      if (DS) {
+        const bool own = wkeys > 0 && qb < rhi && qb + SUB > rlo;
+        if (own) blk = P.ds + (((size_t)kvr * P.n_dsblk + dsoff + ((qb - P.q0) >> 5)) * G + ig) * (SUB * SUB);
+      }
+      fence();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = 2 * (u & 3) + (u >> 2);  // d-tiles innermost: consecutive MFMAs are independent
+        if (u < 6) read_oq(2 * ((u + 2) & 3) + ((u + 2) >> 2));
+        acc[s >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[s & 1], oq[s], acc[s >> 1], 0, 0, 0);
+        if (DS && u == 2) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[0]), (u32x4*)(blk + ds_lane0));
+        if (DS && u == 3) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[1]), (u32x4*)(blk + ds_lane1));
+        fence();
+      }
       cb = next_buf(cb);
       adv(ibi, ig);
     };

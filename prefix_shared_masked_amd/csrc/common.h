@@ -51,23 +51,9 @@ __device__ __forceinline__ void agpr_fence8(f32x16 (&x)[4], f32x16 (&y)[4]) {
                : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
 }
 
-// The same accumulating MFMAs with the accumulator in arch VGPRs (for
-// kernels that run two wavefronts per SIMD, where arch VGPRs and AGPRs share
-// one budget of 256 and a fixed AGPR block would leave too few arch VGPRs).
-__device__ __forceinline__ void mfma32_accv(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32h_accv(f32x16& acc, const f16x8& a, const f16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-// Keeps the A/B operand registers of the last accumulating MFMAs of a step
-// from being rewritten for 32 wait states after their issue: the compiler
-// cannot see the MFMAs inside the asm statements, and a chained MFMA waiting
-// on its predecessor's accumulator still reads them after it issues.
-template <typename A, typename B>
-__device__ __forceinline__ void mfma_operand_hold(A& a0, A& a1, B& b0, B& b1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1));
-}
+// Wait states between VALU writes of accumulators (zero init) and the first
+// MFMA, and between the last MFMA writes and the epilogue reads; the
+// accumulators are asm operands, so neither can move across the fence.
 __device__ __forceinline__ void acc_fence4(f32x16 (&x)[4]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
 }
