@@ -504,12 +504,12 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
   };
   // Each wavefront issues two copies per step (wavefront 0 three), role B
   // two dS stores after them.  Vector memory operations complete in issue
-  // order, so "at most six outstanding" at the end of step j means the
-  // copies of the items up to j + 2 (all the next step reads) have landed:
-  // for role A the six are the copies of items j + 3 .. j + 5; for role B
-  // they are this step's copies and stores and the stores of step j - 1, so
-  // the copies of j + 4 and everything before them (the stores of step
-  // j - 2 included) have completed.
+  // order.  At the end of step j the items up to j + 3 must have landed (the
+  // next step reads item j + 3 ahead, see end_step_a): role A allows four
+  // outstanding operations (the copies of items j + 4 and j + 5; wavefront 0
+  // six).  Role B allows six: this step's copies and stores and the stores of
+  // step j - 1, so its copies of j + 4 and everything before them (the
+  // stores of step j - 2 included) have completed.
   auto end_step = []() {
     asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     __syncthreads();
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
 
 #pragma unroll
   for (int i = 0; i < 5; ++i) stage_next();
-  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // items 0 and 1 landed
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // items 0, 1 and 2 landed
   __syncthreads();
 
   if (!roleB) {
@@ -558,6 +558,25 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
       for (int s = 0; s < 8; ++s)
         Sa = mfma32h(*(const f16x8*)(b0 + L::Q16 + koff[s]), __builtin_bit_cast(f16x8, fr[s]), Sa);
     }
+    f16x8 qn0, qn1;  // the first two Q operands of the next step's score MFMAs
+    {
+      const char* b1 = buf(1);
+      seed(b1, Sb);
+      qn0 = *(const f16x8*)(b1 + L::Q16 + koff[0]);
+      qn1 = *(const f16x8*)(b1 + L::Q16 + koff[1]);
+    }
+    // At the end of step j every wavefront has waited for its copies of the
+    // items up to j + 3 (role A: four copies of items j + 4, j + 5 may be
+    // outstanding, six for wavefront 0, which also copies the seed records;
+    // role B: six, see below), so after the barrier the items up to j + 3 are
+    // in LDS and step j + 1 may read item j + 3 ahead of its own barrier.
+    auto end_step_a = [&]() {
+      if (wv == 0)
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      __syncthreads();
+    };
     // One step per item j, in two runs of eight MFMAs.  The score MFMAs of
     // item j + 1 (a dependent chain) carry the element mask's result and the
     // exponentials of S(j) (computed in the previous step) between them, so
@@ -565,10 +584,14 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
     // the dV += P(j)^T dO(j) MFMAs (d-tiles innermost, so consecutive ones are
     // independent), with P(j) handed to role B through LDS among them.  The
     // copies of item j + 5 go out in the first run.  LDS operands are read two
-    // MFMAs ahead.  The source order is the issue order.
+    // MFMAs ahead; the seed and first two operands of the next step's score
+    // MFMAs (item j + 2) are read at the end of the second run, so the next
+    // step's first MFMA waits for no LDS read.  The source order is the issue
+    // order.
     auto step = [&](int j, f32x16& Sg, f32x16& Sn) {
       const char* gb = buf(cb);
       const char* nb = buf(next_buf(cb));
+      const char* nnb = buf(next_buf(next_buf(cb)));  // item j + 2
       const int qb = qlo + SUB * ibi;
       f16x8 qa[8];
       bf16x8 od[8];  // transpose reads of dO(j): MFMA m = 2 dt + qs
@@ -576,9 +599,8 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
         const char* o = gb + L::DO + (m & 1) * 16 * D * 2;
         od[m] = cat(lds_read_tr((const bf16*)(o + toff[m >> 1][0])), lds_read_tr((const bf16*)(o + toff[m >> 1][1])));
       };
-      seed(nb, Sn);
-      qa[0] = *(const f16x8*)(nb + L::Q16 + koff[0]);
-      qa[1] = *(const f16x8*)(nb + L::Q16 + koff[1]);
+      qa[0] = qn0;  // Sn already holds its seed
+      qa[1] = qn1;
       if (qb < kw + SUB || qb + SUB > rhi || wkeys < SUB) {
         const int d0 = qb + 4 * half - key;
 #pragma unroll
@@ -612,6 +634,11 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
         acc[s >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s & 1], od[s], acc[s >> 1], 0, 0, 0);
         if (u == 2) *(f16x8*)xp = pack_f16_rte(p);
         if (u == 3) *(f16x8*)(xp + 1024) = pack_f16_rte(p + 8);
+        if (u == 6) seed(nnb, Sg);  // S(j) is spent: it becomes S(j + 2)'s seed
+        if (u == 7) {
+          qn0 = *(const f16x8*)(nnb + L::Q16 + koff[0]);
+          qn1 = *(const f16x8*)(nnb + L::Q16 + koff[1]);
+        }
         fence();
       }
       cb = next_buf(cb);
@@ -619,10 +646,10 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
     };
     for (int j = 0; j < nitem; j += 2) {
       step(j, Sa, Sb);
-      end_step();
+      end_step_a();
       if (j + 1 >= nitem) break;
       step(j + 1, Sb, Sa);
-      end_step();
+      end_step_a();
     }
     lds_copies_wait();
     acc_fence4(acc);
@@ -666,17 +693,30 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
       for (int s = 0; s < 8; ++s)
         dPa = mfma32(*(const bf16x8*)(b0 + L::DO + koff[s]), __builtin_bit_cast(bf16x8, fr[s]), dPa);
       stage_next();
-      end_step();
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // items up to 3 landed
+      __syncthreads();
+    }
+    // the first two dO operands of the next step's dP MFMAs; step j + 1's dP
+    // seed is written into the spent dP(j - 1)
+    bf16x8 on0, on1;
+    {
+      const char* b1 = buf(1);
+      seed(b1, dPb);
+      on0 = *(const bf16x8*)(b1 + L::DO + koff[0]);
+      on1 = *(const bf16x8*)(b1 + L::DO + koff[1]);
     }
     // Step j, in two runs of eight MFMAs: the dP MFMAs of item j (unless
     // `last`; a dependent chain) with dS(j - 1) = P dP formed between them
     // (the P role A handed over in step j - 1, dP from the previous step),
     // then dK += dS(j - 1)^T Q(j - 1) (d-tiles innermost) with the two dS
     // stores among them.  The copies of item j + 5 go out in the first run.
-    // LDS operands are read two MFMAs ahead.
+    // LDS operands are read two MFMAs ahead; the seed and first two operands
+    // of the next step's dP MFMAs (item j + 1) are read at the end of the
+    // second run.
     auto step = [&](int j, f32x16& dPg, f32x16& dPn, bool last) {
       const char* gb = buf(cb);               // item j - 1: transpose-read Q
       const char* nb = buf(next_buf(cb));     // item j: dO rows and -D
+      const char* nnb = buf(next_buf(next_buf(cb)));  // item j + 1
       const int qb = qlo + SUB * ibi;
       bf16x8 oa[8];
       f16x8 oq[8];  // transpose reads of Q(j - 1): MFMA m = 2 dt + qs
@@ -688,9 +728,8 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
       const f16x8 ph0 = *(const f16x8*)xp;
       const f16x8 ph1 = *(const f16x8*)(xp + 1024);
       if (!last) {
-        seed(nb, dPn);
-        oa[0] = *(const bf16x8*)(nb + L::DO + koff[0]);
-        oa[1] = *(const bf16x8*)(nb + L::DO + koff[1]);
+        oa[0] = on0;
+        oa[1] = on1;
       }
       fence();
       // dP MFMAs of item j with dS(j - 1) = P dP formed between them
@@ -726,6 +765,11 @@ __global__ __launch_bounds__(512, 1) void dkv_bf16_kernel(KVParams P) {
         acc[s >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[s & 1], oq[s], acc[s >> 1], 0, 0, 0);
         if (DS && u == 2) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[0]), (u32x4*)(blk + ds_lane0));
         if (DS && u == 3) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sa[1]), (u32x4*)(blk + ds_lane1));
+        if (!last && u == 6) seed(nnb, dPg);  // item j + 1
+        if (!last && u == 7) {
+          on0 = *(const bf16x8*)(nnb + L::DO + koff[0]);
+          on1 = *(const bf16x8*)(nnb + L::DO + koff[1]);
+        }
         fence();
       }
       cb = next_buf(cb);
