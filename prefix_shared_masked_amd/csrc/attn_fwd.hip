@@ -36,36 +36,70 @@ namespace ta {
 // RoPE by depth position and/or dtype conversion: y[t, h, :] = mul R(pos[t])
 // x[t, h, :] (transpose=1 gives R^T; base <= 0 converts only), and when y2 is
 // given also y2[t, h, :] = R(pos[t]) x[t, h, :] in bf16.  Rotate-half pairs
-// (i, i + d/2), angle pos * base^(-2i/d); the sine and cosine of a (t, i)
-// pair are computed once and applied to all H heads (consecutive lanes take
-// consecutive i, so every access is coalesced).
+// (i, i + d/2), angle pos * base^(-2i/d).  A thread takes one token and four
+// consecutive pairs (i, i + d/2) .. (i + 3, i + 3 + d/2): the sines and
+// cosines are computed once and applied to all H heads, and every access is
+// a 4-element vector (consecutive threads take consecutive groups of four,
+// so each load and store of a wavefront is one contiguous run per token).
 template <typename T>
-__device__ __forceinline__ T cvt_out(float x, bool&) { return (T)x; }
+__device__ __forceinline__ void ld4(const T* p, float (&v)[4]) {
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  const T4 x = *(const T4*)p;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = (float)x[u];
+}
+template <typename T>
+__device__ __forceinline__ void st4(T* p, const float (&v)[4], bool&) {
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  T4 x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) x[u] = (T)v[u];
+  *(T4*)p = x;
+}
 template <>
-__device__ __forceinline__ f16 cvt_out<f16>(float x, bool& sat) { return to_f16_sat(x, sat); }
+__device__ __forceinline__ void st4<f16>(f16* p, const float (&v)[4], bool& sat) {
+  typedef f16 T4 __attribute__((ext_vector_type(4)));
+  T4 x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) x[u] = to_f16_sat(v[u], sat);
+  *(T4*)p = x;
+}
 
 template <typename Ti, typename To>
 __global__ void rope_kernel(const Ti* x, To* y, bf16* y2, const int32_t* __restrict__ pos,  // x may alias y
                             int N, int H, int d, float base, int transpose, float mul, int32_t* sat_flag) {
   bool sat = false;
-  const int half = d / 2;
-  const size_t total = (size_t)N * half;
+  const int half = d / 2, groups = half / 4;
+  const size_t total = (size_t)N * groups;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
-    const int i = (int)(idx % half);
-    const int t = (int)(idx / half);
-    float s = 0.f, c = 1.f;
-    if (base > 0.f) rope_sincos(pos[t], i, d, base, &s, &c);
-    if (transpose) s = -s;
+    const int i = 4 * (int)(idx % groups);
+    const int t = (int)(idx / groups);
+    float s[4], c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s[u] = 0.f;
+      c[u] = 1.f;
+      if (base > 0.f) rope_sincos(pos[t], i + u, d, base, &s[u], &c[u]);
+      if (transpose) s[u] = -s[u];
+    }
     for (int h = 0; h < H; ++h) {
       const size_t row = ((size_t)t * H + h) * d;
-      const float x1 = (float)x[row + i], x2 = (float)x[row + i + half];
-      const float r1 = x1 * c - x2 * s, r2 = x2 * c + x1 * s;
-      y[row + i] = cvt_out<To>(mul * r1, sat);
-      y[row + i + half] = cvt_out<To>(mul * r2, sat);
+      float x1[4], x2[4], r1[4], r2[4], o1[4], o2[4];
+      ld4(x + row + i, x1);
+      ld4(x + row + i + half, x2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        r1[u] = x1[u] * c[u] - x2[u] * s[u];
+        r2[u] = x2[u] * c[u] + x1[u] * s[u];
+        o1[u] = mul * r1[u];
+        o2[u] = mul * r2[u];
+      }
+      st4(y + row + i, o1, sat);
+      st4(y + row + i + half, o2, sat);
       if (y2) {
-        y2[row + i] = (bf16)r1;
-        y2[row + i + half] = (bf16)r2;
+        st4(y2 + row + i, r1, sat);
+        st4(y2 + row + i + half, r2, sat);
       }
     }
   }
@@ -75,7 +109,7 @@ __global__ void rope_kernel(const Ti* x, To* y, bf16* y2, const int32_t* __restr
 template <typename Ti, typename To>
 hipError_t launch_rope(const Ti* x, To* y, const int32_t* pos, int N, int H, int d, float base, int transpose,
                        hipStream_t st, float mul, bf16* y2, int32_t* sat_flag) {
-  const size_t total = (size_t)N * (d / 2);
+  const size_t total = (size_t)N * (d / 8);  // a thread per (token, four pairs)
   if (total == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
   hipLaunchKernelGGL((rope_kernel<Ti, To>), dim3(blocks), dim3(256), 0, st, x, y, y2, pos, N, H, d, base, transpose,
