@@ -335,13 +335,15 @@ ta_status scratch_ptr(void** out) {
 
 int32_t pick_splits(int32_t max_len, int32_t n_splits) {
   if (n_splits > 0) return n_splits;
-  // about 2K keys (512 per wavefront) per workgroup up to 32 slices, then
-  // about 4K keys per workgroup up to AUTO_SPLITS: at B = 8 and 8 KV heads
-  // this picks 16 / 32 / 32 / 64 slices at 32K / 64K / 128K / 256K keys, the
-  // best or within noise of the best in sweeps of 16 to 120 slices
-  int32_t s = (max_len + 2047) / 2048;
+  // about 4K keys (1K per wavefront) per workgroup up to 32K keys, about 2K
+  // per workgroup up to 32 slices, then about 4K per workgroup up to
+  // AUTO_SPLITS: at B = 8 and 8 KV heads this picks 8 / 32 / 32 / 64 slices
+  // at 32K / 64K / 128K / 256K keys, the best or within noise of the best in
+  // sweeps of 8 to 120 slices
+  if (max_len <= 32768) return std::max<int32_t>(1, (max_len + 4095) / 4096);
+  int32_t s = std::max<int32_t>(8, (max_len + 2047) / 2048);
   if (s > 32) s = std::max<int32_t>(32, std::min<int32_t>(dec::AUTO_SPLITS, (max_len + 4095) / 4096));
-  return s < 1 ? 1 : s;
+  return s;
 }
 }  // namespace
 
