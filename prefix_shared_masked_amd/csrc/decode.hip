@@ -21,7 +21,7 @@ namespace dec {
 
 constexpr int D = 128;
 constexpr int MAX_SPLITS = 120;  // merge keeps S x (2 + D) floats in 64 KB of LDS
-constexpr int AUTO_SPLITS = 64;  // default cap on the slice count
+constexpr int AUTO_SPLITS = 32;  // default cap on the slice count
 
 struct Params {
   const bf16* q;
@@ -335,15 +335,14 @@ ta_status scratch_ptr(void** out) {
 
 int32_t pick_splits(int32_t max_len, int32_t n_splits) {
   if (n_splits > 0) return n_splits;
-  // about 4K keys (1K per wavefront) per workgroup up to 32K keys, about 2K
-  // per workgroup up to 32 slices, then about 4K per workgroup up to
-  // AUTO_SPLITS: at B = 8 and 8 KV heads this picks 8 / 32 / 32 / 64 slices
-  // at 32K / 64K / 128K / 256K keys, the best or within noise of the best in
-  // sweeps of 8 to 120 slices
-  if (max_len <= 32768) return std::max<int32_t>(1, (max_len + 4095) / 4096);
-  int32_t s = std::max<int32_t>(8, (max_len + 2047) / 2048);
-  if (s > 32) s = std::max<int32_t>(32, std::min<int32_t>(dec::AUTO_SPLITS, (max_len + 4095) / 4096));
-  return s;
+  // about 8K keys (2K per wavefront) per workgroup up to 32K keys, otherwise
+  // about 2K per workgroup up to AUTO_SPLITS slices.  At B = 8 and 8 KV heads
+  // this picks 4 / 32 / 32 / 32 slices at 32K / 64K / 128K / 256K keys: one
+  // round of 256 workgroups at 32K, and the best or within noise of the best
+  // of 4 to 64 slices in a sweep of every length on one box (two rounds of
+  // 512 workgroups were the worst shape at every length)
+  if (max_len <= 32768) return std::max<int32_t>(1, (max_len + 8191) / 8192);
+  return std::min<int32_t>(dec::AUTO_SPLITS, (max_len + 2047) / 2048);
 }
 }  // namespace
 
