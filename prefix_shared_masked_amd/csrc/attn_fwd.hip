@@ -76,31 +76,46 @@ __global__ void rope_kernel(const Ti* x, To* y, bf16* y2, const int32_t* __restr
     const int i = 4 * (int)(idx % groups);
     const int t = (int)(idx / groups);
     float s[4], c[4];
+    const int pt = base > 0.f ? pos[t] : 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       s[u] = 0.f;
       c[u] = 1.f;
-      if (base > 0.f) rope_sincos(pos[t], i + u, d, base, &s[u], &c[u]);
+      if (base > 0.f) rope_sincos(pt, i + u, d, base, &s[u], &c[u]);
       if (transpose) s[u] = -s[u];
     }
-    for (int h = 0; h < H; ++h) {
-      const size_t row = ((size_t)t * H + h) * d;
-      float x1[4], x2[4], r1[4], r2[4], o1[4], o2[4];
-      ld4(x + row + i, x1);
-      ld4(x + row + i + half, x2);
+    // Each thread reads and writes only its own elements, so the loads of a
+    // batch of heads may all be issued before any store, also in place: one
+    // memory round trip per batch instead of one per head.  The loads are
+    // unconditional so that none waits for another.
+    constexpr int HB = 8;
+    for (int h0 = 0; h0 < H; h0 += HB) {
+      float x1[HB][4], x2[HB][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        r1[u] = x1[u] * c[u] - x2[u] * s[u];
-        r2[u] = x2[u] * c[u] + x1[u] * s[u];
-        o1[u] = mul * r1[u];
-        o2[u] = mul * r2[u];
+      for (int b = 0; b < HB; ++b) {  // unconditional (a head past H re-reads head H - 1)
+        const size_t row = ((size_t)t * H + min(h0 + b, H - 1)) * d;
+        ld4(x + row + i, x1[b]);
+        ld4(x + row + i + half, x2[b]);
       }
-      st4(y + row + i, o1, sat);
-      st4(y + row + i + half, o2, sat);
-      if (y2) {
-        st4(y2 + row + i, r1, sat);
-        st4(y2 + row + i + half, r2, sat);
-      }
+#pragma unroll
+      for (int b = 0; b < HB; ++b)
+        if (h0 + b < H) {
+          const size_t row = ((size_t)t * H + h0 + b) * d;
+          float r1[4], r2[4], o1[4], o2[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            r1[u] = x1[b][u] * c[u] - x2[b][u] * s[u];
+            r2[u] = x2[b][u] * c[u] + x1[b][u] * s[u];
+            o1[u] = mul * r1[u];
+            o2[u] = mul * r2[u];
+          }
+          st4(y + row + i, o1, sat);
+          st4(y + row + i + half, o2, sat);
+          if (y2) {
+            st4(y2 + row + i, r1, sat);
+            st4(y2 + row + i + half, r2, sat);
+          }
+        }
     }
   }
   report_sat(sat_flag, sat);
